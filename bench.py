@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step of the Qwen3-8B-shaped DFLARE drafter on one GPU.
+
+A step is the whole hot path over one batch: append the 8 newly accepted
+context rows (fusion over T=9 target layers + context K/V for 7 layers),
+draft a 16-token block in one pass over a 4096-token context, and verify it
+greedily against synthetic target logits. Inputs are seeded and synthetic
+(weights ~N(0, 0.02) in bf16, target hidden states ~N(0, 1)); they stand in
+for the trained drafters and benchmark prompts the method is evaluated on.
+
+Prints one JSON line: draft tokens/s (B*(N-1) per step), the roofline of the
+dominant kernel (gate/up projection + SwiGLU, timed with HIP events on its
+launch stream inside the timed region), the whole step against the HBM
+roofline, and the oracle's CPU throughput on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+WORKLOAD = "qwen3_8b"
+METRIC = "draft tokens/sec per GPU (block=16, Qwen3-8B-shape drafter+verify); % roofline"
+
+
+def step_bytes(cfg, L, n_new):
+    """Algorithmic HBM bytes of one step (bf16 weights, KV, logits)."""
+    D, H, I, V, T, N = (cfg[k] for k in ("n_layers", "hidden", "intermediate", "vocab", "n_target_layers",
+                                         "block_size"))
+    qd = cfg["n_q_heads"] * cfg["head_dim"]
+    kvd = cfg["n_kv_heads"] * cfg["head_dim"]
+    ctx_w = 0 if cfg.get("tied_kv") else D * 2 * kvd * H * 2
+    if cfg.get("tied_kv"):
+        ctx_w = 0  # the context reuses the block projections (read again: counted below once)
+    append = n_new * T * H * 2 + (D * 2 * kvd * H * 2) + D * n_new * 2 * kvd * 2
+    layer_w = (qd * H + 2 * kvd * H + H * qd + 2 * I * H + H * I) * 2
+    draft = D * layer_w + V * H * 2 + N * H * 2 + D * L * 2 * kvd * 2
+    verify = N * V * 2
+    return dict(append=append, draft=draft, verify=verify, total=append + draft + verify, ctx_weights=ctx_w)
+
+
+def gate_up_bytes(cfg, M):
+    H, I = cfg["hidden"], cfg["intermediate"]
+    return 2 * I * H * 2 + M * H * 2 + M * I * 2
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "gate_up_qwen3_8b_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, w, hidden_pre, hidden_step, anchor, logits_bits):
+    """The oracle, as it stands, on a bounded sample: one decode step
+    (append 8 rows, draft, verify) after an untimed prefill."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    model = O.OracleModel(cfg, w)
+    cache = O.OracleCache(cfg["n_layers"])
+    O.ctx_append(model, cache, 0, O.bf16_bits_to_f64(hidden_pre))
+    t0 = time.perf_counter()
+    O.ctx_append(model, cache, 0, O.bf16_bits_to_f64(hidden_step))
+    out = O.draft_block(model, cache, 0, int(anchor))
+    O.verify_greedy(out["draft"], O.bf16_bits_to_f64(logits_bits))
+    dt = time.perf_counter() - t0
+    return {"value": (cfg["block_size"] - 1) / dt, "unit": "draft tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "one decode step of the same workload (append 8 rows, draft a 16-block over a "
+                      "4096-token context, greedy verify) after an untimed prefill; float64 numpy",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the drafter's hot path runs on a single MI355X here; "
+              "--gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_diffusion_drafter_softmax_amd import synth
+    from block_diffusion_drafter_softmax_amd import _binding as B
+    from block_diffusion_drafter_softmax_amd.drafter import Drafter
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    cfg = synth.config(WORKLOAD)
+    N, L, n_new, T, H = cfg["block_size"], cfg["context"], cfg["n_new"], cfg["n_target_layers"], cfg["hidden"]
+    seed = 0
+    t0 = time.perf_counter()
+    w = synth.make_weights(cfg, seed)
+    hidden_pre = synth.make_hidden(cfg, L - n_new, seed, "pre/0")
+    hidden_step = synth.make_hidden(cfg, n_new, seed, "step/0")
+    anchor = synth.make_anchor(cfg, 1, seed)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f}s")
+
+    dev = torch.device("cuda")
+    chunk = 512
+    dr = Drafter(cfg, w, max_batch=1, max_new=chunk, max_seqs=1, pages_per_seq=(L + N + 15) // 16 + 1)
+    seq = torch.zeros(1, dtype=torch.int32, device=dev)
+    for r0 in range(0, L - n_new, chunk):
+        rows = hidden_pre[r0: r0 + chunk]
+        buf = np.zeros((1, chunk, T, H), dtype=np.uint16)
+        buf[0, : len(rows)] = rows
+        hid = torch.from_numpy(buf.view(np.int16)).to(dev).view(torch.bfloat16)
+        dr.ctx_append(seq, torch.tensor([len(rows)], dtype=torch.int32, device=dev), hid, chunk)
+    torch.cuda.synchronize()
+    assert int(dr.ctx_len[0]) == L - n_new
+    log("prefill done")
+
+    ctx0 = dr.ctx_len.clone()
+    step_hidden = torch.from_numpy(hidden_step.reshape(1, n_new, T, H).view(np.int16)).to(dev).view(torch.bfloat16)
+    n_new_t = torch.tensor([n_new], dtype=torch.int32, device=dev)
+    anchor_t = torch.from_numpy(anchor).to(dev)
+    draft = torch.zeros((1, N - 1), dtype=torch.int32, device=dev)
+    acc = torch.zeros(1, dtype=torch.int32, device=dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    com = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    # target logits built around the GPU's own draft (timing input only)
+    dr.ctx_append(seq, n_new_t, step_hidden, n_new)
+    dr.draft_block(seq, anchor_t, draft)
+    torch.cuda.synchronize()
+    logits_bits = synth.make_logits(cfg, draft.cpu().numpy(), seed)[0]
+    logits = torch.from_numpy(logits_bits.view(np.int16)).to(dev).view(torch.bfloat16).unsqueeze(0)
+    dr.ctx_len.copy_(ctx0)
+
+    def step():
+        dr.ctx_len.copy_(ctx0)  # the same workload every step: context back to L - 8 before the append
+        dr.ctx_append(seq, n_new_t, step_hidden, n_new)
+        dr.draft_block(seq, anchor_t, draft)
+        dr.verify(seq, draft, logits, acc, nxt, com)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert dr.read_error() == 0
+
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+
+    B.check(B.dflash_kernel_timer(dr.handle, B.K_GATE_UP, 1), "timer")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    rc, gu_ms, gu_n = B.dflash_kernel_timer_read(dr.handle, B.K_GATE_UP)
+    B.check(rc, "timer read")
+    B.dflash_kernel_timer(dr.handle, B.K_GATE_UP, 0)
+    assert dr.read_error() == 0
+
+    ms_step = elapsed * 1e3 / args.steps
+    tok_s = (N - 1) / (ms_step / 1e3)
+    sb = step_bytes(cfg, L, n_new)
+    M = N
+    roof = None
+    if gu_n:
+        gu_avg_s = gu_ms / gu_n / 1e3
+        gbytes = gate_up_bytes(cfg, M)
+        achieved = gbytes / gu_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile(os.path.join(ROOT, "block_diffusion_drafter_softmax_amd", "csrc",
+                                                             "gemm.hip")),
+                "kernel": "gate_up (gate/up projection + SwiGLU)", "bytes_per_launch": gbytes,
+                "avg_launch_us": round(gu_avg_s * 1e6, 2), "launches_timed": gu_n}
+    t_roof_us = sb["total"] / (HBM_PEAK_GBS * 1e9) * 1e6
+    res = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "draft tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-8B-shaped DFLARE drafter decode step: append 8 context rows "
+                               "(T=9 fusion), draft block 16 over ctx 4096 (7 layers, H 4096, 32/8 heads, "
+                               "I 12288, V 151936), greedy verify; batch 1",
+                   "global_batch": 1, "seq_len": L, "block": N, "launch": "graph" if graph else "eager"},
+        "roofline": roof,
+        "step_roofline": {"bound": "hbm", "bytes": sb["total"], "t_roof_us": round(t_roof_us, 1),
+                          "achieved_GBs": round(sb["total"] / (ms_step / 1e3) / 1e9, 1),
+                          "frac": round(t_roof_us / (ms_step * 1e3), 4)},
+    }
+    log(f"{ms_step:.3f} ms/step, {tok_s:.0f} draft tok/s, step roofline {res['step_roofline']['frac']:.3f}")
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (one step)")
+        del graph
+        res["cpu_baseline"] = cpu_baseline(cfg, w, hidden_pre, hidden_step, anchor[0], logits_bits)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

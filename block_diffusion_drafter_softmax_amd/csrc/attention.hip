@@ -1,0 +1,182 @@
+// Block attention: the N block queries of every head attend, with no mask,
+// to all L context keys of their sequence plus the N block keys (the draft
+// is not autoregressive; the fused target context enters each draft layer
+// as keys/values only).
+//
+// Work item = (key chunk, kv head, sequence). Chunk 0 is the block's own N
+// keys; chunks 1.. cover the context in pieces of `chunk` keys read straight
+// from the paged cache. A workgroup holds all R = (n_q/n_kv)*N query rows of
+// one kv head (GQA: the K/V tile is read once for the whole query group),
+// one wave per 16 rows. Per 32-key step a wave computes S^T = K Q^T with
+// MFMA (keys as rows, the lane's query as column), runs an online softmax in
+// the log2 domain, and accumulates O^T += V^T P^T with MFMA: V is stored
+// dim-major per page ([d_h][16 slots]) so its A-operand fragments are
+// contiguous, and P^T is taken from the S^T accumulators without moving
+// data between lanes (both MFMAs use the same permutation of the 32 keys).
+// The chunk's unnormalised O, running max and sum go to a partial buffer;
+// attn_merge_kernel combines the chunks (log-sum-exp merge, chunk order).
+#include "common.h"
+
+
+namespace {
+DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+}
+
+template <int D>
+__global__ __launch_bounds__(1024) void attn_chunk_kernel(AttnArgs a) {
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int seq = clampi(a.seq_ids[b], 0, a.max_seqs - 1);
+  const int L = clampi(a.ctx_len[seq], 0, a.max_pages_per_seq * 16);
+  int key_begin, key_end;
+  if (c == 0) {
+    key_begin = 0;
+    key_end = a.N;
+  } else {
+    key_begin = (c - 1) * a.chunk;
+    key_end = min(L, c * a.chunk);
+    if (key_begin >= key_end) return;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int G = a.n_q / a.n_kv, R = G * a.N;
+  const int r = wave * 16 + r16;
+  const int hq = kvh * G + r / a.N, n = r % a.N;
+  constexpr int KD = D / 32, DT = D / 16;
+
+  bf16x8 qf[KD];
+  const uint16_t* qp = a.q + ((size_t)(b * a.N + n) * a.n_q + hq) * D + 8 * g;
+#pragma unroll
+  for (int kd = 0; kd < KD; ++kd) qf[kd] = ld8(qp + kd * 32);
+
+  f32x4 acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const size_t head_off = (size_t)kvh * 16 * D;
+  const size_t page_elems = (size_t)2 * a.n_kv * 16 * D;
+  for (int k0 = key_begin; k0 < key_end; k0 += 32) {
+    const bool t1 = k0 + 16 < key_end;
+    const uint16_t *kp0, *kp1 = nullptr, *vp0, *vp1 = nullptr;
+    if (c == 0) {
+      kp0 = a.kblk + ((size_t)b * a.n_kv + kvh) * 16 * D;
+      vp0 = a.vblk + ((size_t)b * a.n_kv + kvh) * D * 16;
+    } else {
+      const int* pt = a.page_table + (size_t)seq * a.max_pages_per_seq + k0 / 16;
+      const int pg0 = clampi(pt[0], 0, a.n_pages - 1);
+      kp0 = a.pages + pg0 * page_elems + head_off;
+      vp0 = kp0 + (size_t)a.n_kv * 16 * D;
+      if (t1) {
+        const int pg1 = clampi(pt[1], 0, a.n_pages - 1);
+        kp1 = a.pages + pg1 * page_elems + head_off;
+        vp1 = kp1 + (size_t)a.n_kv * 16 * D;
+      }
+    }
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) s0 = mfma16(ld8(kp0 + r16 * D + kd * 32 + 8 * g), qf[kd], s0);
+    if (t1) {
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) s1 = mfma16(ld8(kp1 + r16 * D + kd * 32 + 8 * g), qf[kd], s1);
+    }
+    // lane holds keys k0 + 4g + i (s0) and k0 + 16 + 4g + i (s1) for query r
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = (k0 + 4 * g + i < key_end) ? s0[i] * a.scale_log2 : -INFINITY;
+      x[4 + i] = (t1 && k0 + 16 + 4 * g + i < key_end) ? s1[i] * a.scale_log2 : -INFINITY;
+    }
+    float mt = x[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float corr = exp2f(m_run - m_new);
+    u16x4 pb0, pb1;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pb0[i] = f2bf(exp2f(x[i] - m_new));
+      pb1[i] = f2bf(exp2f(x[4 + i] - m_new));
+      psum += bf2f(pb0[i]) + bf2f(pb1[i]);
+    }
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(pb0, pb1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      u16x4 v0 = *reinterpret_cast<const u16x4*>(vp0 + (size_t)(t * 16 + r16) * 16 + 4 * g);
+      u16x4 v1 = {0, 0, 0, 0};
+      if (t1) v1 = *reinterpret_cast<const u16x4*>(vp1 + (size_t)(t * 16 + r16) * 16 + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (k0 + 4 * g + i >= key_end) v0[i] = 0;
+        if (k0 + 16 + 4 * g + i >= key_end) v1[i] = 0;
+      }
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[t] = acc[t] * corr;
+      acc[t] = mfma16(vf, pf, acc[t]);
+    }
+  }
+  float l = l_run + __shfl_xor(l_run, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+
+  const size_t unit = ((size_t)b * a.n_kv + kvh) * a.n_ck + c;
+  float* po = a.part_o + (unit * R + r) * D;
+#pragma unroll
+  for (int t = 0; t < DT; ++t) *reinterpret_cast<f32x4*>(po + t * 16 + 4 * g) = acc[t];
+  if (g == 0) {
+    a.part_ml[(unit * R + r) * 2 + 0] = m_run;
+    a.part_ml[(unit * R + r) * 2 + 1] = l;
+  }
+}
+
+// One thread per (sequence, kv head, query row, 4 dims): log-sum-exp merge of
+// the chunk partials in chunk order, normalise, round to bf16.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int B) {
+  const int G = a.n_q / a.n_kv, R = G * a.N;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int dq = idx % (D / 4);
+  const int r = (idx / (D / 4)) % R;
+  const int kvh = (idx / (D / 4) / R) % a.n_kv;
+  const int b = idx / (D / 4) / R / a.n_kv;
+  if (b >= B) return;
+  const int seq = clampi(a.seq_ids[b], 0, a.max_seqs - 1);
+  const int L = clampi(a.ctx_len[seq], 0, a.max_pages_per_seq * 16);
+  const int nc = min(a.n_ck, 1 + (L + a.chunk - 1) / a.chunk);
+  const size_t unit0 = ((size_t)b * a.n_kv + kvh) * a.n_ck;
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_ml[((unit0 + c) * R + r) * 2]);
+  float den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < nc; ++c) {
+    const float w = exp2f(a.part_ml[((unit0 + c) * R + r) * 2] - M);
+    den += w * a.part_ml[((unit0 + c) * R + r) * 2 + 1];
+    num += w * *reinterpret_cast<const f32x4*>(a.part_o + ((unit0 + c) * R + r) * D + dq * 4);
+  }
+  const float inv = 1.0f / den;
+  const int hq = kvh * G + r / a.N, n = r % a.N;
+  u16x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f2bf(num[i] * inv);
+  *reinterpret_cast<u16x4*>(a.o + ((size_t)(b * a.N + n) * a.n_q + hq) * D + dq * 4) = o;
+}
+
+extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
+  const int G = a->n_q / a->n_kv, R = G * a->N;
+  const dim3 grid(a->n_ck, a->n_kv, B), block(64 * (R / 16));
+  if (head_dim == 128) hipLaunchKernelGGL(attn_chunk_kernel<128>, grid, block, 0, st, *a);
+  else hipLaunchKernelGGL(attn_chunk_kernel<64>, grid, block, 0, st, *a);
+  return hipGetLastError();
+}
+
+extern "C" hipError_t dflash_launch_attn_merge(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
+  const int G = a->n_q / a->n_kv, R = G * a->N;
+  const int total = B * a->n_kv * R * (head_dim / 4);
+  const dim3 grid((total + 255) / 256), block(256);
+  if (head_dim == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, grid, block, 0, st, *a, B);
+  else hipLaunchKernelGGL(attn_merge_kernel<64>, grid, block, 0, st, *a, B);
+  return hipGetLastError();
+}

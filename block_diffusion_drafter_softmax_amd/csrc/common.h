@@ -1,0 +1,93 @@
+// Shared device helpers for the gfx950 kernels: bf16 storage, MFMA operand
+// types, wave-level reductions and the kernel argument structs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define DEV __device__ __forceinline__
+
+// bf16 bits -> fp32 (exact).
+DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+DEV uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// 16 bytes = 8 bf16 from global memory.
+DEV bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+DEV bf16x8 zero8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// D(16x16, fp32) += A(16x32) * B(32x16), bf16 operands.
+// Lane l: A row l%16, B column l%16, each holding k = 8*(l/16) .. +7;
+// D rows 4*(l/16) + i (i < 4), column l%16.
+DEV f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sum over a whole workgroup (blockDim.x a multiple of 64, <= 1024).
+// Every thread gets the total; the order of summation is fixed.
+DEV float block_sum(float v, float* lds /* >= 16 floats */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < nw; ++w) t += lds[w];
+  return t;
+}
+
+DEV void set_error(int32_t* err, int bits) { atomicOr(err, bits); }
+
+
+DEV Top2 top2_empty() { return {-INFINITY, 0x7FFFFFFF, -INFINITY}; }
+
+DEV bool better(float va, int ia, float vb, int ib) { return va > vb || (va == vb && ia < ib); }
+
+DEV Top2 top2_merge(Top2 a, Top2 b) {
+  Top2 r;
+  if (better(a.v1, a.i1, b.v1, b.i1)) {
+    r.v1 = a.v1; r.i1 = a.i1; r.v2 = fmaxf(a.v2, b.v1);
+  } else {
+    r.v1 = b.v1; r.i1 = b.i1; r.v2 = fmaxf(b.v2, a.v1);
+  }
+  return r;
+}
+
+DEV Top2 top2_push(Top2 a, float v, int i) { return top2_merge(a, Top2{v, i, -INFINITY}); }
+
+DEV Top2 top2_shfl_xor(Top2 a, int o) {
+  Top2 b;
+  b.v1 = __shfl_xor(a.v1, o, 64);
+  b.i1 = __shfl_xor(a.i1, o, 64);
+  b.v2 = __shfl_xor(a.v2, o, 64);
+  return top2_merge(a, b);
+}
+

@@ -1,0 +1,185 @@
+// Small per-row kernels: call planning (positions, bounds checks), DFLARE
+// layer fusion + RMSNorm, and the residual/embedding + RMSNorm producer of
+// every GEMM input.
+#include "common.h"
+#include "dflash.h"
+
+namespace {
+DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+}
+
+
+// One thread per batch entry. Append: rows t < n_new[b] get positions
+// ctx_len .. ctx_len+n_new-1 and ctx_len advances; a failed check leaves the
+// sequence untouched and all its rows skipped. Draft: rows get positions
+// L .. L+N-1; checks only flag (positions are clamped into the tables).
+__global__ void plan_kernel(PlanArgs a) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= a.B) return;
+  int bad = 0;
+  const int s_raw = a.seq_ids[b];
+  if (s_raw < 0 || s_raw >= a.max_seqs) bad |= DFLASH_DEV_BAD_SEQ;
+  const int seq = clampi(s_raw, 0, a.max_seqs - 1);
+  const int L_raw = a.ctx_len[seq];
+  const int cap = min(a.max_pages_per_seq * 16, a.max_pos);
+  if (L_raw < 0 || L_raw > cap) bad |= DFLASH_DEV_NO_PAGES;
+  const int L = clampi(L_raw, 0, cap);
+  int n = a.rows_per_seq;
+  if (a.append) {
+    n = a.n_new[b];
+    if (n < 0 || n > a.max_new) bad |= DFLASH_DEV_BAD_N_NEW;
+    if (!bad && L + n > cap) bad |= DFLASH_DEV_NO_PAGES;
+    if (!bad) {
+      for (int p = L / 16; p < (L + n + 15) / 16; ++p) {
+        const int pg = a.page_table[(size_t)seq * a.max_pages_per_seq + p];
+        if (pg < 0 || pg >= a.n_pages) bad |= DFLASH_DEV_BAD_PAGE;
+      }
+    }
+  } else {
+    if (L + n > a.max_pos) bad |= DFLASH_DEV_NO_PAGES;
+    const int anc = a.anchor[b];
+    if (anc < 0 || anc >= a.vocab) bad |= DFLASH_DEV_BAD_TOKEN;
+    const int np = min((L + 15) / 16, a.max_pages_per_seq);
+    for (int p = 0; p < np; ++p) {
+      const int pg = a.page_table[(size_t)seq * a.max_pages_per_seq + p];
+      if (pg < 0 || pg >= a.n_pages) bad |= DFLASH_DEV_BAD_PAGE;
+    }
+  }
+  if (bad) set_error(a.err, bad);
+  for (int t = 0; t < a.rows_per_seq; ++t) {
+    int pos;
+    if (a.append) pos = (!bad && t < n) ? L + t : -1;
+    else pos = clampi(L + t, 0, a.max_pos - 1);
+    a.row_pos[b * a.rows_per_seq + t] = pos;
+    a.row_seq[b * a.rows_per_seq + t] = seq;
+  }
+  if (a.append && !bad) a.ctx_len[seq] = L + n;
+}
+
+extern "C" hipError_t dflash_launch_plan(const PlanArgs* a, hipStream_t st) {
+  hipLaunchKernelGGL(plan_kernel, dim3((a->B + 63) / 64), dim3(64), 0, st, *a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ fusion
+
+#define FUSE_MAXV 8  // float4 groups per thread: H <= 256*4*8 = 8192
+
+// One workgroup per appended row: for each draft layer i,
+// s = sum_j alpha[i][j] * h_j (ascending j), f = s / sqrt(mean(s^2) + eps) * g.
+__global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
+  const int m = blockIdx.x;
+  if (a.row_pos[m] < 0) return;
+  __shared__ float red[16];
+  const uint16_t* h = a.hidden + (size_t)m * a.T * a.H;
+  const int nv = (a.H / 4 + 255) / 256;
+  for (int i = 0; i < a.D; ++i) {
+    float s[FUSE_MAXV][4];
+    float ss = 0.f;
+#pragma unroll
+    for (int v = 0; v < FUSE_MAXV; ++v) {
+      const int k = (v * 256 + threadIdx.x) * 4;
+      if (v >= nv || k >= a.H) continue;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < a.T; ++j) {
+        const float al = a.alpha[i * a.T + j];
+        const u16x4 x = *reinterpret_cast<const u16x4*>(h + (size_t)j * a.H + k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += al * bf2f(x[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[v][e] = acc[e];
+        ss += acc[e] * acc[e];
+      }
+    }
+    const float tot = block_sum(ss, red);
+    const float rstd = 1.0f / sqrtf(tot / a.H + a.eps);
+    uint16_t* out = a.f + ((size_t)i * a.rows + m) * a.H;
+    const uint16_t* g = a.g_fuse + (size_t)i * a.H;
+#pragma unroll
+    for (int v = 0; v < FUSE_MAXV; ++v) {
+      const int k = (v * 256 + threadIdx.x) * 4;
+      if (v >= nv || k >= a.H) continue;
+      const u16x4 gv = *reinterpret_cast<const u16x4*>(g + k);
+      u16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = f2bf(s[v][e] * rstd * bf2f(gv[e]));
+      *reinterpret_cast<u16x4*>(out + k) = o;
+    }
+  }
+}
+
+extern "C" hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st) {
+  hipLaunchKernelGGL(fuse_kernel, dim3(a->rows), dim3(256), 0, st, *a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- norm
+
+#define NORM_MAXV 8
+
+// One workgroup per row: build the residual row (embedding gather, or
+// x + the k-split partials of the last projection, summed in split order),
+// then h = x / sqrt(mean(x^2) + eps) * g in bf16.
+__global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
+  const int m = blockIdx.x;
+  __shared__ float red[16];
+  const int nv = (a.H / 4 + 255) / 256;
+  float xv[NORM_MAXV][4];
+  float ss = 0.f;
+  int tok = 0;
+  if (a.mode == 0) {
+    tok = (m % a.N == 0) ? a.anchor[m / a.N] : a.mask_id;
+    tok = clampi(tok, 0, a.V - 1);
+  }
+#pragma unroll
+  for (int v = 0; v < NORM_MAXV; ++v) {
+    const int k = (v * 256 + threadIdx.x) * 4;
+    if (v >= nv || k >= a.H) continue;
+    f32x4 x;
+    if (a.mode == 0) {
+      const u16x4 e = *reinterpret_cast<const u16x4*>(a.embed + (size_t)tok * a.H + k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = bf2f(e[i]);
+    } else {
+      x = *reinterpret_cast<const f32x4*>(a.x + (size_t)m * a.H + k);
+      for (int s = 0; s < a.ks; ++s) x += *reinterpret_cast<const f32x4*>(a.part + ((size_t)s * a.M + m) * a.H + k);
+    }
+    *reinterpret_cast<f32x4*>(a.x + (size_t)m * a.H + k) = x;
+    if (a.dbg) *reinterpret_cast<f32x4*>(a.dbg + (size_t)m * a.H + k) = x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xv[v][i] = x[i];
+      ss += x[i] * x[i];
+    }
+  }
+  const float tot = block_sum(ss, red);
+  const float rstd = 1.0f / sqrtf(tot / a.H + a.eps);
+#pragma unroll
+  for (int v = 0; v < NORM_MAXV; ++v) {
+    const int k = (v * 256 + threadIdx.x) * 4;
+    if (v >= nv || k >= a.H) continue;
+    const u16x4 gv = *reinterpret_cast<const u16x4*>(a.g + k);
+    u16x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = f2bf(xv[v][i] * rstd * bf2f(gv[i]));
+    *reinterpret_cast<u16x4*>(a.h + (size_t)m * a.H + k) = o;
+  }
+}
+
+extern "C" hipError_t dflash_launch_norm(const NormArgs* a, hipStream_t st) {
+  hipLaunchKernelGGL(norm_kernel, dim3(a->M), dim3(256), 0, st, *a);
+  return hipGetLastError();
+}
+
+// Fill a device buffer with 32-bit words (used at set-up; no memset nodes).
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+extern "C" hipError_t dflash_launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(256), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}

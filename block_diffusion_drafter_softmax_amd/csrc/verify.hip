@@ -1,0 +1,202 @@
+// Parallel verification of the drafted blocks against the target's logits
+// (greedy, or temperature-1 rejection sampling).
+//
+// verify_rows_kernel streams every logit once: work item = (vocabulary chunk,
+// block row, sequence). Greedy keeps (max, lowest index); temperature 1 keeps
+// (max, sum of exp(z - max)). The last workgroup of a sequence to finish
+// (device-scope counter, reset by that workgroup) merges the chunks in chunk
+// order and runs the accept scan. Temperature 1 then needs one more pass over
+// the single row it samples from (verify_sample_kernel): Gumbel-max with a
+// counter-based Philox4x64-10 draw per vocabulary entry, which gives the same
+// sample whatever the summation order.
+#include "common.h"
+#include "dflash.h"
+
+
+namespace {
+DEV float load_logit(const VerifyArgs& a, size_t i) {
+  if (a.dtype == DFLASH_DTYPE_F32) return ((const float*)a.logits)[i];
+  return bf2f(((const uint16_t*)a.logits)[i]);
+}
+
+// Philox4x64-10 (Salmon et al., SC 2011), published multipliers and Weyl
+// constants.
+DEV void philox4x64_10(unsigned long long c[4], unsigned long long k0, unsigned long long k1) {
+  const unsigned long long M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const unsigned long long W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const unsigned long long lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
+    const unsigned long long lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
+    const unsigned long long n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+    k0 += W0; k1 += W1;
+  }
+}
+
+// Word 0 of Philox at counter (k, row | stream << 32, seq, step), key (seed, 0).
+DEV unsigned long long rng_word(const VerifyArgs& a, int seq, int row, int k, int stream) {
+  unsigned long long c[4] = {(unsigned long long)(unsigned)k,
+                             (unsigned long long)(unsigned)row | ((unsigned long long)stream << 32),
+                             (unsigned long long)(unsigned)seq, a.step};
+  philox4x64_10(c, a.seed, 0ull);
+  return c[0];
+}
+
+DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+struct ArgMax {
+  float v;
+  int i;
+};
+DEV ArgMax am_merge(ArgMax x, ArgMax y) { return better(x.v, x.i, y.v, y.i) ? x : y; }
+DEV ArgMax am_shfl(ArgMax x, int o) {
+  ArgMax y{__shfl_xor(x.v, o, 64), __shfl_xor(x.i, o, 64)};
+  return am_merge(x, y);
+}
+
+// max and sum of exp(z - max) pairs
+DEV float2 ms_merge(float2 x, float2 y) {
+  const float m = fmaxf(x.x, y.x);
+  if (m == -INFINITY) return make_float2(m, 0.f);
+  return make_float2(m, x.y * __expf(x.x - m) + y.y * __expf(y.x - m));
+}
+}  // namespace
+
+__global__ __launch_bounds__(256) void verify_rows_kernel(VerifyArgs a) {
+  const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const size_t row_off = ((size_t)b * a.N + r) * a.V;
+  const int k0 = c * a.chunk, k1 = min(a.V, k0 + a.chunk);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float2 red[4];
+  __shared__ int last;
+  float2 res;
+  if (!a.temp1) {
+    ArgMax t{-INFINITY, 0x7FFFFFFF};
+    for (int k = k0 + threadIdx.x; k < k1; k += 256) t = am_merge(t, ArgMax{load_logit(a, row_off + k), k});
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) t = am_shfl(t, o);
+    if (lane == 0) red[wave] = make_float2(t.v, __int_as_float(t.i));
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      ArgMax u{red[0].x, __float_as_int(red[0].y)};
+      for (int w = 1; w < 4; ++w) u = am_merge(u, ArgMax{red[w].x, __float_as_int(red[w].y)});
+      res = make_float2(u.v, __int_as_float(u.i));
+    }
+  } else {
+    float m = -INFINITY;
+    for (int k = k0 + threadIdx.x; k < k1; k += 256) m = fmaxf(m, load_logit(a, row_off + k));
+    m = wave_max(m);
+    if (lane == 0) red[wave].x = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0].x, red[1].x), fmaxf(red[2].x, red[3].x));
+    float s = 0.f;
+    for (int k = k0 + threadIdx.x; k < k1; k += 256) s += __expf(load_logit(a, row_off + k) - m);
+    s = wave_sum(s);
+    __syncthreads();
+    if (lane == 0) red[wave].y = s;
+    __syncthreads();
+    if (threadIdx.x == 0) res = make_float2(m, red[0].y + red[1].y + red[2].y + red[3].y);
+  }
+  if (threadIdx.x == 0) {
+    *reinterpret_cast<float2*>(a.part + ((((size_t)b * a.N + r) * a.n_chunks + c) * 2)) = res;
+    __threadfence();
+    const int done = atomicAdd(&a.counters[b], 1);
+    last = (done == a.N * a.n_chunks - 1);
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  if (threadIdx.x != 0) return;
+  a.counters[b] = 0;
+
+  const int seq = a.seq_ids[b];
+  const int* d = a.draft + (size_t)b * (a.N - 1);
+  int acc = 0;
+  if (!a.temp1) {
+    int t_a = 0;
+    for (int row = 0; row < a.N; ++row) {
+      ArgMax u{-INFINITY, 0x7FFFFFFF};
+      for (int cc = 0; cc < a.n_chunks; ++cc) {
+        const float2 p = *reinterpret_cast<const float2*>(a.part + ((((size_t)b * a.N + row) * a.n_chunks + cc) * 2));
+        u = am_merge(u, ArgMax{p.x, __float_as_int(p.y)});
+      }
+      t_a = u.i;
+      if (row == a.N - 1 || d[row] != u.i) break;
+      ++acc;
+    }
+    a.accept_len[b] = acc;
+    a.next_token[b] = t_a;
+    if (a.commit_len) a.commit_len[b] = acc + 1;
+  } else {
+    while (acc < a.N - 1) {
+      float2 ms = make_float2(-INFINITY, 0.f);
+      for (int cc = 0; cc < a.n_chunks; ++cc)
+        ms = ms_merge(ms, *reinterpret_cast<const float2*>(a.part + ((((size_t)b * a.N + acc) * a.n_chunks + cc) * 2)));
+      const float lse = ms.x + __logf(ms.y);
+      int tok = d[acc];
+      if (tok < 0 || tok >= a.V) {
+        set_error(a.err, DFLASH_DEV_BAD_TOKEN);
+        tok = clampi(tok, 0, a.V - 1);
+      }
+      const float p = expf(load_logit(a, ((size_t)b * a.N + acc) * a.V + tok) - lse);
+      const float u = (float)(rng_word(a, seq, acc, 0, 0) >> 40) * 5.9604644775390625e-08f;
+      if (u < p) ++acc;
+      else break;
+    }
+    a.accept_len[b] = acc;
+    if (a.commit_len) a.commit_len[b] = acc + 1;
+    a.state[2 * b + 0] = acc;
+    a.state[2 * b + 1] = acc < a.N - 1 ? d[acc] : -1;
+  }
+}
+
+// Gumbel-max sample of row state[b][0] with token state[b][1] excluded.
+__global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int row = a.state[2 * b + 0], excl = a.state[2 * b + 1];
+  const int seq = a.seq_ids[b];
+  const size_t row_off = ((size_t)b * a.N + row) * a.V;
+  const int k0 = c * a.chunk, k1 = min(a.V, k0 + a.chunk);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  ArgMax t{-INFINITY, 0x7FFFFFFF};
+  for (int k = k0 + threadIdx.x; k < k1; k += 256) {
+    if (k == excl) continue;
+    const unsigned long long w = rng_word(a, seq, row, k, 1);
+    const float u = ((float)(w >> 41) + 0.5f) * 1.1920928955078125e-07f;
+    const float gmb = -logf(-logf(u));
+    t = am_merge(t, ArgMax{load_logit(a, row_off + k) + gmb, k});
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) t = am_shfl(t, o);
+  __shared__ ArgMax red[4];
+  __shared__ int last;
+  if (lane == 0) red[wave] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ArgMax u = red[0];
+    for (int w = 1; w < 4; ++w) u = am_merge(u, red[w]);
+    *reinterpret_cast<float2*>(a.part + (((size_t)b * a.n_chunks + c) * 2)) = make_float2(u.v, __int_as_float(u.i));
+    __threadfence();
+    const int done = atomicAdd(&a.counters[a.B + b], 1);
+    last = (done == a.n_chunks - 1);
+  }
+  __syncthreads();
+  if (!last || threadIdx.x != 0) return;
+  __threadfence();
+  a.counters[a.B + b] = 0;
+  ArgMax u{-INFINITY, 0x7FFFFFFF};
+  for (int cc = 0; cc < a.n_chunks; ++cc) {
+    const float2 p = *reinterpret_cast<const float2*>(a.part + (((size_t)b * a.n_chunks + cc) * 2));
+    u = am_merge(u, ArgMax{p.x, __float_as_int(p.y)});
+  }
+  a.next_token[b] = u.i;
+}
+
+extern "C" hipError_t dflash_launch_verify(const VerifyArgs* a, hipStream_t st) {
+  hipLaunchKernelGGL(verify_rows_kernel, dim3(a->n_chunks, a->N, a->B), dim3(256), 0, st, *a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a->temp1) return e;
+  hipLaunchKernelGGL(verify_sample_kernel, dim3(a->n_chunks, a->B), dim3(256), 0, st, *a);
+  return hipGetLastError();
+}

@@ -1,0 +1,149 @@
+"""Device-memory owner around the C ABI.
+
+PyTorch supplies the device memory (weights, paged KV cache, page table,
+ctx_len, error word, workspace) and the stream; every step of the path runs
+in libdflash.so's kernels. This module only allocates, marshals pointers
+and checks return codes.
+"""
+import numpy as np
+import torch
+
+from . import _binding as B
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _bits_to_bf16(a, device):
+    """uint16 bf16 bit patterns (numpy) -> torch.bfloat16 device tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+class Drafter:
+    """One drafter (weights + paged context cache + workspace) on one GPU.
+
+    cfg: a shape dict (see synth.CONFIGS). weights: dict of bf16 bits
+    (numpy uint16) and float32 w_fuse, or already-placed torch tensors.
+    Pages: `pages_per_seq` per sequence slot; page_order "contiguous" or
+    "shuffled" (a seeded permutation of the pool).
+    """
+
+    def __init__(self, cfg, weights, max_batch, max_new, max_seqs, pages_per_seq, max_pos=None,
+                 device="cuda", page_order="contiguous", seed=0, fill_workspace=None):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        dev = self.device
+        D, H = cfg["n_layers"], cfg["hidden"]
+        n_kv, d = cfg["n_kv_heads"], cfg["head_dim"]
+        self.max_batch, self.max_new, self.max_seqs = max_batch, max_new, max_seqs
+        self.pages_per_seq = pages_per_seq
+        n_pages = max_seqs * pages_per_seq
+        self.n_pages = n_pages
+        self.max_pos = max_pos or pages_per_seq * 16 + cfg["block_size"]
+
+        self.w = {}
+        for k, v in weights.items():
+            if isinstance(v, torch.Tensor):
+                self.w[k] = v.to(dev)
+            elif k == "w_fuse":
+                self.w[k] = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(dev)
+            else:
+                self.w[k] = _bits_to_bf16(v, dev)
+
+        self.kv_pages = torch.zeros((D, n_pages, 2, n_kv, 16 * d), dtype=torch.bfloat16, device=dev)
+        order = np.arange(n_pages, dtype=np.int32)
+        if page_order == "shuffled":
+            order = np.random.default_rng(seed).permutation(n_pages).astype(np.int32)
+        self.page_table_host = order.reshape(max_seqs, pages_per_seq)
+        self.page_table = torch.from_numpy(self.page_table_host.copy()).to(dev)
+        self.ctx_len = torch.zeros(max_seqs, dtype=torch.int32, device=dev)
+        self.error_word = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        c = B.Config()
+        for f, _ in B.Config._fields_:
+            if f in cfg:
+                setattr(c, f, cfg[f])
+        c.page_size = 16
+        c.max_seqs = max_seqs
+        c.max_pages_per_seq = pages_per_seq
+        c.n_pages = n_pages
+        c.max_pos = self.max_pos
+        c.max_batch = max_batch
+        c.max_new = max_new
+        c.mask_token_id = cfg["mask_token_id"]
+        c.tied_kv = int(cfg.get("tied_kv", 0))
+        c.use_rope = int(cfg.get("use_rope", 1))
+        self.c = c
+        ws = B.dflash_workspace_bytes(c)
+        if ws == 0:
+            raise B.DFlashError("unsupported config: " + B.last_error())
+        self.ws_bytes = ws
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        if fill_workspace is not None:  # e.g. NaN bits, to catch reads of unwritten memory
+            self.workspace.view(torch.int32)[: ws // 4].fill_(fill_workspace)
+
+        wt = B.Weights()
+        for f, _ in B.Weights._fields_:
+            t = self.w.get(f)
+            setattr(wt, f, t.data_ptr() if t is not None else None)
+        kv = B.KV(kv_pages=self.kv_pages.data_ptr(), page_table=self.page_table.data_ptr(),
+                  ctx_len=self.ctx_len.data_ptr(), error_word=self.error_word.data_ptr())
+        torch.cuda.synchronize(dev)
+        rc, h = B.dflash_create(c, wt, kv, self.workspace.data_ptr(), ws)
+        B.check(rc, "dflash_create")
+        self.handle = h
+
+    # ---------------------------------------------------------------- calls
+    def ctx_append(self, seq_ids, n_new, hidden, max_new=None, stream=None):
+        """hidden: bf16 tensor [B, max_new, T, H]; seq_ids, n_new: int32 [B]."""
+        Bn = seq_ids.numel()
+        max_new = max_new or hidden.shape[1]
+        rc = B.dflash_ctx_append(self.handle, Bn, seq_ids.data_ptr(), n_new.data_ptr(), hidden.data_ptr(),
+                                 max_new, _stream(stream))
+        return B.check(rc, "dflash_ctx_append")
+
+    def draft_block(self, seq_ids, anchor, draft, gap=None, dbg_hidden=None, dbg_logits=None, stream=None):
+        Bn = seq_ids.numel()
+        p = lambda t: t.data_ptr() if t is not None else None
+        rc = B.dflash_draft_block(self.handle, Bn, seq_ids.data_ptr(), anchor.data_ptr(), draft.data_ptr(),
+                                  p(gap), p(dbg_hidden), p(dbg_logits), _stream(stream))
+        return B.check(rc, "dflash_draft_block")
+
+    def verify(self, seq_ids, draft, logits, accept_len, next_token, commit_len=None, temperature=0.0,
+               seed=0, step=0, stream=None):
+        Bn = seq_ids.numel()
+        dt = B.DTYPE_F32 if logits.dtype == torch.float32 else B.DTYPE_BF16
+        rc = B.dflash_verify(self.handle, Bn, seq_ids.data_ptr(), draft.data_ptr(), logits.data_ptr(), dt,
+                             temperature, seed, step, accept_len.data_ptr(), next_token.data_ptr(),
+                             commit_len.data_ptr() if commit_len is not None else None, _stream(stream))
+        return B.check(rc, "dflash_verify")
+
+    def read_error(self, stream=None):
+        rc, v = B.dflash_read_error(self.handle, _stream(stream))
+        B.check(rc, "dflash_read_error")
+        return v
+
+    def close(self):
+        if getattr(self, "handle", None):
+            B.dflash_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ----------------------------------------------------- host-side views
+    def cache_rows(self, layer, seq, length):
+        """Context K [L, n_kv, d] (rotated) and V [L, n_kv, d] of one
+        sequence, gathered through the page table (host float32)."""
+        n_kv, d = self.cfg["n_kv_heads"], self.cfg["head_dim"]
+        pages = self.page_table_host[seq, : (length + 15) // 16]
+        kv = self.kv_pages[layer, torch.from_numpy(pages.astype(np.int64)).to(self.device)].float().cpu()
+        k = kv[:, 0].reshape(len(pages), n_kv, 16, d).permute(0, 2, 1, 3).reshape(-1, n_kv, d)[:length]
+        v = kv[:, 1].reshape(len(pages), n_kv, d, 16).permute(0, 3, 1, 2).reshape(-1, n_kv, d)[:length]
+        return k.numpy(), v.numpy()

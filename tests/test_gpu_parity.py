@@ -1,0 +1,235 @@
+"""GPU parity of the HIP path against the oracle, through the C ABI.
+
+Every case: seeded inputs -> prefill (several append calls) -> one decode
+step (append, draft, verify) on both sides; the bar is stated in _cases.py.
+Sizes span several tiles of every kernel and end on ragged tails (context
+lengths that are not multiples of the page, chunk or tile sizes; batch
+entries with zero appended rows; shuffled page tables).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from _cases import Case, FLOAT_TOL, rel_err, say, nan_free
+from block_diffusion_drafter_softmax_amd import synth
+from block_diffusion_drafter_softmax_amd import _binding as B
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def small_cfg(**kw):
+    c = synth.config("tiny")
+    c.update(kw)
+    c["mask_token_id"] = c["vocab"] - 1
+    return c
+
+
+def run_step(case, verify=True, check_cache=True):
+    case.prefill()
+    case.step_append()
+    assert case.dr.read_error() == 0
+    g = case.draft(dbg=True)
+    orc = case.oracle_draft()
+    assert nan_free(g["hidden"], g["logits"], g["gap"])
+    he, le, n_cmp, n_exc = case.compare_draft(g, orc)
+    ce = case.check_cache() if check_cache else 0.0
+    say(f"  cache rel {ce:.2e}  hidden rel {he:.2e}  logits rel {le:.2e}  draft compared {n_cmp} excluded {n_exc}")
+    assert ce <= FLOAT_TOL and he <= FLOAT_TOL and le <= FLOAT_TOL
+    assert n_cmp > 0
+    assert case.dr.read_error() == 0
+    if verify:
+        check_verify_greedy(case, orc)
+    return g, orc
+
+
+def check_verify_greedy(case, orc):
+    cfg = case.cfg
+    d_or = np.stack([o["draft"] for o in orc]).astype(np.int32)
+    z = synth.make_logits(cfg, d_or, case.seed)
+    dev = case.dev
+    if z.dtype == np.float32:
+        zt = torch.from_numpy(z).to(dev)
+        zf = z.astype(np.float64)
+    else:
+        zt = torch.from_numpy(z.view(np.int16)).to(dev).view(torch.bfloat16)
+        zf = O.bf16_bits_to_f64(z)
+    acc = torch.full((case.B,), -1, dtype=torch.int32, device=dev)
+    nxt = torch.full((case.B,), -1, dtype=torch.int32, device=dev)
+    com = torch.full((case.B,), -1, dtype=torch.int32, device=dev)
+    case.dr.verify(case.t_i32(case.seq_ids), torch.from_numpy(d_or).to(dev), zt, acc, nxt, com)
+    torch.cuda.synchronize()
+    for b in range(case.B):
+        a, n, c = O.verify_greedy(d_or[b], zf[b])
+        assert (int(acc[b]), int(nxt[b]), int(com[b])) == (a, n, c), b
+    say(f"  verify accept {acc.tolist()} next {nxt.tolist()}")
+
+
+# ------------------------------------------------------------ small shapes
+def test_tiny_single_sequence():
+    run_step(Case(synth.config("tiny"), ctx=[128], n_new=[8], prefill_chunk=40))
+
+
+def test_tiny_ragged_batch_shuffled_pages():
+    # M = 24 draft rows (two 16-row MFMA tiles, ragged), one sequence with no
+    # appended rows, one with an empty context before the step, shuffled pages
+    run_step(Case(synth.config("tiny"), ctx=[37, 133, 301, 5], n_new=[1, 8, 0, 5], seed=3,
+                  page_order="shuffled", prefill_chunk=48))
+
+
+def test_tiny_tied_kv_without_rope():
+    cfg = small_cfg(tied_kv=1, use_rope=0)
+    case = Case(cfg, ctx=[70], n_new=[6], seed=5, prefill_chunk=32)
+    g, orc = run_step(case)
+    # without RoPE, identical mask tokens give identical rows in every layer
+    hid = g["hidden"][:, 0]
+    assert np.array_equal(hid[:, 2:], np.broadcast_to(hid[:, 1:2], hid[:, 2:].shape))
+
+
+def test_head_dim_128_block_16():
+    # the Qwen3 attention geometry (d_h 128, GQA 4:1, N 16) at a small width
+    cfg = small_cfg(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, intermediate=1024,
+                    vocab=8192, n_target_layers=5, block_size=16)
+    run_step(Case(cfg, ctx=[200, 257], n_new=[8, 3], seed=7, page_order="shuffled", prefill_chunk=64))
+
+
+def test_gqa_8_to_1_head_dim_64():
+    # the GPT-OSS attention geometry (d_h 64, GQA 8:1 -> 128 query rows per kv head)
+    cfg = small_cfg(hidden=640, n_q_heads=16, n_kv_heads=2, head_dim=64, intermediate=640,
+                    vocab=4096 + 96, n_target_layers=9, block_size=16)
+    run_step(Case(cfg, ctx=[150], n_new=[8], seed=9, prefill_chunk=72))
+
+
+def test_wide_batch_multi_group_rows():
+    # M = 5 * 16 = 80 rows -> several 64-row groups in the projection kernels
+    cfg = small_cfg(hidden=256, block_size=16, n_q_heads=4, n_kv_heads=4)
+    run_step(Case(cfg, ctx=[40, 41, 96, 0, 129], n_new=[8, 0, 16, 0, 9], seed=11,
+                  page_order="shuffled", prefill_chunk=80))
+
+
+def test_deterministic_bitwise():
+    case = Case(synth.config("tiny"), ctx=[99], n_new=[8], seed=13, prefill_chunk=50)
+    case.prefill()
+    case.step_append()
+    g1 = case.draft(dbg=True)
+    g2 = case.draft(dbg=True)
+    for k in ("draft", "gap", "hidden", "logits"):
+        assert np.array_equal(g1[k].view(np.uint32) if g1[k].dtype == np.float32 else g1[k],
+                              g2[k].view(np.uint32) if g2[k].dtype == np.float32 else g2[k]), k
+
+
+# ------------------------------------------------------- verification only
+def verify_only_drafter(V, N, batch):
+    """A one-layer drafter with the given vocabulary and block: only its
+    verify entry point is used (verification reads no weights)."""
+    from block_diffusion_drafter_softmax_amd.drafter import Drafter
+    cfg = small_cfg(vocab=V, hidden=256, n_layers=1, intermediate=256, block_size=N,
+                    n_q_heads=2, n_kv_heads=2)
+    return Drafter(cfg, synth.make_weights(cfg, 0), max_batch=batch, max_new=1, max_seqs=batch + 3,
+                   pages_per_seq=2)
+
+
+def test_verify_greedy_full_vocab_bf16():
+    cfg = synth.config("qwen3_8b")
+    B_, N, V = 4, cfg["block_size"], cfg["vocab"]
+    rng = np.random.default_rng(21)
+    draft = rng.integers(0, V - 1, size=(B_, N - 1)).astype(np.int32)
+    z = synth.make_logits(cfg, draft, seed=21)
+    dev = torch.device("cuda")
+    dr = verify_only_drafter(V, N, B_)
+    zt = torch.from_numpy(z.view(np.int16)).to(dev).view(torch.bfloat16)
+    acc, nxt, com = (torch.full((B_,), -1, dtype=torch.int32, device=dev) for _ in range(3))
+    seq = torch.arange(B_, dtype=torch.int32, device=dev)
+    dr.verify(seq, torch.from_numpy(draft).to(dev), zt, acc, nxt, com)
+    torch.cuda.synchronize()
+    zf = O.bf16_bits_to_f64(z)
+    for b in range(B_):
+        assert (int(acc[b]), int(nxt[b]), int(com[b])) == O.verify_greedy(draft[b], zf[b]), b
+    say(f"  accept {acc.tolist()}")
+
+
+def test_verify_temperature_one_batched():
+    cfg = synth.config("qwen3_8b_batched")
+    B_, N, V = cfg["batch"], cfg["block_size"], cfg["vocab"]
+    rng = np.random.default_rng(22)
+    draft = rng.integers(0, V - 1, size=(B_, N - 1)).astype(np.int32)
+    z = synth.make_logits(cfg, draft, seed=22)
+    dev = torch.device("cuda")
+    dr = verify_only_drafter(V, N, B_)
+    zt = torch.from_numpy(z.view(np.int16)).to(dev).view(torch.bfloat16)
+    seq_np = np.arange(B_, dtype=np.int32) + 3
+    seed, step = 1234567, 42
+    acc, nxt, com = (torch.full((B_,), -1, dtype=torch.int32, device=dev) for _ in range(3))
+    dr.verify(torch.from_numpy(seq_np).to(dev), torch.from_numpy(draft).to(dev), zt, acc, nxt, com,
+              temperature=1.0, seed=seed, step=step)
+    torch.cuda.synchronize()
+    zf = O.bf16_bits_to_f64(z)
+    compared_a = compared_n = 0
+    for b in range(B_):
+        a, n, c, info = O.verify_temp1(draft[b], zf[b], seed, step, int(seq_np[b]))
+        if any(abs(u - p) < 1e-5 for u, p in zip(info["u"], info["p"])):
+            continue
+        compared_a += 1
+        assert int(acc[b]) == a and int(com[b]) == c, (b, int(acc[b]), a)
+        if info["gumbel_gap"] >= 1e-2:
+            compared_n += 1
+            assert int(nxt[b]) == n, (b, int(nxt[b]), n)
+        if a < N - 1:
+            assert int(nxt[b]) != int(draft[b, a])
+    say(f"  accept {acc.tolist()}  compared {compared_a}/{B_} accept, {compared_n} next")
+    assert compared_a >= B_ - 2 and compared_n >= B_ - 4
+
+
+# ------------------------------------------------------ error word (host-forced)
+def test_device_error_bits_and_skips():
+    cfg = synth.config("tiny")
+    case = Case(cfg, ctx=[20, 20], n_new=[4, 4], seed=31, prefill_chunk=16)
+    case.prefill()
+    dr = case.dr
+    before = dr.ctx_len.clone()
+    T, H = cfg["n_target_layers"], cfg["hidden"]
+    hid = torch.zeros((2, 16, T, H), dtype=torch.bfloat16, device=case.dev)
+    # n_new above the call's max_new: flagged, sequence untouched
+    dr.ctx_append(case.t_i32(case.seq_ids), case.t_i32([17, 2]), hid, 16)
+    err = dr.read_error()
+    assert err & B.DEV_BAD_N_NEW
+    assert int(dr.ctx_len[case.seq_ids[0]]) == int(before[case.seq_ids[0]])
+    assert int(dr.ctx_len[case.seq_ids[1]]) == int(before[case.seq_ids[1]]) + 2
+    # a page-table hole where the append lands
+    pt = dr.page_table.clone()
+    L0 = int(dr.ctx_len[case.seq_ids[0]])
+    dr.page_table[case.seq_ids[0], L0 // 16] = -1
+    dr.ctx_append(case.t_i32(case.seq_ids[:1]), case.t_i32([16]), hid[:1], 16)
+    assert dr.read_error() & B.DEV_BAD_PAGE
+    assert int(dr.ctx_len[case.seq_ids[0]]) == L0
+    dr.page_table.copy_(pt)
+    # out-of-range anchor and sequence id are flagged; kernels stay in bounds
+    draft = torch.zeros((2, cfg["block_size"] - 1), dtype=torch.int32, device=case.dev)
+    dr.draft_block(case.t_i32([case.seq_ids[0], 10 ** 6]), case.t_i32([cfg["vocab"], 0]), draft)
+    err = dr.read_error()
+    assert err & B.DEV_BAD_TOKEN and err & B.DEV_BAD_SEQ
+    # capacity: more rows than the sequence's pages hold
+    dr.ctx_len[case.seq_ids[1]] = dr.pages_per_seq * 16 - 2
+    dr.ctx_append(case.t_i32(case.seq_ids[1:]), case.t_i32([4]), hid[:1], 16)
+    assert dr.read_error() & B.DEV_NO_PAGES
+    assert int(dr.ctx_len[case.seq_ids[1]]) == dr.pages_per_seq * 16 - 2
+
+
+def test_host_validation_enqueues_nothing():
+    cfg = synth.config("tiny")
+    case = Case(cfg, ctx=[16], n_new=[1], seed=33, prefill_chunk=16)
+    dr = case.dr
+    with pytest.raises(B.DFlashError):
+        dr.verify(case.t_i32([1]), case.t_i32(np.zeros((1, 7))), torch.zeros((1, 8, cfg["vocab"]), device=case.dev),
+                  case.t_i32([0]), case.t_i32([0]), temperature=0.5)
+    assert "temperature" in B.last_error()
+    hid = torch.zeros((1, 16, cfg["n_target_layers"], cfg["hidden"]), dtype=torch.bfloat16, device=case.dev)
+    with pytest.raises(B.DFlashError):
+        dr.ctx_append(case.t_i32([1]), case.t_i32([1]), hid, 10 ** 4)
+    assert int(dr.ctx_len.sum()) == 0
