@@ -4,26 +4,34 @@
 // as keys/values only).
 //
 // Work item = (key chunk, kv head, sequence). Chunk 0 is the block's own N
-// keys; chunks 1.. cover the context in pieces of `chunk` keys read straight
-// from the paged cache. A workgroup holds all R = (n_q/n_kv)*N query rows of
-// one kv head (GQA: the K/V tile is read once for the whole query group),
-// one wave per 16 rows. Per 32-key step a wave computes S^T = K Q^T with
-// MFMA (keys as rows, the lane's query as column), runs an online softmax in
-// the log2 domain, and accumulates O^T += V^T P^T with MFMA: V is stored
-// dim-major per page ([d_h][16 slots]) so its A-operand fragments are
-// contiguous, and P^T is taken from the S^T accumulators without moving
-// data between lanes (both MFMAs use the same permutation of the 32 keys).
-// The chunk's unnormalised O, running max and sum go to a partial buffer;
-// attn_merge_kernel combines the chunks (log-sum-exp merge, chunk order).
+// keys; chunks 1.. cover the context in pieces of CH = 128 keys (8 pages).
+// A workgroup holds all R = (n_q/n_kv)*N query rows of one kv head (GQA: a
+// K/V tile is read from HBM once for the whole query group), one wave per 16
+// rows. The chunk's page indices are read first, then every K and V byte of
+// the chunk is requested at once and staged in LDS, so a workgroup waits for
+// two memory latencies in total. Per 32-key step a wave computes S^T = K Q^T
+// with MFMA (keys as rows, the lane's query as column), runs an online
+// softmax in the log2 domain, and accumulates O^T += V^T P^T with MFMA: V is
+// stored dim-major per page ([d_h][16 slots]), so its A-operand fragments are
+// contiguous, and P^T comes straight from the S^T accumulators (both MFMAs use
+// the same permutation of the 32 keys). Unnormalised O, the running max and
+// the sum go to a partial buffer; attn_merge_kernel combines the chunks.
 #include "common.h"
-
+#include "dflash.h"
 
 namespace {
 DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
-}
+constexpr int CH = 128;  // context keys per work item
+}  // namespace
 
 template <int D>
 __global__ __launch_bounds__(1024) void attn_chunk_kernel(AttnArgs a) {
+  constexpr int KP = D + 8;          // padded LDS row of one key (bf16 elements)
+  constexpr int PAGES = CH / 16;
+  __shared__ uint16_t k_lds[CH * KP];
+  __shared__ uint16_t v_lds[PAGES * D * 16];
+  __shared__ int pg[PAGES];
+
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int seq = clampi(a.seq_ids[b], 0, a.max_seqs - 1);
   const int L = clampi(a.ctx_len[seq], 0, a.max_pages_per_seq * 16);
@@ -32,11 +40,51 @@ __global__ __launch_bounds__(1024) void attn_chunk_kernel(AttnArgs a) {
     key_begin = 0;
     key_end = a.N;
   } else {
-    key_begin = (c - 1) * a.chunk;
-    key_end = min(L, c * a.chunk);
+    key_begin = (c - 1) * CH;
+    key_end = min(L, c * CH);
     if (key_begin >= key_end) return;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nkeys = key_end - key_begin;
+  const int np = (nkeys + 15) / 16;
+  const int tid = threadIdx.x, nthreads = blockDim.x;
+  const size_t page_elems = (size_t)2 * a.n_kv * 16 * D;
+
+  if (tid < np) {
+    int p = 0;
+    if (c > 0) {
+      const int raw = a.page_table[(size_t)seq * a.max_pages_per_seq + key_begin / 16 + tid];
+      if (raw < 0 || raw >= a.n_pages) set_error(a.err, DFLASH_DEV_BAD_PAGE);
+      p = clampi(raw, 0, a.n_pages - 1);
+    }
+    pg[tid] = p;
+  }
+  __syncthreads();
+
+  // Stage K (slot-major rows) and V (dim-major) of the chunk's pages in LDS:
+  // per page, 2*D*16 bf16 = 4*D 16-byte units (K units first, then V units).
+  constexpr int UNITS_PER_PAGE = 4 * D;
+  for (int uidx = tid; uidx < np * UNITS_PER_PAGE; uidx += nthreads) {
+    const int p = uidx / UNITS_PER_PAGE, w = uidx % UNITS_PER_PAGE;
+    const uint16_t *kb, *vb;
+    if (c == 0) {
+      kb = a.kblk + ((size_t)b * a.n_kv + kvh) * 16 * D;
+      vb = a.vblk + ((size_t)b * a.n_kv + kvh) * D * 16;
+    } else {
+      kb = a.pages + pg[p] * page_elems + (size_t)kvh * 16 * D;
+      vb = kb + (size_t)a.n_kv * 16 * D;
+    }
+    if (w < 2 * D) {  // K: 16 slots x D, 8 elements per unit
+      const int slot = w / (D / 8), col = (w % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&k_lds[(p * 16 + slot) * KP + col]) =
+          *reinterpret_cast<const u32x4*>(kb + slot * D + col);
+    } else {
+      const int w2 = w - 2 * D;
+      *reinterpret_cast<u32x4*>(&v_lds[p * D * 16 + w2 * 8]) = *reinterpret_cast<const u32x4*>(vb + w2 * 8);
+    }
+  }
+  __syncthreads();
+
+  const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int G = a.n_q / a.n_kv, R = G * a.N;
   const int r = wave * 16 + r16;
@@ -53,38 +101,23 @@ __global__ __launch_bounds__(1024) void attn_chunk_kernel(AttnArgs a) {
   for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const size_t head_off = (size_t)kvh * 16 * D;
-  const size_t page_elems = (size_t)2 * a.n_kv * 16 * D;
-  for (int k0 = key_begin; k0 < key_end; k0 += 32) {
-    const bool t1 = k0 + 16 < key_end;
-    const uint16_t *kp0, *kp1 = nullptr, *vp0, *vp1 = nullptr;
-    if (c == 0) {
-      kp0 = a.kblk + ((size_t)b * a.n_kv + kvh) * 16 * D;
-      vp0 = a.vblk + ((size_t)b * a.n_kv + kvh) * D * 16;
-    } else {
-      const int* pt = a.page_table + (size_t)seq * a.max_pages_per_seq + k0 / 16;
-      const int pg0 = clampi(pt[0], 0, a.n_pages - 1);
-      kp0 = a.pages + pg0 * page_elems + head_off;
-      vp0 = kp0 + (size_t)a.n_kv * 16 * D;
-      if (t1) {
-        const int pg1 = clampi(pt[1], 0, a.n_pages - 1);
-        kp1 = a.pages + pg1 * page_elems + head_off;
-        vp1 = kp1 + (size_t)a.n_kv * 16 * D;
-      }
-    }
+  for (int k0 = 0; k0 < nkeys; k0 += 32) {  // chunk-relative keys
+    const bool t1 = k0 + 16 < nkeys;
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd) s0 = mfma16(ld8(kp0 + r16 * D + kd * 32 + 8 * g), qf[kd], s0);
+    for (int kd = 0; kd < KD; ++kd)
+      s0 = mfma16(*reinterpret_cast<const bf16x8*>(&k_lds[(k0 + r16) * KP + kd * 32 + 8 * g]), qf[kd], s0);
     if (t1) {
 #pragma unroll
-      for (int kd = 0; kd < KD; ++kd) s1 = mfma16(ld8(kp1 + r16 * D + kd * 32 + 8 * g), qf[kd], s1);
+      for (int kd = 0; kd < KD; ++kd)
+        s1 = mfma16(*reinterpret_cast<const bf16x8*>(&k_lds[(k0 + 16 + r16) * KP + kd * 32 + 8 * g]), qf[kd], s1);
     }
     // lane holds keys k0 + 4g + i (s0) and k0 + 16 + 4g + i (s1) for query r
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[i] = (k0 + 4 * g + i < key_end) ? s0[i] * a.scale_log2 : -INFINITY;
-      x[4 + i] = (t1 && k0 + 16 + 4 * g + i < key_end) ? s1[i] * a.scale_log2 : -INFINITY;
+      x[i] = (k0 + 4 * g + i < nkeys) ? s0[i] * a.scale_log2 : -INFINITY;
+      x[4 + i] = (t1 && k0 + 16 + 4 * g + i < nkeys) ? s1[i] * a.scale_log2 : -INFINITY;
     }
     float mt = x[0];
 #pragma unroll
@@ -104,15 +137,17 @@ __global__ __launch_bounds__(1024) void attn_chunk_kernel(AttnArgs a) {
     l_run = l_run * corr + psum;
     m_run = m_new;
     const bf16x8 pf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(pb0, pb1, 0, 1, 2, 3, 4, 5, 6, 7));
+    const uint16_t* vp0 = &v_lds[(k0 / 16) * D * 16];
+    const uint16_t* vp1 = vp0 + D * 16;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      u16x4 v0 = *reinterpret_cast<const u16x4*>(vp0 + (size_t)(t * 16 + r16) * 16 + 4 * g);
+      u16x4 v0 = *reinterpret_cast<const u16x4*>(vp0 + (t * 16 + r16) * 16 + 4 * g);
       u16x4 v1 = {0, 0, 0, 0};
-      if (t1) v1 = *reinterpret_cast<const u16x4*>(vp1 + (size_t)(t * 16 + r16) * 16 + 4 * g);
+      if (t1) v1 = *reinterpret_cast<const u16x4*>(vp1 + (t * 16 + r16) * 16 + 4 * g);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (k0 + 4 * g + i >= key_end) v0[i] = 0;
-        if (k0 + 16 + 4 * g + i >= key_end) v1[i] = 0;
+        if (k0 + 4 * g + i >= nkeys) v0[i] = 0;
+        if (k0 + 16 + 4 * g + i >= nkeys) v1[i] = 0;
       }
       const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[t] = acc[t] * corr;
@@ -132,8 +167,9 @@ __global__ __launch_bounds__(1024) void attn_chunk_kernel(AttnArgs a) {
   }
 }
 
-// One thread per (sequence, kv head, query row, 4 dims): log-sum-exp merge of
-// the chunk partials in chunk order, normalise, round to bf16.
+// One thread per (sequence, kv head, query row, 4 dims): single-pass
+// log-sum-exp merge of the chunk partials in chunk order, normalise, round
+// to bf16 and write the O-projection's packed activation.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int B) {
   const int G = a.n_q / a.n_kv, R = G * a.N;
@@ -145,23 +181,28 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int B) {
   if (b >= B) return;
   const int seq = clampi(a.seq_ids[b], 0, a.max_seqs - 1);
   const int L = clampi(a.ctx_len[seq], 0, a.max_pages_per_seq * 16);
-  const int nc = min(a.n_ck, 1 + (L + a.chunk - 1) / a.chunk);
+  const int nc = min(a.n_ck, 1 + (L + CH - 1) / CH);
   const size_t unit0 = ((size_t)b * a.n_kv + kvh) * a.n_ck;
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_ml[((unit0 + c) * R + r) * 2]);
-  float den = 0.f;
+  float M = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int c = 0; c < nc; ++c) {
-    const float w = exp2f(a.part_ml[((unit0 + c) * R + r) * 2] - M);
-    den += w * a.part_ml[((unit0 + c) * R + r) * 2 + 1];
-    num += w * *reinterpret_cast<const f32x4*>(a.part_o + ((unit0 + c) * R + r) * D + dq * 4);
+    const size_t row = (unit0 + c) * R + r;
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + row * 2);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(a.part_o + row * D + dq * 4);
+    const float Mn = fmaxf(M, ml.x);
+    const float wo = exp2f(M - Mn), wn = exp2f(ml.x - Mn);
+    den = den * wo + ml.y * wn;
+    num = num * wo + o * wn;
+    M = Mn;
   }
   const float inv = 1.0f / den;
   const int hq = kvh * G + r / a.N, n = r % a.N;
+  const int m = b * a.N + n, qd = a.n_q * D;
   u16x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f2bf(num[i] * inv);
-  *reinterpret_cast<u16x4*>(a.o + ((size_t)(b * a.N + n) * a.n_q + hq) * D + dq * 4) = o;
+  *reinterpret_cast<u16x4*>(a.o + pk_index(m, hq * D + dq * 4, qd)) = o;
 }
 
 extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_t st) {

@@ -1,8 +1,10 @@
-// Host side of the C ABI: validation, workspace layout, set-up tables and the
-// launch sequence of each entry point. Everything after dflash_create is
-// enqueued on the caller's stream with no host synchronisation.
+// Host side of the C ABI: validation, workspace layout, set-up (fusion
+// weights, RoPE table, weight packing) and the launch sequence of each entry
+// point. Everything after dflash_create is enqueued on the caller's stream
+// with no host synchronisation.
 #include "dflash.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -26,35 +28,44 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-#define HIP_OK(expr)                                                                  \
-  do {                                                                                \
-    hipError_t e_ = (expr);                                                           \
-    if (e_ != hipSuccess) return fail(DFLASH_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+#define HIP_OK(expr)                                                                               \
+  do {                                                                                             \
+    hipError_t e_ = (expr);                                                                        \
+    if (e_ != hipSuccess) return fail(DFLASH_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_));     \
   } while (0)
 
-constexpr int kAttnChunk = 128;   // context keys per attention work item
-constexpr int kVerifyChunk = 8192;
-constexpr int kKsMax = 8;
+constexpr int kAttnChunk = 128;     // context keys per attention work item (attention.hip: CH)
+constexpr int kVerifyChunk = 8192;  // logits per verification work item
+constexpr int kKsMax = 16;          // largest k split of a streaming GEMM
+constexpr int kTargetWaves = 1536;  // streaming waves to aim for (~6 per CU)
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Byte offsets of everything the library keeps in the caller's workspace.
 struct Layout {
-  size_t alpha, rope, rowpos_a, rowseq_a, rowpos_d, rowseq_d, f, x, h, q, o, kblk, vblk, mm, gpart;
+  // set-up tables and packed weights
+  size_t alpha, rope, wq, wk_d, wv_d, wk_t, wv_t, wo, wg, wu, wd, lm;
+  // per-call buffers
+  size_t rowpos_a, rowseq_a, rowpos_d, rowseq_d, f, x, h, q, o, kblk, vblk, mm, gpart, cpart;
   size_t apo, aml, lmpart, vpart, vstate, counters, total;
-  int n_ck, n_lm_wg, n_vchunks, m_max, rows_a_max;
+  size_t gpart_floats, cpart_floats;
+  int n_ck, n_vchunks, m_max, rows_a_max;
 };
 
 Layout make_layout(const dflash_config& c) {
   Layout L{};
-  const size_t H = c.hidden, D = c.n_layers, T = c.n_target_layers, N = c.block_size;
-  const size_t qd = (size_t)c.n_q_heads * c.head_dim;
+  const size_t H = c.hidden, D = c.n_layers, T = c.n_target_layers, N = c.block_size, I = c.intermediate;
+  const size_t qd = (size_t)c.n_q_heads * c.head_dim, kvd = (size_t)c.n_kv_heads * c.head_dim;
   const size_t Bm = c.max_batch;
   const size_t R = (size_t)(c.n_q_heads / c.n_kv_heads) * N;
   L.m_max = (int)(Bm * N);
   L.rows_a_max = (int)(Bm * c.max_new);
+  const size_t mp = pad16(L.m_max), rp = pad16(L.rows_a_max);
   L.n_ck = 1 + (c.max_pages_per_seq * 16 + kAttnChunk - 1) / kAttnChunk;
-  L.n_lm_wg = (c.vocab / 32 + 3) / 4;
   L.n_vchunks = (c.vocab + kVerifyChunk - 1) / kVerifyChunk;
+  const size_t ncol_d = std::max(qd + 2 * kvd, H), ncol_c = D * 2 * kvd;
+  L.gpart_floats = ncol_d * std::max<size_t>(256, 2 * (size_t)L.m_max);
+  L.cpart_floats = ncol_c * std::max<size_t>(256, 2 * (size_t)L.rows_a_max);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -63,22 +74,33 @@ Layout make_layout(const dflash_config& c) {
   };
   L.alpha = take(D * T * 4);
   L.rope = take((size_t)c.max_pos * (c.head_dim / 2) * 2 * 4);
+  L.wq = take(D * qd * H * 2);
+  L.wk_d = take(D * kvd * H * 2);
+  L.wv_d = take(D * kvd * H * 2);
+  L.wk_t = c.tied_kv ? L.wk_d : take(D * kvd * H * 2);
+  L.wv_t = c.tied_kv ? L.wv_d : take(D * kvd * H * 2);
+  L.wo = take(D * H * qd * 2);
+  L.wg = take(D * I * H * 2);
+  L.wu = take(D * I * H * 2);
+  L.wd = take(D * H * I * 2);
+  L.lm = take((size_t)c.vocab * H * 2);
   L.rowpos_a = take(L.rows_a_max * 4);
   L.rowseq_a = take(L.rows_a_max * 4);
   L.rowpos_d = take(L.m_max * 4);
   L.rowseq_d = take(L.m_max * 4);
-  L.f = take(D * L.rows_a_max * H * 2);
+  L.f = take(D * rp * H * 2);
   L.x = take(L.m_max * H * 4);
-  L.h = take(L.m_max * H * 2);
+  L.h = take(mp * H * 2);
   L.q = take(L.m_max * qd * 2);
-  L.o = take(L.m_max * qd * 2);
-  L.kblk = take(Bm * c.n_kv_heads * 16 * c.head_dim * 2);
-  L.vblk = take(Bm * c.n_kv_heads * 16 * c.head_dim * 2);
-  L.mm = take((size_t)L.m_max * c.intermediate * 2);
-  L.gpart = take((size_t)kKsMax * L.m_max * H * 4);
+  L.o = take(mp * qd * 2);
+  L.kblk = take(Bm * kvd * 16 * 2);
+  L.vblk = take(Bm * kvd * 16 * 2);
+  L.mm = take(mp * I * 2);
+  L.gpart = take(L.gpart_floats * 4);
+  L.cpart = take(L.cpart_floats * 4);
   L.apo = take(Bm * c.n_kv_heads * L.n_ck * R * c.head_dim * 4);
   L.aml = take(Bm * c.n_kv_heads * L.n_ck * R * 2 * 4);
-  L.lmpart = take((size_t)L.n_lm_wg * L.m_max * sizeof(Top2));
+  L.lmpart = take((size_t)(c.vocab / 32) * L.m_max * sizeof(Top2));
   L.vpart = take(Bm * N * L.n_vchunks * 2 * 4);
   L.vstate = take(Bm * 2 * 4);
   L.counters = take(Bm * 2 * 4);
@@ -95,7 +117,8 @@ int check_config(const dflash_config* c) {
     return fail(DFLASH_ERR_INVALID_ARG, "config sizes must be positive");
   if (c->page_size != 16) return fail(DFLASH_ERR_UNSUPPORTED, "page_size must be 16 (got %d)", c->page_size);
   if (c->head_dim != 64 && c->head_dim != 128) return fail(DFLASH_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-  if (c->hidden % 32 || c->hidden > 8192) return fail(DFLASH_ERR_UNSUPPORTED, "hidden must be a multiple of 32, <= 8192");
+  if (c->hidden % 32 || c->hidden > 8192)
+    return fail(DFLASH_ERR_UNSUPPORTED, "hidden must be a multiple of 32, <= 8192");
   if (c->intermediate % 32) return fail(DFLASH_ERR_UNSUPPORTED, "intermediate must be a multiple of 32");
   if (c->vocab % 32) return fail(DFLASH_ERR_UNSUPPORTED, "vocab must be a multiple of 32");
   if (c->n_q_heads % c->n_kv_heads) return fail(DFLASH_ERR_INVALID_ARG, "n_q_heads must be a multiple of n_kv_heads");
@@ -103,9 +126,11 @@ int check_config(const dflash_config* c) {
   const int R = (c->n_q_heads / c->n_kv_heads) * c->block_size;
   if (R % 16 || R > 256)
     return fail(DFLASH_ERR_UNSUPPORTED, "(n_q/n_kv)*block_size must be a multiple of 16 and <= 256 (got %d)", R);
-  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return fail(DFLASH_ERR_INVALID_ARG, "mask_token_id out of range");
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab)
+    return fail(DFLASH_ERR_INVALID_ARG, "mask_token_id out of range");
   if (c->max_pos < c->block_size) return fail(DFLASH_ERR_INVALID_ARG, "max_pos too small");
-  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) return fail(DFLASH_ERR_INVALID_ARG, "rms_eps > 0 and rope_theta > 1 required");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f))
+    return fail(DFLASH_ERR_INVALID_ARG, "rms_eps > 0 and rope_theta > 1 required");
   return DFLASH_OK;
 }
 
@@ -153,56 +178,40 @@ struct dflash_ctx {
     }
     return DFLASH_OK;
   }
-
-  GemmArgs gemm_base(int M, int K) const {
-    GemmArgs g;
-    std::memset(&g, 0, sizeof(g));
-    g.K = K;
-    g.M = M;
-    g.ks = 1;
-    g.head_dim = c.head_dim;
-    g.n_kv = c.n_kv_heads;
-    g.block = c.block_size;
-    g.max_pages_per_seq = c.max_pages_per_seq;
-    g.n_pages = c.n_pages;
-    g.max_pos = c.max_pos;
-    g.page_table = kv.page_table;
-    g.kv_pages = kv.kv_pages;
-    g.layer_stride = (long long)c.n_pages * 2 * c.n_kv_heads * 16 * c.head_dim;
-    g.rope = c.use_rope ? at<float>(L.rope) : nullptr;
-    return g;
-  }
 };
 
 namespace {
 
-void add_seg(GemmArgs& g, const uint16_t* w0, const uint16_t* w1, const uint16_t* act, void* out, int pairs,
-             int mode, int epi, int layer) {
-  GemmSeg& s = g.seg[g.nseg];
+void add_seg(WsArgs& a, const uint16_t* w0, const uint16_t* w1, const uint16_t* act, int units, int col0) {
+  WsSeg& s = a.seg[a.nseg];
   s.w0 = w0;
   s.w1 = w1;
   s.act = act;
-  s.out = out;
-  s.pairs = pairs;
-  s.mode = mode;
-  s.epi = epi;
-  s.layer = layer;
-  g.seg_start[g.nseg + 1] = g.seg_start[g.nseg] + pairs;
-  g.nseg++;
+  s.units = units;
+  s.col0 = col0;
+  a.unit_start[a.nseg + 1] = a.unit_start[a.nseg] + units;
+  a.nseg++;
 }
 
-int total_pairs(const GemmArgs& g) { return g.seg_start[g.nseg]; }
-
-// Workgroup count and k split for a launch: aim for >= 512 workgroups while
-// every wave keeps >= 4 k-steps of 32.
-int choose_ks(int pairs, int K, int kw, bool can_split) {
-  int ks = 1;
-  if (!can_split) return 1;
-  while (pairs * ks < 512 && ks * 2 <= kKsMax && (K / 32) / (kw * ks * 2) >= 4) ks *= 2;
-  return ks;
+WsArgs ws_base(int M, int K, int n_cols) {
+  WsArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.M = M;
+  a.K = K;
+  a.ks = 1;
+  a.n_cols = n_cols;
+  return a;
 }
 
-int gemm_kw(int pairs) { return pairs < 384 ? 8 : 4; }
+// k split of a streaming GEMM: enough waves to keep ~6 per CU streaming, at
+// least 8 k steps per wave, and within the partial buffer.
+int pick_ks(int units, int K, int M, int n_cols, size_t cap_floats) {
+  int ks = (kTargetWaves + units - 1) / units;
+  ks = std::min(ks, std::max(1, (K / 32) / 8));
+  ks = std::min(ks, kKsMax);
+  ks = std::min<long long>(ks, (long long)(cap_floats / ((size_t)M * n_cols)));
+  return std::max(ks, 1);
+}
 
 }  // namespace
 
@@ -261,13 +270,31 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, const dflas
   std::vector<int32_t> zeros((size_t)c.max_batch * 2, 0);
   HIP_OK(hipMemcpy(ws + L.counters, zeros.data(), zeros.size() * 4, hipMemcpyHostToDevice));
 
+  // Pack every streamed matrix into the MFMA-operand layout (layers are
+  // stacked along rows, so one pass per matrix).
+  const int D = c.n_layers, H = c.hidden, I = c.intermediate;
+  const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  struct Job {
+    const uint16_t* src;
+    size_t dst;
+    int R, K;
+  };
+  std::vector<Job> jobs = {{w->wq, L.wq, D * qd, H},   {w->wk_d, L.wk_d, D * kvd, H}, {w->wv_d, L.wv_d, D * kvd, H},
+                           {w->wo, L.wo, D * H, qd},   {w->wg, L.wg, D * I, H},       {w->wu, L.wu, D * I, H},
+                           {w->wd, L.wd, D * H, I},    {w->lm_head, L.lm, c.vocab, H}};
+  if (!c.tied_kv) {
+    jobs.push_back({w->wk_t, L.wk_t, D * kvd, H});
+    jobs.push_back({w->wv_t, L.wv_t, D * kvd, H});
+  }
+  for (const Job& j : jobs) {
+    PackArgs pa{j.src, reinterpret_cast<uint16_t*>(ws + j.dst), j.R, j.K};
+    HIP_OK(dflash_launch_pack(&pa, nullptr));
+  }
+  HIP_OK(hipStreamSynchronize(nullptr));
+
   dflash_ctx* ctx = new dflash_ctx();
   ctx->c = c;
   ctx->w = *w;
-  if (c.tied_kv) {
-    ctx->w.wk_t = w->wk_d;
-    ctx->w.wv_t = w->wv_d;
-  }
   ctx->kv = *kv;
   ctx->ws = ws;
   ctx->L = L;
@@ -292,7 +319,7 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
   if (!seq_ids || !n_new || !target_hidden) return fail(DFLASH_ERR_INVALID_ARG, "null input pointer");
   const Layout& L = ctx->L;
   const int rows = B * max_new;
-  const size_t H = c.hidden, kvd = (size_t)c.n_kv_heads * c.head_dim;
+  const int H = c.hidden, D = c.n_layers, kvd = c.n_kv_heads * c.head_dim;
   int rc;
 
   PlanArgs pa{};
@@ -322,26 +349,44 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
   fa.row_pos = pa.row_pos;
   fa.rows = rows;
   fa.T = c.n_target_layers;
-  fa.H = c.hidden;
-  fa.D = c.n_layers;
+  fa.H = H;
+  fa.D = D;
   fa.eps = c.rms_eps;
   if ((rc = ctx->launch(DFLASH_K_FUSE, stream, [&] { return dflash_launch_fuse(&fa, stream); }))) return rc;
 
-  // Context K (RoPE pairs) and V of up to 8 layers per launch.
-  for (int l0 = 0; l0 < c.n_layers; l0 += GEMM_MAX_SEG / 2) {
-    GemmArgs g = ctx->gemm_base(rows, c.hidden);
-    g.row_pos = pa.row_pos;
-    g.row_seq = pa.row_seq;
-    for (int i = l0; i < c.n_layers && i < l0 + GEMM_MAX_SEG / 2; ++i) {
-      const uint16_t* act = ctx->at<uint16_t>(L.f) + (size_t)i * rows * H;
-      add_seg(g, ctx->w.wk_t + (size_t)i * kvd * H, nullptr, act, nullptr, (int)(kvd / 32), PAIR_ROPE, EPI_CTX_K, i);
-      add_seg(g, ctx->w.wv_t + (size_t)i * kvd * H, nullptr, act, nullptr, (int)(kvd / 32), PAIR_PLAIN, EPI_CTX_V, i);
+  // Context K and V of every layer: fp32 split partials, columns
+  // [layer][K | V], then one finisher (RoPE, bf16, page scatter).
+  const int n_cols = D * 2 * kvd;
+  int ks = 1;
+  for (int l0 = 0; l0 < D; l0 += WS_MAX_SEG / 2) {
+    WsArgs g = ws_base(rows, H, n_cols);
+    g.part = ctx->at<float>(L.cpart);
+    for (int i = l0; i < D && i < l0 + WS_MAX_SEG / 2; ++i) {
+      const uint16_t* act = ctx->at<uint16_t>(L.f) + (size_t)i * pad16(rows) * H;
+      add_seg(g, ctx->at<uint16_t>(L.wk_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd);
+      add_seg(g, ctx->at<uint16_t>(L.wv_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd + kvd);
     }
-    const int kw = gemm_kw(total_pairs(g));
-    if ((rc = ctx->launch(DFLASH_K_CTX_KV, stream, [&] { return dflash_launch_gemm(&g, total_pairs(g), kw, stream); })))
+    if (l0 == 0) ks = pick_ks(g.unit_start[g.nseg] * ((D + 7) / 8), H, rows, n_cols, L.cpart_floats);
+    g.ks = ks;
+    if ((rc = ctx->launch(DFLASH_K_CTX_KV, stream, [&] { return dflash_launch_ws(&g, WS_PARTIAL, stream); })))
       return rc;
   }
-  return DFLASH_OK;
+  CtxFinishArgs ca{};
+  ca.part = ctx->at<float>(L.cpart);
+  ca.ks = ks;
+  ca.M = rows;
+  ca.D = D;
+  ca.n_kv = c.n_kv_heads;
+  ca.d = c.head_dim;
+  ca.row_pos = pa.row_pos;
+  ca.row_seq = pa.row_seq;
+  ca.page_table = ctx->kv.page_table;
+  ca.max_pages_per_seq = c.max_pages_per_seq;
+  ca.n_pages = c.n_pages;
+  ca.rope = c.use_rope ? ctx->at<float>(L.rope) : nullptr;
+  ca.kv_pages = ctx->kv.kv_pages;
+  ca.layer_stride = (long long)c.n_pages * 2 * kvd * 16;
+  return ctx->launch(DFLASH_K_CTX_FINISH, stream, [&] { return dflash_launch_ctx_finish(&ca, stream); });
 }
 
 int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor, int32_t* draft,
@@ -352,8 +397,8 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   if (!seq_ids || !anchor || !draft) return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
   const Layout& L = ctx->L;
   const int N = c.block_size, M = B * N;
-  const size_t H = c.hidden, I = c.intermediate, qd = (size_t)c.n_q_heads * c.head_dim;
-  const size_t kvd = (size_t)c.n_kv_heads * c.head_dim;
+  const int H = c.hidden, I = c.intermediate, D = c.n_layers;
+  const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
   int rc;
 
   PlanArgs pa{};
@@ -392,21 +437,35 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   na.g = ctx->w.g_attn;
   na.h = h;
   na.dbg = dbg_hidden;
-  na.H = c.hidden;
+  na.H = H;
   na.M = M;
   na.eps = c.rms_eps;
   if ((rc = ctx->launch(DFLASH_K_NORM, stream, [&] { return dflash_launch_norm(&na, stream); }))) return rc;
 
+  QkvFinishArgs qa{};
+  qa.part = gpart;
+  qa.M = M;
+  qa.n_q = c.n_q_heads;
+  qa.n_kv = c.n_kv_heads;
+  qa.d = c.head_dim;
+  qa.N = N;
+  qa.row_pos = pa.row_pos;
+  qa.rope = c.use_rope ? ctx->at<float>(L.rope) : nullptr;
+  qa.q = ctx->at<uint16_t>(L.q);
+  qa.kblk = ctx->at<uint16_t>(L.kblk);
+  qa.vblk = ctx->at<uint16_t>(L.vblk);
+
   AttnArgs aa{};
-  aa.q = ctx->at<uint16_t>(L.q);
-  aa.kblk = ctx->at<uint16_t>(L.kblk);
-  aa.vblk = ctx->at<uint16_t>(L.vblk);
+  aa.q = qa.q;
+  aa.kblk = qa.kblk;
+  aa.vblk = qa.vblk;
   aa.page_table = ctx->kv.page_table;
   aa.ctx_len = ctx->kv.ctx_len;
   aa.seq_ids = seq_ids;
   aa.part_o = ctx->at<float>(L.apo);
   aa.part_ml = ctx->at<float>(L.aml);
   aa.o = ctx->at<uint16_t>(L.o);
+  aa.err = ctx->kv.error_word;
   aa.N = N;
   aa.n_q = c.n_q_heads;
   aa.n_kv = c.n_kv_heads;
@@ -416,22 +475,20 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   aa.n_pages = c.n_pages;
   aa.max_seqs = c.max_seqs;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
-  const long long layer_stride = (long long)c.n_pages * 2 * c.n_kv_heads * 16 * c.head_dim;
+  const long long layer_stride = (long long)c.n_pages * 2 * kvd * 16;
 
-  for (int i = 0; i < c.n_layers; ++i) {
-    {  // Q, block K (RoPE) and block V
-      GemmArgs g = ctx->gemm_base(M, c.hidden);
-      g.row_pos = pa.row_pos;
-      g.row_seq = pa.row_seq;
-      g.n_out = (int)qd;
-      add_seg(g, ctx->w.wq + (size_t)i * qd * H, nullptr, h, ctx->at<uint16_t>(L.q), (int)(qd / 32), PAIR_ROPE,
-              EPI_Q, i);
-      add_seg(g, ctx->w.wk_d + (size_t)i * kvd * H, nullptr, h, ctx->at<uint16_t>(L.kblk), (int)(kvd / 32),
-              PAIR_ROPE, EPI_KBLK, i);
-      add_seg(g, ctx->w.wv_d + (size_t)i * kvd * H, nullptr, h, ctx->at<uint16_t>(L.vblk), (int)(kvd / 32),
-              PAIR_PLAIN, EPI_VBLK, i);
-      const int kw = gemm_kw(total_pairs(g));
-      if ((rc = ctx->launch(DFLASH_K_QKV, stream, [&] { return dflash_launch_gemm(&g, total_pairs(g), kw, stream); })))
+  for (int i = 0; i < D; ++i) {
+    {  // Q, block K and block V: split partials, then RoPE/layout
+      WsArgs g = ws_base(M, H, qd + 2 * kvd);
+      g.part = gpart;
+      add_seg(g, ctx->at<uint16_t>(L.wq) + (size_t)i * qd * H, nullptr, h, qd / 32, 0);
+      add_seg(g, ctx->at<uint16_t>(L.wk_d) + (size_t)i * kvd * H, nullptr, h, kvd / 32, qd);
+      add_seg(g, ctx->at<uint16_t>(L.wv_d) + (size_t)i * kvd * H, nullptr, h, kvd / 32, qd + kvd);
+      g.ks = pick_ks(g.unit_start[g.nseg], H, M, g.n_cols, L.gpart_floats);
+      qa.ks = g.ks;
+      if ((rc = ctx->launch(DFLASH_K_QKV, stream, [&] { return dflash_launch_ws(&g, WS_PARTIAL, stream); })))
+        return rc;
+      if ((rc = ctx->launch(DFLASH_K_QKV_FINISH, stream, [&] { return dflash_launch_qkv_finish(&qa, stream); })))
         return rc;
     }
     aa.pages = ctx->kv.kv_pages + (size_t)i * layer_stride;
@@ -440,54 +497,47 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
     if ((rc = ctx->launch(DFLASH_K_ATTN_MERGE, stream,
                           [&] { return dflash_launch_attn_merge(&aa, B, c.head_dim, stream); })))
       return rc;
-    int ks_o;
-    {  // O projection -> split partials
-      GemmArgs g = ctx->gemm_base(M, (int)qd);
-      g.n_out = c.hidden;
-      add_seg(g, ctx->w.wo + (size_t)i * H * qd, nullptr, aa.o, gpart, c.hidden / 32, PAIR_PLAIN, EPI_PARTIAL, i);
-      const int kw = gemm_kw(total_pairs(g));
-      g.ks = ks_o = choose_ks(total_pairs(g), (int)qd, kw, true);
-      if ((rc = ctx->launch(DFLASH_K_OPROJ, stream, [&] { return dflash_launch_gemm(&g, total_pairs(g), kw, stream); })))
+    {  // O projection -> split partials, added by the next norm
+      WsArgs g = ws_base(M, qd, H);
+      g.part = gpart;
+      add_seg(g, ctx->at<uint16_t>(L.wo) + (size_t)i * H * qd, nullptr, aa.o, H / 32, 0);
+      g.ks = pick_ks(g.unit_start[g.nseg], qd, M, H, L.gpart_floats);
+      na.ks = g.ks;
+      if ((rc = ctx->launch(DFLASH_K_OPROJ, stream, [&] { return dflash_launch_ws(&g, WS_PARTIAL, stream); })))
         return rc;
     }
     na.mode = 1;
-    na.ks = ks_o;
     na.g = ctx->w.g_mlp + (size_t)i * H;
     na.dbg = nullptr;
     if ((rc = ctx->launch(DFLASH_K_NORM, stream, [&] { return dflash_launch_norm(&na, stream); }))) return rc;
-    {  // gate/up + SwiGLU
-      GemmArgs g = ctx->gemm_base(M, c.hidden);
-      g.n_out = (int)I;
-      add_seg(g, ctx->w.wg + (size_t)i * I * H, ctx->w.wu + (size_t)i * I * H, h, ctx->at<uint16_t>(L.mm),
-              (int)(I / 16), PAIR_DUAL, EPI_SWIGLU, i);
-      const int kw = gemm_kw(total_pairs(g));
-      if ((rc = ctx->launch(DFLASH_K_GATE_UP, stream,
-                            [&] { return dflash_launch_gemm(&g, total_pairs(g), kw, stream); })))
+    {  // gate/up + SwiGLU (full k per wave)
+      WsArgs g = ws_base(M, H, I);
+      g.out = ctx->at<uint16_t>(L.mm);
+      add_seg(g, ctx->at<uint16_t>(L.wg) + (size_t)i * I * H, ctx->at<uint16_t>(L.wu) + (size_t)i * I * H, h,
+              I / 16, 0);
+      if ((rc = ctx->launch(DFLASH_K_GATE_UP, stream, [&] { return dflash_launch_ws(&g, WS_SWIGLU, stream); })))
         return rc;
     }
-    int ks_d;
     {  // down -> split partials
-      GemmArgs g = ctx->gemm_base(M, (int)I);
-      g.n_out = c.hidden;
-      add_seg(g, ctx->w.wd + (size_t)i * H * I, nullptr, ctx->at<uint16_t>(L.mm), gpart, c.hidden / 32, PAIR_PLAIN,
-              EPI_PARTIAL, i);
-      const int kw = gemm_kw(total_pairs(g));
-      g.ks = ks_d = choose_ks(total_pairs(g), (int)I, kw, true);
-      if ((rc = ctx->launch(DFLASH_K_DOWN, stream, [&] { return dflash_launch_gemm(&g, total_pairs(g), kw, stream); })))
+      WsArgs g = ws_base(M, I, H);
+      g.part = gpart;
+      add_seg(g, ctx->at<uint16_t>(L.wd) + (size_t)i * H * I, nullptr, ctx->at<uint16_t>(L.mm), H / 32, 0);
+      g.ks = pick_ks(g.unit_start[g.nseg], I, M, H, L.gpart_floats);
+      na.ks = g.ks;
+      if ((rc = ctx->launch(DFLASH_K_DOWN, stream, [&] { return dflash_launch_ws(&g, WS_PARTIAL, stream); })))
         return rc;
     }
     na.mode = 1;
-    na.ks = ks_d;
-    na.g = (i + 1 < c.n_layers) ? ctx->w.g_attn + (size_t)(i + 1) * H : ctx->w.g_final;
+    na.g = (i + 1 < D) ? ctx->w.g_attn + (size_t)(i + 1) * H : ctx->w.g_final;
     na.dbg = dbg_hidden ? dbg_hidden + (size_t)(i + 1) * M * H : nullptr;
     if ((rc = ctx->launch(DFLASH_K_NORM, stream, [&] { return dflash_launch_norm(&na, stream); }))) return rc;
   }
 
   LmArgs la{};
-  la.w = ctx->w.lm_head;
+  la.w = ctx->at<uint16_t>(L.lm);
   la.act = h;
   la.M = M;
-  la.K = c.hidden;
+  la.K = H;
   la.V = c.vocab;
   la.N = N;
   la.part = ctx->at<Top2>(L.lmpart);
@@ -496,7 +546,7 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
 
   ArgmaxArgs ma{};
   ma.part = la.part;
-  ma.n_wg = L.n_lm_wg;
+  ma.n_parts = c.vocab / 32;
   ma.M = M;
   ma.N = N;
   ma.V = c.vocab;

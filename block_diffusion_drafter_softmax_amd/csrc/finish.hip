@@ -1,0 +1,105 @@
+// Finishers of the split-k projections: add the k-split partial sums in split
+// order, apply RoPE to keys/queries (rotate-half pairs (j, j + d/2) at the
+// row's position, cos/sin from the set-up table), round to bf16 and write the
+// layout the consumer wants: the attention's query rows and block K/V, or the
+// paged context cache (keys slot-major, values dim-major).
+#include "common.h"
+
+namespace {
+DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+DEV float split_sum(const float* part, int ks, int M, int n_cols, int m, int col) {
+  float s = 0.f;
+  for (int k = 0; k < ks; ++k) s += part[((size_t)k * M + m) * n_cols + col];
+  return s;
+}
+
+DEV void rotate(float& x1, float& x2, const float* rope, int pos, int half, int j) {
+  if (rope == nullptr) return;
+  const float c = rope[((size_t)pos * half + j) * 2 + 0];
+  const float s = rope[((size_t)pos * half + j) * 2 + 1];
+  const float y1 = x1 * c - x2 * s;
+  const float y2 = x2 * c + x1 * s;
+  x1 = y1;
+  x2 = y2;
+}
+}  // namespace
+
+// One thread per (row, rotation pair of a query or block-key head) or per
+// (row, block-value element).
+__global__ __launch_bounds__(256) void qkv_finish_kernel(QkvFinishArgs a) {
+  const int d = a.d, half = d / 2;
+  const int pq = a.n_q * half, pk = a.n_kv * half, nv = a.n_kv * d;
+  const int per_row = pq + pk + nv;
+  const int n_cols = (a.n_q + 2 * a.n_kv) * d;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.M * per_row) return;
+  const int m = idx / per_row, j = idx % per_row;
+  const int b = m / a.N, n = m % a.N;
+  if (j < pq + pk) {
+    const bool isq = j < pq;
+    const int jj = isq ? j : j - pq;
+    const int head = jj / half, i = jj % half;
+    const int col = (isq ? 0 : a.n_q * d) + head * d + i;
+    float x1 = split_sum(a.part, a.ks, a.M, n_cols, m, col);
+    float x2 = split_sum(a.part, a.ks, a.M, n_cols, m, col + half);
+    rotate(x1, x2, a.rope, a.row_pos[m], half, i);
+    uint16_t* dst = isq ? a.q + ((size_t)m * a.n_q + head) * d
+                        : a.kblk + (((size_t)b * a.n_kv + head) * 16 + n) * d;
+    dst[i] = f2bf(x1);
+    dst[i + half] = f2bf(x2);
+  } else {
+    const int jj = j - pq - pk;
+    const int head = jj / d, dd = jj % d;
+    const float v = split_sum(a.part, a.ks, a.M, n_cols, m, (a.n_q + a.n_kv) * d + jj);
+    a.vblk[(((size_t)b * a.n_kv + head) * d + dd) * 16 + n] = f2bf(v);
+  }
+}
+
+extern "C" hipError_t dflash_launch_qkv_finish(const QkvFinishArgs* a, hipStream_t st) {
+  const int per_row = (a->n_q + a->n_kv) * (a->d / 2) + a->n_kv * a->d;
+  const int total = a->M * per_row;
+  hipLaunchKernelGGL(qkv_finish_kernel, dim3((total + 255) / 256), dim3(256), 0, st, *a);
+  return hipGetLastError();
+}
+
+// One thread per (appended row, layer, key rotation pair or value element).
+__global__ __launch_bounds__(256) void ctx_finish_kernel(CtxFinishArgs a) {
+  const int d = a.d, half = d / 2, kvd = a.n_kv * d;
+  const int pk = a.n_kv * half;
+  const int per_layer = pk + kvd;
+  const int per_row = a.D * per_layer;
+  const int n_cols = a.D * 2 * kvd;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.M * per_row) return;
+  const int m = idx / per_row, rem = idx % per_row;
+  const int pos = a.row_pos[m];
+  if (pos < 0) return;
+  const int layer = rem / per_layer, j = rem % per_layer;
+  const int seq = a.row_seq[m];
+  const int page = clampi(a.page_table[(size_t)seq * a.max_pages_per_seq + pos / 16], 0, a.n_pages - 1);
+  const int slot = pos % 16;
+  uint16_t* base = a.kv_pages + layer * a.layer_stride + (size_t)page * 2 * kvd * 16;
+  if (j < pk) {
+    const int head = j / half, i = j % half;
+    const int col = layer * 2 * kvd + head * d + i;
+    float x1 = split_sum(a.part, a.ks, a.M, n_cols, m, col);
+    float x2 = split_sum(a.part, a.ks, a.M, n_cols, m, col + half);
+    rotate(x1, x2, a.rope, pos, half, i);
+    uint16_t* dst = base + ((size_t)head * 16 + slot) * d;
+    dst[i] = f2bf(x1);
+    dst[i + half] = f2bf(x2);
+  } else {
+    const int jj = j - pk;
+    const int head = jj / d, dd = jj % d;
+    const float v = split_sum(a.part, a.ks, a.M, n_cols, m, layer * 2 * kvd + kvd + jj);
+    base[(size_t)kvd * 16 + ((size_t)head * d + dd) * 16 + slot] = f2bf(v);
+  }
+}
+
+extern "C" hipError_t dflash_launch_ctx_finish(const CtxFinishArgs* a, hipStream_t st) {
+  const int per_row = a->D * (a->n_kv * (a->d / 2) + a->n_kv * a->d);
+  const int total = a->M * per_row;
+  hipLaunchKernelGGL(ctx_finish_kernel, dim3((total + 255) / 256), dim3(256), 0, st, *a);
+  return hipGetLastError();
+}

@@ -1,5 +1,5 @@
 // Kernel argument structs and launchers shared by the HIP kernels and the
-// host library (plain data: no device code here).
+// host library (plain data; the one helper is usable on host and device).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -13,59 +13,76 @@ struct Top2 {
   float v2;
 };
 
-// ------------------------------------------------------------ GEMM args
-// Tile pairing of the two 16-row weight tiles a wave multiplies.
-enum PairMode : int {
-  PAIR_PLAIN = 0,  // rows 32p .. 32p+15 and 32p+16 .. 32p+31 of w0
-  PAIR_ROPE = 1,   // rows j and j + d_h/2 of one head (rotation partners)
-  PAIR_DUAL = 2,   // rows 16p .. 16p+15 of w0 and of w1 (gate, up)
+// MFMA-operand packed layout, used for every weight matrix the GEMMs stream
+// and for every activation they read. Element (r, k) of an [R][K] matrix
+// (R a multiple of 16 after padding, K a multiple of 32) lives at
+//   ((r/16 * K/32 + k/32) * 64 + lane) * 8 + k%8,  lane = r%16 + 16*((k%32)/8),
+// so the 16x32 operand block of one 16x16x32 MFMA is 1 KB of contiguous
+// memory in lane order and a wave loads it with one 16-byte load per lane.
+__host__ __device__ inline size_t pk_index(int r, int k, int K) {
+  const int lane = (r & 15) | (((k >> 3) & 3) << 4);
+  return (((size_t)(r >> 4) * (K >> 5) + (k >> 5)) * 64 + lane) * 8 + (k & 7);
+}
+__host__ __device__ inline int pad16(int m) { return (m + 15) & ~15; }
+
+// ------------------------------------------------------------ streaming GEMM
+enum WsMode : int {
+  WS_PARTIAL = 0,  // fp32 partial sums part[split][M][n_cols]
+  WS_SWIGLU = 1,   // silu(gate) * up -> bf16, packed activation of the next GEMM (K_next = n_cols)
 };
 
-enum Epilogue : int {
-  EPI_PARTIAL = 0,  // fp32 partial sums [split][M][n_out] (residual added by the next norm)
-  EPI_Q = 1,        // RoPE -> bf16 q [M][n_q*d_h]
-  EPI_KBLK = 2,     // RoPE -> bf16 block keys [B][n_kv][16][d_h]
-  EPI_VBLK = 3,     // bf16 block values, dim-major [B][n_kv][d_h][16]
-  EPI_SWIGLU = 4,   // bf16 silu(gate) * up [M][I]
-  EPI_CTX_K = 5,    // RoPE -> bf16 into the key part of the row's page slot
-  EPI_CTX_V = 6,    // bf16 into the value part of the row's page slot
+#define WS_MAX_SEG 16
+
+struct WsSeg {
+  const uint16_t* w0;   // packed weights [tiles][K/32][512]
+  const uint16_t* w1;   // WS_SWIGLU: packed up weights (w0 holds gate)
+  const uint16_t* act;  // packed activation [pad16(M)/16][K/32][512]
+  int units;            // work units (NT tiles of 16 rows each)
+  int col0;             // first output column of this segment
 };
 
-#define GEMM_MAX_SEG 16
-
-struct GemmSeg {
-  const uint16_t* w0;
-  const uint16_t* w1;
-  const uint16_t* act;  // [M][K] bf16
-  void* out;
-  int pairs;
-  int mode;
-  int epi;
-  int layer;
-};
-
-struct GemmArgs {
-  GemmSeg seg[GEMM_MAX_SEG];
-  int seg_start[GEMM_MAX_SEG + 1];
+struct WsArgs {
+  WsSeg seg[WS_MAX_SEG];
+  int unit_start[WS_MAX_SEG + 1];
   int nseg;
-  int K;          // reduction length (multiple of 32)
-  int M;          // activation rows
-  int ks;         // splits of K across workgroups
-  int n_out;      // output columns for EPI_PARTIAL
-  int head_dim;
-  int n_kv;
-  int block;      // N, rows per sequence in the draft
-  int max_pages_per_seq;
-  int n_pages;
-  int max_pos;
-  const int* row_pos;   // [M] position of each row, < 0: skip the row
-  const int* row_seq;   // [M] sequence id of each row
-  const int* page_table;
-  uint16_t* kv_pages;
-  long long layer_stride;  // elements per layer of kv_pages
-  const float* rope;       // [max_pos][d_h/2][2] (cos, sin)
+  int K;        // reduction length (multiple of 32)
+  int M;        // activation rows
+  int ks;       // k splits (one wave per (unit, split))
+  int n_cols;   // row length of the partial buffer / SwiGLU features
+  float* part;  // WS_PARTIAL: [ks][M][n_cols]
+  uint16_t* out;  // WS_SWIGLU: packed [pad16(M)/16][n_cols/32][512]
 };
 
+struct PackArgs {
+  const uint16_t* src;  // [R][K] row-major
+  uint16_t* dst;        // packed
+  int R, K;
+};
+
+// ------------------------------------------------------------ finishers
+struct QkvFinishArgs {
+  const float* part;  // [ks][M][n_q*d + 2*n_kv*d]: Q columns, then block K, then block V
+  int ks, M, n_q, n_kv, d, N;
+  const int* row_pos;
+  const float* rope;  // [max_pos][d/2][2] or null (no rotation)
+  uint16_t* q;        // [M][n_q][d]
+  uint16_t* kblk;     // [B][n_kv][16][d]
+  uint16_t* vblk;     // [B][n_kv][d][16]
+};
+
+struct CtxFinishArgs {
+  const float* part;  // [ks][M][D * 2 * n_kv*d]: per layer K columns then V columns
+  int ks, M, D, n_kv, d;
+  const int* row_pos;  // < 0: row skipped
+  const int* row_seq;
+  const int* page_table;
+  int max_pages_per_seq, n_pages;
+  const float* rope;
+  uint16_t* kv_pages;
+  long long layer_stride;
+};
+
+// ------------------------------------------------------------ attention
 struct AttnArgs {
   const uint16_t* q;       // [B*N][n_q][d]
   const uint16_t* kblk;    // [B][n_kv][16][d]
@@ -76,11 +93,13 @@ struct AttnArgs {
   const int* seq_ids;
   float* part_o;           // [B][n_kv][n_ck][R][d]
   float* part_ml;          // [B][n_kv][n_ck][R][2]
-  uint16_t* o;             // merge output [B*N][n_q*d]
+  uint16_t* o;             // merge output, packed activation [pad16(B*N)/16][n_q*d/32][512]
+  int32_t* err;
   int N, n_q, n_kv, chunk, n_ck, max_pages_per_seq, n_pages, max_seqs;
   float scale_log2;        // log2(e) / sqrt(d)
 };
 
+// ------------------------------------------------------------ small kernels
 struct PlanArgs {
   int B, rows_per_seq;  // max_new (append) or N (draft)
   const int* seq_ids;
@@ -99,7 +118,7 @@ struct FuseArgs {
   const uint16_t* hidden;  // [rows][T][H]
   const float* alpha;      // [D][T]
   const uint16_t* g_fuse;  // [D][H]
-  uint16_t* f;             // [D][rows][H]
+  uint16_t* f;             // per layer packed [pad16(rows)/16][H/32][512], layer stride pad16(rows)*H
   const int* row_pos;
   int rows, T, H, D;
   float eps;
@@ -114,23 +133,23 @@ struct NormArgs {
   const float* part;       // [ks][M][H]
   int ks;
   const uint16_t* g;       // gain [H]
-  uint16_t* h;             // [M][H] bf16 out
+  uint16_t* h;             // packed [pad16(M)/16][H/32][512] bf16 out
   float* dbg;              // nullable [M][H]
   int H, M;
   float eps;
 };
 
 struct LmArgs {
-  const uint16_t* w;    // [V][K]
-  const uint16_t* act;  // [M][K] normed rows
+  const uint16_t* w;    // packed [V/16][K/32][512]
+  const uint16_t* act;  // packed normed rows
   int M, K, V, N;       // N = block rows per sequence
-  Top2* part;           // [n_wg][M]
+  Top2* part;           // [V/32][M]
   float* dbg_logits;    // nullable [B][N-1][V]
 };
 
 struct ArgmaxArgs {
-  const Top2* part;  // [n_wg][M]
-  int n_wg, M, N, V;
+  const Top2* part;  // [n_parts][M]
+  int n_parts, M, N, V;
   int* draft;        // [B][N-1]
   float* gap;        // nullable [B][N-1]
   int32_t* err;
@@ -154,7 +173,10 @@ struct VerifyArgs {
 };
 
 extern "C" {
-hipError_t dflash_launch_gemm(const GemmArgs* args, int total_pairs, int kw, hipStream_t st);
+hipError_t dflash_launch_ws(const WsArgs* a, int mode, hipStream_t st);
+hipError_t dflash_launch_pack(const PackArgs* a, hipStream_t st);
+hipError_t dflash_launch_qkv_finish(const QkvFinishArgs* a, hipStream_t st);
+hipError_t dflash_launch_ctx_finish(const CtxFinishArgs* a, hipStream_t st);
 hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_t st);
 hipError_t dflash_launch_attn_merge(const AttnArgs* a, int B, int head_dim, hipStream_t st);
 hipError_t dflash_launch_plan(const PlanArgs* a, hipStream_t st);

@@ -1,110 +1,61 @@
 // LM head + argmax: z = y W_lm^T over the whole vocabulary, reduced on the fly
-// to a per-workgroup top-2 (value, lowest index) for every block row, so the
-// [rows, V] logits never go to memory (except as an optional debug copy).
-// Same streaming scheme as the projection GEMM: each wave owns 32 vocabulary
-// rows over the full hidden size, A operand from HBM, the normed rows as the
-// B operand. argmax_reduce_kernel then merges the per-workgroup top-2 of each
-// row; the merge is order independent, so the draft is deterministic.
-#include "common.h"
+// to a top-2 (value, lowest index) per block row for every 32 vocabulary
+// rows, so the [rows, V] logits never go to memory (except as an optional
+// debug copy). One wave per workgroup streams two packed 16-row tiles of
+// W_lm over the full hidden size with the pipelined loop of stream.h;
+// argmax_reduce_kernel then merges the V/32 partial top-2 of each row. The
+// merge is order independent, so the draft is deterministic.
 #include "dflash.h"
-
+#include "stream.h"
 
 template <int MT, int U>
-__global__ __launch_bounds__(256) void lmhead_kernel(LmArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g4 = (lane >> 4) * 4, r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int npairs = a.V / 32;
-  const int p = blockIdx.x * 4 + wave;
-  const bool live = p < npairs;
-  const int rowA = 32 * (live ? p : 0), rowB = rowA + 16;
-  const int K = a.K, steps = K / 32;
-  const uint16_t* pa = a.w + (size_t)(rowA + r16) * K + kq;
-  const uint16_t* pb = a.w + (size_t)(rowB + r16) * K + kq;
-  __shared__ Top2 red[4][16 * MT];
-
-  const int n_mg = (a.M + 16 * MT - 1) / (16 * MT);
-  for (int mg = 0; mg < n_mg; ++mg) {
-    const int m0 = mg * 16 * MT;
-    f32x4 accA[MT], accB[MT];
+__global__ __launch_bounds__(64) void lmhead_kernel(LmArgs a) {
+  const int lane = threadIdx.x;
+  const int g4 = (lane >> 4) * 4, r16 = lane & 15;
+  const int p = blockIdx.x;  // vocabulary rows 32p .. 32p+31
+  const int steps = a.K >> 5;
+  const uint16_t* pw[2] = {a.w + (size_t)(2 * p) * steps * 512 + lane * 8,
+                           a.w + (size_t)(2 * p + 1) * steps * 512 + lane * 8};
+  const int m_tiles = pad16(a.M) >> 4;
+  for (int mg = 0; mg < m_tiles; mg += MT) {
     const uint16_t* px[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      accA[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accB[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      int m = m0 + mt * 16 + r16;
-      m = m < a.M ? m : a.M - 1;
-      px[mt] = a.act + (size_t)m * K + kq;
-    }
-    if (live) {
-      int st = 0;
-      for (; st + U <= steps; st += U) {
-        bf16x8 fa[U], fb[U], fx[U][MT];
+    for (int mt = 0; mt < MT; ++mt) px[mt] = a.act + (size_t)min(mg + mt, m_tiles - 1) * steps * 512 + lane * 8;
+    f32x4 acc[2][MT];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          fa[u] = ld8(pa + (st + u) * 32);
-          fb[u] = ld8(pb + (st + u) * 32);
-        }
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) fx[u][mt] = ld8(px[mt] + (st + u) * 32);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            accA[mt] = mfma16(fa[u], fx[u][mt], accA[mt]);
-            accB[mt] = mfma16(fb[u], fx[u][mt], accB[mt]);
-          }
-      }
-      for (; st < steps; ++st) {
-        const bf16x8 fa = ld8(pa + st * 32), fb = ld8(pb + st * 32);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const bf16x8 fx = ld8(px[mt] + st * 32);
-          accA[mt] = mfma16(fa, fx, accA[mt]);
-          accB[mt] = mfma16(fb, fx, accB[mt]);
-        }
-      }
-    }
+      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_ksteps<2, MT, U>(pw, px, 0, steps, acc);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       Top2 t = top2_empty();
-      if (live) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t = top2_push(t, accA[mt][i], rowA + g4 + i);
+      for (int i = 0; i < 4; ++i) t = top2_push(t, acc[0][mt][i], 32 * p + g4 + i);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t = top2_push(t, accB[mt][i], rowB + g4 + i);
-      }
+      for (int i = 0; i < 4; ++i) t = top2_push(t, acc[1][mt][i], 32 * p + 16 + g4 + i);
       t = top2_shfl_xor(t, 16);
       t = top2_shfl_xor(t, 32);
-      if (lane < 16) red[wave][mt * 16 + lane] = t;
-      const int m = m0 + mt * 16 + r16;
-      if (a.dbg_logits && live && m < a.M && (m % a.N) != 0) {
+      const int m = (mg + mt) * 16 + r16;
+      if (mg + mt >= m_tiles || m >= a.M) continue;
+      if (lane < 16) a.part[(size_t)p * a.M + m] = t;
+      if (a.dbg_logits && (m % a.N) != 0) {
         float* dst = a.dbg_logits + ((size_t)(m / a.N) * (a.N - 1) + (m % a.N) - 1) * a.V;
-        *reinterpret_cast<f32x4*>(dst + rowA + g4) = accA[mt];
-        *reinterpret_cast<f32x4*>(dst + rowB + g4) = accB[mt];
+        *reinterpret_cast<f32x4*>(dst + 32 * p + g4) = acc[0][mt];
+        *reinterpret_cast<f32x4*>(dst + 32 * p + 16 + g4) = acc[1][mt];
       }
     }
-    __syncthreads();
-    if (threadIdx.x < 16 * MT) {
-      const int m = m0 + threadIdx.x;
-      Top2 t = red[0][threadIdx.x];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) t = top2_merge(t, red[w][threadIdx.x]);
-      if (m < a.M) a.part[(size_t)blockIdx.x * a.M + m] = t;
-    }
-    __syncthreads();
   }
 }
 
 extern "C" hipError_t dflash_launch_lmhead(const LmArgs* a, hipStream_t st) {
-  const int n_wg = (a->V / 32 + 3) / 4;
-  if (a->M <= 16) hipLaunchKernelGGL((lmhead_kernel<1, 8>), dim3(n_wg), dim3(256), 0, st, *a);
-  else if (a->M <= 32) hipLaunchKernelGGL((lmhead_kernel<2, 4>), dim3(n_wg), dim3(256), 0, st, *a);
-  else hipLaunchKernelGGL((lmhead_kernel<4, 4>), dim3(n_wg), dim3(256), 0, st, *a);
+  const dim3 grid(a->V / 32), block(64);
+  const int m_tiles = pad16(a->M) >> 4;
+  if (m_tiles <= 1) hipLaunchKernelGGL((lmhead_kernel<1, 4>), grid, block, 0, st, *a);
+  else if (m_tiles <= 2) hipLaunchKernelGGL((lmhead_kernel<2, 2>), grid, block, 0, st, *a);
+  else hipLaunchKernelGGL((lmhead_kernel<4, 2>), grid, block, 0, st, *a);
   return hipGetLastError();
 }
-
 
 // One workgroup per block row m (rows with m % N == 0 are the anchors and
 // produce nothing).
@@ -112,7 +63,7 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(ArgmaxArgs a) {
   const int m = blockIdx.x;
   if (m % a.N == 0) return;
   Top2 t = top2_empty();
-  for (int j = threadIdx.x; j < a.n_wg; j += 256) t = top2_merge(t, a.part[(size_t)j * a.M + m]);
+  for (int j = threadIdx.x; j < a.n_parts; j += 256) t = top2_merge(t, a.part[(size_t)j * a.M + m]);
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) t = top2_shfl_xor(t, o);
   __shared__ Top2 red[4];

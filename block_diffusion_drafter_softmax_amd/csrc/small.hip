@@ -36,14 +36,10 @@ __global__ void plan_kernel(PlanArgs a) {
       }
     }
   } else {
+    // context pages are validated by the attention kernel that reads them
     if (L + n > a.max_pos) bad |= DFLASH_DEV_NO_PAGES;
     const int anc = a.anchor[b];
     if (anc < 0 || anc >= a.vocab) bad |= DFLASH_DEV_BAD_TOKEN;
-    const int np = min((L + 15) / 16, a.max_pages_per_seq);
-    for (int p = 0; p < np; ++p) {
-      const int pg = a.page_table[(size_t)seq * a.max_pages_per_seq + p];
-      if (pg < 0 || pg >= a.n_pages) bad |= DFLASH_DEV_BAD_PAGE;
-    }
   }
   if (bad) set_error(a.err, bad);
   for (int t = 0; t < a.rows_per_seq; ++t) {
@@ -66,7 +62,8 @@ extern "C" hipError_t dflash_launch_plan(const PlanArgs* a, hipStream_t st) {
 #define FUSE_MAXV 8  // float4 groups per thread: H <= 256*4*8 = 8192
 
 // One workgroup per appended row: for each draft layer i,
-// s = sum_j alpha[i][j] * h_j (ascending j), f = s / sqrt(mean(s^2) + eps) * g.
+// s = sum_j alpha[i][j] * h_j (ascending j), f = s / sqrt(mean(s^2) + eps) * g,
+// written packed as the activation of the context K/V projection.
 __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
   const int m = blockIdx.x;
   if (a.row_pos[m] < 0) return;
@@ -95,7 +92,7 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
     }
     const float tot = block_sum(ss, red);
     const float rstd = 1.0f / sqrtf(tot / a.H + a.eps);
-    uint16_t* out = a.f + ((size_t)i * a.rows + m) * a.H;
+    uint16_t* out = a.f + (size_t)i * pad16(a.rows) * a.H;
     const uint16_t* g = a.g_fuse + (size_t)i * a.H;
 #pragma unroll
     for (int v = 0; v < FUSE_MAXV; ++v) {
@@ -105,7 +102,7 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
       u16x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = f2bf(s[v][e] * rstd * bf2f(gv[e]));
-      *reinterpret_cast<u16x4*>(out + k) = o;
+      *reinterpret_cast<u16x4*>(out + pk_index(m, k, a.H)) = o;
     }
   }
 }
@@ -121,7 +118,8 @@ extern "C" hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st) {
 
 // One workgroup per row: build the residual row (embedding gather, or
 // x + the k-split partials of the last projection, summed in split order),
-// then h = x / sqrt(mean(x^2) + eps) * g in bf16.
+// then h = x / sqrt(mean(x^2) + eps) * g in bf16, written in the packed
+// activation layout the next projection streams.
 __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
   const int m = blockIdx.x;
   __shared__ float red[16];
@@ -164,7 +162,7 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
     u16x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = f2bf(xv[v][i] * rstd * bf2f(gv[i]));
-    *reinterpret_cast<u16x4*>(a.h + (size_t)m * a.H + k) = o;
+    *reinterpret_cast<u16x4*>(a.h + pk_index(m, k, a.H)) = o;
   }
 }
 

@@ -63,6 +63,30 @@ DEV float2 ms_merge(float2 x, float2 y) {
 }
 }  // namespace
 
+namespace {
+// Eight consecutive logits k .. k+7 (k % 8 == 0) as fp32.
+DEV void load8(const VerifyArgs& a, size_t i, float (&z)[8]) {
+  if (a.dtype == DFLASH_DTYPE_F32) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>((const float*)a.logits + i);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>((const float*)a.logits + i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      z[e] = lo[e];
+      z[4 + e] = hi[e];
+    }
+  } else {
+    const u32x4 v = *reinterpret_cast<const u32x4*>((const uint16_t*)a.logits + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      z[2 * e] = __uint_as_float(v[e] << 16);
+      z[2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+    }
+  }
+}
+}  // namespace
+
+// Work item = (vocabulary chunk, block row, sequence); chunk % 8 == 0 and
+// V % 8 == 0, so every thread reads whole 8-logit groups.
 __global__ __launch_bounds__(256) void verify_rows_kernel(VerifyArgs a) {
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const size_t row_off = ((size_t)b * a.N + r) * a.V;
@@ -70,10 +94,17 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(VerifyArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float2 red[4];
   __shared__ int last;
-  float2 res;
+  __shared__ float2 rowres[32];
+  __shared__ float prob[32], unif[32];
+  float2 res = make_float2(0.f, 0.f);
   if (!a.temp1) {
     ArgMax t{-INFINITY, 0x7FFFFFFF};
-    for (int k = k0 + threadIdx.x; k < k1; k += 256) t = am_merge(t, ArgMax{load_logit(a, row_off + k), k});
+    for (int k = k0 + threadIdx.x * 8; k < k1; k += 256 * 8) {
+      float z[8];
+      load8(a, row_off + k, z);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t = am_merge(t, ArgMax{z[e], k + e});
+    }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) t = am_shfl(t, o);
     if (lane == 0) red[wave] = make_float2(t.v, __int_as_float(t.i));
@@ -85,16 +116,32 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(VerifyArgs a) {
     }
   } else {
     float m = -INFINITY;
-    for (int k = k0 + threadIdx.x; k < k1; k += 256) m = fmaxf(m, load_logit(a, row_off + k));
+    float zs[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // chunk <= 256 * 8 * 4
+      const int k = k0 + (threadIdx.x + 256 * j) * 8;
+      if (k < k1) {
+        load8(a, row_off + k, zs[j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, zs[j][e]);
+      }
+    }
     m = wave_max(m);
     if (lane == 0) red[wave].x = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0].x, red[1].x), fmaxf(red[2].x, red[3].x));
-    float s = 0.f;
-    for (int k = k0 + threadIdx.x; k < k1; k += 256) s += __expf(load_logit(a, row_off + k) - m);
-    s = wave_sum(s);
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = k0 + (threadIdx.x + 256 * j) * 8;
+      if (k < k1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += __expf(zs[j][e] - m);
+      }
+    }
+    sum = wave_sum(sum);
     __syncthreads();
-    if (lane == 0) red[wave].y = s;
+    if (lane == 0) red[wave].y = sum;
     __syncthreads();
     if (threadIdx.x == 0) res = make_float2(m, red[0].y + red[1].y + red[2].y + red[3].y);
   }
@@ -107,43 +154,46 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(VerifyArgs a) {
   __syncthreads();
   if (!last) return;
   __threadfence();
-  if (threadIdx.x != 0) return;
-  a.counters[b] = 0;
 
+  // Last workgroup of this sequence: thread `row` merges that row's chunks
+  // (chunk order), then thread 0 runs the accept scan.
   const int seq = a.seq_ids[b];
   const int* d = a.draft + (size_t)b * (a.N - 1);
-  int acc = 0;
-  if (!a.temp1) {
-    int t_a = 0;
-    for (int row = 0; row < a.N; ++row) {
+  const int row = threadIdx.x;
+  if (row < a.N) {
+    if (!a.temp1) {
       ArgMax u{-INFINITY, 0x7FFFFFFF};
       for (int cc = 0; cc < a.n_chunks; ++cc) {
         const float2 p = *reinterpret_cast<const float2*>(a.part + ((((size_t)b * a.N + row) * a.n_chunks + cc) * 2));
         u = am_merge(u, ArgMax{p.x, __float_as_int(p.y)});
       }
-      t_a = u.i;
-      if (row == a.N - 1 || d[row] != u.i) break;
-      ++acc;
-    }
-    a.accept_len[b] = acc;
-    a.next_token[b] = t_a;
-    if (a.commit_len) a.commit_len[b] = acc + 1;
-  } else {
-    while (acc < a.N - 1) {
+      rowres[row] = make_float2(u.v, __int_as_float(u.i));
+    } else if (row < a.N - 1) {
       float2 ms = make_float2(-INFINITY, 0.f);
       for (int cc = 0; cc < a.n_chunks; ++cc)
-        ms = ms_merge(ms, *reinterpret_cast<const float2*>(a.part + ((((size_t)b * a.N + acc) * a.n_chunks + cc) * 2)));
+        ms = ms_merge(ms, *reinterpret_cast<const float2*>(a.part + ((((size_t)b * a.N + row) * a.n_chunks + cc) * 2)));
       const float lse = ms.x + __logf(ms.y);
-      int tok = d[acc];
+      int tok = d[row];
       if (tok < 0 || tok >= a.V) {
         set_error(a.err, DFLASH_DEV_BAD_TOKEN);
         tok = clampi(tok, 0, a.V - 1);
       }
-      const float p = expf(load_logit(a, ((size_t)b * a.N + acc) * a.V + tok) - lse);
-      const float u = (float)(rng_word(a, seq, acc, 0, 0) >> 40) * 5.9604644775390625e-08f;
-      if (u < p) ++acc;
-      else break;
+      float zt = load_logit(a, ((size_t)b * a.N + row) * a.V + tok);
+      prob[row] = expf(zt - lse);
+      unif[row] = (float)(rng_word(a, seq, row, 0, 0) >> 40) * 5.9604644775390625e-08f;
     }
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  a.counters[b] = 0;
+  int acc = 0;
+  if (!a.temp1) {
+    while (acc < a.N - 1 && d[acc] == __float_as_int(rowres[acc].y)) ++acc;
+    a.accept_len[b] = acc;
+    a.next_token[b] = __float_as_int(rowres[acc].y);
+    if (a.commit_len) a.commit_len[b] = acc + 1;
+  } else {
+    while (acc < a.N - 1 && unif[acc] < prob[acc]) ++acc;
     a.accept_len[b] = acc;
     if (a.commit_len) a.commit_len[b] = acc + 1;
     a.state[2 * b + 0] = acc;

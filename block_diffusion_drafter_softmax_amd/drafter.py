@@ -95,6 +95,9 @@ class Drafter:
         rc, h = B.dflash_create(c, wt, kv, self.workspace.data_ptr(), ws)
         B.check(rc, "dflash_create")
         self.handle = h
+        # the library keeps its own packed copies of the streamed matrices
+        for k in ("wq", "wk_d", "wv_d", "wk_t", "wv_t", "wo", "wg", "wu", "wd", "lm_head"):
+            self.w.pop(k, None)
 
     # ---------------------------------------------------------------- calls
     def ctx_append(self, seq_ids, n_new, hidden, max_new=None, stream=None):

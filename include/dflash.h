@@ -102,7 +102,11 @@ typedef struct dflash_config {
  *   wo [D, H, n_q*d_h]          wg, wu [D, I, H]             wd [D, H, I]
  *   embed, lm_head [V, H]       g_fuse, g_attn, g_mlp [D, H] g_final [H]
  *   w_fuse [D, T] fp32: alpha^(i) = softmax(w_fuse[i, :])    [DFLARE 2.1]
- * The memory must stay valid and unchanged until dflash_destroy. */
+ * dflash_create copies every projection matrix and lm_head into the
+ * workspace in the layout the kernels stream (16x32 MFMA operand blocks, 1 KB
+ * contiguous each); after it returns only embed, the gains and w_fuse are
+ * read again and must stay valid and unchanged until dflash_destroy; the
+ * other weight buffers may be freed. */
 typedef struct dflash_weights {
   const float* w_fuse;
   const uint16_t *g_fuse, *g_attn, *g_mlp, *g_final;
@@ -134,7 +138,8 @@ size_t dflash_workspace_bytes(const dflash_config* cfg);
 
 /* Validate shapes, compute alpha = softmax(w_fuse) rows [DFLARE 2.1] and the
  * RoPE cos/sin table (float64 angles rounded to fp32) on the host, copy them
- * into the workspace and clear its counters (synchronous, null stream).
+ * into the workspace, pack the streamed weights into it and clear its
+ * counters (synchronous, null stream; the weights must be ready).
  * workspace: device memory of at least dflash_workspace_bytes(cfg) bytes,
  * owned by the caller, exclusively used by this handle until destroy. */
 int dflash_create(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv,
@@ -197,9 +202,9 @@ int dflash_read_error(dflash_ctx* ctx, hipStream_t stream, int32_t* out);
  * every launch of one kernel kind. Off by default; switching it on costs
  * two event records per launch of that kind. */
 #define DFLASH_K_FUSE 0      /* append: layer fusion + RMSNorm */
-#define DFLASH_K_CTX_KV 1    /* append: context K/V projection + RoPE + page scatter */
+#define DFLASH_K_CTX_KV 1    /* append: context K/V projection (split-k partials) */
 #define DFLASH_K_NORM 2      /* embedding / residual reduce + RMSNorm */
-#define DFLASH_K_QKV 3       /* block Q/K/V projection + RoPE */
+#define DFLASH_K_QKV 3       /* block Q/K/V projection (split-k partials) */
 #define DFLASH_K_ATTN 4      /* split-context block attention */
 #define DFLASH_K_ATTN_MERGE 5
 #define DFLASH_K_OPROJ 6
@@ -209,7 +214,9 @@ int dflash_read_error(dflash_ctx* ctx, hipStream_t stream, int32_t* out);
 #define DFLASH_K_ARGMAX 10
 #define DFLASH_K_VERIFY 11
 #define DFLASH_K_PLAN 12
-#define DFLASH_K_COUNT 13
+#define DFLASH_K_QKV_FINISH 13 /* split-k sum + RoPE + layout of Q and block K/V */
+#define DFLASH_K_CTX_FINISH 14 /* split-k sum + RoPE + page scatter of context K/V */
+#define DFLASH_K_COUNT 15
 
 /* Start (enable != 0) or stop timing kernel kind `kind`; starting clears
  * the totals. Capacity: 4096 launches between reads. */
