@@ -25,7 +25,7 @@ constexpr int CH = 128;  // context keys per work item
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(1024) void attn_chunk_kernel(AttnArgs a) {
+__global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs a) {
   constexpr int KP = D + 8;          // padded LDS row of one key (bf16 elements)
   constexpr int PAGES = CH / 16;
   __shared__ uint16_t k_lds[CH * KP];
@@ -62,24 +62,37 @@ __global__ __launch_bounds__(1024) void attn_chunk_kernel(AttnArgs a) {
 
   // Stage K (slot-major rows) and V (dim-major) of the chunk's pages in LDS:
   // per page, 2*D*16 bf16 = 4*D 16-byte units (K units first, then V units).
+  // Batches of 8 loads per thread, all in flight before the LDS stores: unit
+  // indices are clamped (a clamped duplicate loads valid memory and is not
+  // stored), so no branch separates the loads.
   constexpr int UNITS_PER_PAGE = 4 * D;
-  for (int uidx = tid; uidx < np * UNITS_PER_PAGE; uidx += nthreads) {
-    const int p = uidx / UNITS_PER_PAGE, w = uidx % UNITS_PER_PAGE;
-    const uint16_t *kb, *vb;
-    if (c == 0) {
-      kb = a.kblk + ((size_t)b * a.n_kv + kvh) * 16 * D;
-      vb = a.vblk + ((size_t)b * a.n_kv + kvh) * D * 16;
-    } else {
-      kb = a.pages + pg[p] * page_elems + (size_t)kvh * 16 * D;
-      vb = kb + (size_t)a.n_kv * 16 * D;
+  const int total_units = np * UNITS_PER_PAGE;
+  const uint16_t* blk_k = a.kblk + ((size_t)b * a.n_kv + kvh) * 16 * D;
+  const uint16_t* blk_v = a.vblk + ((size_t)b * a.n_kv + kvh) * D * 16;
+  for (int base = 0; base < total_units; base += 8 * nthreads) {
+    int uu[8], pgv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) uu[j] = min(base + j * nthreads + tid, total_units - 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pgv[j] = pg[uu[j] / UNITS_PER_PAGE];
+    u32x4 buf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = uu[j] / UNITS_PER_PAGE, w = uu[j] % UNITS_PER_PAGE;
+      const uint16_t* kb = (c == 0) ? blk_k : a.pages + pgv[j] * page_elems + (size_t)kvh * 16 * D;
+      const uint16_t* vb = (c == 0) ? blk_v : kb + (size_t)a.n_kv * 16 * D;
+      const uint16_t* src = (w < 2 * D) ? kb + (w / (D / 8)) * D + (w % (D / 8)) * 8 : vb + (w - 2 * D) * 8;
+      buf[j] = *reinterpret_cast<const u32x4*>(src);
     }
-    if (w < 2 * D) {  // K: 16 slots x D, 8 elements per unit
-      const int slot = w / (D / 8), col = (w % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&k_lds[(p * 16 + slot) * KP + col]) =
-          *reinterpret_cast<const u32x4*>(kb + slot * D + col);
-    } else {
-      const int w2 = w - 2 * D;
-      *reinterpret_cast<u32x4*>(&v_lds[p * D * 16 + w2 * 8]) = *reinterpret_cast<const u32x4*>(vb + w2 * 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (base + j * nthreads + tid >= total_units) continue;
+      const int p = uu[j] / UNITS_PER_PAGE, w = uu[j] % UNITS_PER_PAGE;
+      if (w < 2 * D) {  // K: 16 slots x D, 8 elements per unit
+        *reinterpret_cast<u32x4*>(&k_lds[(p * 16 + w / (D / 8)) * KP + (w % (D / 8)) * 8]) = buf[j];
+      } else {
+        *reinterpret_cast<u32x4*>(&v_lds[p * D * 16 + (w - 2 * D) * 8]) = buf[j];
+      }
     }
   }
   __syncthreads();
@@ -171,7 +184,7 @@ __global__ __launch_bounds__(1024) void attn_chunk_kernel(AttnArgs a) {
 // log-sum-exp merge of the chunk partials in chunk order, normalise, round
 // to bf16 and write the O-projection's packed activation.
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int B) {
+__global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs a, int B) {
   const int G = a.n_q / a.n_kv, R = G * a.N;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   const int dq = idx % (D / 4);
@@ -185,16 +198,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int B) {
   const size_t unit0 = ((size_t)b * a.n_kv + kvh) * a.n_ck;
   float M = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int c = 0; c < nc; ++c) {
-    const size_t row = (unit0 + c) * R + r;
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + row * 2);
-    const f32x4 o = *reinterpret_cast<const f32x4*>(a.part_o + row * D + dq * 4);
-    const float Mn = fmaxf(M, ml.x);
-    const float wo = exp2f(M - Mn), wn = exp2f(ml.x - Mn);
-    den = den * wo + ml.y * wn;
-    num = num * wo + o * wn;
-    M = Mn;
+  constexpr int GRP = 16;  // chunks whose loads are in flight together
+  for (int c0 = 0; c0 < nc; c0 += GRP) {
+    float2 ml[GRP];
+    f32x4 ov[GRP];
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      const size_t row = (unit0 + min(c0 + j, nc - 1)) * R + r;
+      ml[j] = *reinterpret_cast<const float2*>(a.part_ml + row * 2);
+      ov[j] = *reinterpret_cast<const f32x4*>(a.part_o + row * D + dq * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      if (c0 + j >= nc) break;
+      const float Mn = fmaxf(M, ml[j].x);
+      const float wo = exp2f(M - Mn), wn = exp2f(ml[j].x - Mn);
+      den = den * wo + ml[j].y * wn;
+      num = num * wo + ov[j] * wn;
+      M = Mn;
+    }
   }
   const float inv = 1.0f / den;
   const int hq = kvh * G + r / a.N, n = r % a.N;

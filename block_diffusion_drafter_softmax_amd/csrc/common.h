@@ -13,6 +13,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define DEV __device__ __forceinline__
 
+// Kernels with small grids whose time is memory latency: let the scheduler
+// use up to 128 VGPRs (<= 4 waves per SIMD) so that independent loads are all
+// issued before the first wait, instead of serialising them to reach an
+// occupancy these grids never use.
+#define LATENCY_BOUND __attribute__((amdgpu_waves_per_eu(1, 4)))
+
 // bf16 bits -> fp32 (exact).
 DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
@@ -65,6 +71,35 @@ DEV float block_sum(float v, float* lds /* >= 16 floats */) {
 }
 
 DEV void set_error(int32_t* err, int bits) { atomicOr(err, bits); }
+
+// Largest k split a streaming GEMM uses; reducers unroll over it.
+#define KS_MAX 16
+
+// Sum of the ks split partials part[k*stride + off], k = 0..ks-1, in k
+// order. All loads are issued before the first add, so the reduction costs
+// one memory latency instead of ks.
+DEV float split_sum1(const float* part, int ks, size_t stride, size_t off) {
+  float v[KS_MAX];
+#pragma unroll
+  for (int k = 0; k < KS_MAX; ++k) v[k] = k < ks ? part[k * stride + off] : 0.f;
+  float s = v[0];
+#pragma unroll
+  for (int k = 1; k < KS_MAX; ++k)
+    if (k < ks) s += v[k];
+  return s;
+}
+
+DEV f32x4 split_sum4(const float* part, int ks, size_t stride, size_t off) {
+  f32x4 v[KS_MAX];
+#pragma unroll
+  for (int k = 0; k < KS_MAX; ++k)
+    v[k] = k < ks ? *reinterpret_cast<const f32x4*>(part + k * stride + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 s = v[0];
+#pragma unroll
+  for (int k = 1; k < KS_MAX; ++k)
+    if (k < ks) s += v[k];
+  return s;
+}
 
 
 DEV Top2 top2_empty() { return {-INFINITY, 0x7FFFFFFF, -INFINITY}; }

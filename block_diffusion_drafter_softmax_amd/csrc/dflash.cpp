@@ -122,6 +122,8 @@ int check_config(const dflash_config* c) {
   if (c->intermediate % 32) return fail(DFLASH_ERR_UNSUPPORTED, "intermediate must be a multiple of 32");
   if (c->vocab % 32) return fail(DFLASH_ERR_UNSUPPORTED, "vocab must be a multiple of 32");
   if (c->n_q_heads % c->n_kv_heads) return fail(DFLASH_ERR_INVALID_ARG, "n_q_heads must be a multiple of n_kv_heads");
+  if (c->n_target_layers > 16) return fail(DFLASH_ERR_UNSUPPORTED, "n_target_layers must be <= 16");
+  if (c->n_layers > 64) return fail(DFLASH_ERR_UNSUPPORTED, "n_layers must be <= 64");
   if (c->block_size < 2 || c->block_size > 16) return fail(DFLASH_ERR_UNSUPPORTED, "block_size must be in [2, 16]");
   const int R = (c->n_q_heads / c->n_kv_heads) * c->block_size;
   if (R % 16 || R > 256)
@@ -401,25 +403,6 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
   int rc;
 
-  PlanArgs pa{};
-  pa.B = B;
-  pa.rows_per_seq = N;
-  pa.seq_ids = seq_ids;
-  pa.anchor = anchor;
-  pa.ctx_len = ctx->kv.ctx_len;
-  pa.page_table = ctx->kv.page_table;
-  pa.max_seqs = c.max_seqs;
-  pa.max_pages_per_seq = c.max_pages_per_seq;
-  pa.n_pages = c.n_pages;
-  pa.max_pos = c.max_pos;
-  pa.max_new = c.max_new;
-  pa.vocab = c.vocab;
-  pa.row_pos = ctx->at<int>(L.rowpos_d);
-  pa.row_seq = ctx->at<int>(L.rowseq_d);
-  pa.err = ctx->kv.error_word;
-  pa.append = 0;
-  if ((rc = ctx->launch(DFLASH_K_PLAN, stream, [&] { return dflash_launch_plan(&pa, stream); }))) return rc;
-
   float* x = ctx->at<float>(L.x);
   uint16_t* h = ctx->at<uint16_t>(L.h);
   float* gpart = ctx->at<float>(L.gpart);
@@ -437,6 +420,11 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   na.g = ctx->w.g_attn;
   na.h = h;
   na.dbg = dbg_hidden;
+  na.seq_ids = seq_ids;
+  na.ctx_len = ctx->kv.ctx_len;
+  na.max_seqs = c.max_seqs;
+  na.max_pos = c.max_pos;
+  na.err = ctx->kv.error_word;
   na.H = H;
   na.M = M;
   na.eps = c.rms_eps;
@@ -449,7 +437,10 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   qa.n_kv = c.n_kv_heads;
   qa.d = c.head_dim;
   qa.N = N;
-  qa.row_pos = pa.row_pos;
+  qa.seq_ids = seq_ids;
+  qa.ctx_len = ctx->kv.ctx_len;
+  qa.max_seqs = c.max_seqs;
+  qa.max_pos = c.max_pos;
   qa.rope = c.use_rope ? ctx->at<float>(L.rope) : nullptr;
   qa.q = ctx->at<uint16_t>(L.q);
   qa.kblk = ctx->at<uint16_t>(L.kblk);

@@ -9,9 +9,7 @@ namespace {
 DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 DEV float split_sum(const float* part, int ks, int M, int n_cols, int m, int col) {
-  float s = 0.f;
-  for (int k = 0; k < ks; ++k) s += part[((size_t)k * M + m) * n_cols + col];
-  return s;
+  return split_sum1(part, ks, (size_t)M * n_cols, (size_t)m * n_cols + col);
 }
 
 DEV void rotate(float& x1, float& x2, const float* rope, int pos, int half, int j) {
@@ -27,7 +25,7 @@ DEV void rotate(float& x1, float& x2, const float* rope, int pos, int half, int 
 
 // One thread per (row, rotation pair of a query or block-key head) or per
 // (row, block-value element).
-__global__ __launch_bounds__(256) void qkv_finish_kernel(QkvFinishArgs a) {
+__global__ __launch_bounds__(256) LATENCY_BOUND void qkv_finish_kernel(QkvFinishArgs a) {
   const int d = a.d, half = d / 2;
   const int pq = a.n_q * half, pk = a.n_kv * half, nv = a.n_kv * d;
   const int per_row = pq + pk + nv;
@@ -43,7 +41,8 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(QkvFinishArgs a) {
     const int col = (isq ? 0 : a.n_q * d) + head * d + i;
     float x1 = split_sum(a.part, a.ks, a.M, n_cols, m, col);
     float x2 = split_sum(a.part, a.ks, a.M, n_cols, m, col + half);
-    rotate(x1, x2, a.rope, a.row_pos[m], half, i);
+    rotate(x1, x2, a.rope, clampi(a.ctx_len[clampi(a.seq_ids[b], 0, a.max_seqs - 1)] + n, 0, a.max_pos - 1),
+           half, i);
     uint16_t* dst = isq ? a.q + ((size_t)m * a.n_q + head) * d
                         : a.kblk + (((size_t)b * a.n_kv + head) * 16 + n) * d;
     dst[i] = f2bf(x1);
@@ -64,7 +63,7 @@ extern "C" hipError_t dflash_launch_qkv_finish(const QkvFinishArgs* a, hipStream
 }
 
 // One thread per (appended row, layer, key rotation pair or value element).
-__global__ __launch_bounds__(256) void ctx_finish_kernel(CtxFinishArgs a) {
+__global__ __launch_bounds__(256) LATENCY_BOUND void ctx_finish_kernel(CtxFinishArgs a) {
   const int d = a.d, half = d / 2, kvd = a.n_kv * d;
   const int pk = a.n_kv * half;
   const int per_layer = pk + kvd;

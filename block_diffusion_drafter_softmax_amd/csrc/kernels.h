@@ -63,7 +63,9 @@ struct PackArgs {
 struct QkvFinishArgs {
   const float* part;  // [ks][M][n_q*d + 2*n_kv*d]: Q columns, then block K, then block V
   int ks, M, n_q, n_kv, d, N;
-  const int* row_pos;
+  const int* seq_ids;  // row m = b*N + n sits at position ctx_len[seq_ids[b]] + n
+  const int* ctx_len;
+  int max_seqs, max_pos;
   const float* rope;  // [max_pos][d/2][2] or null (no rotation)
   uint16_t* q;        // [M][n_q][d]
   uint16_t* kblk;     // [B][n_kv][16][d]
@@ -129,6 +131,10 @@ struct NormArgs {
   const uint16_t* embed;   // [V][H]
   const int* anchor;       // [B]
   int mask_id, N, V;
+  const int* seq_ids;      // mode 0: checks of the draft call (error word)
+  const int* ctx_len;
+  int max_seqs, max_pos;
+  int32_t* err;
   float* x;                // [M][H] residual stream (fp32)
   const float* part;       // [ks][M][H]
   int ks;

@@ -59,11 +59,20 @@ extern "C" hipError_t dflash_launch_lmhead(const LmArgs* a, hipStream_t st) {
 
 // One workgroup per block row m (rows with m % N == 0 are the anchors and
 // produce nothing).
-__global__ __launch_bounds__(256) void argmax_reduce_kernel(ArgmaxArgs a) {
+__global__ __launch_bounds__(256) LATENCY_BOUND void argmax_reduce_kernel(ArgmaxArgs a) {
   const int m = blockIdx.x;
   if (m % a.N == 0) return;
   Top2 t = top2_empty();
-  for (int j = threadIdx.x; j < a.n_parts; j += 256) t = top2_merge(t, a.part[(size_t)j * a.M + m]);
+  for (int j0 = 0; j0 < a.n_parts; j0 += 256 * 8) {  // 8 loads in flight per thread
+    Top2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * 256 + threadIdx.x;
+      v[u] = j < a.n_parts ? a.part[(size_t)j * a.M + m] : top2_empty();
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t = top2_merge(t, v[u]);
+  }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) t = top2_shfl_xor(t, o);
   __shared__ Top2 red[4];

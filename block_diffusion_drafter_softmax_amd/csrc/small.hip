@@ -1,6 +1,8 @@
 // Small per-row kernels: call planning (positions, bounds checks), DFLARE
 // layer fusion + RMSNorm, and the residual/embedding + RMSNorm producer of
 // every GEMM input.
+#include <algorithm>
+
 #include "common.h"
 #include "dflash.h"
 
@@ -13,7 +15,7 @@ DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); 
 // ctx_len .. ctx_len+n_new-1 and ctx_len advances; a failed check leaves the
 // sequence untouched and all its rows skipped. Draft: rows get positions
 // L .. L+N-1; checks only flag (positions are clamped into the tables).
-__global__ void plan_kernel(PlanArgs a) {
+__global__ LATENCY_BOUND void plan_kernel(PlanArgs a) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= a.B) return;
   int bad = 0;
@@ -59,30 +61,51 @@ extern "C" hipError_t dflash_launch_plan(const PlanArgs* a, hipStream_t st) {
 
 // ------------------------------------------------------------ fusion
 
-#define FUSE_MAXV 8  // float4 groups per thread: H <= 256*4*8 = 8192
+#define FUSE_MAXV 2   // float4 groups per thread: H <= 1024 * 4 * 2
+#define FUSE_TMAX 16  // target layers held in registers
+#define FUSE_DMAX 64  // draft layers whose fusion weights fit the LDS table
 
-// One workgroup per appended row: for each draft layer i,
+// One workgroup per appended row, one float4 group of the row per thread.
+// The row's T target states are loaded once into registers (every load in
+// flight together); then for each draft layer i:
 // s = sum_j alpha[i][j] * h_j (ascending j), f = s / sqrt(mean(s^2) + eps) * g,
 // written packed as the activation of the context K/V projection.
-__global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
+__global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
   const int m = blockIdx.x;
   if (a.row_pos[m] < 0) return;
   __shared__ float red[16];
+  __shared__ float alpha[FUSE_DMAX * FUSE_TMAX];
+  for (int i = threadIdx.x; i < a.D * a.T; i += blockDim.x) alpha[i] = a.alpha[i];
   const uint16_t* h = a.hidden + (size_t)m * a.T * a.H;
-  const int nv = (a.H / 4 + 255) / 256;
+  const int nv = (a.H / 4 + blockDim.x - 1) / blockDim.x;
+  // Unconditional loads from clamped addresses (values past T or H are never
+  // used), so that no branch separates them and all are issued together.
+  u16x4 hv[FUSE_MAXV][FUSE_TMAX];
+#pragma unroll
+  for (int v = 0; v < FUSE_MAXV; ++v) {
+    const int k = min((v * (int)blockDim.x + (int)threadIdx.x) * 4, a.H - 4);
+#pragma unroll
+    for (int j = 0; j < FUSE_TMAX; ++j)
+      hv[v][j] = *reinterpret_cast<const u16x4*>(h + (size_t)min(j, a.T - 1) * a.H + k);
+  }
+  __syncthreads();  // alpha table staged
   for (int i = 0; i < a.D; ++i) {
     float s[FUSE_MAXV][4];
     float ss = 0.f;
 #pragma unroll
     for (int v = 0; v < FUSE_MAXV; ++v) {
-      const int k = (v * 256 + threadIdx.x) * 4;
-      if (v >= nv || k >= a.H) continue;
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < a.T; ++j) {
-        const float al = a.alpha[i * a.T + j];
-        const u16x4 x = *reinterpret_cast<const u16x4*>(h + (size_t)j * a.H + k);
+      if (v >= nv || (v * (int)blockDim.x + (int)threadIdx.x) * 4 >= a.H) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += al * bf2f(x[e]);
+        for (int e = 0; e < 4; ++e) s[v][e] = 0.f;
+        continue;
+      }
+#pragma unroll
+      for (int j = 0; j < FUSE_TMAX; ++j) {
+        if (j >= a.T) break;
+        const float al = alpha[i * a.T + j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += al * bf2f(hv[v][j][e]);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -96,7 +119,7 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
     const uint16_t* g = a.g_fuse + (size_t)i * a.H;
 #pragma unroll
     for (int v = 0; v < FUSE_MAXV; ++v) {
-      const int k = (v * 256 + threadIdx.x) * 4;
+      const int k = (v * blockDim.x + threadIdx.x) * 4;
       if (v >= nv || k >= a.H) continue;
       const u16x4 gv = *reinterpret_cast<const u16x4*>(g + k);
       u16x4 o;
@@ -108,32 +131,46 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
 }
 
 extern "C" hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st) {
-  hipLaunchKernelGGL(fuse_kernel, dim3(a->rows), dim3(256), 0, st, *a);
+  const int threads = std::min(1024, ((a->H / 4 + 63) / 64) * 64);
+  hipLaunchKernelGGL(fuse_kernel, dim3(a->rows), dim3(threads), 0, st, *a);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------- norm
 
-#define NORM_MAXV 8
+#define NORM_MAXV 2  // float4 groups per thread: H <= 1024 * 4 * 2
 
-// One workgroup per row: build the residual row (embedding gather, or
-// x + the k-split partials of the last projection, summed in split order),
-// then h = x / sqrt(mean(x^2) + eps) * g in bf16, written in the packed
-// activation layout the next projection streams.
-__global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
+// One workgroup per row, one float4 of the row per thread: build the
+// residual row (embedding gather, or x + the k-split partials of the last
+// projection, summed in split order), then h = x / sqrt(mean(x^2) + eps) * g
+// in bf16, written in the packed activation layout the next projection
+// streams. Mode 0 (first kernel of a draft call) also checks the call's
+// sequence ids, anchors and position capacity.
+__global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
   const int m = blockIdx.x;
   __shared__ float red[16];
-  const int nv = (a.H / 4 + 255) / 256;
+  const int nv = (a.H / 4 + blockDim.x - 1) / blockDim.x;
   float xv[NORM_MAXV][4];
   float ss = 0.f;
   int tok = 0;
   if (a.mode == 0) {
-    tok = (m % a.N == 0) ? a.anchor[m / a.N] : a.mask_id;
+    const int b = m / a.N;
+    tok = (m % a.N == 0) ? a.anchor[b] : a.mask_id;
+    if (threadIdx.x == 0 && m % a.N == 0) {
+      int bad = 0;
+      const int s_raw = a.seq_ids[b];
+      if (s_raw < 0 || s_raw >= a.max_seqs) bad |= DFLASH_DEV_BAD_SEQ;
+      if (tok < 0 || tok >= a.V) bad |= DFLASH_DEV_BAD_TOKEN;
+      const int L = a.ctx_len[clampi(s_raw, 0, a.max_seqs - 1)];
+      if (L < 0 || L + a.N > a.max_pos) bad |= DFLASH_DEV_NO_PAGES;
+      if (bad) set_error(a.err, bad);
+    }
     tok = clampi(tok, 0, a.V - 1);
   }
+  const size_t split_stride = (size_t)a.M * a.H;
 #pragma unroll
   for (int v = 0; v < NORM_MAXV; ++v) {
-    const int k = (v * 256 + threadIdx.x) * 4;
+    const int k = (v * blockDim.x + threadIdx.x) * 4;
     if (v >= nv || k >= a.H) continue;
     f32x4 x;
     if (a.mode == 0) {
@@ -142,7 +179,7 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
       for (int i = 0; i < 4; ++i) x[i] = bf2f(e[i]);
     } else {
       x = *reinterpret_cast<const f32x4*>(a.x + (size_t)m * a.H + k);
-      for (int s = 0; s < a.ks; ++s) x += *reinterpret_cast<const f32x4*>(a.part + ((size_t)s * a.M + m) * a.H + k);
+      x += split_sum4(a.part, a.ks, split_stride, (size_t)m * a.H + k);
     }
     *reinterpret_cast<f32x4*>(a.x + (size_t)m * a.H + k) = x;
     if (a.dbg) *reinterpret_cast<f32x4*>(a.dbg + (size_t)m * a.H + k) = x;
@@ -156,7 +193,7 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
   const float rstd = 1.0f / sqrtf(tot / a.H + a.eps);
 #pragma unroll
   for (int v = 0; v < NORM_MAXV; ++v) {
-    const int k = (v * 256 + threadIdx.x) * 4;
+    const int k = (v * blockDim.x + threadIdx.x) * 4;
     if (v >= nv || k >= a.H) continue;
     const u16x4 gv = *reinterpret_cast<const u16x4*>(a.g + k);
     u16x4 o;
@@ -167,7 +204,8 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
 }
 
 extern "C" hipError_t dflash_launch_norm(const NormArgs* a, hipStream_t st) {
-  hipLaunchKernelGGL(norm_kernel, dim3(a->M), dim3(256), 0, st, *a);
+  const int threads = std::min(1024, ((a->H / 4 + 63) / 64) * 64);
+  hipLaunchKernelGGL(norm_kernel, dim3(a->M), dim3(threads), 0, st, *a);
   return hipGetLastError();
 }
 

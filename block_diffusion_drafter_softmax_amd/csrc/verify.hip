@@ -65,8 +65,9 @@ DEV float2 ms_merge(float2 x, float2 y) {
 
 namespace {
 // Eight consecutive logits k .. k+7 (k % 8 == 0) as fp32.
+template <int DTYPE>
 DEV void load8(const VerifyArgs& a, size_t i, float (&z)[8]) {
-  if (a.dtype == DFLASH_DTYPE_F32) {
+  if (DTYPE == DFLASH_DTYPE_F32) {
     const f32x4 lo = *reinterpret_cast<const f32x4*>((const float*)a.logits + i);
     const f32x4 hi = *reinterpret_cast<const f32x4*>((const float*)a.logits + i + 4);
 #pragma unroll
@@ -87,7 +88,8 @@ DEV void load8(const VerifyArgs& a, size_t i, float (&z)[8]) {
 
 // Work item = (vocabulary chunk, block row, sequence); chunk % 8 == 0 and
 // V % 8 == 0, so every thread reads whole 8-logit groups.
-__global__ __launch_bounds__(256) void verify_rows_kernel(VerifyArgs a) {
+template <int DTYPE>
+__global__ __launch_bounds__(256) LATENCY_BOUND void verify_rows_kernel(VerifyArgs a) {
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const size_t row_off = ((size_t)b * a.N + r) * a.V;
   const int k0 = c * a.chunk, k1 = min(a.V, k0 + a.chunk);
@@ -99,11 +101,19 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(VerifyArgs a) {
   float2 res = make_float2(0.f, 0.f);
   if (!a.temp1) {
     ArgMax t{-INFINITY, 0x7FFFFFFF};
-    for (int k = k0 + threadIdx.x * 8; k < k1; k += 256 * 8) {
-      float z[8];
-      load8(a, row_off + k, z);
+    float zs[4][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t = am_merge(t, ArgMax{z[e], k + e});
+    for (int j = 0; j < 4; ++j) {  // chunk <= 256 * 8 * 4: all loads in flight (clamped, unused past k1)
+      const int k = min(k0 + (int)(threadIdx.x + 256 * j) * 8, k1 - 8);
+      load8<DTYPE>(a, row_off + k, zs[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = k0 + (threadIdx.x + 256 * j) * 8;
+      if (k < k1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t = am_merge(t, ArgMax{zs[j][e], k + e});
+      }
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) t = am_shfl(t, o);
@@ -118,13 +128,15 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(VerifyArgs a) {
     float m = -INFINITY;
     float zs[4][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // chunk <= 256 * 8 * 4
-      const int k = k0 + (threadIdx.x + 256 * j) * 8;
-      if (k < k1) {
-        load8(a, row_off + k, zs[j]);
+    for (int j = 0; j < 4; ++j) {  // chunk <= 256 * 8 * 4: clamped loads, all in flight
+      const int k = min(k0 + (int)(threadIdx.x + 256 * j) * 8, k1 - 8);
+      load8<DTYPE>(a, row_off + k, zs[j]);
+    }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, zs[j][e]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      if (k0 + (int)(threadIdx.x + 256 * j) * 8 >= k1) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, zs[j][e]);
     }
     m = wave_max(m);
     if (lane == 0) red[wave].x = m;
@@ -163,6 +175,7 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(VerifyArgs a) {
   if (row < a.N) {
     if (!a.temp1) {
       ArgMax u{-INFINITY, 0x7FFFFFFF};
+#pragma unroll 8
       for (int cc = 0; cc < a.n_chunks; ++cc) {
         const float2 p = *reinterpret_cast<const float2*>(a.part + ((((size_t)b * a.N + row) * a.n_chunks + cc) * 2));
         u = am_merge(u, ArgMax{p.x, __float_as_int(p.y)});
@@ -170,6 +183,7 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(VerifyArgs a) {
       rowres[row] = make_float2(u.v, __int_as_float(u.i));
     } else if (row < a.N - 1) {
       float2 ms = make_float2(-INFINITY, 0.f);
+#pragma unroll 8
       for (int cc = 0; cc < a.n_chunks; ++cc)
         ms = ms_merge(ms, *reinterpret_cast<const float2*>(a.part + ((((size_t)b * a.N + row) * a.n_chunks + cc) * 2)));
       const float lse = ms.x + __logf(ms.y);
@@ -202,7 +216,7 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(VerifyArgs a) {
 }
 
 // Gumbel-max sample of row state[b][0] with token state[b][1] excluded.
-__global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(256) LATENCY_BOUND void verify_sample_kernel(VerifyArgs a) {
   const int c = blockIdx.x, b = blockIdx.y;
   const int row = a.state[2 * b + 0], excl = a.state[2 * b + 1];
   const int seq = a.seq_ids[b];
@@ -244,7 +258,10 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
 }
 
 extern "C" hipError_t dflash_launch_verify(const VerifyArgs* a, hipStream_t st) {
-  hipLaunchKernelGGL(verify_rows_kernel, dim3(a->n_chunks, a->N, a->B), dim3(256), 0, st, *a);
+  if (a->dtype == DFLASH_DTYPE_F32)
+    hipLaunchKernelGGL(verify_rows_kernel<DFLASH_DTYPE_F32>, dim3(a->n_chunks, a->N, a->B), dim3(256), 0, st, *a);
+  else
+    hipLaunchKernelGGL(verify_rows_kernel<DFLASH_DTYPE_BF16>, dim3(a->n_chunks, a->N, a->B), dim3(256), 0, st, *a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a->temp1) return e;
   hipLaunchKernelGGL(verify_sample_kernel, dim3(a->n_chunks, a->B), dim3(256), 0, st, *a);

@@ -147,12 +147,15 @@ class Case:
             if g["logits"] is not None:
                 for j in range(o["logits"].shape[0]):
                     le = max(le, rel_err(g["logits"][b, j], o["logits"][j]))
+        for b, o in enumerate(orc):
             for j in range(len(o["draft"])):
                 if o["gap"][j] < GAP_MIN:
                     excluded += 1
                     continue
                 compared += 1
-                assert int(g["draft"][b, j]) == int(o["draft"][j]), (b, j, g["draft"][b], o["draft"], o["gap"])
+                assert int(g["draft"][b, j]) == int(o["draft"][j]), (
+                    f"draft mismatch seq {b} pos {j}: gpu {g['draft'][b]} oracle {o['draft']} gap {o['gap']} "
+                    f"(hidden rel {he:.2e}, logits rel {le:.2e})")
         return he, le, compared, excluded
 
 
