@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
   const size_t unit0 = ((size_t)b * a.n_kv + kvh) * a.n_ck;
   float M = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  constexpr int GRP = 16;  // chunks whose loads are in flight together
+  constexpr int GRP = 8;  // chunks whose loads are in flight together (more costs time on gfx950)
   for (int c0 = 0; c0 < nc; c0 += GRP) {
     float2 ml[GRP];
     f32x4 ov[GRP];

@@ -72,8 +72,9 @@ DEV float block_sum(float v, float* lds /* >= 16 floats */) {
 
 DEV void set_error(int32_t* err, int bits) { atomicOr(err, bits); }
 
-// Largest k split a streaming GEMM uses; reducers unroll over it.
-#define KS_MAX 16
+// Largest k split a streaming GEMM uses; reducers unroll over it (one batch
+// of at most 8 loads per thread: bigger batches cost time on gfx950).
+#define KS_MAX 8
 
 // Sum of the ks split partials part[k*stride + off], k = 0..ks-1, in k
 // order. All loads are issued before the first add, so the reduction costs

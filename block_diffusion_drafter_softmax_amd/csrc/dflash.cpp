@@ -36,7 +36,7 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int kAttnChunk = 128;     // context keys per attention work item (attention.hip: CH)
 constexpr int kVerifyChunk = 8192;  // logits per verification work item
-constexpr int kKsMax = 16;          // largest k split of a streaming GEMM
+constexpr int kKsMax = 8;           // largest k split of a streaming GEMM (KS_MAX in common.h)
 constexpr int kTargetWaves = 1536;  // streaming waves to aim for (~6 per CU)
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

@@ -62,50 +62,38 @@ extern "C" hipError_t dflash_launch_plan(const PlanArgs* a, hipStream_t st) {
 // ------------------------------------------------------------ fusion
 
 #define FUSE_MAXV 2   // float4 groups per thread: H <= 1024 * 4 * 2
-#define FUSE_TMAX 16  // target layers held in registers
 #define FUSE_DMAX 64  // draft layers whose fusion weights fit the LDS table
+#define FUSE_TMAX 16  // target layers
 
 // One workgroup per appended row, one float4 group of the row per thread.
-// The row's T target states are loaded once into registers (every load in
-// flight together); then for each draft layer i:
-// s = sum_j alpha[i][j] * h_j (ascending j), f = s / sqrt(mean(s^2) + eps) * g,
-// written packed as the activation of the context K/V projection.
+// For each draft layer i: s = sum_j alpha[i][j] * h_j (ascending j; the T
+// states are re-read per layer from cache, 8 loads in flight per batch),
+// f = s / sqrt(mean(s^2) + eps) * g, written packed as the activation of the
+// context K/V projection. The fusion weights are staged in LDS once.
 __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
   const int m = blockIdx.x;
   if (a.row_pos[m] < 0) return;
   __shared__ float red[16];
   __shared__ float alpha[FUSE_DMAX * FUSE_TMAX];
   for (int i = threadIdx.x; i < a.D * a.T; i += blockDim.x) alpha[i] = a.alpha[i];
+  __syncthreads();
   const uint16_t* h = a.hidden + (size_t)m * a.T * a.H;
   const int nv = (a.H / 4 + blockDim.x - 1) / blockDim.x;
-  // Unconditional loads from clamped addresses (values past T or H are never
-  // used), so that no branch separates them and all are issued together.
-  u16x4 hv[FUSE_MAXV][FUSE_TMAX];
-#pragma unroll
-  for (int v = 0; v < FUSE_MAXV; ++v) {
-    const int k = min((v * (int)blockDim.x + (int)threadIdx.x) * 4, a.H - 4);
-#pragma unroll
-    for (int j = 0; j < FUSE_TMAX; ++j)
-      hv[v][j] = *reinterpret_cast<const u16x4*>(h + (size_t)min(j, a.T - 1) * a.H + k);
-  }
-  __syncthreads();  // alpha table staged
   for (int i = 0; i < a.D; ++i) {
     float s[FUSE_MAXV][4];
     float ss = 0.f;
 #pragma unroll
     for (int v = 0; v < FUSE_MAXV; ++v) {
+      const int k = (v * (int)blockDim.x + (int)threadIdx.x) * 4;
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      if (v >= nv || (v * (int)blockDim.x + (int)threadIdx.x) * 4 >= a.H) {
+      if (v < nv && k < a.H) {
+#pragma unroll 8
+        for (int j = 0; j < a.T; ++j) {
+          const u16x4 x = *reinterpret_cast<const u16x4*>(h + (size_t)j * a.H + k);
+          const float al = alpha[i * a.T + j];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[v][e] = 0.f;
-        continue;
-      }
-#pragma unroll
-      for (int j = 0; j < FUSE_TMAX; ++j) {
-        if (j >= a.T) break;
-        const float al = alpha[i * a.T + j];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += al * bf2f(hv[v][j][e]);
+          for (int e = 0; e < 4; ++e) acc[e] += al * bf2f(x[e]);
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
