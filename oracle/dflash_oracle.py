@@ -31,16 +31,16 @@ four norms (fusion, pre-attention, pre-MLP, final); no biases; argmax ties
 go to the lowest index; target row r predicts the token after block
 position r.
 
-Arithmetic is float64 throughout. The storage precision that the method
-fixes for this path -- bf16 weights, bf16 GEMM inputs and a bf16 KV cache,
-fp32 (here fp64) accumulation, norms and softmax -- is modelled by rounding
-to bf16 (round to nearest even, 8 significant bits) at exactly these
-points: the fused context f, the rotated/unrotated context K and V, the
-normed GEMM inputs h and h2, the rotated Q, block K and block V, the
-attention output O, the SwiGLU output, and the final normed y. Passing
-``storage=False`` turns every such rounding off (exact float64), which the
-pins use. Logits are rounded to float32 before the argmax, the precision in
-which the kernel takes that decision.
+Arithmetic is float64 throughout. The stated precision of the path is bf16
+storage with fp32 accumulation; what is stored in bf16 is the weights (given
+as bf16 values) and the keys/values: the rotated context K and the context V
+in the cache, and the rotated block K and block V the draft attends to. Those
+four are rounded to bf16 (round to nearest even, 8 significant bits) here;
+transient activations (fused context, normed rows, queries, attention output,
+SwiGLU output) are not storage and stay exact. Passing ``storage=False``
+turns the K/V rounding off too (exact float64), which the pins use. Logits
+are rounded to float32 before the argmax, the precision in which the kernel
+takes that decision.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py``
 against closed forms, invariants, library routines (torch's RMSNorm,
@@ -108,7 +108,7 @@ def rmsnorm(x, g, eps):
     return x / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
 
 
-def fuse_context(alpha_i, h, g, eps, storage=True):
+def fuse_context(alpha_i, h, g, eps):
     """f^(i)_t = RMSNorm(sum_j alpha^(i)_j h^(j)_t) * g_fuse^(i).
 
     DFLARE summary, section 2.1. ``h`` is [n, T, H] (the T selected target
@@ -118,7 +118,7 @@ def fuse_context(alpha_i, h, g, eps, storage=True):
     s = np.zeros((h.shape[0], h.shape[2]), dtype=np.float64)
     for j in range(h.shape[1]):
         s = s + alpha_i[j] * h[:, j, :]
-    return _store(rmsnorm(s, g, eps), storage)
+    return rmsnorm(s, g, eps)
 
 
 # ------------------------------------------------------------------- RoPE
@@ -242,8 +242,7 @@ def ctx_append(model, cache, seq, hidden, storage=True):
     p0 = cache.length(seq)
     pos = p0 + np.arange(n)
     for i in range(c["n_layers"]):
-        f = fuse_context(model.alpha[i], hidden, model.f64("g_fuse", i),
-                         c["rms_eps"], storage)
+        f = fuse_context(model.alpha[i], hidden, model.f64("g_fuse", i), c["rms_eps"])
         k = (f @ model.f64("wk_t", i).T).reshape(n, n_kv, d)
         v = (f @ model.f64("wv_t", i).T).reshape(n, n_kv, d)
         if c.get("use_rope", 1):
@@ -288,28 +287,28 @@ def draft_block(model, cache, seq, anchor, storage=True, tokens=None):
     hidden = [x.copy()]
     block_k, block_v = [], []
     for i in range(c["n_layers"]):
-        h = _store(rmsnorm(x, model.f64("g_attn", i), eps), storage)
+        h = rmsnorm(x, model.f64("g_attn", i), eps)
         q = (h @ model.f64("wq", i).T).reshape(N, n_q, d)
         kb = (h @ model.f64("wk_d", i).T).reshape(N, n_kv, d)
         vb = (h @ model.f64("wv_d", i).T).reshape(N, n_kv, d)
         if use_rope:
             q = rope(q, pos, theta)
             kb = rope(kb, pos, theta)
-        q, kb, vb = _store(q, storage), _store(kb, storage), _store(vb, storage)
+        kb, vb = _store(kb, storage), _store(vb, storage)
         block_k.append(kb)
         block_v.append(vb)
         kc = cache.k[i].get(seq, np.zeros((0, n_kv, d)))
         vc = cache.v[i].get(seq, np.zeros((0, n_kv, d)))
         o = attention(q, np.concatenate([kc, kb]), np.concatenate([vc, vb]))
-        o = _store(o.reshape(N, n_q * d), storage)
+        o = o.reshape(N, n_q * d)
         x = x + o @ model.f64("wo", i).T
-        h2 = _store(rmsnorm(x, model.f64("g_mlp", i), eps), storage)
+        h2 = rmsnorm(x, model.f64("g_mlp", i), eps)
         a = h2 @ model.f64("wg", i).T
         b = h2 @ model.f64("wu", i).T
-        m = _store(silu(a) * b, storage)
+        m = silu(a) * b
         x = x + m @ model.f64("wd", i).T
         hidden.append(x.copy())
-    y = _store(rmsnorm(x[1:], model.f64("g_final"), eps), storage)
+    y = rmsnorm(x[1:], model.f64("g_final"), eps)
     # Output columns are computed a slice of the vocabulary at a time only
     # to bound memory; each logit is the same full dot product.
     vocab = model.w["lm_head"].shape[0]

@@ -90,7 +90,7 @@ def test_one_hot_fusion_is_rmsnorm_of_that_layer():
     h = r.standard_normal((5, 4, 32))
     g = 1 + 0.1 * r.standard_normal(32)
     alpha = np.array([0.0, 0.0, 1.0, 0.0])
-    f = O.fuse_context(alpha, h, g, 1e-6, storage=False)
+    f = O.fuse_context(alpha, h, g, 1e-6)
     ref = F.rms_norm(torch.from_numpy(h[:, 2, :]), (32,), torch.from_numpy(g), eps=1e-6).numpy()
     assert np.allclose(f, ref, rtol=1e-12, atol=1e-14)
 
@@ -99,7 +99,7 @@ def test_fusion_of_two_layers_matches_library_norm_of_mean():
     r = np.random.default_rng(4)
     h = r.standard_normal((3, 2, 16))
     g = np.ones(16)
-    f = O.fuse_context(np.array([0.5, 0.5]), h, g, 1e-6, storage=False)
+    f = O.fuse_context(np.array([0.5, 0.5]), h, g, 1e-6)
     mean = torch.from_numpy(h.mean(axis=1))
     ref = F.rms_norm(mean, (16,), eps=1e-6).numpy()
     assert np.allclose(f, ref, rtol=1e-12, atol=1e-14)
@@ -110,7 +110,7 @@ def test_fusion_constant_vector_closed_form():
     g = np.linspace(0.5, 1.5, 8)
     for c in (1e-3, -2e-3, 0.7):
         h = np.full((1, 1, 8), c)
-        f = O.fuse_context(np.array([1.0]), h, g, 1e-6, storage=False)
+        f = O.fuse_context(np.array([1.0]), h, g, 1e-6)
         assert np.allclose(f[0], c / math.sqrt(c * c + 1e-6) * g, rtol=1e-13, atol=0)
 
 
@@ -322,7 +322,7 @@ def test_tied_kv_is_dflash_shared_projection():
     L = 5
     cache, h = _prefill(m, c, L)
     out = O.draft_block(m, cache, 0, 3, storage=False)
-    f = O.fuse_context(m.alpha[0], h, w["g_fuse"][0], c["rms_eps"], storage=False)
+    f = O.fuse_context(m.alpha[0], h, w["g_fuse"][0], c["rms_eps"])
     tokens = [3] + [c["mask_token_id"]] * (c["block_size"] - 1)
     hb = O.rmsnorm(w["embed"][tokens], w["g_attn"][0], c["rms_eps"])
     both = np.concatenate([f, hb])
@@ -338,7 +338,7 @@ def test_untied_context_uses_its_own_projection():
     w = tiny_weights(c, seed=23)
     m = _model(c, w)
     cache, h = _prefill(m, c, 4)
-    f = O.fuse_context(m.alpha[0], h, w["g_fuse"][0], c["rms_eps"], storage=False)
+    f = O.fuse_context(m.alpha[0], h, w["g_fuse"][0], c["rms_eps"])
     v_t = (f @ w["wv_t"][0].T).reshape(4, c["n_kv_heads"], -1)
     v_d = (f @ w["wv_d"][0].T).reshape(4, c["n_kv_heads"], -1)
     assert np.allclose(cache.v[0][0], v_t, atol=1e-12)
@@ -370,13 +370,20 @@ def test_identical_mask_rows_without_rope_give_identical_outputs():
 
 
 def test_storage_rounding_lands_on_bf16_grid():
+    """K/V (context cache and block) are bf16 storage; the residual stream
+    and the other activations are not rounded."""
     c = tiny_cfg()
     m = _model(c, tiny_weights(c, seed=27))
-    cache, _ = O.OracleCache(2), None
+    cache = O.OracleCache(2)
     O.ctx_append(m, cache, 0, np.random.default_rng(28).standard_normal((5, 3, 32)))
     for i in range(2):
-        k = cache.k[i][0]
-        assert np.array_equal(O.bf16_round(k), k)
+        for t in (cache.k[i][0], cache.v[i][0]):
+            assert np.array_equal(O.bf16_round(t), t)
+    out = O.draft_block(m, cache, 0, 3)
+    for i in range(2):
+        assert np.array_equal(O.bf16_round(out["block_k"][i]), out["block_k"][i])
+        assert np.array_equal(O.bf16_round(out["block_v"][i]), out["block_v"][i])
+    assert not np.array_equal(O.bf16_round(out["hidden"][-1]), out["hidden"][-1])
 
 
 # ---------------------------------------------------- greedy verification
