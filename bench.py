@@ -34,14 +34,11 @@ def step_bytes(cfg, L, n_new):
                                          "block_size"))
     qd = cfg["n_q_heads"] * cfg["head_dim"]
     kvd = cfg["n_kv_heads"] * cfg["head_dim"]
-    ctx_w = 0 if cfg.get("tied_kv") else D * 2 * kvd * H * 2
-    if cfg.get("tied_kv"):
-        ctx_w = 0  # the context reuses the block projections (read again: counted below once)
     append = n_new * T * H * 2 + (D * 2 * kvd * H * 2) + D * n_new * 2 * kvd * 2
     layer_w = (qd * H + 2 * kvd * H + H * qd + 2 * I * H + H * I) * 2
     draft = D * layer_w + V * H * 2 + N * H * 2 + D * L * 2 * kvd * 2
     verify = N * V * 2
-    return dict(append=append, draft=draft, verify=verify, total=append + draft + verify, ctx_weights=ctx_w)
+    return dict(append=append, draft=draft, verify=verify, total=append + draft + verify)
 
 
 def gate_up_bytes(cfg, M):
@@ -49,18 +46,27 @@ def gate_up_bytes(cfg, M):
     return 2 * I * H * 2 + M * H * 2 + M * I * 2
 
 
-def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+# Sources the streaming GEMM kernel is compiled from.
+KERNEL_SOURCES = [os.path.join(ROOT, "block_diffusion_drafter_softmax_amd", "csrc", f)
+                  for f in ("gemm.hip", "stream.h", "common.h", "kernels.h")]
 
 
-def traffic_from_profile(kernel_src):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the gate/up kernel from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary, if it was taken on the current
+    kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", "gate_up_qwen3_8b_traffic.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("source_sha256_16") != source_hash(kernel_src):
+    if d.get("source_sha256_16") != source_hash(KERNEL_SOURCES):
         return None
     return d.get("bytes_per_launch")
 
@@ -76,7 +82,8 @@ def cpu_baseline(cfg, w, hidden_pre, hidden_step, anchor, logits_bits):
         threads = 1
     model = O.OracleModel(cfg, w)
     cache = O.OracleCache(cfg["n_layers"])
-    O.ctx_append(model, cache, 0, O.bf16_bits_to_f64(hidden_pre))
+    for r0 in range(0, len(hidden_pre), 1024):  # untimed prefill, in row chunks
+        O.ctx_append(model, cache, 0, O.bf16_bits_to_f64(hidden_pre[r0: r0 + 1024]))
     t0 = time.perf_counter()
     O.ctx_append(model, cache, 0, O.bf16_bits_to_f64(hidden_step))
     out = O.draft_block(model, cache, 0, int(anchor))
@@ -199,8 +206,7 @@ def main():
         achieved = gbytes / gu_avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profile(os.path.join(ROOT, "block_diffusion_drafter_softmax_amd", "csrc",
-                                                             "gemm.hip")),
+                "traffic": traffic_from_profile(),
                 "kernel": "gate_up (gate/up projection + SwiGLU)", "bytes_per_launch": gbytes,
                 "avg_launch_us": round(gu_avg_s * 1e6, 2), "launches_timed": gu_n}
     t_roof_us = sb["total"] / (HBM_PEAK_GBS * 1e9) * 1e6

@@ -14,8 +14,10 @@
 // softmax in the log2 domain, and accumulates O^T += V^T P^T with MFMA: V is
 // stored dim-major per page ([d_h][16 slots]), so its A-operand fragments are
 // contiguous, and P^T comes straight from the S^T accumulators (both MFMAs use
-// the same permutation of the 32 keys). Unnormalised O, the running max and
-// the sum go to a partial buffer; attn_merge_kernel combines the chunks.
+// the same permutation of the 32 keys). Q and P are fp32 values entering
+// the MFMAs as hi/lo bf16 pairs (two MFMAs each); K and V are bf16 storage.
+// Unnormalised O, the running max and the sum go to a partial buffer;
+// attn_merge_kernel combines the chunks.
 #include "common.h"
 #include "dflash.h"
 
@@ -104,10 +106,14 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   const int hq = kvh * G + r / a.N, n = r % a.N;
   constexpr int KD = D / 32, DT = D / 16;
 
-  bf16x8 qf[KD];
+  bf16x8 qh[KD], ql[KD];
   const uint16_t* qp = a.q + ((size_t)(b * a.N + n) * a.n_q + hq) * D + 8 * g;
+  const size_t q_lo = (size_t)gridDim.z * a.N * a.n_q * D;
 #pragma unroll
-  for (int kd = 0; kd < KD; ++kd) qf[kd] = ld8(qp + kd * 32);
+  for (int kd = 0; kd < KD; ++kd) {
+    qh[kd] = ld8(qp + kd * 32);
+    ql[kd] = ld8(qp + q_lo + kd * 32);
+  }
 
   f32x4 acc[DT];
 #pragma unroll
@@ -118,12 +124,18 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
     const bool t1 = k0 + 16 < nkeys;
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd)
-      s0 = mfma16(*reinterpret_cast<const bf16x8*>(&k_lds[(k0 + r16) * KP + kd * 32 + 8 * g]), qf[kd], s0);
+    for (int kd = 0; kd < KD; ++kd) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[(k0 + r16) * KP + kd * 32 + 8 * g]);
+      s0 = mfma16(kf, qh[kd], s0);
+      s0 = mfma16(kf, ql[kd], s0);
+    }
     if (t1) {
 #pragma unroll
-      for (int kd = 0; kd < KD; ++kd)
-        s1 = mfma16(*reinterpret_cast<const bf16x8*>(&k_lds[(k0 + 16 + r16) * KP + kd * 32 + 8 * g]), qf[kd], s1);
+      for (int kd = 0; kd < KD; ++kd) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[(k0 + 16 + r16) * KP + kd * 32 + 8 * g]);
+        s1 = mfma16(kf, qh[kd], s1);
+        s1 = mfma16(kf, ql[kd], s1);
+      }
     }
     // lane holds keys k0 + 4g + i (s0) and k0 + 16 + 4g + i (s1) for query r
     float x[8];
@@ -139,17 +151,21 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
     const float corr = exp2f(m_run - m_new);
-    u16x4 pb0, pb1;
+    f32x4 p0, p1;
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pb0[i] = f2bf(exp2f(x[i] - m_new));
-      pb1[i] = f2bf(exp2f(x[4 + i] - m_new));
-      psum += bf2f(pb0[i]) + bf2f(pb1[i]);
+      p0[i] = exp2f(x[i] - m_new);
+      p1[i] = exp2f(x[4 + i] - m_new);
+      psum += p0[i] + p1[i];
     }
     l_run = l_run * corr + psum;
     m_run = m_new;
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(pb0, pb1, 0, 1, 2, 3, 4, 5, 6, 7));
+    u16x4 h0, l0, h1, l1;
+    split4(p0, h0, l0);
+    split4(p1, h1, l1);
+    const bf16x8 ph = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+    const bf16x8 pl = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
     const uint16_t* vp0 = &v_lds[(k0 / 16) * D * 16];
     const uint16_t* vp1 = vp0 + D * 16;
 #pragma unroll
@@ -164,7 +180,8 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
       }
       const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[t] = acc[t] * corr;
-      acc[t] = mfma16(vf, pf, acc[t]);
+      acc[t] = mfma16(vf, ph, acc[t]);
+      acc[t] = mfma16(vf, pl, acc[t]);
     }
   }
   float l = l_run + __shfl_xor(l_run, 16, 64);
@@ -181,8 +198,8 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
 }
 
 // One thread per (sequence, kv head, query row, 4 dims): single-pass
-// log-sum-exp merge of the chunk partials in chunk order, normalise, round
-// to bf16 and write the O-projection's packed activation.
+// log-sum-exp merge of the chunk partials in chunk order, normalise, and
+// write the O-projection's packed split activation.
 template <int D>
 __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs a, int B) {
   const int G = a.n_q / a.n_kv, R = G * a.N;
@@ -221,10 +238,11 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
   const float inv = 1.0f / den;
   const int hq = kvh * G + r / a.N, n = r % a.N;
   const int m = b * a.N + n, qd = a.n_q * D;
-  u16x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f2bf(num[i] * inv);
-  *reinterpret_cast<u16x4*>(a.o + pk_index(m, hq * D + dq * 4, qd)) = o;
+  u16x4 hi, lo;
+  split4(num * inv, hi, lo);
+  uint16_t* dst = a.o + pk_index(m, hq * D + dq * 4, qd);
+  *reinterpret_cast<u16x4*>(dst) = hi;
+  *reinterpret_cast<u16x4*>(dst + act_plane(B * a.N, qd)) = lo;
 }
 
 extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_t st) {

@@ -29,6 +29,22 @@ DEV uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// fp32 -> bf16 pair (hi, lo) with hi + lo = x to about 2^-17 relative.
+DEV void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
+}
+
+DEV void split4(const f32x4& x, u16x4& hi, u16x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint16_t a, b;
+    split_bf16(x[i], a, b);
+    hi[i] = a;
+    lo[i] = b;
+  }
+}
+
 // 16 bytes = 8 bf16 from global memory.
 DEV bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 

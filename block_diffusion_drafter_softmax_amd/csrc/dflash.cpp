@@ -88,14 +88,15 @@ Layout make_layout(const dflash_config& c) {
   L.rowseq_a = take(L.rows_a_max * 4);
   L.rowpos_d = take(L.m_max * 4);
   L.rowseq_d = take(L.m_max * 4);
-  L.f = take(D * rp * H * 2);
+  // activations are split hi/lo bf16 pairs: two planes each
+  L.f = take(D * 2 * rp * H * 2);
   L.x = take(L.m_max * H * 4);
-  L.h = take(mp * H * 2);
-  L.q = take(L.m_max * qd * 2);
-  L.o = take(mp * qd * 2);
+  L.h = take(2 * mp * H * 2);
+  L.q = take(2 * L.m_max * qd * 2);
+  L.o = take(2 * mp * qd * 2);
   L.kblk = take(Bm * kvd * 16 * 2);
   L.vblk = take(Bm * kvd * 16 * 2);
-  L.mm = take(mp * I * 2);
+  L.mm = take(2 * mp * I * 2);
   L.gpart = take(L.gpart_floats * 4);
   L.cpart = take(L.cpart_floats * 4);
   L.apo = take(Bm * c.n_kv_heads * L.n_ck * R * c.head_dim * 4);
@@ -364,7 +365,7 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
     WsArgs g = ws_base(rows, H, n_cols);
     g.part = ctx->at<float>(L.cpart);
     for (int i = l0; i < D && i < l0 + WS_MAX_SEG / 2; ++i) {
-      const uint16_t* act = ctx->at<uint16_t>(L.f) + (size_t)i * pad16(rows) * H;
+      const uint16_t* act = ctx->at<uint16_t>(L.f) + (size_t)i * 2 * act_plane(rows, H);
       add_seg(g, ctx->at<uint16_t>(L.wk_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd);
       add_seg(g, ctx->at<uint16_t>(L.wv_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd + kvd);
     }

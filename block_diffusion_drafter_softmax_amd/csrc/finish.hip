@@ -1,8 +1,9 @@
 // Finishers of the split-k projections: add the k-split partial sums in split
 // order, apply RoPE to keys/queries (rotate-half pairs (j, j + d/2) at the
-// row's position, cos/sin from the set-up table), round to bf16 and write the
-// layout the consumer wants: the attention's query rows and block K/V, or the
-// paged context cache (keys slot-major, values dim-major).
+// row's position, cos/sin from the set-up table) and write the layout the
+// consumer wants: the attention's query rows (split hi/lo activation) and
+// block K/V (bf16), or the paged context cache (bf16; keys slot-major,
+// values dim-major).
 #include "common.h"
 
 namespace {
@@ -43,10 +44,16 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void qkv_finish_kernel(QkvFinish
     float x2 = split_sum(a.part, a.ks, a.M, n_cols, m, col + half);
     rotate(x1, x2, a.rope, clampi(a.ctx_len[clampi(a.seq_ids[b], 0, a.max_seqs - 1)] + n, 0, a.max_pos - 1),
            half, i);
-    uint16_t* dst = isq ? a.q + ((size_t)m * a.n_q + head) * d
-                        : a.kblk + (((size_t)b * a.n_kv + head) * 16 + n) * d;
-    dst[i] = f2bf(x1);
-    dst[i + half] = f2bf(x2);
+    if (isq) {  // query: split activation of the attention
+      uint16_t* dst = a.q + ((size_t)m * a.n_q + head) * d;
+      const size_t lo = (size_t)a.M * a.n_q * d;
+      split_bf16(x1, dst[i], dst[lo + i]);
+      split_bf16(x2, dst[i + half], dst[lo + i + half]);
+    } else {  // block key: bf16 storage
+      uint16_t* dst = a.kblk + (((size_t)b * a.n_kv + head) * 16 + n) * d;
+      dst[i] = f2bf(x1);
+      dst[i + half] = f2bf(x2);
+    }
   } else {
     const int jj = j - pq - pk;
     const int head = jj / d, dd = jj % d;

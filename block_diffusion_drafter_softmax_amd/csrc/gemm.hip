@@ -1,4 +1,5 @@
-// Weight-streaming GEMM for few activation rows: y[m][n] = sum_k x[m][k] * W[n][k].
+// Weight-streaming GEMM for few activation rows: y[m][n] = sum_k x[m][k] * W[n][k],
+// x a split (hi + lo) activation, W bf16.
 //
 // At a decode step the activation has M = B*N rows (16 for one sequence and a
 // block of 16) while W has thousands of rows, so every weight byte is used M
@@ -10,7 +11,8 @@
 // fp32 partial tiles go to part[split][M][n_cols] and the consumer (RMSNorm
 // or a finisher) adds the splits in split order, so results are deterministic.
 // With ks == 1 the gate/up projection applies SwiGLU in registers: the wave's
-// two tiles are the gate and up rows of the same 16 features.
+// two tiles are the gate and up rows of the same 16 features, and the
+// product is written as the split activation of the down projection.
 #include "stream.h"
 
 template <int MT, int U, int MODE>
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(64) void ws_kernel(WsArgs a) {
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    stream_ksteps<NT, MT, U>(pw, px, s0, s1, acc);
+    stream_ksteps<NT, MT, U>(pw, px, act_plane(a.M, a.K), s0, s1, acc);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = (mg + mt) * 16 + r16;
@@ -57,13 +59,17 @@ __global__ __launch_bounds__(64) void ws_kernel(WsArgs a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(out + (u * NT + t) * 16 + g4) = acc[t][mt];
       } else {
-        u16x4 o;
+        f32x4 y;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float gt = acc[0][mt][i];
-          o[i] = f2bf(gt / (1.0f + __expf(-gt)) * acc[1][mt][i]);
+          y[i] = gt / (1.0f + __expf(-gt)) * acc[1][mt][i];
         }
-        *reinterpret_cast<u16x4*>(a.out + pk_index(m, sg.col0 + u * 16 + g4, a.n_cols)) = o;
+        u16x4 hi, lo;
+        split4(y, hi, lo);
+        uint16_t* dst = a.out + pk_index(m, sg.col0 + u * 16 + g4, a.n_cols);
+        *reinterpret_cast<u16x4*>(dst) = hi;
+        *reinterpret_cast<u16x4*>(dst + act_plane(a.M, a.n_cols)) = lo;
       }
     }
   }

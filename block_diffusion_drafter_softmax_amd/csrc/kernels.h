@@ -25,6 +25,14 @@ __host__ __device__ inline size_t pk_index(int r, int k, int K) {
 }
 __host__ __device__ inline int pad16(int m) { return (m + 15) & ~15; }
 
+// Activations (GEMM inputs, attention queries) are fp32 values carried as a
+// bf16 pair: a hi plane holding bf16(x) followed by a lo plane holding
+// bf16(x - hi), so x = hi + lo to about 2^-17 relative and a product with a
+// bf16 weight, taken as two MFMAs, keeps fp32-level accuracy. In the packed
+// layout each plane has act_plane(R, K) elements; only weights and the K/V
+// data are single bf16.
+__host__ __device__ inline size_t act_plane(int R, int K) { return (size_t)pad16(R) * K; }
+
 // ------------------------------------------------------------ streaming GEMM
 enum WsMode : int {
   WS_PARTIAL = 0,  // fp32 partial sums part[split][M][n_cols]
@@ -36,7 +44,7 @@ enum WsMode : int {
 struct WsSeg {
   const uint16_t* w0;   // packed weights [tiles][K/32][512]
   const uint16_t* w1;   // WS_SWIGLU: packed up weights (w0 holds gate)
-  const uint16_t* act;  // packed activation [pad16(M)/16][K/32][512]
+  const uint16_t* act;  // packed split activation: hi plane, lo plane at + act_plane(M, K)
   int units;            // work units (NT tiles of 16 rows each)
   int col0;             // first output column of this segment
 };
@@ -50,7 +58,7 @@ struct WsArgs {
   int ks;       // k splits (one wave per (unit, split))
   int n_cols;   // row length of the partial buffer / SwiGLU features
   float* part;  // WS_PARTIAL: [ks][M][n_cols]
-  uint16_t* out;  // WS_SWIGLU: packed [pad16(M)/16][n_cols/32][512]
+  uint16_t* out;  // WS_SWIGLU: packed split activation, planes of act_plane(M, n_cols)
 };
 
 struct PackArgs {
@@ -67,7 +75,7 @@ struct QkvFinishArgs {
   const int* ctx_len;
   int max_seqs, max_pos;
   const float* rope;  // [max_pos][d/2][2] or null (no rotation)
-  uint16_t* q;        // [M][n_q][d]
+  uint16_t* q;        // split: hi [M][n_q][d], lo at + M*n_q*d
   uint16_t* kblk;     // [B][n_kv][16][d]
   uint16_t* vblk;     // [B][n_kv][d][16]
 };
@@ -86,7 +94,7 @@ struct CtxFinishArgs {
 
 // ------------------------------------------------------------ attention
 struct AttnArgs {
-  const uint16_t* q;       // [B*N][n_q][d]
+  const uint16_t* q;       // split: hi [B*N][n_q][d], lo at + B*N*n_q*d
   const uint16_t* kblk;    // [B][n_kv][16][d]
   const uint16_t* vblk;    // [B][n_kv][d][16]
   const uint16_t* pages;   // this layer's pages [n_pages][2][n_kv][16*d]
@@ -95,7 +103,7 @@ struct AttnArgs {
   const int* seq_ids;
   float* part_o;           // [B][n_kv][n_ck][R][d]
   float* part_ml;          // [B][n_kv][n_ck][R][2]
-  uint16_t* o;             // merge output, packed activation [pad16(B*N)/16][n_q*d/32][512]
+  uint16_t* o;             // merge output, packed split activation (planes of act_plane(B*N, n_q*d))
   int32_t* err;
   int N, n_q, n_kv, chunk, n_ck, max_pages_per_seq, n_pages, max_seqs;
   float scale_log2;        // log2(e) / sqrt(d)
@@ -120,7 +128,7 @@ struct FuseArgs {
   const uint16_t* hidden;  // [rows][T][H]
   const float* alpha;      // [D][T]
   const uint16_t* g_fuse;  // [D][H]
-  uint16_t* f;             // per layer packed [pad16(rows)/16][H/32][512], layer stride pad16(rows)*H
+  uint16_t* f;             // per layer packed split activation, layer stride 2*act_plane(rows, H)
   const int* row_pos;
   int rows, T, H, D;
   float eps;
@@ -139,7 +147,7 @@ struct NormArgs {
   const float* part;       // [ks][M][H]
   int ks;
   const uint16_t* g;       // gain [H]
-  uint16_t* h;             // packed [pad16(M)/16][H/32][512] bf16 out
+  uint16_t* h;             // packed split activation out (planes of act_plane(M, H))
   float* dbg;              // nullable [M][H]
   int H, M;
   float eps;
@@ -147,7 +155,7 @@ struct NormArgs {
 
 struct LmArgs {
   const uint16_t* w;    // packed [V/16][K/32][512]
-  const uint16_t* act;  // packed normed rows
+  const uint16_t* act;  // packed split activation of the normed rows
   int M, K, V, N;       // N = block rows per sequence
   Top2* part;           // [V/32][M]
   float* dbg_logits;    // nullable [B][N-1][V]

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(64) void lmhead_kernel(LmArgs a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    stream_ksteps<2, MT, U>(pw, px, 0, steps, acc);
+    stream_ksteps<2, MT, U>(pw, px, act_plane(a.M, a.K), 0, steps, acc);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       Top2 t = top2_empty();

@@ -68,8 +68,8 @@ extern "C" hipError_t dflash_launch_plan(const PlanArgs* a, hipStream_t st) {
 // One workgroup per appended row, one float4 group of the row per thread.
 // For each draft layer i: s = sum_j alpha[i][j] * h_j (ascending j; the T
 // states are re-read per layer from cache, 8 loads in flight per batch),
-// f = s / sqrt(mean(s^2) + eps) * g, written packed as the activation of the
-// context K/V projection. The fusion weights are staged in LDS once.
+// f = s / sqrt(mean(s^2) + eps) * g, written as the packed split activation
+// of the context K/V projection. The fusion weights are staged in LDS once.
 __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
   const int m = blockIdx.x;
   if (a.row_pos[m] < 0) return;
@@ -103,17 +103,21 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
     }
     const float tot = block_sum(ss, red);
     const float rstd = 1.0f / sqrtf(tot / a.H + a.eps);
-    uint16_t* out = a.f + (size_t)i * pad16(a.rows) * a.H;
+    const size_t plane = act_plane(a.rows, a.H);
+    uint16_t* out = a.f + (size_t)i * 2 * plane;
     const uint16_t* g = a.g_fuse + (size_t)i * a.H;
 #pragma unroll
     for (int v = 0; v < FUSE_MAXV; ++v) {
       const int k = (v * blockDim.x + threadIdx.x) * 4;
       if (v >= nv || k >= a.H) continue;
       const u16x4 gv = *reinterpret_cast<const u16x4*>(g + k);
-      u16x4 o;
+      f32x4 y;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = f2bf(s[v][e] * rstd * bf2f(gv[e]));
-      *reinterpret_cast<u16x4*>(out + pk_index(m, k, a.H)) = o;
+      for (int e = 0; e < 4; ++e) y[e] = s[v][e] * rstd * bf2f(gv[e]);
+      u16x4 hi, lo;
+      split4(y, hi, lo);
+      *reinterpret_cast<u16x4*>(out + pk_index(m, k, a.H)) = hi;
+      *reinterpret_cast<u16x4*>(out + plane + pk_index(m, k, a.H)) = lo;
     }
   }
 }
@@ -131,8 +135,7 @@ extern "C" hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st) {
 // One workgroup per row, one float4 of the row per thread: build the
 // residual row (embedding gather, or x + the k-split partials of the last
 // projection, summed in split order), then h = x / sqrt(mean(x^2) + eps) * g
-// in bf16, written in the packed activation layout the next projection
-// streams. Mode 0 (first kernel of a draft call) also checks the call's
+// as the packed split activation the next projection streams. Mode 0 (first kernel of a draft call) also checks the call's
 // sequence ids, anchors and position capacity.
 __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
   const int m = blockIdx.x;
@@ -184,10 +187,13 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
     const int k = (v * blockDim.x + threadIdx.x) * 4;
     if (v >= nv || k >= a.H) continue;
     const u16x4 gv = *reinterpret_cast<const u16x4*>(a.g + k);
-    u16x4 o;
+    f32x4 y;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = f2bf(xv[v][i] * rstd * bf2f(gv[i]));
-    *reinterpret_cast<u16x4*>(a.h + pk_index(m, k, a.H)) = o;
+    for (int i = 0; i < 4; ++i) y[i] = xv[v][i] * rstd * bf2f(gv[i]);
+    u16x4 hi, lo;
+    split4(y, hi, lo);
+    *reinterpret_cast<u16x4*>(a.h + pk_index(m, k, a.H)) = hi;
+    *reinterpret_cast<u16x4*>(a.h + act_plane(a.M, a.H) + pk_index(m, k, a.H)) = lo;
   }
 }
 

@@ -43,7 +43,7 @@ class Case:
     """
 
     def __init__(self, cfg, ctx, n_new, seed=0, page_order="contiguous", seq_offset=1,
-                 prefill_chunk=64, extra_pages=1):
+                 prefill_chunk=64, extra_pages=1, oracle_seqs=None, oracle_chunk=1024):
         self.cfg = cfg
         self.B = len(ctx)
         self.ctx = [int(x) for x in ctx]
@@ -69,6 +69,10 @@ class Case:
         self.hidden_step = [synth.make_hidden(cfg, n, seed, f"step/{b}") for b, n in enumerate(self.n_new)]
         self.anchor = synth.make_anchor(cfg, self.B, seed)
         self.prefill_chunk = prefill_chunk
+        # batch entries the oracle reproduces (sequences never interact, so a
+        # sample of them checks the batched launch); appends in row chunks
+        self.oracle_seqs = list(range(self.B)) if oracle_seqs is None else list(oracle_seqs)
+        self.oracle_chunk = oracle_chunk
 
     def t_i32(self, a):
         return torch.tensor(np.asarray(a, dtype=np.int32), device=self.dev)
@@ -93,13 +97,14 @@ class Case:
                 rows.append(self.hidden_pre[b][done[b]: done[b] + n])
                 done[b] += n
             self._append_gpu(rows, self.prefill_chunk)
-        for b in range(self.B):
-            if pre[b]:
-                O.ctx_append(self.model, self.cache, self.seq_ids[b], O.bf16_bits_to_f64(self.hidden_pre[b]))
+        for b in self.oracle_seqs:
+            for r0 in range(0, pre[b], self.oracle_chunk):
+                rows = self.hidden_pre[b][r0: r0 + self.oracle_chunk]
+                O.ctx_append(self.model, self.cache, self.seq_ids[b], O.bf16_bits_to_f64(rows))
 
     def step_append(self):
         self._append_gpu(self.hidden_step, max(1, max(self.n_new)))
-        for b in range(self.B):
+        for b in self.oracle_seqs:
             if self.n_new[b]:
                 O.ctx_append(self.model, self.cache, self.seq_ids[b], O.bf16_bits_to_f64(self.hidden_step[b]))
 
@@ -119,14 +124,15 @@ class Case:
         return {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
 
     def oracle_draft(self):
+        """Oracle drafts of the sampled batch entries, in oracle_seqs order."""
         return [O.draft_block(self.model, self.cache, self.seq_ids[b], int(self.anchor[b]))
-                for b in range(self.B)]
+                for b in self.oracle_seqs]
 
     # ------------------------------------------------------------ checks
     def check_cache(self):
         errs = []
         for i in range(self.cfg["n_layers"]):
-            for b in range(self.B):
+            for b in self.oracle_seqs:
                 L = self.ctx[b]
                 if L == 0:
                     continue
@@ -140,14 +146,14 @@ class Case:
         """Returns (max hidden rel err, max logits rel err, n compared, n excluded)."""
         he, le = 0.0, 0.0
         compared = excluded = 0
-        for b, o in enumerate(orc):
+        for b, o in zip(self.oracle_seqs, orc):
             if g["hidden"] is not None:
                 for layer in range(o["hidden"].shape[0]):
                     he = max(he, rel_err(g["hidden"][layer, b], o["hidden"][layer]))
             if g["logits"] is not None:
                 for j in range(o["logits"].shape[0]):
                     le = max(le, rel_err(g["logits"][b, j], o["logits"][j]))
-        for b, o in enumerate(orc):
+        for b, o in zip(self.oracle_seqs, orc):
             for j in range(len(o["draft"])):
                 if o["gap"][j] < GAP_MIN:
                     excluded += 1

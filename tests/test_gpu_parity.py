@@ -51,6 +51,7 @@ def run_step(case, verify=True, check_cache=True):
 
 def check_verify_greedy(case, orc):
     cfg = case.cfg
+    assert case.oracle_seqs == list(range(case.B))
     d_or = np.stack([o["draft"] for o in orc]).astype(np.int32)
     z = synth.make_logits(cfg, d_or, case.seed)
     dev = case.dev
