@@ -248,8 +248,8 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
 extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
   const int G = a->n_q / a->n_kv, R = G * a->N;
   const dim3 grid(a->n_ck, a->n_kv, B), block(64 * (R / 16));
-  if (head_dim == 128) hipLaunchKernelGGL(attn_chunk_kernel<128>, grid, block, 0, st, *a);
-  else hipLaunchKernelGGL(attn_chunk_kernel<64>, grid, block, 0, st, *a);
+  if (head_dim == 128) launch_kernel(attn_chunk_kernel<128>, grid, block, 0, st, *a);
+  else launch_kernel(attn_chunk_kernel<64>, grid, block, 0, st, *a);
   return hipGetLastError();
 }
 
@@ -257,7 +257,7 @@ extern "C" hipError_t dflash_launch_attn_merge(const AttnArgs* a, int B, int hea
   const int G = a->n_q / a->n_kv, R = G * a->N;
   const int total = B * a->n_kv * R * (head_dim / 4);
   const dim3 grid((total + 255) / 256), block(256);
-  if (head_dim == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, grid, block, 0, st, *a, B);
-  else hipLaunchKernelGGL(attn_merge_kernel<64>, grid, block, 0, st, *a, B);
+  if (head_dim == 128) launch_kernel(attn_merge_kernel<128>, grid, block, 0, st, *a, B);
+  else launch_kernel(attn_merge_kernel<64>, grid, block, 0, st, *a, B);
   return hipGetLastError();
 }

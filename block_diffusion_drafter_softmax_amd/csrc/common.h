@@ -1,6 +1,7 @@
 // Shared device helpers for the gfx950 kernels: bf16 storage, MFMA operand
 // types, wave-level reductions and the kernel argument structs.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -12,6 +13,21 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define DEV __device__ __forceinline__
+
+// Host: launch kernel k with the given arguments, timed into
+// dflash_launch_events when the kernel timer is on.
+template <typename... Args>
+inline hipError_t launch_args(void (*k)(Args...), dim3 g, dim3 b, uint32_t shmem, hipStream_t st, Args... args) {
+  void* ptrs[] = {(void*)&args...};
+  const LaunchEvents ev = dflash_launch_events;
+  if (ev.start) return hipExtLaunchKernel((const void*)k, g, b, ptrs, shmem, st, ev.start, ev.stop, 0);
+  return hipLaunchKernel((const void*)k, g, b, ptrs, shmem, st);
+}
+
+template <typename... Args, typename... P>
+inline hipError_t launch_kernel(void (*k)(Args...), dim3 g, dim3 b, uint32_t shmem, hipStream_t st, P... p) {
+  return launch_args<Args...>(k, g, b, shmem, st, static_cast<Args>(p)...);
+}
 
 // Kernels with small grids whose time is memory latency: let the scheduler
 // use up to 128 VGPRs (<= 4 waves per SIMD) so that independent loads are all

@@ -14,6 +14,8 @@
 
 #include "kernels.h"
 
+thread_local LaunchEvents dflash_launch_events = {nullptr, nullptr};
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -156,12 +158,15 @@ struct dflash_ctx {
   template <class T>
   T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
 
-  // Launch `fn` (returns hipError_t), with event records around it when
-  // kind `kind` is being timed.
+  // Launch `fn` (returns hipError_t). When kind `kind` is being timed, a
+  // single-kernel launcher records the kernel's own start/end into a pair
+  // of events (dflash_launch_events); verification, which may launch two
+  // kernels, gets event records around the launcher instead.
   template <class F>
   int launch(int kind, hipStream_t st, F fn) {
     Timer& t = timers[kind];
     hipEvent_t e0 = nullptr, e1 = nullptr;
+    const bool around = kind == DFLASH_K_VERIFY;
     if (t.on) {
       if (t.used + 2 > 2 * 4096) return fail(DFLASH_ERR_CAPACITY, "kernel timer full: read it first");
       while (t.ev.size() < t.used + 2) {
@@ -171,12 +176,14 @@ struct dflash_ctx {
       }
       e0 = t.ev[t.used];
       e1 = t.ev[t.used + 1];
-      HIP_OK(hipEventRecord(e0, st));
+      if (around) HIP_OK(hipEventRecord(e0, st));
+      else dflash_launch_events = LaunchEvents{e0, e1};
     }
     hipError_t e = fn();
+    dflash_launch_events = LaunchEvents{nullptr, nullptr};
     if (e != hipSuccess) return fail(DFLASH_ERR_HIP, "kernel launch (kind %d): %s", kind, hipGetErrorString(e));
     if (t.on) {
-      HIP_OK(hipEventRecord(e1, st));
+      if (around) HIP_OK(hipEventRecord(e1, st));
       t.used += 2;
     }
     return DFLASH_OK;

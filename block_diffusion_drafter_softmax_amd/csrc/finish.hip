@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void qkv_finish_kernel(QkvFinish
 extern "C" hipError_t dflash_launch_qkv_finish(const QkvFinishArgs* a, hipStream_t st) {
   const int per_row = (a->n_q + a->n_kv) * (a->d / 2) + a->n_kv * a->d;
   const int total = a->M * per_row;
-  hipLaunchKernelGGL(qkv_finish_kernel, dim3((total + 255) / 256), dim3(256), 0, st, *a);
+  launch_kernel(qkv_finish_kernel, dim3((total + 255) / 256), dim3(256), 0, st, *a);
   return hipGetLastError();
 }
 
@@ -106,6 +106,6 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void ctx_finish_kernel(CtxFinish
 extern "C" hipError_t dflash_launch_ctx_finish(const CtxFinishArgs* a, hipStream_t st) {
   const int per_row = a->D * (a->n_kv * (a->d / 2) + a->n_kv * a->d);
   const int total = a->M * per_row;
-  hipLaunchKernelGGL(ctx_finish_kernel, dim3((total + 255) / 256), dim3(256), 0, st, *a);
+  launch_kernel(ctx_finish_kernel, dim3((total + 255) / 256), dim3(256), 0, st, *a);
   return hipGetLastError();
 }

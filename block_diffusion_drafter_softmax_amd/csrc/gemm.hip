@@ -79,13 +79,13 @@ extern "C" hipError_t dflash_launch_ws(const WsArgs* a, int mode, hipStream_t st
   const dim3 grid(a->unit_start[a->nseg] * a->ks), block(64);
   const int m_tiles = pad16(a->M) >> 4;
   if (mode == WS_SWIGLU) {
-    if (m_tiles <= 1) hipLaunchKernelGGL((ws_kernel<1, 4, WS_SWIGLU>), grid, block, 0, st, *a);
-    else if (m_tiles <= 2) hipLaunchKernelGGL((ws_kernel<2, 2, WS_SWIGLU>), grid, block, 0, st, *a);
-    else hipLaunchKernelGGL((ws_kernel<4, 2, WS_SWIGLU>), grid, block, 0, st, *a);
+    if (m_tiles <= 1) launch_kernel((ws_kernel<1, 4, WS_SWIGLU>), grid, block, 0, st, *a);
+    else if (m_tiles <= 2) launch_kernel((ws_kernel<2, 2, WS_SWIGLU>), grid, block, 0, st, *a);
+    else launch_kernel((ws_kernel<4, 2, WS_SWIGLU>), grid, block, 0, st, *a);
   } else {
-    if (m_tiles <= 1) hipLaunchKernelGGL((ws_kernel<1, 4, WS_PARTIAL>), grid, block, 0, st, *a);
-    else if (m_tiles <= 2) hipLaunchKernelGGL((ws_kernel<2, 2, WS_PARTIAL>), grid, block, 0, st, *a);
-    else hipLaunchKernelGGL((ws_kernel<4, 2, WS_PARTIAL>), grid, block, 0, st, *a);
+    if (m_tiles <= 1) launch_kernel((ws_kernel<1, 4, WS_PARTIAL>), grid, block, 0, st, *a);
+    else if (m_tiles <= 2) launch_kernel((ws_kernel<2, 2, WS_PARTIAL>), grid, block, 0, st, *a);
+    else launch_kernel((ws_kernel<4, 2, WS_PARTIAL>), grid, block, 0, st, *a);
   }
   return hipGetLastError();
 }
@@ -106,6 +106,6 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 }
 
 extern "C" hipError_t dflash_launch_pack(const PackArgs* a, hipStream_t st) {
-  hipLaunchKernelGGL(pack_kernel, dim3(2048), dim3(256), 0, st, *a);
+  launch_kernel(pack_kernel, dim3(2048), dim3(256), 0, st, *a);
   return hipGetLastError();
 }

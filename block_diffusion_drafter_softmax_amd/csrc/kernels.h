@@ -186,6 +186,15 @@ struct VerifyArgs {
   int32_t* err;
 };
 
+// Kernel timer hook: while `start` is non-null, every single-kernel launcher
+// launches through hipExtLaunchKernel with these events, which then hold the
+// kernel's own start and end (no dispatch gap in the measured duration).
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+extern thread_local LaunchEvents dflash_launch_events;
+
 extern "C" {
 hipError_t dflash_launch_ws(const WsArgs* a, int mode, hipStream_t st);
 hipError_t dflash_launch_pack(const PackArgs* a, hipStream_t st);

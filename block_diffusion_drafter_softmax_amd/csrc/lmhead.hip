@@ -51,9 +51,9 @@ __global__ __launch_bounds__(64) void lmhead_kernel(LmArgs a) {
 extern "C" hipError_t dflash_launch_lmhead(const LmArgs* a, hipStream_t st) {
   const dim3 grid(a->V / 32), block(64);
   const int m_tiles = pad16(a->M) >> 4;
-  if (m_tiles <= 1) hipLaunchKernelGGL((lmhead_kernel<1, 4>), grid, block, 0, st, *a);
-  else if (m_tiles <= 2) hipLaunchKernelGGL((lmhead_kernel<2, 2>), grid, block, 0, st, *a);
-  else hipLaunchKernelGGL((lmhead_kernel<4, 2>), grid, block, 0, st, *a);
+  if (m_tiles <= 1) launch_kernel((lmhead_kernel<1, 4>), grid, block, 0, st, *a);
+  else if (m_tiles <= 2) launch_kernel((lmhead_kernel<2, 2>), grid, block, 0, st, *a);
+  else launch_kernel((lmhead_kernel<4, 2>), grid, block, 0, st, *a);
   return hipGetLastError();
 }
 
@@ -94,6 +94,6 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void argmax_reduce_kernel(Argmax
 }
 
 extern "C" hipError_t dflash_launch_argmax(const ArgmaxArgs* a, hipStream_t st) {
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(a->M), dim3(256), 0, st, *a);
+  launch_kernel(argmax_reduce_kernel, dim3(a->M), dim3(256), 0, st, *a);
   return hipGetLastError();
 }

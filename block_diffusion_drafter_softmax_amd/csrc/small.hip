@@ -55,7 +55,7 @@ __global__ LATENCY_BOUND void plan_kernel(PlanArgs a) {
 }
 
 extern "C" hipError_t dflash_launch_plan(const PlanArgs* a, hipStream_t st) {
-  hipLaunchKernelGGL(plan_kernel, dim3((a->B + 63) / 64), dim3(64), 0, st, *a);
+  launch_kernel(plan_kernel, dim3((a->B + 63) / 64), dim3(64), 0, st, *a);
   return hipGetLastError();
 }
 
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
 
 extern "C" hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st) {
   const int threads = std::min(1024, ((a->H / 4 + 63) / 64) * 64);
-  hipLaunchKernelGGL(fuse_kernel, dim3(a->rows), dim3(threads), 0, st, *a);
+  launch_kernel(fuse_kernel, dim3(a->rows), dim3(threads), 0, st, *a);
   return hipGetLastError();
 }
 
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
 
 extern "C" hipError_t dflash_launch_norm(const NormArgs* a, hipStream_t st) {
   const int threads = std::min(1024, ((a->H / 4 + 63) / 64) * 64);
-  hipLaunchKernelGGL(norm_kernel, dim3(a->M), dim3(threads), 0, st, *a);
+  launch_kernel(norm_kernel, dim3(a->M), dim3(threads), 0, st, *a);
   return hipGetLastError();
 }
 
@@ -210,6 +210,6 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
 
 extern "C" hipError_t dflash_launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(256), dim3(256), 0, st, p, n, v);
+  launch_kernel(fill_u32_kernel, dim3(256), dim3(256), 0, st, p, n, v);
   return hipGetLastError();
 }
