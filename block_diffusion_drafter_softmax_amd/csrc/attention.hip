@@ -3,237 +3,290 @@
 // is not autoregressive; the fused target context enters each draft layer
 // as keys/values only).
 //
-// Work item = (key chunk, kv head, sequence). Chunk 0 is the block's own N
-// keys; chunks 1.. cover the context in pieces of CH = 128 keys (8 pages).
-// A workgroup holds all R = (n_q/n_kv)*N query rows of one kv head (GQA: a
-// K/V tile is read from HBM once for the whole query group), one wave per 16
-// rows. The chunk's page indices are read first, then every K and V byte of
-// the chunk is requested at once and staged in LDS, so a workgroup waits for
-// two memory latencies in total. Per 32-key step a wave computes S^T = K Q^T
-// with MFMA (keys as rows, the lane's query as column), runs an online
-// softmax in the log2 domain, and accumulates O^T += V^T P^T with MFMA: V is
-// stored dim-major per page ([d_h][16 slots]), so its A-operand fragments are
-// contiguous, and P^T comes straight from the S^T accumulators (both MFMAs use
-// the same permutation of the 32 keys). Q and P are fp32 values entering
-// the MFMAs as hi/lo bf16 pairs (two MFMAs each); K and V are bf16 storage.
-// Unnormalised O, the running max and the sum go to a partial buffer;
-// attn_merge_kernel combines the chunks.
+// Keys are numbered in a virtual order: slots 0..15 are the block's own K/V
+// (laid out like one cache page; slots >= N are invalid), then context key
+// j is virtual key 16 + j, so virtual page p >= 1 is context page p - 1.
+// Work item = (chunk of CH = 128 virtual keys, kv head, sequence). A
+// workgroup holds all R = (n_q/n_kv)*N query rows of one kv head (GQA: a
+// K/V tile is read from HBM once for the whole query group), one computing
+// wave per 16 rows, and at least 8 waves for staging. The chunk's page
+// indices and the queries are loaded together; then every K and V byte of
+// the chunk is requested at once (one batch of <= 8 16-byte loads per
+// thread) and staged in LDS, V values of invalid slots written as zeros.
+// A computing wave then takes the whole chunk in one pass: S^T = K Q^T with
+// MFMA (keys as rows, the lane's query as column; hi and lo products in
+// separate accumulators where registers allow), one softmax in the log2
+// domain (the scale
+// log2(e)/sqrt(d_h) is applied to Q when it is written), and O^T += V^T P^T:
+// V is staged per page as [half][d_h][8 slots], so an A-operand fragment
+// is one 16-byte read, and P^T comes straight from the S^T
+// accumulators (both MFMAs use the same permutation of the keys, chosen so
+// that every LDS read is a conflict-free 16-byte read). Q and P
+// are fp32 values entering the MFMAs as hi/lo bf16 pairs (two MFMAs each);
+// K and V are bf16 storage. Unnormalised O, the chunk's max and sum go to a
+// partial buffer, and attn_merge_kernel combines the chunks.
+#include <algorithm>
+
 #include "common.h"
 #include "dflash.h"
 
 namespace {
 DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
-constexpr int CH = 128;  // context keys per work item
+constexpr int CH = 128;  // virtual keys per work item
+constexpr int PAGES = CH / 16;
+constexpr int MIN_WAVES = 8;  // staging waves per workgroup
+
+// LDS row of chunk key k. Within each 32-key group (two pages), key 8a + b
+// goes to row 4a + b of the group's first 16-row tile for b < 4 and of its
+// second tile for b >= 4. A lane then holds S for keys 8g .. 8g+3 (first
+// tile) and 8g+4 .. 8g+7 (second tile): its 8 P values of a k-step are 8
+// consecutive slots of one page, so the matching V fragment is one 16-byte
+// LDS read (V is kept per page as [half][dim][8 slots]).
+DEV int krow(int k) {
+  const int b = k & 7;
+  return (k & ~31) + (b & 4) * 4 + ((k >> 3) & 3) * 4 + (b & 3);
+}
+// Chunk key held by lane group g, accumulator i, of key tile j.
+DEV int tile_key(int j, int g, int i) { return (j >> 1) * 32 + 8 * g + (j & 1) * 4 + i; }
 }  // namespace
 
-template <int D>
+// NACC: accumulator sets for the S products (2: hi and lo separately, more
+// independent MFMA chains; 1 where 1024-thread workgroups cap the registers).
+template <int D, int NACC>
 __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs a) {
-  constexpr int KP = D + 8;          // padded LDS row of one key (bf16 elements)
-  constexpr int PAGES = CH / 16;
-  __shared__ uint16_t k_lds[CH * KP];
-  __shared__ uint16_t v_lds[PAGES * D * 16];
-  __shared__ int pg[PAGES];
+  constexpr int KP = D + 8;  // padded LDS row of one key (bf16 elements)
+  constexpr int K_ELEMS = CH * KP, V_ELEMS = PAGES * D * 16;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[K_ELEMS + V_ELEMS];
+  __shared__ int pg[PAGES];   // page of each chunk page slot (-1: the block)
+  __shared__ int cnt[PAGES];  // valid key slots of each chunk page slot
 
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int seq = clampi(a.seq_ids[b], 0, a.max_seqs - 1);
   const int L = clampi(a.ctx_len[seq], 0, a.max_pages_per_seq * 16);
-  int key_begin, key_end;
-  if (c == 0) {
-    key_begin = 0;
-    key_end = a.N;
-  } else {
-    key_begin = (c - 1) * CH;
-    key_end = min(L, c * CH);
-    if (key_begin >= key_end) return;
-  }
-  const int nkeys = key_end - key_begin;
-  const int np = (nkeys + 15) / 16;
+  const int v_begin = c * CH;
+  const int nv = min(16 + L, v_begin + CH) - v_begin;  // virtual keys in this chunk
+  if (nv <= 0) return;
+  const int np = (nv + 15) / 16;
   const int tid = threadIdx.x, nthreads = blockDim.x;
   const size_t page_elems = (size_t)2 * a.n_kv * 16 * D;
 
-  if (tid < np) {
-    int p = 0;
-    if (c > 0) {
-      const int raw = a.page_table[(size_t)seq * a.max_pages_per_seq + key_begin / 16 + tid];
-      if (raw < 0 || raw >= a.n_pages) set_error(a.err, DFLASH_DEV_BAD_PAGE);
-      p = clampi(raw, 0, a.n_pages - 1);
+  if (tid < PAGES) {
+    int p = -1, n_ok = 0;
+    if (tid < np) {
+      const int vp = v_begin / 16 + tid;
+      if (vp > 0) {
+        const int raw = a.page_table[(size_t)seq * a.max_pages_per_seq + vp - 1];
+        if (raw < 0 || raw >= a.n_pages) set_error(a.err, DFLASH_DEV_BAD_PAGE);
+        p = clampi(raw, 0, a.n_pages - 1);
+      }
+      n_ok = vp == 0 ? a.N : min(16, nv - 16 * tid);
     }
     pg[tid] = p;
+    cnt[tid] = n_ok;
+  }
+
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int G = a.n_q / a.n_kv, R = G * a.N, n_wr = R / 16;
+  const int r = min(wave, n_wr - 1) * 16 + r16;
+  const int hq = kvh * G + r / a.N, n = r % a.N;
+  constexpr int KD = D / 32, DT = D / 16;
+
+  // queries (softmax scale already applied): in flight with the page reads
+  bf16x8 qh[KD], ql[KD];
+  {
+    const uint16_t* qp = a.q + ((size_t)(b * a.N + n) * a.n_q + hq) * D + 8 * g;
+    const size_t q_lo = (size_t)gridDim.z * a.N * a.n_q * D;
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) {
+      qh[kd] = ld8(qp + kd * 32);
+      ql[kd] = ld8(qp + q_lo + kd * 32);
+    }
   }
   __syncthreads();
 
-  // Stage K (slot-major rows) and V (dim-major) of the chunk's pages in LDS:
-  // per page, 2*D*16 bf16 = 4*D 16-byte units (K units first, then V units).
-  // Batches of 8 loads per thread, all in flight before the LDS stores: unit
-  // indices are clamped (a clamped duplicate loads valid memory and is not
-  // stored), so no branch separates the loads.
+  // Stage K (slot-major rows) and V (dim-major) of all PAGES page slots in
+  // LDS: per page, 2*D*16 bf16 = 4*D 16-byte units (K units first, then V
+  // units). Slots past the chunk's pages read the block (valid memory) and
+  // count 0 valid keys, so every V value of an invalid key is stored as 0
+  // and the MFMAs never meet stale values; K of invalid keys is masked in S.
+  // One batch of 8 loads per thread when nthreads * 8 covers the chunk.
   constexpr int UNITS_PER_PAGE = 4 * D;
-  const int total_units = np * UNITS_PER_PAGE;
+  constexpr int TOTAL_UNITS = PAGES * UNITS_PER_PAGE;
   const uint16_t* blk_k = a.kblk + ((size_t)b * a.n_kv + kvh) * 16 * D;
   const uint16_t* blk_v = a.vblk + ((size_t)b * a.n_kv + kvh) * D * 16;
-  for (int base = 0; base < total_units; base += 8 * nthreads) {
-    int uu[8], pgv[8];
+  for (int base = 0; base < TOTAL_UNITS; base += 8 * nthreads) {
+    int uu[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) uu[j] = min(base + j * nthreads + tid, total_units - 1);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pgv[j] = pg[uu[j] / UNITS_PER_PAGE];
+    for (int j = 0; j < 8; ++j) uu[j] = min(base + j * nthreads + tid, TOTAL_UNITS - 1);
     u32x4 buf[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int p = uu[j] / UNITS_PER_PAGE, w = uu[j] % UNITS_PER_PAGE;
-      const uint16_t* kb = (c == 0) ? blk_k : a.pages + pgv[j] * page_elems + (size_t)kvh * 16 * D;
-      const uint16_t* vb = (c == 0) ? blk_v : kb + (size_t)a.n_kv * 16 * D;
+      const int pgv = pg[p];
+      const uint16_t* kb = pgv < 0 ? blk_k : a.pages + pgv * page_elems + (size_t)kvh * 16 * D;
+      const uint16_t* vb = pgv < 0 ? blk_v : kb + (size_t)a.n_kv * 16 * D;
       const uint16_t* src = (w < 2 * D) ? kb + (w / (D / 8)) * D + (w % (D / 8)) * 8 : vb + (w - 2 * D) * 8;
       buf[j] = *reinterpret_cast<const u32x4*>(src);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (base + j * nthreads + tid >= total_units) continue;
+      // a clamped duplicate rewrites the last unit with the same value
       const int p = uu[j] / UNITS_PER_PAGE, w = uu[j] % UNITS_PER_PAGE;
-      if (w < 2 * D) {  // K: 16 slots x D, 8 elements per unit
-        *reinterpret_cast<u32x4*>(&k_lds[(p * 16 + w / (D / 8)) * KP + (w % (D / 8)) * 8]) = buf[j];
-      } else {
-        *reinterpret_cast<u32x4*>(&v_lds[p * D * 16 + (w - 2 * D) * 8]) = buf[j];
-      }
+      const bool isk = w < 2 * D;
+      const int valid = isk ? 8 : cnt[p] - ((w - 2 * D) & 1) * 8;  // V unit: slots 8*(w&1) .. +7
+      u32x4 m;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m[e] = (2 * e < valid ? 0xFFFFu : 0u) | (2 * e + 1 < valid ? 0xFFFF0000u : 0u);
+      const int key = p * 16 + w / (D / 8);  // K unit: chunk key, 8 dims
+      const int e = w - 2 * D;               // V unit: dim e/2, slots 8*(e&1) .. +7
+      const int off = isk ? krow(key) * KP + (w % (D / 8)) * 8
+                          : K_ELEMS + p * D * 16 + (e & 1) * D * 8 + (e >> 1) * 8;
+      *reinterpret_cast<u32x4*>(&lds[off]) = buf[j] & m;
     }
   }
   __syncthreads();
+  if (wave >= n_wr) return;
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int G = a.n_q / a.n_kv, R = G * a.N;
-  const int r = wave * 16 + r16;
-  const int hq = kvh * G + r / a.N, n = r % a.N;
-  constexpr int KD = D / 32, DT = D / 16;
-
-  bf16x8 qh[KD], ql[KD];
-  const uint16_t* qp = a.q + ((size_t)(b * a.N + n) * a.n_q + hq) * D + 8 * g;
-  const size_t q_lo = (size_t)gridDim.z * a.N * a.n_q * D;
-#pragma unroll
-  for (int kd = 0; kd < KD; ++kd) {
-    qh[kd] = ld8(qp + kd * 32);
-    ql[kd] = ld8(qp + q_lo + kd * 32);
-  }
-
+  // Key tile j = LDS rows 16j .. 16j+15; the lane holds S for keys
+  // tile_key(j, g, 0..3) of its query.
+  constexpr int NT = CH / 16;
   f32x4 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  for (int k0 = 0; k0 < nkeys; k0 += 32) {  // chunk-relative keys
-    const bool t1 = k0 + 16 < nkeys;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  float mx = -INFINITY, l = 0.f;
+  {
+    f32x4 s[NT];
+    {
+      f32x4 sa[NACC][NT];
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[(k0 + r16) * KP + kd * 32 + 8 * g]);
-      s0 = mfma16(kf, qh[kd], s0);
-      s0 = mfma16(kf, ql[kd], s0);
-    }
-    if (t1) {
+      for (int h = 0; h < NACC; ++h)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) sa[h][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kd = 0; kd < KD; ++kd) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[(k0 + 16 + r16) * KP + kd * 32 + 8 * g]);
-        s1 = mfma16(kf, qh[kd], s1);
-        s1 = mfma16(kf, ql[kd], s1);
+        bf16x8 kf[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          kf[j] = *reinterpret_cast<const bf16x8*>(&lds[(16 * j + r16) * KP + kd * 32 + 8 * g]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          sa[0][j] = mfma16(kf[j], qh[kd], sa[0][j]);
+          sa[NACC - 1][j] = mfma16(kf[j], ql[kd], sa[NACC - 1][j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) s[j] = NACC == 2 ? sa[0][j] + sa[NACC - 1][j] : sa[0][j];
+    }
+    if (v_begin < 16 || nv < CH) {  // edge chunk: mask invalid keys
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int k0 = tile_key(j, g, 0);  // 4 keys k0 .. k0+3 of one page
+        const int nj = cnt[k0 >> 4] - (k0 & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[j][i] = i < nj ? s[j][i] : -INFINITY;
       }
     }
-    // lane holds keys k0 + 4g + i (s0) and k0 + 16 + 4g + i (s1) for query r
-    float x[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = (k0 + 4 * g + i < nkeys) ? s0[i] * a.scale_log2 : -INFINITY;
-      x[4 + i] = (t1 && k0 + 16 + 4 * g + i < nkeys) ? s1[i] * a.scale_log2 : -INFINITY;
-    }
-    float mt = x[0];
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float corr = exp2f(m_run - m_new);
-    f32x4 p0, p1;
-    float psum = 0.f;
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // finite: every chunk has a valid key
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p0[i] = exp2f(x[i] - m_new);
-      p1[i] = exp2f(x[4 + i] - m_new);
-      psum += p0[i] + p1[i];
-    }
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-    u16x4 h0, l0, h1, l1;
-    split4(p0, h0, l0);
-    split4(p1, h1, l1);
-    const bf16x8 ph = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
-    const bf16x8 pl = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
-    const uint16_t* vp0 = &v_lds[(k0 / 16) * D * 16];
-    const uint16_t* vp1 = vp0 + D * 16;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      u16x4 v0 = *reinterpret_cast<const u16x4*>(vp0 + (t * 16 + r16) * 16 + 4 * g);
-      u16x4 v1 = {0, 0, 0, 0};
-      if (t1) v1 = *reinterpret_cast<const u16x4*>(vp1 + (t * 16 + r16) * 16 + 4 * g);
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (k0 + 4 * g + i >= nkeys) v0[i] = 0;
-        if (k0 + 16 + 4 * g + i >= nkeys) v1[i] = 0;
+        s[j][i] = exp2f(s[j][i] - mx);
+        l += s[j][i];
       }
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[t] = acc[t] * corr;
-      acc[t] = mfma16(vf, ph, acc[t]);
-      acc[t] = mfma16(vf, pl, acc[t]);
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+
+#pragma unroll
+    for (int j = 0; j < NT; j += 2) {  // k-step: key tiles j and j+1 (32 keys, 2 pages)
+      // lane's keys: slots 8*(g&1) .. +7 of the step's page g>>1
+      bf16x8 vf[DT];
+      const uint16_t* vp = &lds[K_ELEMS + (j + (g >> 1)) * D * 16 + (g & 1) * D * 8 + r16 * 8];
+#pragma unroll
+      for (int t = 0; t < DT; ++t) vf[t] = *reinterpret_cast<const bf16x8*>(vp + t * 128);
+      u16x4 h0, l0, h1, l1;
+      split4(s[j], h0, l0);
+      split4(s[j + 1], h1, l1);
+      const bf16x8 ph = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8 pl = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        acc[t] = mfma16(vf[t], ph, acc[t]);
+        acc[t] = mfma16(vf[t], pl, acc[t]);
+      }
     }
   }
-  float l = l_run + __shfl_xor(l_run, 16, 64);
-  l += __shfl_xor(l, 32, 64);
 
   const size_t unit = ((size_t)b * a.n_kv + kvh) * a.n_ck + c;
   float* po = a.part_o + (unit * R + r) * D;
 #pragma unroll
   for (int t = 0; t < DT; ++t) *reinterpret_cast<f32x4*>(po + t * 16 + 4 * g) = acc[t];
   if (g == 0) {
-    a.part_ml[(unit * R + r) * 2 + 0] = m_run;
+    a.part_ml[(unit * R + r) * 2 + 0] = mx;
     a.part_ml[(unit * R + r) * 2 + 1] = l;
   }
 }
 
-// One thread per (sequence, kv head, query row, 4 dims): single-pass
-// log-sum-exp merge of the chunk partials in chunk order, normalise, and
-// write the O-projection's packed split activation.
+// One workgroup per (sequence, kv head, query row): thread (cg, dq) merges
+// chunks cg, cg + CG, ... for dims 4*dq .. 4*dq+3 (all its loads in one
+// batch of <= 8), then the CG partial merges are combined in cg order
+// through LDS; the result is normalised and written as the O projection's
+// packed split activation. Deterministic (fixed order).
 template <int D>
 __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs a, int B) {
+  constexpr int TPR = D / 4, CG = 256 / TPR;
+  __shared__ float sm[CG], sd[CG];
+  __shared__ f32x4 sn[CG][TPR];
   const int G = a.n_q / a.n_kv, R = G * a.N;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  const int dq = idx % (D / 4);
-  const int r = (idx / (D / 4)) % R;
-  const int kvh = (idx / (D / 4) / R) % a.n_kv;
-  const int b = idx / (D / 4) / R / a.n_kv;
-  if (b >= B) return;
+  const int r = blockIdx.x % R;
+  const int kvh = (blockIdx.x / R) % a.n_kv;
+  const int b = blockIdx.x / R / a.n_kv;
+  const int dq = threadIdx.x % TPR, cg = threadIdx.x / TPR;
   const int seq = clampi(a.seq_ids[b], 0, a.max_seqs - 1);
   const int L = clampi(a.ctx_len[seq], 0, a.max_pages_per_seq * 16);
-  const int nc = min(a.n_ck, 1 + (L + CH - 1) / CH);
+  const int nc = min(a.n_ck, (16 + L + CH - 1) / CH);
   const size_t unit0 = ((size_t)b * a.n_kv + kvh) * a.n_ck;
   float M = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  constexpr int GRP = 8;  // chunks whose loads are in flight together (more costs time on gfx950)
-  for (int c0 = 0; c0 < nc; c0 += GRP) {
+  constexpr int GRP = 8;  // loads in flight per thread (more costs time on gfx950)
+  for (int c0 = cg; c0 < nc; c0 += GRP * CG) {
     float2 ml[GRP];
     f32x4 ov[GRP];
 #pragma unroll
     for (int j = 0; j < GRP; ++j) {
-      const size_t row = (unit0 + min(c0 + j, nc - 1)) * R + r;
+      const size_t row = (unit0 + min(c0 + j * CG, nc - 1)) * R + r;
       ml[j] = *reinterpret_cast<const float2*>(a.part_ml + row * 2);
       ov[j] = *reinterpret_cast<const f32x4*>(a.part_o + row * D + dq * 4);
     }
 #pragma unroll
     for (int j = 0; j < GRP; ++j) {
-      if (c0 + j >= nc) break;
+      if (c0 + j * CG >= nc) break;
       const float Mn = fmaxf(M, ml[j].x);
       const float wo = exp2f(M - Mn), wn = exp2f(ml[j].x - Mn);
       den = den * wo + ml[j].y * wn;
       num = num * wo + ov[j] * wn;
       M = Mn;
     }
+  }
+  if (dq == 0) {
+    sm[cg] = M;
+    sd[cg] = den;
+  }
+  sn[cg][dq] = num;
+  __syncthreads();
+  if (cg != 0) return;
+  for (int k = 1; k < CG && k < nc; ++k) {  // group k holds >= 1 chunk
+    const float Mn = fmaxf(M, sm[k]);
+    const float wo = exp2f(M - Mn), wn = exp2f(sm[k] - Mn);
+    den = den * wo + sd[k] * wn;
+    num = num * wo + sn[k][dq] * wn;
+    M = Mn;
   }
   const float inv = 1.0f / den;
   const int hq = kvh * G + r / a.N, n = r % a.N;
@@ -246,17 +299,22 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
 }
 
 extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
-  const int G = a->n_q / a->n_kv, R = G * a->N;
-  const dim3 grid(a->n_ck, a->n_kv, B), block(64 * (R / 16));
-  if (head_dim == 128) launch_kernel(attn_chunk_kernel<128>, grid, block, 0, st, *a);
-  else launch_kernel(attn_chunk_kernel<64>, grid, block, 0, st, *a);
+  const int G = a->n_q / a->n_kv, n_wr = G * a->N / 16;
+  const int waves = std::max(n_wr, MIN_WAVES);
+  const dim3 grid(a->n_ck, a->n_kv, B), block(64 * waves);
+  if (head_dim == 128) {
+    if (waves <= 8) launch_kernel(attn_chunk_kernel<128, 2>, grid, block, 0, st, *a);
+    else launch_kernel(attn_chunk_kernel<128, 1>, grid, block, 0, st, *a);
+  } else {
+    if (waves <= 8) launch_kernel(attn_chunk_kernel<64, 2>, grid, block, 0, st, *a);
+    else launch_kernel(attn_chunk_kernel<64, 1>, grid, block, 0, st, *a);
+  }
   return hipGetLastError();
 }
 
 extern "C" hipError_t dflash_launch_attn_merge(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
   const int G = a->n_q / a->n_kv, R = G * a->N;
-  const int total = B * a->n_kv * R * (head_dim / 4);
-  const dim3 grid((total + 255) / 256), block(256);
+  const dim3 grid(B * a->n_kv * R), block(256);
   if (head_dim == 128) launch_kernel(attn_merge_kernel<128>, grid, block, 0, st, *a, B);
   else launch_kernel(attn_merge_kernel<64>, grid, block, 0, st, *a, B);
   return hipGetLastError();

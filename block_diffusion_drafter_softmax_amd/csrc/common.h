@@ -38,12 +38,11 @@ inline hipError_t launch_kernel(void (*k)(Args...), dim3 g, dim3 b, uint32_t shm
 // bf16 bits -> fp32 (exact).
 DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-DEV uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even (the hardware conversion).
+DEV uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
 // fp32 -> bf16 pair (hi, lo) with hi + lo = x to about 2^-17 relative.
 DEV void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
@@ -51,14 +50,20 @@ DEV void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
   lo = f2bf(x - bf2f(hi));
 }
 
+// Two values at a time with the packed hardware conversion.
+DEV void split2(f32x2 x, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = __builtin_convertvector(x, bf16x2);
+  const bf16x2 l = __builtin_convertvector(x - __builtin_convertvector(h, f32x2), bf16x2);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 DEV void split4(const f32x4& x, u16x4& hi, u16x4& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint16_t a, b;
-    split_bf16(x[i], a, b);
-    hi[i] = a;
-    lo[i] = b;
-  }
+  uint32_t h0, l0, h1, l1;
+  split2(f32x2{x[0], x[1]}, h0, l0);
+  split2(f32x2{x[2], x[3]}, h1, l1);
+  hi = __builtin_bit_cast(u16x4, (uint32_t __attribute__((ext_vector_type(2)))){h0, h1});
+  lo = __builtin_bit_cast(u16x4, (uint32_t __attribute__((ext_vector_type(2)))){l0, l1});
 }
 
 // 16 bytes = 8 bf16 from global memory.

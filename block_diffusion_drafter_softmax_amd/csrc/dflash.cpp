@@ -36,7 +36,7 @@ int fail(int code, const char* fmt, ...) {
     if (e_ != hipSuccess) return fail(DFLASH_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_));     \
   } while (0)
 
-constexpr int kAttnChunk = 128;     // context keys per attention work item (attention.hip: CH)
+constexpr int kAttnChunk = 128;     // virtual keys (16 block slots + context) per attention work item
 constexpr int kVerifyChunk = 8192;  // logits per verification work item
 constexpr int kKsMax = 8;           // largest k split of a streaming GEMM (KS_MAX in common.h)
 constexpr int kTargetWaves = 1536;  // streaming waves to aim for (~6 per CU)
@@ -63,7 +63,7 @@ Layout make_layout(const dflash_config& c) {
   L.m_max = (int)(Bm * N);
   L.rows_a_max = (int)(Bm * c.max_new);
   const size_t mp = pad16(L.m_max), rp = pad16(L.rows_a_max);
-  L.n_ck = 1 + (c.max_pages_per_seq * 16 + kAttnChunk - 1) / kAttnChunk;
+  L.n_ck = (16 + c.max_pages_per_seq * 16 + kAttnChunk - 1) / kAttnChunk;
   L.n_vchunks = (c.vocab + kVerifyChunk - 1) / kVerifyChunk;
   const size_t ncol_d = std::max(qd + 2 * kvd, H), ncol_c = D * 2 * kvd;
   L.gpart_floats = ncol_d * std::max<size_t>(256, 2 * (size_t)L.m_max);
@@ -139,10 +139,12 @@ int check_config(const dflash_config* c) {
   return DFLASH_OK;
 }
 
+constexpr size_t kTimerCap = 4096;  // timed launches between reads
+
 struct Timer {
   bool on = false;
   std::vector<hipEvent_t> ev;  // pairs (start, stop)
-  size_t used = 0;             // events in use (2 per launch)
+  size_t used = 0;             // launches timed
 };
 
 }  // namespace
@@ -168,14 +170,14 @@ struct dflash_ctx {
     hipEvent_t e0 = nullptr, e1 = nullptr;
     const bool around = kind == DFLASH_K_VERIFY;
     if (t.on) {
-      if (t.used + 2 > 2 * 4096) return fail(DFLASH_ERR_CAPACITY, "kernel timer full: read it first");
-      while (t.ev.size() < t.used + 2) {
+      if (t.used >= kTimerCap) return fail(DFLASH_ERR_CAPACITY, "kernel timer full: read it first");
+      while (t.ev.size() < 2 * t.used + 2) {
         hipEvent_t e;
         HIP_OK(hipEventCreate(&e));
         t.ev.push_back(e);
       }
-      e0 = t.ev[t.used];
-      e1 = t.ev[t.used + 1];
+      e0 = t.ev[2 * t.used];
+      e1 = t.ev[2 * t.used + 1];
       if (around) HIP_OK(hipEventRecord(e0, st));
       else dflash_launch_events = LaunchEvents{e0, e1};
     }
@@ -184,7 +186,7 @@ struct dflash_ctx {
     if (e != hipSuccess) return fail(DFLASH_ERR_HIP, "kernel launch (kind %d): %s", kind, hipGetErrorString(e));
     if (t.on) {
       if (around) HIP_OK(hipEventRecord(e1, st));
-      t.used += 2;
+      t.used += 1;
     }
     return DFLASH_OK;
   }
@@ -473,7 +475,7 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   aa.max_pages_per_seq = c.max_pages_per_seq;
   aa.n_pages = c.n_pages;
   aa.max_seqs = c.max_seqs;
-  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+  qa.q_scale = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
   const long long layer_stride = (long long)c.n_pages * 2 * kvd * 16;
 
   for (int i = 0; i < D; ++i) {
@@ -614,14 +616,14 @@ int dflash_kernel_timer_read(dflash_ctx* ctx, int32_t kind, double* total_ms, in
     return fail(DFLASH_ERR_INVALID_ARG, "bad arguments");
   Timer& t = ctx->timers[kind];
   double tot = 0;
-  for (size_t i = 0; i + 1 < t.used; i += 2) {
-    HIP_OK(hipEventSynchronize(t.ev[i + 1]));
+  for (size_t i = 0; i < t.used; ++i) {
+    HIP_OK(hipEventSynchronize(t.ev[2 * i + 1]));
     float ms = 0.f;
-    HIP_OK(hipEventElapsedTime(&ms, t.ev[i], t.ev[i + 1]));
+    HIP_OK(hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]));
     tot += ms;
   }
   *total_ms = tot;
-  *launches = (int64_t)(t.used / 2);
+  *launches = (int64_t)t.used;
   t.used = 0;
   return DFLASH_OK;
 }

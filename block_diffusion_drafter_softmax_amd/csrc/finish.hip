@@ -44,11 +44,11 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void qkv_finish_kernel(QkvFinish
     float x2 = split_sum(a.part, a.ks, a.M, n_cols, m, col + half);
     rotate(x1, x2, a.rope, clampi(a.ctx_len[clampi(a.seq_ids[b], 0, a.max_seqs - 1)] + n, 0, a.max_pos - 1),
            half, i);
-    if (isq) {  // query: split activation of the attention
+    if (isq) {  // query, scaled for a log2-domain softmax: split activation of the attention
       uint16_t* dst = a.q + ((size_t)m * a.n_q + head) * d;
       const size_t lo = (size_t)a.M * a.n_q * d;
-      split_bf16(x1, dst[i], dst[lo + i]);
-      split_bf16(x2, dst[i + half], dst[lo + i + half]);
+      split_bf16(x1 * a.q_scale, dst[i], dst[lo + i]);
+      split_bf16(x2 * a.q_scale, dst[i + half], dst[lo + i + half]);
     } else {  // block key: bf16 storage
       uint16_t* dst = a.kblk + (((size_t)b * a.n_kv + head) * 16 + n) * d;
       dst[i] = f2bf(x1);

@@ -75,6 +75,7 @@ struct QkvFinishArgs {
   const int* ctx_len;
   int max_seqs, max_pos;
   const float* rope;  // [max_pos][d/2][2] or null (no rotation)
+  float q_scale;      // applied to rotated queries: log2(e) / sqrt(d) (attention works in log2 units)
   uint16_t* q;        // split: hi [M][n_q][d], lo at + M*n_q*d
   uint16_t* kblk;     // [B][n_kv][16][d]
   uint16_t* vblk;     // [B][n_kv][d][16]
@@ -94,7 +95,7 @@ struct CtxFinishArgs {
 
 // ------------------------------------------------------------ attention
 struct AttnArgs {
-  const uint16_t* q;       // split: hi [B*N][n_q][d], lo at + B*N*n_q*d
+  const uint16_t* q;       // split: hi [B*N][n_q][d], lo at + B*N*n_q*d; pre-scaled by log2(e)/sqrt(d)
   const uint16_t* kblk;    // [B][n_kv][16][d]
   const uint16_t* vblk;    // [B][n_kv][d][16]
   const uint16_t* pages;   // this layer's pages [n_pages][2][n_kv][16*d]
@@ -106,7 +107,6 @@ struct AttnArgs {
   uint16_t* o;             // merge output, packed split activation (planes of act_plane(B*N, n_q*d))
   int32_t* err;
   int N, n_q, n_kv, chunk, n_ck, max_pages_per_seq, n_pages, max_seqs;
-  float scale_log2;        // log2(e) / sqrt(d)
 };
 
 // ------------------------------------------------------------ small kernels
@@ -194,6 +194,7 @@ struct LaunchEvents {
   hipEvent_t stop;
 };
 extern thread_local LaunchEvents dflash_launch_events;
+
 
 extern "C" {
 hipError_t dflash_launch_ws(const WsArgs* a, int mode, hipStream_t st);

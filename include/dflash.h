@@ -222,7 +222,8 @@ int dflash_read_error(dflash_ctx* ctx, hipStream_t stream, int32_t* out);
  * the totals. Capacity: 4096 launches between reads. A timed launch of a
  * single-kernel kind records the kernel's own start and end (the events of
  * hipExtLaunchKernel); DFLASH_K_VERIFY is timed between event records on
- * the stream around its one or two kernels. Timing is meant for eager
+ * the stream around its one or two kernels. Timing adds a few microseconds
+ * of stream idle time around each timed launch; it is meant for eager
  * launches, not for graph capture. */
 int dflash_kernel_timer(dflash_ctx* ctx, int32_t kind, int32_t enable);
 /* Synchronise the recorded events; *total_ms = summed launch durations,

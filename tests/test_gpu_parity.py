@@ -107,6 +107,17 @@ def test_gqa_8_to_1_head_dim_64():
     run_step(Case(cfg, ctx=[150], n_new=[8], seed=9, prefill_chunk=72))
 
 
+def test_gqa_16_to_1_rows_256_both_head_dims():
+    # 256 query rows per kv head: the attention's one-wave-per-row-group
+    # variant (16 computing waves), for d_h 64 and 128; contexts end inside
+    # and at the edge of a 128-key chunk; an empty context attends to the
+    # block alone
+    for d, ctx, n_new in ((64, [200, 112], [8, 3]), (128, [241, 0], [8, 0])):
+        cfg = small_cfg(hidden=256, n_q_heads=16, n_kv_heads=1, head_dim=d, intermediate=512,
+                        vocab=2048, block_size=16)
+        run_step(Case(cfg, ctx=ctx, n_new=n_new, seed=17 + d, page_order="shuffled", prefill_chunk=64))
+
+
 def test_wide_batch_multi_group_rows():
     # M = 5 * 16 = 80 rows -> several 64-row groups in the projection kernels
     cfg = small_cfg(hidden=256, block_size=16, n_q_heads=4, n_kv_heads=4)
