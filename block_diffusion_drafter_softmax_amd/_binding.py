@@ -27,8 +27,8 @@ DTYPE_BF16 = 0
 DTYPE_F32 = 1
 
 K_FUSE, K_CTX_KV, K_NORM, K_QKV, K_ATTN, K_ATTN_MERGE, K_OPROJ, K_GATE_UP, K_DOWN, \
-    K_LM_HEAD, K_ARGMAX, K_VERIFY, K_PLAN, K_QKV_FINISH, K_CTX_FINISH = range(15)
-K_COUNT = 15
+    K_LM_HEAD, K_ARGMAX, K_VERIFY, K_QKV_FINISH, K_CTX_FINISH = range(14)
+K_COUNT = 14
 KERNEL_NAMES = ["fuse", "ctx_kv", "norm", "qkv", "attn", "attn_merge", "o_proj", "gate_up",
                 "down", "lm_head", "argmax", "verify", "plan", "qkv_finish", "ctx_finish"]
 

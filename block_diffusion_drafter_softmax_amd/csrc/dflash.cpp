@@ -37,7 +37,8 @@ int fail(int code, const char* fmt, ...) {
   } while (0)
 
 constexpr int kAttnChunk = 128;     // virtual keys (16 block slots + context) per attention work item
-constexpr int kVerifyChunk = 8192;  // logits per verification work item
+constexpr int kVerifyChunk = 32768;       // logits per verification work item (rows pass)
+constexpr int kSampleChunk = 8192;        // logits per work item of the temperature-1 sampling pass
 constexpr int kKsMax = 8;           // largest k split of a streaming GEMM (KS_MAX in common.h)
 constexpr int kTargetWaves = 1536;  // streaming waves to aim for (~6 per CU)
 
@@ -48,10 +49,10 @@ struct Layout {
   // set-up tables and packed weights
   size_t alpha, rope, wq, wk_d, wv_d, wk_t, wv_t, wo, wg, wu, wd, lm;
   // per-call buffers
-  size_t rowpos_a, rowseq_a, rowpos_d, rowseq_d, f, x, h, q, o, kblk, vblk, mm, gpart, cpart;
+  size_t rowpos_a, rowseq_a, f, x, h, q, o, kblk, vblk, mm, gpart, cpart;
   size_t apo, aml, lmpart, vpart, vstate, counters, total;
   size_t gpart_floats, cpart_floats;
-  int n_ck, n_vchunks, m_max, rows_a_max;
+  int n_ck, n_vchunks, n_schunks, m_max, rows_a_max;
 };
 
 Layout make_layout(const dflash_config& c) {
@@ -65,6 +66,7 @@ Layout make_layout(const dflash_config& c) {
   const size_t mp = pad16(L.m_max), rp = pad16(L.rows_a_max);
   L.n_ck = (16 + c.max_pages_per_seq * 16 + kAttnChunk - 1) / kAttnChunk;
   L.n_vchunks = (c.vocab + kVerifyChunk - 1) / kVerifyChunk;
+  L.n_schunks = (c.vocab + kSampleChunk - 1) / kSampleChunk;
   const size_t ncol_d = std::max(qd + 2 * kvd, H), ncol_c = D * 2 * kvd;
   L.gpart_floats = ncol_d * std::max<size_t>(256, 2 * (size_t)L.m_max);
   L.cpart_floats = ncol_c * std::max<size_t>(256, 2 * (size_t)L.rows_a_max);
@@ -88,8 +90,6 @@ Layout make_layout(const dflash_config& c) {
   L.lm = take((size_t)c.vocab * H * 2);
   L.rowpos_a = take(L.rows_a_max * 4);
   L.rowseq_a = take(L.rows_a_max * 4);
-  L.rowpos_d = take(L.m_max * 4);
-  L.rowseq_d = take(L.m_max * 4);
   // activations are split hi/lo bf16 pairs: two planes each
   L.f = take(D * 2 * rp * H * 2);
   L.x = take(L.m_max * H * 4);
@@ -103,8 +103,8 @@ Layout make_layout(const dflash_config& c) {
   L.cpart = take(L.cpart_floats * 4);
   L.apo = take(Bm * c.n_kv_heads * L.n_ck * R * c.head_dim * 4);
   L.aml = take(Bm * c.n_kv_heads * L.n_ck * R * 2 * 4);
-  L.lmpart = take((size_t)(c.vocab / 32) * L.m_max * sizeof(Top2));
-  L.vpart = take(Bm * N * L.n_vchunks * 2 * 4);
+  L.lmpart = take((size_t)((c.vocab / 32 + 3) / 4) * L.m_max * sizeof(Top2));
+  L.vpart = take(Bm * std::max<size_t>(N * L.n_vchunks, L.n_schunks) * 2 * 4);
   L.vstate = take(Bm * 2 * 4);
   L.counters = take(Bm * 2 * 4);
   L.total = off;
@@ -131,6 +131,8 @@ int check_config(const dflash_config* c) {
   const int R = (c->n_q_heads / c->n_kv_heads) * c->block_size;
   if (R % 16 || R > 256)
     return fail(DFLASH_ERR_UNSUPPORTED, "(n_q/n_kv)*block_size must be a multiple of 16 and <= 256 (got %d)", R);
+  if ((long long)c->block_size * ((c->vocab + kVerifyChunk - 1) / kVerifyChunk) > VERIFY_MAX_PARTS)
+    return fail(DFLASH_ERR_UNSUPPORTED, "block_size * ceil(vocab / %d) must be <= %d", kVerifyChunk, VERIFY_MAX_PARTS);
   if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab)
     return fail(DFLASH_ERR_INVALID_ARG, "mask_token_id out of range");
   if (c->max_pos < c->block_size) return fail(DFLASH_ERR_INVALID_ARG, "max_pos too small");
@@ -334,31 +336,24 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
   const int H = c.hidden, D = c.n_layers, kvd = c.n_kv_heads * c.head_dim;
   int rc;
 
-  PlanArgs pa{};
-  pa.B = B;
-  pa.rows_per_seq = max_new;
-  pa.seq_ids = seq_ids;
-  pa.n_new = n_new;
-  pa.ctx_len = ctx->kv.ctx_len;
-  pa.page_table = ctx->kv.page_table;
-  pa.max_seqs = c.max_seqs;
-  pa.max_pages_per_seq = c.max_pages_per_seq;
-  pa.n_pages = c.n_pages;
-  pa.max_pos = c.max_pos;
-  pa.max_new = max_new;
-  pa.vocab = c.vocab;
-  pa.row_pos = ctx->at<int>(L.rowpos_a);
-  pa.row_seq = ctx->at<int>(L.rowseq_a);
-  pa.err = ctx->kv.error_word;
-  pa.append = 1;
-  if ((rc = ctx->launch(DFLASH_K_PLAN, stream, [&] { return dflash_launch_plan(&pa, stream); }))) return rc;
-
   FuseArgs fa{};
   fa.hidden = target_hidden;
   fa.alpha = ctx->at<float>(L.alpha);
   fa.g_fuse = ctx->w.g_fuse;
   fa.f = ctx->at<uint16_t>(L.f);
-  fa.row_pos = pa.row_pos;
+  fa.B = B;
+  fa.max_new = max_new;
+  fa.seq_ids = seq_ids;
+  fa.n_new = n_new;
+  fa.ctx_len = ctx->kv.ctx_len;
+  fa.page_table = ctx->kv.page_table;
+  fa.max_seqs = c.max_seqs;
+  fa.max_pages_per_seq = c.max_pages_per_seq;
+  fa.n_pages = c.n_pages;
+  fa.max_pos = c.max_pos;
+  fa.row_pos = ctx->at<int>(L.rowpos_a);
+  fa.row_seq = ctx->at<int>(L.rowseq_a);
+  fa.err = ctx->kv.error_word;
   fa.rows = rows;
   fa.T = c.n_target_layers;
   fa.H = H;
@@ -390,8 +385,12 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
   ca.D = D;
   ca.n_kv = c.n_kv_heads;
   ca.d = c.head_dim;
-  ca.row_pos = pa.row_pos;
-  ca.row_seq = pa.row_seq;
+  ca.row_pos = fa.row_pos;
+  ca.row_seq = fa.row_seq;
+  ca.B = B;
+  ca.max_new = max_new;
+  ca.n_new = n_new;
+  ca.ctx_len = ctx->kv.ctx_len;
   ca.page_table = ctx->kv.page_table;
   ca.max_pages_per_seq = c.max_pages_per_seq;
   ca.n_pages = c.n_pages;
@@ -547,7 +546,7 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
 
   ArgmaxArgs ma{};
   ma.part = la.part;
-  ma.n_parts = c.vocab / 32;
+  ma.n_parts = (c.vocab / 32 + 3) / 4;  // one per LM-head workgroup (4 waves of 32 vocabulary rows)
   ma.M = M;
   ma.N = N;
   ma.V = c.vocab;
@@ -578,6 +577,8 @@ int dflash_verify(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int3
   va.V = c.vocab;
   va.chunk = kVerifyChunk;
   va.n_chunks = L.n_vchunks;
+  va.s_chunk = kSampleChunk;
+  va.s_n_chunks = L.n_schunks;
   va.seq_ids = seq_ids;
   va.draft = draft;
   va.part = ctx->at<float>(L.vpart);

@@ -69,7 +69,9 @@ extern "C" hipError_t dflash_launch_qkv_finish(const QkvFinishArgs* a, hipStream
   return hipGetLastError();
 }
 
-// One thread per (appended row, layer, key rotation pair or value element).
+// One thread per (appended row, layer, key rotation pair or value element);
+// the first B threads also advance the context length of the call's
+// sequences (the append's last kernel: nothing after it reads the old one).
 __global__ __launch_bounds__(256) LATENCY_BOUND void ctx_finish_kernel(CtxFinishArgs a) {
   const int d = a.d, half = d / 2, kvd = a.n_kv * d;
   const int pk = a.n_kv * half;
@@ -77,6 +79,10 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void ctx_finish_kernel(CtxFinish
   const int per_row = a.D * per_layer;
   const int n_cols = a.D * 2 * kvd;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < a.B) {
+    const int m0 = idx * a.max_new;
+    if (a.row_pos[m0] >= 0) a.ctx_len[a.row_seq[m0]] = a.row_pos[m0] + a.n_new[idx];
+  }
   if (idx >= a.M * per_row) return;
   const int m = idx / per_row, rem = idx % per_row;
   const int pos = a.row_pos[m];

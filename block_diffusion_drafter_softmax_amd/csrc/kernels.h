@@ -84,6 +84,9 @@ struct QkvFinishArgs {
 struct CtxFinishArgs {
   const float* part;  // [ks][M][D * 2 * n_kv*d]: per layer K columns then V columns
   int ks, M, D, n_kv, d;
+  int B, max_new;     // the call's sequences: ctx_len[seq] advances by n_new[b]
+  const int* n_new;
+  int* ctx_len;
   const int* row_pos;  // < 0: row skipped
   const int* row_seq;
   const int* page_table;
@@ -110,26 +113,22 @@ struct AttnArgs {
 };
 
 // ------------------------------------------------------------ small kernels
-struct PlanArgs {
-  int B, rows_per_seq;  // max_new (append) or N (draft)
-  const int* seq_ids;
-  const int* n_new;     // append only
-  const int* anchor;    // draft only
-  int* ctx_len;
-  const int* page_table;
-  int max_seqs, max_pages_per_seq, n_pages, max_pos, max_new, vocab;
-  int* row_pos;         // [B*rows_per_seq]
-  int* row_seq;
-  int32_t* err;
-  int append;           // 1: append plan (advances ctx_len), 0: draft plan
-};
-
+// Context append, first kernel: the call's plan (positions, checks) and
+// DFLARE fusion + RMSNorm of every appended row for every draft layer.
 struct FuseArgs {
-  const uint16_t* hidden;  // [rows][T][H]
+  const uint16_t* hidden;  // [rows][T][H], row m = b*max_new + t
   const float* alpha;      // [D][T]
   const uint16_t* g_fuse;  // [D][H]
   uint16_t* f;             // per layer packed split activation, layer stride 2*act_plane(rows, H)
-  const int* row_pos;
+  int B, max_new;
+  const int* seq_ids;
+  const int* n_new;
+  const int* ctx_len;      // read only: the context finisher advances it
+  const int* page_table;
+  int max_seqs, max_pages_per_seq, n_pages, max_pos;
+  int* row_pos;            // [rows]: position, or -1 (row skipped)
+  int* row_seq;            // [rows]
+  int32_t* err;
   int rows, T, H, D;
   float eps;
 };
@@ -157,7 +156,7 @@ struct LmArgs {
   const uint16_t* w;    // packed [V/16][K/32][512]
   const uint16_t* act;  // packed split activation of the normed rows
   int M, K, V, N;       // N = block rows per sequence
-  Top2* part;           // [V/32][M]
+  Top2* part;           // [ceil(V/32/4)][M]: one top-2 per workgroup of 4 waves
   float* dbg_logits;    // nullable [B][N-1][V]
 };
 
@@ -169,13 +168,16 @@ struct ArgmaxArgs {
   int32_t* err;
 };
 
+#define VERIFY_MAX_PARTS 2048  // block rows * vocabulary chunks of one sequence
+
 struct VerifyArgs {
   const void* logits;   // [B][N][V]
   int dtype;            // DFLASH_DTYPE_*
-  int B, N, V, chunk, n_chunks;
+  int B, N, V, chunk, n_chunks;  // rows pass: logits per work item, work items per row
+  int s_chunk, s_n_chunks;       // temperature-1 sampling pass: the same for the sampled row
   const int* seq_ids;
   const int* draft;     // [B][N-1]
-  float* part;          // [B][N][n_chunks][2]
+  float* part;          // rows pass [B][N][n_chunks][2]; sampling pass [B][s_n_chunks][2]
   int* counters;        // [2*B], zero between calls
   int* state;           // [B][2]: sample row, excluded token
   int* accept_len;
@@ -203,7 +205,6 @@ hipError_t dflash_launch_qkv_finish(const QkvFinishArgs* a, hipStream_t st);
 hipError_t dflash_launch_ctx_finish(const CtxFinishArgs* a, hipStream_t st);
 hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_t st);
 hipError_t dflash_launch_attn_merge(const AttnArgs* a, int B, int head_dim, hipStream_t st);
-hipError_t dflash_launch_plan(const PlanArgs* a, hipStream_t st);
 hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st);
 hipError_t dflash_launch_norm(const NormArgs* a, hipStream_t st);
 hipError_t dflash_launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t st);

@@ -11,120 +11,111 @@ DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); 
 }
 
 
-// One thread per batch entry. Append: rows t < n_new[b] get positions
-// ctx_len .. ctx_len+n_new-1 and ctx_len advances; a failed check leaves the
-// sequence untouched and all its rows skipped. Draft: rows get positions
-// L .. L+N-1; checks only flag (positions are clamped into the tables).
-__global__ LATENCY_BOUND void plan_kernel(PlanArgs a) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= a.B) return;
-  int bad = 0;
-  const int s_raw = a.seq_ids[b];
-  if (s_raw < 0 || s_raw >= a.max_seqs) bad |= DFLASH_DEV_BAD_SEQ;
-  const int seq = clampi(s_raw, 0, a.max_seqs - 1);
-  const int L_raw = a.ctx_len[seq];
-  const int cap = min(a.max_pages_per_seq * 16, a.max_pos);
-  if (L_raw < 0 || L_raw > cap) bad |= DFLASH_DEV_NO_PAGES;
-  const int L = clampi(L_raw, 0, cap);
-  int n = a.rows_per_seq;
-  if (a.append) {
-    n = a.n_new[b];
-    if (n < 0 || n > a.max_new) bad |= DFLASH_DEV_BAD_N_NEW;
-    if (!bad && L + n > cap) bad |= DFLASH_DEV_NO_PAGES;
-    if (!bad) {
-      for (int p = L / 16; p < (L + n + 15) / 16; ++p) {
-        const int pg = a.page_table[(size_t)seq * a.max_pages_per_seq + p];
-        if (pg < 0 || pg >= a.n_pages) bad |= DFLASH_DEV_BAD_PAGE;
-      }
-    }
-  } else {
-    // context pages are validated by the attention kernel that reads them
-    if (L + n > a.max_pos) bad |= DFLASH_DEV_NO_PAGES;
-    const int anc = a.anchor[b];
-    if (anc < 0 || anc >= a.vocab) bad |= DFLASH_DEV_BAD_TOKEN;
-  }
-  if (bad) set_error(a.err, bad);
-  for (int t = 0; t < a.rows_per_seq; ++t) {
-    int pos;
-    if (a.append) pos = (!bad && t < n) ? L + t : -1;
-    else pos = clampi(L + t, 0, a.max_pos - 1);
-    a.row_pos[b * a.rows_per_seq + t] = pos;
-    a.row_seq[b * a.rows_per_seq + t] = seq;
-  }
-  if (a.append && !bad) a.ctx_len[seq] = L + n;
-}
-
-extern "C" hipError_t dflash_launch_plan(const PlanArgs* a, hipStream_t st) {
-  launch_kernel(plan_kernel, dim3((a->B + 63) / 64), dim3(64), 0, st, *a);
-  return hipGetLastError();
-}
-
 // ------------------------------------------------------------ fusion
 
 #define FUSE_MAXV 2   // float4 groups per thread: H <= 1024 * 4 * 2
-#define FUSE_DMAX 64  // draft layers whose fusion weights fit the LDS table
 #define FUSE_TMAX 16  // target layers
 
-// One workgroup per appended row, one float4 group of the row per thread.
-// For each draft layer i: s = sum_j alpha[i][j] * h_j (ascending j; the T
-// states are re-read per layer from cache, 8 loads in flight per batch),
-// f = s / sqrt(mean(s^2) + eps) * g, written as the packed split activation
-// of the context K/V projection. The fusion weights are staged in LDS once.
+// One workgroup per (appended row m = b*max_new + t, draft layer i), one
+// float4 group of the row per thread. While the row's T target states are
+// in flight, thread 0 plans the row: sequence b's checks (sequence id,
+// n_new, position capacity; its page-table entries are checked by the first
+// threads) give position ctx_len + t, or -1 if t >= n_new or a check fails
+// (the whole sequence is then skipped and its error bits set once, by row
+// t = 0 of layer 0). Layer 0 records the positions for the context
+// finisher, which advances ctx_len. Then s = sum_j alpha[i][j] * h_j
+// (ascending j), f = s / sqrt(mean(s^2) + eps) * g, written as the packed
+// split activation of the context K/V projection.
 __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
-  const int m = blockIdx.x;
-  if (a.row_pos[m] < 0) return;
+  const int m = blockIdx.x, i = blockIdx.y;
+  const int b = m / a.max_new, t = m % a.max_new;
   __shared__ float red[16];
-  __shared__ float alpha[FUSE_DMAX * FUSE_TMAX];
-  for (int i = threadIdx.x; i < a.D * a.T; i += blockDim.x) alpha[i] = a.alpha[i];
+  __shared__ int plan[4];  // seq, L, n, bad
+  if (threadIdx.x == 0) {
+    int bad = 0;
+    const int s_raw = a.seq_ids[b];
+    if (s_raw < 0 || s_raw >= a.max_seqs) bad |= DFLASH_DEV_BAD_SEQ;
+    const int seq = clampi(s_raw, 0, a.max_seqs - 1);
+    const int L_raw = a.ctx_len[seq];
+    const int cap = min(a.max_pages_per_seq * 16, a.max_pos);
+    if (L_raw < 0 || L_raw > cap) bad |= DFLASH_DEV_NO_PAGES;
+    const int L = clampi(L_raw, 0, cap);
+    const int n = a.n_new[b];
+    if (n < 0 || n > a.max_new) bad |= DFLASH_DEV_BAD_N_NEW;
+    if (!bad && L + n > cap) bad |= DFLASH_DEV_NO_PAGES;
+    plan[0] = seq;
+    plan[1] = L;
+    plan[2] = bad ? 0 : n;
+    plan[3] = bad;
+  }
   __syncthreads();
+  {  // page-table entries the sequence's append writes to (one per thread)
+    const int L = plan[1], n = plan[2];
+    for (int p = L / 16 + (int)threadIdx.x; n > 0 && p < (L + n + 15) / 16; p += blockDim.x) {
+      const int pg = a.page_table[(size_t)plan[0] * a.max_pages_per_seq + p];
+      if (pg < 0 || pg >= a.n_pages) atomicOr(&plan[3], DFLASH_DEV_BAD_PAGE);
+    }
+  }
+  __syncthreads();
+  const int bad = plan[3];
+  const int pos = (!bad && t < plan[2]) ? plan[1] + t : -1;
+  if (i == 0 && threadIdx.x == 0) {
+    a.row_pos[m] = pos;
+    a.row_seq[m] = plan[0];
+    if (t == 0 && bad) set_error(a.err, bad);
+  }
+  if (pos < 0) return;
   const uint16_t* h = a.hidden + (size_t)m * a.T * a.H;
+  const float* al = a.alpha + (size_t)i * a.T;
   const int nv = (a.H / 4 + blockDim.x - 1) / blockDim.x;
-  for (int i = 0; i < a.D; ++i) {
-    float s[FUSE_MAXV][4];
-    float ss = 0.f;
+  float s[FUSE_MAXV][4];
+  float ss = 0.f;
 #pragma unroll
-    for (int v = 0; v < FUSE_MAXV; ++v) {
-      const int k = (v * (int)blockDim.x + (int)threadIdx.x) * 4;
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      if (v < nv && k < a.H) {
-#pragma unroll 8
-        for (int j = 0; j < a.T; ++j) {
-          const u16x4 x = *reinterpret_cast<const u16x4*>(h + (size_t)j * a.H + k);
-          const float al = alpha[i * a.T + j];
+  for (int v = 0; v < FUSE_MAXV; ++v) {
+    const int k = min((v * (int)blockDim.x + (int)threadIdx.x) * 4, a.H - 4);  // clamped: no branch around loads
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < a.T; j0 += 8) {
+      u16x4 x[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] += al * bf2f(x[e]);
-        }
-      }
+      for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const u16x4*>(h + (size_t)min(j0 + j, a.T - 1) * a.H + k);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[v][e] = acc[e];
-        ss += acc[e] * acc[e];
+      for (int j = 0; j < 8; ++j) {
+        if (j0 + j >= a.T) break;
+        const float w = al[j0 + j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += w * bf2f(x[j][e]);
       }
     }
-    const float tot = block_sum(ss, red);
-    const float rstd = 1.0f / sqrtf(tot / a.H + a.eps);
-    const size_t plane = act_plane(a.rows, a.H);
-    uint16_t* out = a.f + (size_t)i * 2 * plane;
-    const uint16_t* g = a.g_fuse + (size_t)i * a.H;
+    const bool mine = v < nv && (v * (int)blockDim.x + (int)threadIdx.x) * 4 < a.H;
 #pragma unroll
-    for (int v = 0; v < FUSE_MAXV; ++v) {
-      const int k = (v * blockDim.x + threadIdx.x) * 4;
-      if (v >= nv || k >= a.H) continue;
-      const u16x4 gv = *reinterpret_cast<const u16x4*>(g + k);
-      f32x4 y;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = s[v][e] * rstd * bf2f(gv[e]);
-      u16x4 hi, lo;
-      split4(y, hi, lo);
-      *reinterpret_cast<u16x4*>(out + pk_index(m, k, a.H)) = hi;
-      *reinterpret_cast<u16x4*>(out + plane + pk_index(m, k, a.H)) = lo;
+    for (int e = 0; e < 4; ++e) {
+      s[v][e] = acc[e];
+      if (mine) ss += acc[e] * acc[e];
     }
+  }
+  const float tot = block_sum(ss, red);
+  const float rstd = 1.0f / sqrtf(tot / a.H + a.eps);
+  const size_t plane = act_plane(a.rows, a.H);
+  uint16_t* out = a.f + (size_t)i * 2 * plane;
+  const uint16_t* g = a.g_fuse + (size_t)i * a.H;
+#pragma unroll
+  for (int v = 0; v < FUSE_MAXV; ++v) {
+    const int k = (v * blockDim.x + threadIdx.x) * 4;
+    if (v >= nv || k >= a.H) continue;
+    const u16x4 gv = *reinterpret_cast<const u16x4*>(g + k);
+    f32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = s[v][e] * rstd * bf2f(gv[e]);
+    u16x4 hi, lo;
+    split4(y, hi, lo);
+    *reinterpret_cast<u16x4*>(out + pk_index(m, k, a.H)) = hi;
+    *reinterpret_cast<u16x4*>(out + plane + pk_index(m, k, a.H)) = lo;
   }
 }
 
 extern "C" hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st) {
   const int threads = std::min(1024, ((a->H / 4 + 63) / 64) * 64);
-  launch_kernel(fuse_kernel, dim3(a->rows), dim3(threads), 0, st, *a);
+  launch_kernel(fuse_kernel, dim3(a->rows, a->D), dim3(threads), 0, st, *a);
   return hipGetLastError();
 }
 

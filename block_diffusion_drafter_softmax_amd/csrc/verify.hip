@@ -1,8 +1,8 @@
 // Parallel verification of the drafted blocks against the target's logits
 // (greedy, or temperature-1 rejection sampling).
 //
-// verify_rows_kernel streams every logit once: work item = (vocabulary chunk,
-// block row, sequence). Greedy keeps (max, lowest index); temperature 1 keeps
+// verify_rows_kernel streams every logit once: work item = (vocabulary chunk
+// of up to 32768 logits, block row, sequence). Greedy keeps (max, lowest index); temperature 1 keeps
 // (max, sum of exp(z - max)). The last workgroup of a sequence to finish
 // (device-scope counter, reset by that workgroup) merges the chunks in chunk
 // order and runs the accept scan. Temperature 1 then needs one more pass over
@@ -87,32 +87,39 @@ DEV void load8(const VerifyArgs& a, size_t i, float (&z)[8]) {
 }  // namespace
 
 // Work item = (vocabulary chunk, block row, sequence); chunk % 8 == 0 and
-// V % 8 == 0, so every thread reads whole 8-logit groups.
+// V % 8 == 0, so every thread reads whole 8-logit groups, 8 groups in
+// flight per batch.
+#define VERIFY_THREADS 1024
+#define VG 4  // 8-logit groups per thread in flight: a 32768-logit chunk in one batch
 template <int DTYPE>
-__global__ __launch_bounds__(256) LATENCY_BOUND void verify_rows_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(VERIFY_THREADS) LATENCY_BOUND void verify_rows_kernel(VerifyArgs a) {
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const size_t row_off = ((size_t)b * a.N + r) * a.V;
   const int k0 = c * a.chunk, k1 = min(a.V, k0 + a.chunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ float2 red[4];
+  constexpr int NW = VERIFY_THREADS / 64;
+  __shared__ float2 red[NW];
   __shared__ int last;
   __shared__ float2 rowres[32];
   __shared__ float prob[32], unif[32];
+  __shared__ float2 parts[VERIFY_MAX_PARTS];
   float2 res = make_float2(0.f, 0.f);
   if (!a.temp1) {
     ArgMax t{-INFINITY, 0x7FFFFFFF};
-    float zs[4][8];
+    for (int base = k0; base < k1; base += VERIFY_THREADS * 8 * VG) {
+      float zs[VG][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // chunk <= 256 * 8 * 4: all loads in flight (clamped, unused past k1)
-      const int k = min(k0 + (int)(threadIdx.x + 256 * j) * 8, k1 - 8);
-      load8<DTYPE>(a, row_off + k, zs[j]);
-    }
+      for (int j = 0; j < VG; ++j) {  // clamped loads, all in flight; unused past k1
+        const int k = min(base + (int)(threadIdx.x + VERIFY_THREADS * j) * 8, k1 - 8);
+        load8<DTYPE>(a, row_off + k, zs[j]);
+      }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = k0 + (threadIdx.x + 256 * j) * 8;
-      if (k < k1) {
+      for (int j = 0; j < VG; ++j) {
+        const int k = base + (threadIdx.x + VERIFY_THREADS * j) * 8;
+        if (k < k1) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) t = am_merge(t, ArgMax{zs[j][e], k + e});
+          for (int e = 0; e < 8; ++e) t = am_merge(t, ArgMax{zs[j][e], k + e});
+        }
       }
     }
 #pragma unroll
@@ -121,41 +128,44 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void verify_rows_kernel(VerifyAr
     __syncthreads();
     if (threadIdx.x == 0) {
       ArgMax u{red[0].x, __float_as_int(red[0].y)};
-      for (int w = 1; w < 4; ++w) u = am_merge(u, ArgMax{red[w].x, __float_as_int(red[w].y)});
+      for (int w = 1; w < NW; ++w) u = am_merge(u, ArgMax{red[w].x, __float_as_int(red[w].y)});
       res = make_float2(u.v, __int_as_float(u.i));
     }
   } else {
-    float m = -INFINITY;
-    float zs[4][8];
+    float2 ms = make_float2(-INFINITY, 0.f);  // (max, sum of exp(z - max)) of this thread's logits
+    for (int base = k0; base < k1; base += VERIFY_THREADS * 8 * VG) {
+      float zs[VG][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // chunk <= 256 * 8 * 4: clamped loads, all in flight
-      const int k = min(k0 + (int)(threadIdx.x + 256 * j) * 8, k1 - 8);
-      load8<DTYPE>(a, row_off + k, zs[j]);
-    }
+      for (int j = 0; j < VG; ++j) {
+        const int k = min(base + (int)(threadIdx.x + VERIFY_THREADS * j) * 8, k1 - 8);
+        load8<DTYPE>(a, row_off + k, zs[j]);
+      }
+      float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (k0 + (int)(threadIdx.x + 256 * j) * 8 >= k1) continue;
+      for (int j = 0; j < VG; ++j) {
+        if (base + (int)(threadIdx.x + VERIFY_THREADS * j) * 8 >= k1) continue;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, zs[j][e]);
-    }
-    m = wave_max(m);
-    if (lane == 0) red[wave].x = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(red[0].x, red[1].x), fmaxf(red[2].x, red[3].x));
-    float sum = 0.f;
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, zs[j][e]);
+      }
+      float sum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = k0 + (threadIdx.x + 256 * j) * 8;
-      if (k < k1) {
+      for (int j = 0; j < VG; ++j) {
+        if (base + (int)(threadIdx.x + VERIFY_THREADS * j) * 8 >= k1) continue;
 #pragma unroll
         for (int e = 0; e < 8; ++e) sum += __expf(zs[j][e] - m);
       }
+      ms = ms_merge(ms, make_float2(m, sum));
     }
-    sum = wave_sum(sum);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+      ms = ms_merge(ms, make_float2(__shfl_xor(ms.x, o, 64), __shfl_xor(ms.y, o, 64)));
+    if (lane == 0) red[wave] = ms;
     __syncthreads();
-    if (lane == 0) red[wave].y = sum;
-    __syncthreads();
-    if (threadIdx.x == 0) res = make_float2(m, red[0].y + red[1].y + red[2].y + red[3].y);
+    if (threadIdx.x == 0) {
+      float2 u = red[0];
+      for (int w = 1; w < NW; ++w) u = ms_merge(u, red[w]);
+      res = u;
+    }
   }
   if (threadIdx.x == 0) {
     *reinterpret_cast<float2*>(a.part + ((((size_t)b * a.N + r) * a.n_chunks + c) * 2)) = res;
@@ -167,25 +177,34 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void verify_rows_kernel(VerifyAr
   if (!last) return;
   __threadfence();
 
-  // Last workgroup of this sequence: thread `row` merges that row's chunks
-  // (chunk order), then thread 0 runs the accept scan.
+  // Last workgroup of this sequence: every (row, chunk) result is loaded
+  // in one batch into LDS, thread `row` merges its row's chunks in chunk
+  // order, then thread 0 runs the accept scan.
   const int seq = a.seq_ids[b];
   const int* d = a.draft + (size_t)b * (a.N - 1);
+  const int n_parts = a.N * a.n_chunks;  // <= VERIFY_MAX_PARTS (host check)
+  const float2* src = reinterpret_cast<const float2*>(a.part) + (size_t)b * n_parts;
+  for (int p0 = 0; p0 < n_parts; p0 += VERIFY_THREADS * 8) {
+    float2 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src[min(p0 + j * VERIFY_THREADS + (int)threadIdx.x, n_parts - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (p0 + j * VERIFY_THREADS + (int)threadIdx.x < n_parts) parts[p0 + j * VERIFY_THREADS + threadIdx.x] = v[j];
+  }
+  __syncthreads();
   const int row = threadIdx.x;
   if (row < a.N) {
     if (!a.temp1) {
       ArgMax u{-INFINITY, 0x7FFFFFFF};
-#pragma unroll 8
       for (int cc = 0; cc < a.n_chunks; ++cc) {
-        const float2 p = *reinterpret_cast<const float2*>(a.part + ((((size_t)b * a.N + row) * a.n_chunks + cc) * 2));
+        const float2 p = parts[row * a.n_chunks + cc];
         u = am_merge(u, ArgMax{p.x, __float_as_int(p.y)});
       }
       rowres[row] = make_float2(u.v, __int_as_float(u.i));
     } else if (row < a.N - 1) {
       float2 ms = make_float2(-INFINITY, 0.f);
-#pragma unroll 8
-      for (int cc = 0; cc < a.n_chunks; ++cc)
-        ms = ms_merge(ms, *reinterpret_cast<const float2*>(a.part + ((((size_t)b * a.N + row) * a.n_chunks + cc) * 2)));
+      for (int cc = 0; cc < a.n_chunks; ++cc) ms = ms_merge(ms, parts[row * a.n_chunks + cc]);
       const float lse = ms.x + __logf(ms.y);
       int tok = d[row];
       if (tok < 0 || tok >= a.V) {
@@ -221,7 +240,7 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void verify_sample_kernel(Verify
   const int row = a.state[2 * b + 0], excl = a.state[2 * b + 1];
   const int seq = a.seq_ids[b];
   const size_t row_off = ((size_t)b * a.N + row) * a.V;
-  const int k0 = c * a.chunk, k1 = min(a.V, k0 + a.chunk);
+  const int k0 = c * a.s_chunk, k1 = min(a.V, k0 + a.s_chunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   ArgMax t{-INFINITY, 0x7FFFFFFF};
   for (int k = k0 + threadIdx.x; k < k1; k += 256) {
@@ -240,30 +259,28 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void verify_sample_kernel(Verify
   if (threadIdx.x == 0) {
     ArgMax u = red[0];
     for (int w = 1; w < 4; ++w) u = am_merge(u, red[w]);
-    *reinterpret_cast<float2*>(a.part + (((size_t)b * a.n_chunks + c) * 2)) = make_float2(u.v, __int_as_float(u.i));
+    *reinterpret_cast<float2*>(a.part + (((size_t)b * a.s_n_chunks + c) * 2)) = make_float2(u.v, __int_as_float(u.i));
     __threadfence();
     const int done = atomicAdd(&a.counters[a.B + b], 1);
-    last = (done == a.n_chunks - 1);
+    last = (done == a.s_n_chunks - 1);
   }
   __syncthreads();
   if (!last || threadIdx.x != 0) return;
   __threadfence();
   a.counters[a.B + b] = 0;
   ArgMax u{-INFINITY, 0x7FFFFFFF};
-  for (int cc = 0; cc < a.n_chunks; ++cc) {
-    const float2 p = *reinterpret_cast<const float2*>(a.part + (((size_t)b * a.n_chunks + cc) * 2));
+  for (int cc = 0; cc < a.s_n_chunks; ++cc) {
+    const float2 p = *reinterpret_cast<const float2*>(a.part + (((size_t)b * a.s_n_chunks + cc) * 2));
     u = am_merge(u, ArgMax{p.x, __float_as_int(p.y)});
   }
   a.next_token[b] = u.i;
 }
 
 extern "C" hipError_t dflash_launch_verify(const VerifyArgs* a, hipStream_t st) {
-  if (a->dtype == DFLASH_DTYPE_F32)
-    hipLaunchKernelGGL(verify_rows_kernel<DFLASH_DTYPE_F32>, dim3(a->n_chunks, a->N, a->B), dim3(256), 0, st, *a);
-  else
-    hipLaunchKernelGGL(verify_rows_kernel<DFLASH_DTYPE_BF16>, dim3(a->n_chunks, a->N, a->B), dim3(256), 0, st, *a);
-  hipError_t e = hipGetLastError();
+  const dim3 grid(a->n_chunks, a->N, a->B), block(VERIFY_THREADS);
+  hipError_t e;
+  if (a->dtype == DFLASH_DTYPE_F32) e = launch_kernel(verify_rows_kernel<DFLASH_DTYPE_F32>, grid, block, 0, st, *a);
+  else e = launch_kernel(verify_rows_kernel<DFLASH_DTYPE_BF16>, grid, block, 0, st, *a);
   if (e != hipSuccess || !a->temp1) return e;
-  hipLaunchKernelGGL(verify_sample_kernel, dim3(a->n_chunks, a->B), dim3(256), 0, st, *a);
-  return hipGetLastError();
+  return launch_kernel(verify_sample_kernel, dim3(a->s_n_chunks, a->B), dim3(256), 0, st, *a);
 }

@@ -201,7 +201,7 @@ int dflash_read_error(dflash_ctx* ctx, hipStream_t stream, int32_t* out);
  * Per-kernel timing with HIP events recorded on the launch stream around
  * every launch of one kernel kind. Off by default; switching it on costs
  * two event records per launch of that kind. */
-#define DFLASH_K_FUSE 0      /* append: layer fusion + RMSNorm */
+#define DFLASH_K_FUSE 0      /* append: call plan + layer fusion + RMSNorm */
 #define DFLASH_K_CTX_KV 1    /* append: context K/V projection (split-k partials) */
 #define DFLASH_K_NORM 2      /* embedding / residual reduce + RMSNorm */
 #define DFLASH_K_QKV 3       /* block Q/K/V projection (split-k partials) */
@@ -213,10 +213,9 @@ int dflash_read_error(dflash_ctx* ctx, hipStream_t stream, int32_t* out);
 #define DFLASH_K_LM_HEAD 9   /* LM head + per-tile top-2 */
 #define DFLASH_K_ARGMAX 10
 #define DFLASH_K_VERIFY 11
-#define DFLASH_K_PLAN 12
-#define DFLASH_K_QKV_FINISH 13 /* split-k sum + RoPE + layout of Q and block K/V */
-#define DFLASH_K_CTX_FINISH 14 /* split-k sum + RoPE + page scatter of context K/V */
-#define DFLASH_K_COUNT 15
+#define DFLASH_K_QKV_FINISH 12 /* split-k sum + RoPE + layout of Q and block K/V */
+#define DFLASH_K_CTX_FINISH 13 /* split-k sum + RoPE + page scatter of context K/V; advances ctx_len */
+#define DFLASH_K_COUNT 14
 
 /* Start (enable != 0) or stop timing kernel kind `kind`; starting clears
  * the totals. Capacity: 4096 launches between reads. A timed launch of a

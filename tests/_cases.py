@@ -154,6 +154,11 @@ class Case:
                 for j in range(o["logits"].shape[0]):
                     le = max(le, rel_err(g["logits"][b, j], o["logits"][j]))
         for b, o in zip(self.oracle_seqs, orc):
+            if g["gap"] is not None:  # the top-2 gap is a float output: same bar, on the row's logit scale
+                for j in range(len(o["draft"])):
+                    scale = float(np.max(np.abs(o["logits"][j])))
+                    assert abs(float(g["gap"][b, j]) - o["gap"][j]) <= FLOAT_TOL * scale, (
+                        f"gap mismatch seq {b} pos {j}: gpu {g['gap'][b, j]} oracle {o['gap'][j]} (|logit| {scale})")
             for j in range(len(o["draft"])):
                 if o["gap"][j] < GAP_MIN:
                     excluded += 1
