@@ -103,7 +103,7 @@ Layout make_layout(const dflash_config& c) {
   L.cpart = take(L.cpart_floats * 4);
   L.apo = take(Bm * c.n_kv_heads * L.n_ck * R * c.head_dim * 4);
   L.aml = take(Bm * c.n_kv_heads * L.n_ck * R * 2 * 4);
-  L.lmpart = take((size_t)((c.vocab / 32 + 3) / 4) * L.m_max * sizeof(Top2));
+  L.lmpart = take((size_t)((c.vocab / 32 + 1) / 2) * L.m_max * sizeof(Top2));
   L.vpart = take(Bm * std::max<size_t>(N * L.n_vchunks, L.n_schunks) * 2 * 4);
   L.vstate = take(Bm * 2 * 4);
   L.counters = take(Bm * 2 * 4);
@@ -546,7 +546,7 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
 
   ArgmaxArgs ma{};
   ma.part = la.part;
-  ma.n_parts = (c.vocab / 32 + 3) / 4;  // one per LM-head workgroup (4 waves of 32 vocabulary rows)
+  ma.n_parts = (c.vocab / 32 + 1) / 2;  // one per LM-head workgroup (2 waves of 32 vocabulary rows)
   ma.M = M;
   ma.N = N;
   ma.V = c.vocab;

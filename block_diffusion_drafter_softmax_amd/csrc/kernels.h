@@ -156,7 +156,7 @@ struct LmArgs {
   const uint16_t* w;    // packed [V/16][K/32][512]
   const uint16_t* act;  // packed split activation of the normed rows
   int M, K, V, N;       // N = block rows per sequence
-  Top2* part;           // [ceil(V/32/4)][M]: one top-2 per workgroup of 4 waves
+  Top2* part;           // [ceil(V/32/2)][M]: one top-2 per workgroup of 2 waves
   float* dbg_logits;    // nullable [B][N-1][V]
 };
 

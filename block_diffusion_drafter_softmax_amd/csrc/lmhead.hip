@@ -9,7 +9,7 @@
 #include "dflash.h"
 #include "stream.h"
 
-#define LM_WAVES 4  // waves per workgroup (32 vocabulary rows each)
+#define LM_WAVES 2  // waves per workgroup (32 vocabulary rows each)
 
 template <int MT, int U>
 __global__ __launch_bounds__(64 * LM_WAVES) void lmhead_kernel(LmArgs a) {

@@ -31,6 +31,13 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
   const int b = m / a.max_new, t = m % a.max_new;
   __shared__ float red[16];
   __shared__ int plan[4];  // seq, L, n, bad
+  // the row's first 8 target states (this thread's first float4 group) are
+  // requested before the plan, which takes three dependent reads
+  const uint16_t* h = a.hidden + (size_t)m * a.T * a.H;
+  const int kq = min((int)threadIdx.x * 4, a.H - 4);  // clamped: no branch around loads
+  u16x4 pre[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pre[j] = *reinterpret_cast<const u16x4*>(h + (size_t)min(j, a.T - 1) * a.H + kq);
   if (threadIdx.x == 0) {
     int bad = 0;
     const int s_raw = a.seq_ids[b];
@@ -65,19 +72,22 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
     if (t == 0 && bad) set_error(a.err, bad);
   }
   if (pos < 0) return;
-  const uint16_t* h = a.hidden + (size_t)m * a.T * a.H;
   const float* al = a.alpha + (size_t)i * a.T;
   const int nv = (a.H / 4 + blockDim.x - 1) / blockDim.x;
   float s[FUSE_MAXV][4];
   float ss = 0.f;
 #pragma unroll
   for (int v = 0; v < FUSE_MAXV; ++v) {
-    const int k = min((v * (int)blockDim.x + (int)threadIdx.x) * 4, a.H - 4);  // clamped: no branch around loads
+    const int k = min((v * (int)blockDim.x + (int)threadIdx.x) * 4, a.H - 4);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < a.T; j0 += 8) {
+#pragma unroll
+    for (int j0 = 0; j0 < FUSE_TMAX; j0 += 8) {  // T <= FUSE_TMAX: at most two batches
+      if (j0 >= a.T) break;
       u16x4 x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const u16x4*>(h + (size_t)min(j0 + j, a.T - 1) * a.H + k);
+      for (int j = 0; j < 8; ++j)
+        x[j] = (v == 0 && j0 == 0) ? pre[j]
+                                   : *reinterpret_cast<const u16x4*>(h + (size_t)min(j0 + j, a.T - 1) * a.H + k);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j0 + j >= a.T) break;
