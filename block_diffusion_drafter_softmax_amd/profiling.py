@@ -4,7 +4,7 @@
 device-to-device copy of 256 MiB three times: the reference workload whose
 FETCH_SIZE / WRITE_SIZE readings calibrate the HBM traffic counters.
 
-``... profiling stats <kernel_stats.csv> <out.md> <command> [<kernel_trace.csv>]`` and
+``... profiling stats <kernel_stats.csv> <out.md> <command> [<kernel_trace.csv> [<skip_last>]]`` and
 ``... profiling traffic <kernel regex> <fetch.csv> <write.csv> <copy_fetch.csv>
 <copy_write.csv> <out.json> <out.md> <commands...>`` turn rocprofv3 CSV output
 into the short text summaries kept with the sources.
@@ -65,7 +65,7 @@ def copy_factor(path, counter):
     return (COPY_BYTES / 1024) / counted_kib, counted_kib
 
 
-def write_stats(stats_csv, out_md, command, trace_csv=None, top=24):
+def write_stats(stats_csv, out_md, command, trace_csv=None, skip_last=0, top=24):
     rows = _rows(stats_csv)
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     lines = ["# Kernel time, rocprofv3 --kernel-trace --stats", "", "Command:", "", "```", command, "```", "",
@@ -78,17 +78,20 @@ def write_stats(stats_csv, out_md, command, trace_csv=None, top=24):
                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
     if trace_csv:
-        lines += ["", "## One decode step", ""] + step_breakdown(trace_csv)
+        lines += ["", "## One decode step", ""] + step_breakdown(trace_csv, skip_last=skip_last)
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
-def step_breakdown(trace_csv, last_kernel="verify_rows", steps=10):
-    """Per-kernel time of one decode step, averaged over the last `steps`
-    steps of a kernel trace (a step ends with the verification kernel)."""
+def step_breakdown(trace_csv, last_kernel="verify_rows", steps=10, skip_last=0):
+    """Per-kernel time of one decode step, averaged over `steps` steps of a
+    kernel trace (a step ends with the verification kernel), leaving out the
+    final `skip_last` steps (e.g. a pass run with a kernel timer attached)."""
     rows = _rows(trace_csv)
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     ends = [i for i, r in enumerate(rows) if r["Kernel_Name"].startswith("void " + last_kernel)]
+    if skip_last:
+        ends = ends[:-skip_last]
     steps = min(steps, len(ends) - 1)
     agg, span, busy = {}, 0.0, 0.0
     for a, b in zip(ends[-steps - 1:-1], ends[-steps:]):
@@ -100,7 +103,8 @@ def step_breakdown(trace_csv, last_kernel="verify_rows", steps=10):
             n, t = agg.get(k, (0, 0.0))
             agg[k] = (n + 1, t + dt)
             busy += dt
-    out = [f"Per step, mean of the last {steps} steps: first kernel start to last kernel end "
+    out = [f"Per step, mean of {steps} steps (the last {skip_last} of the trace left out): "
+           f"first kernel start to last kernel end "
            f"{span / steps:.1f} us, kernels busy {busy / steps:.1f} us.", "",
            "| kernel | launches/step | us/step | avg us |", "|---|---|---|---|"]
     for k, (n, t) in sorted(agg.items(), key=lambda x: -x[1][1]):
@@ -143,7 +147,8 @@ def main(argv):
     if argv[0] == "copy":
         copy_probe()
     elif argv[0] == "stats":
-        write_stats(argv[1], argv[2], argv[3], argv[4] if len(argv) > 4 else None)
+        write_stats(argv[1], argv[2], argv[3], argv[4] if len(argv) > 4 else None,
+                    int(argv[5]) if len(argv) > 5 else 0)
     elif argv[0] == "traffic":
         print(json.dumps(write_traffic(*argv[1:8], argv[8:])))
     else:
