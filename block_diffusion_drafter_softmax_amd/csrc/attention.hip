@@ -25,6 +25,12 @@
 // are fp32 values entering the MFMAs as hi/lo bf16 pairs (two MFMAs each);
 // K and V are bf16 storage. Unnormalised O, the chunk's max and sum go to a
 // partial buffer, and attn_merge_kernel combines the chunks.
+//
+// Large batches have far more chunks than the chip holds at once. There
+// (d_h 64) a work item is cpi > 1 consecutive chunks, taken one after the
+// other by the same workgroup (stage, compute, stage, ...) with the running
+// max, sum and O rescaled per chunk as in any online softmax, and one
+// partial per item goes to the merge: cpi times fewer partial bytes.
 #include <algorithm>
 
 #include "common.h"
@@ -35,6 +41,7 @@ DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); 
 constexpr int CH = 128;  // virtual keys per work item
 constexpr int PAGES = CH / 16;
 constexpr int MIN_WAVES = 8;  // staging waves per workgroup
+constexpr int CPI_MAX = 8;    // chunks per work item, at most
 
 // LDS row of chunk key k. Within each 32-key group (two pages), key 8a + b
 // goes to row 4a + b of the group's first 16-row tile for b < 4 and of its
@@ -52,45 +59,49 @@ DEV int tile_key(int j, int g, int i) { return (j >> 1) * 32 + 8 * g + (j & 1) *
 
 // NACC: accumulator sets for the S products (2: hi and lo separately, more
 // independent MFMA chains; 1 where 1024-thread workgroups cap the registers).
-template <int D, int NACC>
+// MULTI: work items of up to CPI_MAX chunks.
+template <int D, int NACC, bool MULTI>
 __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs a) {
   constexpr int KP = D + 8;  // padded LDS row of one key (bf16 elements)
   constexpr int K_ELEMS = CH * KP, V_ELEMS = PAGES * D * 16;
+  constexpr int SLOTS = (MULTI ? CPI_MAX : 1) * PAGES;
   __shared__ __attribute__((aligned(16))) uint16_t lds[K_ELEMS + V_ELEMS];
-  __shared__ int pg[PAGES];   // page of each chunk page slot (-1: the block)
-  __shared__ int cnt[PAGES];  // valid key slots of each chunk page slot
+  __shared__ int pg[SLOTS];   // page of each page slot of the item (-1: the block)
+  __shared__ int cnt[SLOTS];  // valid key slots of each page slot
 
-  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int item = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int cpi = MULTI ? a.cpi : 1;
   const int seq = clampi(a.seq_ids[b], 0, a.max_seqs - 1);
   const int L = clampi(a.ctx_len[seq], 0, a.max_pages_per_seq * 16);
-  const int v_begin = c * CH;
-  const int nv = min(16 + L, v_begin + CH) - v_begin;  // virtual keys in this chunk
-  if (nv <= 0) return;
-  const int np = (nv + 15) / 16;
+  const int item_begin = item * cpi * CH;
+  const int item_nv = min(16 + L, item_begin + cpi * CH) - item_begin;  // virtual keys in this item
+  if (item_nv <= 0) return;
+  const int n_chunks = MULTI ? (item_nv + CH - 1) / CH : 1;
   const int tid = threadIdx.x, nthreads = blockDim.x;
   const size_t page_elems = (size_t)2 * a.n_kv * 16 * D;
 
-  if (tid < PAGES) {
+  for (int t = tid; t < n_chunks * PAGES; t += nthreads) {
     int p = -1, n_ok = 0;
-    if (tid < np) {
-      const int vp = v_begin / 16 + tid;
+    if (16 * t < item_nv) {
+      const int vp = item_begin / 16 + t;
       if (vp > 0) {
         const int raw = a.page_table[(size_t)seq * a.max_pages_per_seq + vp - 1];
         if (raw < 0 || raw >= a.n_pages) set_error(a.err, DFLASH_DEV_BAD_PAGE);
         p = clampi(raw, 0, a.n_pages - 1);
       }
-      n_ok = vp == 0 ? a.N : min(16, nv - 16 * tid);
+      n_ok = vp == 0 ? a.N : min(16, item_nv - 16 * t);
     }
-    pg[tid] = p;
-    cnt[tid] = n_ok;
+    pg[t] = p;
+    cnt[t] = n_ok;
   }
 
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int G = a.n_q / a.n_kv, R = G * a.N, n_wr = R / 16;
+  const bool computing = wave < n_wr;
   const int r = min(wave, n_wr - 1) * 16 + r16;
   const int hq = kvh * G + r / a.N, n = r % a.N;
-  constexpr int KD = D / 32, DT = D / 16;
+  constexpr int KD = D / 32, DT = D / 16, NT = CH / 16;
 
   // queries (softmax scale already applied): in flight with the page reads
   bf16x8 qh[KD], ql[KD];
@@ -103,59 +114,65 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
       ql[kd] = ld8(qp + q_lo + kd * 32);
     }
   }
-  __syncthreads();
 
-  // Stage K (slot-major rows) and V (dim-major) of all PAGES page slots in
-  // LDS: per page, 2*D*16 bf16 = 4*D 16-byte units (K units first, then V
-  // units). Slots past the chunk's pages read the block (valid memory) and
-  // count 0 valid keys, so every V value of an invalid key is stored as 0
-  // and the MFMAs never meet stale values; K of invalid keys is masked in S.
-  // One batch of 8 loads per thread when nthreads * 8 covers the chunk.
-  constexpr int UNITS_PER_PAGE = 4 * D;
-  constexpr int TOTAL_UNITS = PAGES * UNITS_PER_PAGE;
-  const uint16_t* blk_k = a.kblk + ((size_t)b * a.n_kv + kvh) * 16 * D;
-  const uint16_t* blk_v = a.vblk + ((size_t)b * a.n_kv + kvh) * D * 16;
-  for (int base = 0; base < TOTAL_UNITS; base += 8 * nthreads) {
-    int uu[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) uu[j] = min(base + j * nthreads + tid, TOTAL_UNITS - 1);
-    u32x4 buf[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int p = uu[j] / UNITS_PER_PAGE, w = uu[j] % UNITS_PER_PAGE;
-      const int pgv = pg[p];
-      const uint16_t* kb = pgv < 0 ? blk_k : a.pages + pgv * page_elems + (size_t)kvh * 16 * D;
-      const uint16_t* vb = pgv < 0 ? blk_v : kb + (size_t)a.n_kv * 16 * D;
-      const uint16_t* src = (w < 2 * D) ? kb + (w / (D / 8)) * D + (w % (D / 8)) * 8 : vb + (w - 2 * D) * 8;
-      buf[j] = *reinterpret_cast<const u32x4*>(src);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      // a clamped duplicate rewrites the last unit with the same value
-      const int p = uu[j] / UNITS_PER_PAGE, w = uu[j] % UNITS_PER_PAGE;
-      const bool isk = w < 2 * D;
-      const int valid = isk ? 8 : cnt[p] - ((w - 2 * D) & 1) * 8;  // V unit: slots 8*(w&1) .. +7
-      u32x4 m;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) m[e] = (2 * e < valid ? 0xFFFFu : 0u) | (2 * e + 1 < valid ? 0xFFFF0000u : 0u);
-      const int key = p * 16 + w / (D / 8);  // K unit: chunk key, 8 dims
-      const int e = w - 2 * D;               // V unit: dim e/2, slots 8*(e&1) .. +7
-      const int off = isk ? krow(key) * KP + (w % (D / 8)) * 8
-                          : K_ELEMS + p * D * 16 + (e & 1) * D * 8 + (e >> 1) * 8;
-      *reinterpret_cast<u32x4*>(&lds[off]) = buf[j] & m;
-    }
-  }
-  __syncthreads();
-  if (wave >= n_wr) return;
-
-  // Key tile j = LDS rows 16j .. 16j+15; the lane holds S for keys
-  // tile_key(j, g, 0..3) of its query.
-  constexpr int NT = CH / 16;
   f32x4 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mx = -INFINITY, l = 0.f;
-  {
+  const uint16_t* blk_k = a.kblk + ((size_t)b * a.n_kv + kvh) * 16 * D;
+  const uint16_t* blk_v = a.vblk + ((size_t)b * a.n_kv + kvh) * D * 16;
+
+  for (int ci = 0; ci < n_chunks; ++ci) {
+    const int v_begin = item_begin + ci * CH;
+    const int nv = min(item_nv - ci * CH, CH);  // virtual keys in this chunk
+    const int* cpg = pg + ci * PAGES;
+    const int* ccnt = cnt + ci * PAGES;
+    __syncthreads();  // page slots written; the previous chunk's LDS reads done
+
+    // Stage K (slot-major rows) and V (dim-major) of all PAGES page slots
+    // in LDS: per page, 2*D*16 bf16 = 4*D 16-byte units (K units first,
+    // then V units). Slots past the chunk's pages read the block (valid
+    // memory) and count 0 valid keys, so every V value of an invalid key is
+    // stored as 0 and the MFMAs never meet stale values; K of invalid keys
+    // is masked in S. One batch of 8 loads per thread when nthreads * 8
+    // covers the chunk.
+    constexpr int UNITS_PER_PAGE = 4 * D;
+    constexpr int TOTAL_UNITS = PAGES * UNITS_PER_PAGE;
+    for (int base = 0; base < TOTAL_UNITS; base += 8 * nthreads) {
+      int uu[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) uu[j] = min(base + j * nthreads + tid, TOTAL_UNITS - 1);
+      u32x4 buf[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int p = uu[j] / UNITS_PER_PAGE, w = uu[j] % UNITS_PER_PAGE;
+        const int pgv = cpg[p];
+        const uint16_t* kb = pgv < 0 ? blk_k : a.pages + pgv * page_elems + (size_t)kvh * 16 * D;
+        const uint16_t* vb = pgv < 0 ? blk_v : kb + (size_t)a.n_kv * 16 * D;
+        const uint16_t* src = (w < 2 * D) ? kb + (w / (D / 8)) * D + (w % (D / 8)) * 8 : vb + (w - 2 * D) * 8;
+        buf[j] = *reinterpret_cast<const u32x4*>(src);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // a clamped duplicate rewrites the last unit with the same value
+        const int p = uu[j] / UNITS_PER_PAGE, w = uu[j] % UNITS_PER_PAGE;
+        const bool isk = w < 2 * D;
+        const int valid = isk ? 8 : ccnt[p] - ((w - 2 * D) & 1) * 8;  // V unit: slots 8*(w&1) .. +7
+        u32x4 m;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m[e] = (2 * e < valid ? 0xFFFFu : 0u) | (2 * e + 1 < valid ? 0xFFFF0000u : 0u);
+        const int key = p * 16 + w / (D / 8);  // K unit: chunk key, 8 dims
+        const int e = w - 2 * D;               // V unit: dim e/2, slots 8*(e&1) .. +7
+        const int off = isk ? krow(key) * KP + (w % (D / 8)) * 8
+                            : K_ELEMS + p * D * 16 + (e & 1) * D * 8 + (e >> 1) * 8;
+        *reinterpret_cast<u32x4*>(&lds[off]) = buf[j] & m;
+      }
+    }
+    __syncthreads();
+    if (!computing) continue;
+
+    // Key tile j = LDS rows 16j .. 16j+15; the lane holds S for keys
+    // tile_key(j, g, 0..3) of its query.
     f32x4 s[NT];
     {
       f32x4 sa[NACC][NT];
@@ -182,26 +199,36 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const int k0 = tile_key(j, g, 0);  // 4 keys k0 .. k0+3 of one page
-        const int nj = cnt[k0 >> 4] - (k0 & 15);
+        const int nj = ccnt[k0 >> 4] - (k0 & 15);
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[j][i] = i < nj ? s[j][i] : -INFINITY;
       }
     }
+    float cm = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // finite: every chunk has a valid key
+      for (int i = 0; i < 4; ++i) cm = fmaxf(cm, s[j][i]);
+    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));  // finite: every chunk has a valid key
+    const float mn = fmaxf(mx, cm);
+    const float scale = exp2f(mx - mn);  // 0 at the first chunk
+    mx = mn;
+    float cs = 0.f;
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         s[j][i] = exp2f(s[j][i] - mx);
-        l += s[j][i];
+        cs += s[j][i];
       }
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    cs += __shfl_xor(cs, 16, 64);
+    cs += __shfl_xor(cs, 32, 64);
+    l = l * scale + cs;
+    if (MULTI) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) acc[t] *= scale;
+    }
 
 #pragma unroll
     for (int j = 0; j < NT; j += 2) {  // k-step: key tiles j and j+1 (32 keys, 2 pages)
@@ -222,8 +249,9 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
       }
     }
   }
+  if (!computing) return;
 
-  const size_t unit = ((size_t)b * a.n_kv + kvh) * a.n_ck + c;
+  const size_t unit = ((size_t)b * a.n_kv + kvh) * a.n_ck + item;
   float* po = a.part_o + (unit * R + r) * D;
 #pragma unroll
   for (int t = 0; t < DT; ++t) *reinterpret_cast<f32x4*>(po + t * 16 + 4 * g) = acc[t];
@@ -234,7 +262,7 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
 }
 
 // One workgroup per (sequence, kv head, query row): thread (cg, dq) merges
-// chunks cg, cg + CG, ... for dims 4*dq .. 4*dq+3 (all its loads in one
+// work items cg, cg + CG, ... for dims 4*dq .. 4*dq+3 (all its loads in one
 // batch of <= 8), then the CG partial merges are combined in cg order
 // through LDS; the result is normalised and written as the O projection's
 // packed split activation. Deterministic (fixed order).
@@ -250,7 +278,7 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
   const int dq = threadIdx.x % TPR, cg = threadIdx.x / TPR;
   const int seq = clampi(a.seq_ids[b], 0, a.max_seqs - 1);
   const int L = clampi(a.ctx_len[seq], 0, a.max_pages_per_seq * 16);
-  const int nc = min(a.n_ck, (16 + L + CH - 1) / CH);
+  const int nc = min(a.n_ck, (16 + L + a.cpi * CH - 1) / (a.cpi * CH));  // work items of the sequence
   const size_t unit0 = ((size_t)b * a.n_kv + kvh) * a.n_ck;
   float M = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
@@ -301,13 +329,15 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
 extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
   const int G = a->n_q / a->n_kv, n_wr = G * a->N / 16;
   const int waves = std::max(n_wr, MIN_WAVES);
-  const dim3 grid(a->n_ck, a->n_kv, B), block(64 * waves);
-  if (head_dim == 128) {
-    if (waves <= 8) launch_kernel(attn_chunk_kernel<128, 2>, grid, block, 0, st, *a);
-    else launch_kernel(attn_chunk_kernel<128, 1>, grid, block, 0, st, *a);
+  const dim3 grid((a->n_ck + a->cpi - 1) / a->cpi, a->n_kv, B), block(64 * waves);
+  if (head_dim == 128) {  // cpi == 1 (the host's choice for d_h 128)
+    if (waves <= 8) launch_kernel(attn_chunk_kernel<128, 2, false>, grid, block, 0, st, *a);
+    else launch_kernel(attn_chunk_kernel<128, 1, false>, grid, block, 0, st, *a);
+  } else if (a->cpi > 1) {
+    launch_kernel(attn_chunk_kernel<64, 1, true>, grid, block, 0, st, *a);
   } else {
-    if (waves <= 8) launch_kernel(attn_chunk_kernel<64, 2>, grid, block, 0, st, *a);
-    else launch_kernel(attn_chunk_kernel<64, 1>, grid, block, 0, st, *a);
+    if (waves <= 8) launch_kernel(attn_chunk_kernel<64, 2, false>, grid, block, 0, st, *a);
+    else launch_kernel(attn_chunk_kernel<64, 1, false>, grid, block, 0, st, *a);
   }
   return hipGetLastError();
 }

@@ -36,13 +36,24 @@ int fail(int code, const char* fmt, ...) {
     if (e_ != hipSuccess) return fail(DFLASH_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_));     \
   } while (0)
 
-constexpr int kAttnChunk = 128;     // virtual keys (16 block slots + context) per attention work item
+constexpr int kAttnChunk = 128;     // virtual keys (16 block slots + context) per attention chunk
+constexpr int kAttnItems = 4096;    // attention work items to aim for; larger batches take several chunks per item
 constexpr int kVerifyChunk = 32768;       // logits per verification work item (rows pass)
 constexpr int kSampleChunk = 8192;        // logits per work item of the temperature-1 sampling pass
 constexpr int kKsMax = 8;           // largest k split of a streaming GEMM (KS_MAX in common.h)
 constexpr int kTargetWaves = 1536;  // streaming waves to aim for (~6 per CU)
+constexpr int kMmMinRows = 64;      // from this many activation rows on, GEMMs use the tiled MFMA kernels
+constexpr int kMmCols = 128;        // vocabulary rows per tiled LM-head workgroup (one top-2 each)
+constexpr int kMmRows = 128;        // activation rows per tiled-GEMM workgroup
+constexpr int kMmTargetWgs = 512;   // tiled-GEMM workgroups to aim for (2 resident per CU)
+// Partial-sum floats a tiled GEMM may need: a k split is only taken while
+// the grid is under 2 * kMmTargetWgs workgroups of 128 x 128 outputs.
+constexpr size_t kMmPartFloats = (size_t)2 * kMmTargetWgs * 128 * 128;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Partial top-2 per row that the LM head leaves for the argmax reduction.
+int lm_parts(int vocab, int M) { return M >= kMmMinRows ? (vocab + kMmCols - 1) / kMmCols : (vocab / 32 + 1) / 2; }
 
 // Byte offsets of everything the library keeps in the caller's workspace.
 struct Layout {
@@ -68,8 +79,9 @@ Layout make_layout(const dflash_config& c) {
   L.n_vchunks = (c.vocab + kVerifyChunk - 1) / kVerifyChunk;
   L.n_schunks = (c.vocab + kSampleChunk - 1) / kSampleChunk;
   const size_t ncol_d = std::max(qd + 2 * kvd, H), ncol_c = D * 2 * kvd;
-  L.gpart_floats = ncol_d * std::max<size_t>(256, 2 * (size_t)L.m_max);
-  L.cpart_floats = ncol_c * std::max<size_t>(256, 2 * (size_t)L.rows_a_max);
+  L.gpart_floats = std::max(ncol_d * std::max<size_t>(256, 2 * (size_t)L.m_max), kMmPartFloats);
+  L.cpart_floats = std::max(ncol_c * std::max<size_t>(256, 2 * (size_t)L.rows_a_max), kMmPartFloats);
+
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -103,7 +115,7 @@ Layout make_layout(const dflash_config& c) {
   L.cpart = take(L.cpart_floats * 4);
   L.apo = take(Bm * c.n_kv_heads * L.n_ck * R * c.head_dim * 4);
   L.aml = take(Bm * c.n_kv_heads * L.n_ck * R * 2 * 4);
-  L.lmpart = take((size_t)((c.vocab / 32 + 1) / 2) * L.m_max * sizeof(Top2));
+  L.lmpart = take((size_t)std::max(lm_parts(c.vocab, 1), lm_parts(c.vocab, kMmMinRows)) * L.m_max * sizeof(Top2));
   L.vpart = take(Bm * std::max<size_t>(N * L.n_vchunks, L.n_schunks) * 2 * 4);
   L.vstate = take(Bm * 2 * 4);
   L.counters = take(Bm * 2 * 4);
@@ -226,6 +238,28 @@ int pick_ks(int units, int K, int M, int n_cols, size_t cap_floats) {
   ks = std::min<long long>(ks, (long long)(cap_floats / ((size_t)M * n_cols)));
   return std::max(ks, 1);
 }
+
+// Few rows: the weight-streaming GEMM with a k split (none for SwiGLU).
+// Many rows: the tiled MFMA GEMM, split in k only while its grid of
+// 128 x 128 output tiles is too small to fill the chip.
+int gemm_ks(const WsArgs& g, int mode, size_t cap_floats) {
+  const int units = g.unit_start[g.nseg];
+  if (g.M < kMmMinRows) return mode == WS_SWIGLU ? 1 : pick_ks(units, g.K, g.M, g.n_cols, cap_floats);
+  int blocks = 0;
+  for (int s = 0; s < g.nseg; ++s) blocks += (g.seg[s].units + 3) / 4;
+  blocks *= (g.M + kMmRows - 1) / kMmRows;
+  int ks = (kMmTargetWgs + blocks - 1) / blocks;
+  ks = std::min(ks, std::max(1, (g.K / 32) / 8));
+  ks = std::min(ks, kKsMax);
+  const size_t cols = (size_t)g.n_cols * (mode == WS_SWIGLU ? 2 : 1);
+  ks = std::min<long long>(ks, (long long)(cap_floats / ((size_t)g.M * cols)));
+  return std::max(ks, 1);
+}
+
+hipError_t launch_gemm(const WsArgs& g, int mode, hipStream_t st) {
+  return g.M >= kMmMinRows ? dflash_launch_mm(&g, mode, st) : dflash_launch_ws(&g, mode, st);
+}
+
 
 }  // namespace
 
@@ -373,9 +407,9 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
       add_seg(g, ctx->at<uint16_t>(L.wk_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd);
       add_seg(g, ctx->at<uint16_t>(L.wv_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd + kvd);
     }
-    if (l0 == 0) ks = pick_ks(g.unit_start[g.nseg] * ((D + 7) / 8), H, rows, n_cols, L.cpart_floats);
+    if (l0 == 0) ks = gemm_ks(g, WS_PARTIAL, L.cpart_floats);
     g.ks = ks;
-    if ((rc = ctx->launch(DFLASH_K_CTX_KV, stream, [&] { return dflash_launch_ws(&g, WS_PARTIAL, stream); })))
+    if ((rc = ctx->launch(DFLASH_K_CTX_KV, stream, [&] { return launch_gemm(g, WS_PARTIAL, stream); })))
       return rc;
   }
   CtxFinishArgs ca{};
@@ -471,6 +505,13 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   aa.n_kv = c.n_kv_heads;
   aa.chunk = kAttnChunk;
   aa.n_ck = L.n_ck;
+  {  // chunks per work item, from the largest grid the batch can have
+    const long long chunks = (long long)B * c.n_kv_heads * L.n_ck;
+    aa.cpi = (int)std::min<long long>(8, std::max<long long>(1, (chunks + kAttnItems - 1) / kAttnItems));
+    // d_h 128: O accumulators kept across chunks would not fit the
+    // registers of two co-resident workgroups per CU; one chunk per item.
+    if (c.head_dim != 64) aa.cpi = 1;
+  }
   aa.max_pages_per_seq = c.max_pages_per_seq;
   aa.n_pages = c.n_pages;
   aa.max_seqs = c.max_seqs;
@@ -484,9 +525,9 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
       add_seg(g, ctx->at<uint16_t>(L.wq) + (size_t)i * qd * H, nullptr, h, qd / 32, 0);
       add_seg(g, ctx->at<uint16_t>(L.wk_d) + (size_t)i * kvd * H, nullptr, h, kvd / 32, qd);
       add_seg(g, ctx->at<uint16_t>(L.wv_d) + (size_t)i * kvd * H, nullptr, h, kvd / 32, qd + kvd);
-      g.ks = pick_ks(g.unit_start[g.nseg], H, M, g.n_cols, L.gpart_floats);
+      g.ks = gemm_ks(g, WS_PARTIAL, L.gpart_floats);
       qa.ks = g.ks;
-      if ((rc = ctx->launch(DFLASH_K_QKV, stream, [&] { return dflash_launch_ws(&g, WS_PARTIAL, stream); })))
+      if ((rc = ctx->launch(DFLASH_K_QKV, stream, [&] { return launch_gemm(g, WS_PARTIAL, stream); })))
         return rc;
       if ((rc = ctx->launch(DFLASH_K_QKV_FINISH, stream, [&] { return dflash_launch_qkv_finish(&qa, stream); })))
         return rc;
@@ -501,9 +542,9 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
       WsArgs g = ws_base(M, qd, H);
       g.part = gpart;
       add_seg(g, ctx->at<uint16_t>(L.wo) + (size_t)i * H * qd, nullptr, aa.o, H / 32, 0);
-      g.ks = pick_ks(g.unit_start[g.nseg], qd, M, H, L.gpart_floats);
+      g.ks = gemm_ks(g, WS_PARTIAL, L.gpart_floats);
       na.ks = g.ks;
-      if ((rc = ctx->launch(DFLASH_K_OPROJ, stream, [&] { return dflash_launch_ws(&g, WS_PARTIAL, stream); })))
+      if ((rc = ctx->launch(DFLASH_K_OPROJ, stream, [&] { return launch_gemm(g, WS_PARTIAL, stream); })))
         return rc;
     }
     na.mode = 1;
@@ -515,16 +556,21 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
       g.out = ctx->at<uint16_t>(L.mm);
       add_seg(g, ctx->at<uint16_t>(L.wg) + (size_t)i * I * H, ctx->at<uint16_t>(L.wu) + (size_t)i * I * H, h,
               I / 16, 0);
-      if ((rc = ctx->launch(DFLASH_K_GATE_UP, stream, [&] { return dflash_launch_ws(&g, WS_SWIGLU, stream); })))
+      g.ks = gemm_ks(g, WS_SWIGLU, L.gpart_floats);
+      g.part = gpart;
+      if ((rc = ctx->launch(DFLASH_K_GATE_UP, stream, [&] { return launch_gemm(g, WS_SWIGLU, stream); })))
+        return rc;
+      if (g.ks > 1 &&
+          (rc = ctx->launch(DFLASH_K_GATE_UP, stream, [&] { return dflash_launch_swiglu_finish(&g, stream); })))
         return rc;
     }
     {  // down -> split partials
       WsArgs g = ws_base(M, I, H);
       g.part = gpart;
       add_seg(g, ctx->at<uint16_t>(L.wd) + (size_t)i * H * I, nullptr, ctx->at<uint16_t>(L.mm), H / 32, 0);
-      g.ks = pick_ks(g.unit_start[g.nseg], I, M, H, L.gpart_floats);
+      g.ks = gemm_ks(g, WS_PARTIAL, L.gpart_floats);
       na.ks = g.ks;
-      if ((rc = ctx->launch(DFLASH_K_DOWN, stream, [&] { return dflash_launch_ws(&g, WS_PARTIAL, stream); })))
+      if ((rc = ctx->launch(DFLASH_K_DOWN, stream, [&] { return launch_gemm(g, WS_PARTIAL, stream); })))
         return rc;
     }
     na.mode = 1;
@@ -542,11 +588,14 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   la.N = N;
   la.part = ctx->at<Top2>(L.lmpart);
   la.dbg_logits = dbg_logits;
-  if ((rc = ctx->launch(DFLASH_K_LM_HEAD, stream, [&] { return dflash_launch_lmhead(&la, stream); }))) return rc;
+  if ((rc = ctx->launch(DFLASH_K_LM_HEAD, stream, [&] {
+         return M >= kMmMinRows ? dflash_launch_lmhead_mm(&la, stream) : dflash_launch_lmhead(&la, stream);
+       })))
+    return rc;
 
   ArgmaxArgs ma{};
   ma.part = la.part;
-  ma.n_parts = (c.vocab / 32 + 1) / 2;  // one per LM-head workgroup (2 waves of 32 vocabulary rows)
+  ma.n_parts = lm_parts(c.vocab, M);  // one per LM-head workgroup
   ma.M = M;
   ma.N = N;
   ma.V = c.vocab;

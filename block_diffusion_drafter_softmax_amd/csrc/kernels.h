@@ -57,7 +57,7 @@ struct WsArgs {
   int M;        // activation rows
   int ks;       // k splits (one wave per (unit, split))
   int n_cols;   // row length of the partial buffer / SwiGLU features
-  float* part;  // WS_PARTIAL: [ks][M][n_cols]
+  float* part;  // WS_PARTIAL: [ks][M][n_cols]; tiled WS_SWIGLU with ks > 1: [ks][M][2*n_cols] (gate | up)
   uint16_t* out;  // WS_SWIGLU: packed split activation, planes of act_plane(M, n_cols)
 };
 
@@ -105,11 +105,12 @@ struct AttnArgs {
   const int* page_table;
   const int* ctx_len;
   const int* seq_ids;
-  float* part_o;           // [B][n_kv][n_ck][R][d]
+  float* part_o;           // [B][n_kv][n_ck][R][d]: one per work item (item < ceil(n_ck / cpi))
   float* part_ml;          // [B][n_kv][n_ck][R][2]
   uint16_t* o;             // merge output, packed split activation (planes of act_plane(B*N, n_q*d))
   int32_t* err;
   int N, n_q, n_kv, chunk, n_ck, max_pages_per_seq, n_pages, max_seqs;
+  int cpi;                 // chunks of `chunk` virtual keys per work item (1 .. 8)
 };
 
 // ------------------------------------------------------------ small kernels
@@ -156,7 +157,7 @@ struct LmArgs {
   const uint16_t* w;    // packed [V/16][K/32][512]
   const uint16_t* act;  // packed split activation of the normed rows
   int M, K, V, N;       // N = block rows per sequence
-  Top2* part;           // [ceil(V/32/2)][M]: one top-2 per workgroup of 2 waves
+  Top2* part;           // [n_parts][M]: one top-2 per workgroup (64 or 128 vocabulary rows)
   float* dbg_logits;    // nullable [B][N-1][V]
 };
 
@@ -200,6 +201,8 @@ extern thread_local LaunchEvents dflash_launch_events;
 
 extern "C" {
 hipError_t dflash_launch_ws(const WsArgs* a, int mode, hipStream_t st);
+hipError_t dflash_launch_mm(const WsArgs* a, int mode, hipStream_t st);
+hipError_t dflash_launch_swiglu_finish(const WsArgs* a, hipStream_t st);
 hipError_t dflash_launch_pack(const PackArgs* a, hipStream_t st);
 hipError_t dflash_launch_qkv_finish(const QkvFinishArgs* a, hipStream_t st);
 hipError_t dflash_launch_ctx_finish(const CtxFinishArgs* a, hipStream_t st);
@@ -209,6 +212,7 @@ hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st);
 hipError_t dflash_launch_norm(const NormArgs* a, hipStream_t st);
 hipError_t dflash_launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
 hipError_t dflash_launch_lmhead(const LmArgs* a, hipStream_t st);
+hipError_t dflash_launch_lmhead_mm(const LmArgs* a, hipStream_t st);
 hipError_t dflash_launch_argmax(const ArgmaxArgs* a, hipStream_t st);
 hipError_t dflash_launch_verify(const VerifyArgs* a, hipStream_t st);
 }

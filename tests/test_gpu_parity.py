@@ -118,11 +118,46 @@ def test_gqa_16_to_1_rows_256_both_head_dims():
         run_step(Case(cfg, ctx=ctx, n_new=n_new, seed=17 + d, page_order="shuffled", prefill_chunk=64))
 
 
+def test_attention_multi_chunk_items():
+    # GPT-OSS attention geometry (d_h 64, 8 kv heads, 128 query rows per kv
+    # head) with a page pool large enough (2100 pages per sequence) that the
+    # batch's chunk grid (4 x 8 x 263) exceeds the attention's work-item
+    # target 3-fold: every work item then takes 3 chunks of 128 virtual keys
+    # in a row. Contexts end inside an item's first chunk (383: 399 virtual
+    # keys), hold only the block, and end with partial items of 1 and 3
+    # chunks.
+    cfg = small_cfg(hidden=512, n_q_heads=64, n_kv_heads=8, head_dim=64, intermediate=512, vocab=2048,
+                    block_size=16)
+    ctx, n_new = [1200, 383, 0, 2317], [8, 5, 0, 16]
+    pps_min = (max(ctx) + 16 + 15) // 16
+    run_step(Case(cfg, ctx=ctx, n_new=n_new, seed=51, page_order="shuffled", prefill_chunk=256,
+                  extra_pages=2100 - pps_min))
+
+
 def test_wide_batch_multi_group_rows():
     # M = 5 * 16 = 80 rows -> several 64-row groups in the projection kernels
     cfg = small_cfg(hidden=256, block_size=16, n_q_heads=4, n_kv_heads=4)
     run_step(Case(cfg, ctx=[40, 41, 96, 0, 129], n_new=[8, 0, 16, 0, 9], seed=11,
                   page_order="shuffled", prefill_chunk=80))
+
+
+def test_many_rows_tiled_gemm_tails():
+    # 19 sequences x 8 block rows = 152 rows: the tiled MFMA GEMMs and LM
+    # head, with a partial last row tile in a second row block, odd numbers
+    # of k steps, column blocks that end inside a segment and a vocabulary
+    # of 250 tiles; the 24-row prefill chunks take the same kernels for the
+    # context K/V. Hidden 352 (11 k steps) keeps every product in one k
+    # split except the down projection (23 steps, 2 splits); hidden 544 (17
+    # steps) also splits the gate/up projection, whose SwiGLU then runs in
+    # the last workgroup of each tile.
+    for hidden, inter, seed in ((352, 736, 41), (544, 608, 43)):
+        cfg = small_cfg(hidden=hidden, n_q_heads=4, n_kv_heads=2, head_dim=64, intermediate=inter, vocab=4000,
+                        block_size=8)
+        rng = np.random.default_rng(seed)
+        n_new = rng.integers(0, 9, size=19)
+        ctx = n_new + rng.integers(0, 70, size=19)
+        run_step(Case(cfg, ctx=ctx.tolist(), n_new=n_new.tolist(), seed=seed, page_order="shuffled",
+                      prefill_chunk=24))
 
 
 def test_deterministic_bitwise():
