@@ -43,12 +43,12 @@ constexpr int kSampleChunk = 8192;        // logits per work item of the tempera
 constexpr int kKsMax = 8;           // largest k split of a streaming GEMM (KS_MAX in common.h)
 constexpr int kTargetWaves = 1536;  // streaming waves to aim for (~6 per CU)
 constexpr int kMmMinRows = 64;      // from this many activation rows on, GEMMs use the tiled MFMA kernels
-constexpr int kMmCols = 128;        // vocabulary rows per tiled LM-head workgroup (one top-2 each)
-constexpr int kMmRows = 128;        // activation rows per tiled-GEMM workgroup
+constexpr int kMmCols = MM_COL_TILES * 16;  // output columns (vocabulary rows) per tiled-GEMM workgroup
+constexpr int kMmRows = MM_ROW_TILES * 16;  // activation rows per tiled-GEMM workgroup
 constexpr int kMmTargetWgs = 512;   // tiled-GEMM workgroups to aim for (2 resident per CU)
 // Partial-sum floats a tiled GEMM may need: a k split is only taken while
-// the grid is under 2 * kMmTargetWgs workgroups of 128 x 128 outputs.
-constexpr size_t kMmPartFloats = (size_t)2 * kMmTargetWgs * 128 * 128;
+// the grid is under 2 * kMmTargetWgs workgroup tiles.
+constexpr size_t kMmPartFloats = (size_t)2 * kMmTargetWgs * kMmRows * kMmCols;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -61,7 +61,7 @@ struct Layout {
   size_t alpha, rope, wq, wk_d, wv_d, wk_t, wv_t, wo, wg, wu, wd, lm;
   // per-call buffers
   size_t rowpos_a, rowseq_a, f, x, h, q, o, kblk, vblk, mm, gpart, cpart;
-  size_t apo, aml, lmpart, vpart, vstate, counters, total;
+  size_t apo, aml, lmpart, vpart, spart, total;
   size_t gpart_floats, cpart_floats;
   int n_ck, n_vchunks, n_schunks, m_max, rows_a_max;
 };
@@ -116,9 +116,8 @@ Layout make_layout(const dflash_config& c) {
   L.apo = take(Bm * c.n_kv_heads * L.n_ck * R * c.head_dim * 4);
   L.aml = take(Bm * c.n_kv_heads * L.n_ck * R * 2 * 4);
   L.lmpart = take((size_t)std::max(lm_parts(c.vocab, 1), lm_parts(c.vocab, kMmMinRows)) * L.m_max * sizeof(Top2));
-  L.vpart = take(Bm * std::max<size_t>(N * L.n_vchunks, L.n_schunks) * 2 * 4);
-  L.vstate = take(Bm * 2 * 4);
-  L.counters = take(Bm * 2 * 4);
+  L.vpart = take(Bm * N * L.n_vchunks * 2 * 4);
+  L.spart = take(Bm * L.n_schunks * 2 * 4);
   L.total = off;
   return L;
 }
@@ -246,7 +245,7 @@ int gemm_ks(const WsArgs& g, int mode, size_t cap_floats) {
   const int units = g.unit_start[g.nseg];
   if (g.M < kMmMinRows) return mode == WS_SWIGLU ? 1 : pick_ks(units, g.K, g.M, g.n_cols, cap_floats);
   int blocks = 0;
-  for (int s = 0; s < g.nseg; ++s) blocks += (g.seg[s].units + 3) / 4;
+  for (int s = 0; s < g.nseg; ++s) blocks += (2 * g.seg[s].units + MM_COL_TILES - 1) / MM_COL_TILES;
   blocks *= (g.M + kMmRows - 1) / kMmRows;
   int ks = (kMmTargetWgs + blocks - 1) / blocks;
   ks = std::min(ks, std::max(1, (g.K / 32) / 8));
@@ -315,8 +314,6 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, const dflas
   char* ws = static_cast<char*>(workspace);
   HIP_OK(hipMemcpy(ws + L.alpha, alpha.data(), alpha.size() * 4, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(ws + L.rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
-  std::vector<int32_t> zeros((size_t)c.max_batch * 2, 0);
-  HIP_OK(hipMemcpy(ws + L.counters, zeros.data(), zeros.size() * 4, hipMemcpyHostToDevice));
 
   // Pack every streamed matrix into the MFMA-operand layout (layers are
   // stacked along rows, so one pass per matrix).
@@ -631,8 +628,7 @@ int dflash_verify(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int3
   va.seq_ids = seq_ids;
   va.draft = draft;
   va.part = ctx->at<float>(L.vpart);
-  va.counters = ctx->at<int>(L.counters);
-  va.state = ctx->at<int>(L.vstate);
+  va.spart = ctx->at<float>(L.spart);
   va.accept_len = accept_len;
   va.next_token = next_token;
   va.commit_len = commit_len;

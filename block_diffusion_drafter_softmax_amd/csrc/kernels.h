@@ -41,6 +41,11 @@ enum WsMode : int {
 
 #define WS_MAX_SEG 16
 
+// Output tile of one tiled-GEMM workgroup (many activation rows): 16-row
+// activation tiles by 16-row weight tiles.
+#define MM_ROW_TILES 8
+#define MM_COL_TILES 16
+
 struct WsSeg {
   const uint16_t* w0;   // packed weights [tiles][K/32][512]
   const uint16_t* w1;   // WS_SWIGLU: packed up weights (w0 holds gate)
@@ -178,9 +183,8 @@ struct VerifyArgs {
   int s_chunk, s_n_chunks;       // temperature-1 sampling pass: the same for the sampled row
   const int* seq_ids;
   const int* draft;     // [B][N-1]
-  float* part;          // rows pass [B][N][n_chunks][2]; sampling pass [B][s_n_chunks][2]
-  int* counters;        // [2*B], zero between calls
-  int* state;           // [B][2]: sample row, excluded token
+  float* part;          // rows pass [B][N][n_chunks][2]
+  float* spart;         // sampling pass [B][s_n_chunks][2]
   int* accept_len;
   int* next_token;
   int* commit_len;      // nullable

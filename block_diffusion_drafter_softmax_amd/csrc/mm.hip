@@ -4,12 +4,16 @@
 // When a call carries many block rows (a batch of sequences, or a context
 // append of hundreds of rows) every weight byte meets M >= 64 activation rows
 // and the product is bound by the matrix cores, not by the weight stream.
-// Each workgroup of 4 waves computes a 128 x 128 output tile: 8 activation
-// tiles, staged through LDS in chunks of MM_KC k steps (double buffered,
-// read by every wave), times 8 weight tiles that the waves load straight
-// from memory one chunk ahead. Wave (wm, wn) owns activation tiles
-// 4wm..4wm+3 and weight tiles 4wn..4wn+3: per k step 8 LDS reads, 4 global
-// loads and 32 MFMA 16x16x32 (hi and lo halves of 16 tile products).
+// What limits a tile loop here is the bandwidth from L2 into the CUs: at the
+// MFMA rate, every byte a CU loads must serve as many MFMAs as possible.
+// So each workgroup of 4 waves computes a 128 x 256 output tile (MM_ROW_TILES
+// activation tiles by MM_COL_TILES weight tiles) with both operands staged
+// once per workgroup through double-buffered LDS, one k step per stage, and
+// each wave owns a 64 x 128 sub-tile (4 activation tiles x 8 weight tiles:
+// 16 LDS reads feed 64 MFMA 16x16x32, the hi and lo halves of 32 tile
+// products). Per k step a workgroup loads 32 KB for 256 MFMAs, straight
+// from memory into LDS (global_load_lds, 1 KB per wave instruction, no
+// registers held for staging), issued right after the step's LDS reads.
 // Workgroups of one column block (same weights, different row blocks) are
 // placed on one XCD and dispatched together, so the weights leave HBM about
 // once per call. Narrow products whose tiles would not fill the chip split
@@ -19,12 +23,14 @@
 // swiglu_finish_kernel) and the LM head's top-2 reduction.
 #include "stream.h"
 
-#define MM_T 8   // activation tiles and weight tiles per workgroup
-#define MM_KC 2  // k steps per LDS chunk
-
 namespace {
 
-constexpr int kChunkBlocks = MM_KC * MM_T * 2;  // 1 KB blocks per chunk: (k step, tile, plane)
+constexpr int XT = MM_ROW_TILES;           // activation tiles per workgroup
+constexpr int WT = MM_COL_TILES;           // weight tiles per workgroup
+constexpr int XW = XT / 2, WW = WT / 2;    // per wave (2 x 2 waves)
+constexpr int kStageBlocks = 2 * XT + WT;  // 1 KB blocks per stage: X tile t plane p at 2t+p, W tile u at 2XT+u
+constexpr int kLoads = kStageBlocks / 4;   // 16-byte loads per thread and stage (4 waves)
+static_assert(kStageBlocks % 4 == 0 && XT % 4 == 0, "stage blocks are dealt to 4 waves");
 
 // Workgroup -> (column block, k split, row block). The grid is a multiple
 // of 8 and the hardware deals workgroups to the 8 XCDs round robin;
@@ -40,117 +46,88 @@ DEV bool mm_place(int total, int MB, int ks, int& nb, int& split, int& mb) {
   return true;
 }
 
-struct MmLoop {
-  const uint16_t* pw[4];  // this wave's weight tiles at the split's first k step, + lane*8
-  const uint16_t* xg[4];  // this thread's activation sources at that k step (see mm_store_x)
-  int steps;              // k steps of the split
+// Global sources (wave-uniform) of the wave's kLoads blocks of a stage at
+// the split's first k step; k step s adds s*512 and lane l reads the 16
+// bytes at l*8. Wave w moves stage blocks w + 4j: for j < XT/2 activation
+// tile (w>>1) + 2j, plane w&1; after that weight tile w + 4j - 2XT.
+struct MmSrc {
+  const uint16_t* p[kLoads];
+  int steps;  // k steps of the split
 };
 
-template <int KC>
-DEV void mm_load_w(bf16x8 (&w)[KC][4], const MmLoop& p, int c) {
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    const int s = min(c * KC + kc, p.steps - 1);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      w[kc][t] = *reinterpret_cast<const bf16x8*>(p.pw[t] + (size_t)s * 512);
-  }
-}
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
-template <int KC>
-DEV void mm_load_x(u32x4 (&st)[KC][4], const MmLoop& p, int c) {
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    const int s = min(c * KC + kc, p.steps - 1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) st[kc][j] = *reinterpret_cast<const u32x4*>(p.xg[j] + (size_t)s * 512);
-  }
-}
-
-// Chunk block (kc, tile t, plane p) sits at LDS block kc*16 + 2t + p. Thread
-// (wave w, lane) moves blocks kc*16 + 4j + w, i.e. tile (w>>1) + 2j, plane w&1.
-template <int KC>
-DEV void mm_store_x(u32x4* xs, const u32x4 (&st)[KC][4]) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xs[(kc * 16 + 4 * j + w) * 64 + lane] = st[kc][j];
-}
-
-template <int KC>
-DEV void mm_compute(const u32x4* xs, const bf16x8 (&w)[KC][4], int c, int steps, int wm, f32x4 (&acc)[4][4]) {
+// Stage k step s into `stage` (kStageBlocks blocks of 1 KB): each wave
+// instruction writes one whole block, lane l at byte 16 l.
+DEV void mm_dma(u32x4* stage, const MmSrc& src, int s, int w) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    if (c * KC + kc >= steps) break;
-    bf16x8 xh[4], xl[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xh[i] = __builtin_bit_cast(bf16x8, xs[(kc * 16 + (4 * wm + i) * 2) * 64 + lane]);
-      xl[i] = __builtin_bit_cast(bf16x8, xs[(kc * 16 + (4 * wm + i) * 2 + 1) * 64 + lane]);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[t][i] = mfma16(w[kc][t], xh[i], acc[t][i]);
-        acc[t][i] = mfma16(w[kc][t], xl[i], acc[t][i]);
-      }
-  }
+  for (int j = 0; j < kLoads; ++j)
+    __builtin_amdgcn_global_load_lds(src.p[j] + (size_t)s * 512 + lane * 8, (lds_ptr)(stage + (w + 4 * j) * 64), 16, 0,
+                                     0);
 }
 
-// acc[t][i]: weight tile t of this wave by activation tile i of this wave.
-DEV void mm_ksteps(const MmLoop& p, u32x4 (*xs)[kChunkBlocks * 64], int wm, f32x4 (&acc)[4][4]) {
+DEV void mm_wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One k step: the wave's fragments are read from stage `cur` first, then
+// the next step's blocks are requested into stage `nxt` (the LDS reads are
+// ordered before those writes, and whatever the compiler waits for before
+// the next LDS read has already been waited for at the step's barrier),
+// then acc[t][i] += W tile (wn*WW + t) x X tile (wm*XW + i), hi and lo.
+DEV void mm_step(const u32x4* cur, u32x4* nxt, const MmSrc& src, int s, int w, f32x4 (&acc)[WW][XW]) {
+  const int lane = threadIdx.x & 63, wm = w & 1, wn = w >> 1;
+  bf16x8 xh[XW], xl[XW], wf[WW];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int i = 0; i < XW; ++i) {
+    xh[i] = __builtin_bit_cast(bf16x8, cur[(2 * (wm * XW + i)) * 64 + lane]);
+    xl[i] = __builtin_bit_cast(bf16x8, cur[(2 * (wm * XW + i) + 1) * 64 + lane]);
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int n_chunks = (p.steps + MM_KC - 1) / MM_KC;
-  bf16x8 wa[MM_KC][4], wb[MM_KC][4];
-  u32x4 st[MM_KC][4];
-  mm_load_w(wa, p, 0);
-  mm_load_x(st, p, 0);
-  mm_store_x(xs[0], st);
-  __syncthreads();
-  for (int c = 0; c < n_chunks; c += 2) {
-    // chunk c: weights in wa, activations in LDS buffer 0
-    if (c + 1 < n_chunks) {
-      mm_load_w(wb, p, c + 1);
-      mm_load_x(st, p, c + 1);
+  for (int t = 0; t < WW; ++t) wf[t] = __builtin_bit_cast(bf16x8, cur[(2 * XT + wn * WW + t) * 64 + lane]);
+  if (s + 1 < src.steps) mm_dma(nxt, src, s + 1, w);
+#pragma unroll
+  for (int t = 0; t < WW; ++t)
+#pragma unroll
+    for (int i = 0; i < XW; ++i) {
+      acc[t][i] = mfma16(wf[t], xh[i], acc[t][i]);
+      acc[t][i] = mfma16(wf[t], xl[i], acc[t][i]);
     }
-    mm_compute(xs[0], wa, c, p.steps, wm, acc);
-    if (c + 1 < n_chunks) mm_store_x(xs[1], st);
+}
+
+DEV void mm_ksteps(const MmSrc& src, u32x4 (*stages)[kStageBlocks * 64], int w, f32x4 (&acc)[WW][XW]) {
+#pragma unroll
+  for (int t = 0; t < WW; ++t)
+#pragma unroll
+    for (int i = 0; i < XW; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  mm_dma(stages[0], src, 0, w);
+  for (int s = 0; s < src.steps; ++s) {
+    // the wait sits at the top of the trip, so the MFMAs of step s-1 (which
+    // touch no memory and could otherwise sink below it) are issued first
+    mm_wait_dma();
     __syncthreads();
-    if (c + 1 >= n_chunks) break;
-    // chunk c + 1: weights in wb, activations in LDS buffer 1
-    if (c + 2 < n_chunks) {
-      mm_load_w(wa, p, c + 2);
-      mm_load_x(st, p, c + 2);
-    }
-    mm_compute(xs[1], wb, c + 1, p.steps, wm, acc);
-    if (c + 2 < n_chunks) mm_store_x(xs[0], st);
-    __syncthreads();
+    mm_step(stages[s & 1], stages[(s + 1) & 1], src, s, w, acc);
   }
+  __syncthreads();  // every wave's last LDS reads are done before the epilogue reuses LDS
 }
 
-// Activation sources of this thread: tile (w>>1) + 2j of the row block
-// (clamped to the last real tile), plane w&1, from k step s0 (steps per tile).
-DEV void mm_x_sources(MmLoop& p, const uint16_t* act, size_t lo, int mb, int m_tiles, int steps, int s0) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+DEV void mm_x_sources(MmSrc& src, const uint16_t* act, size_t lo, int mb, int m_tiles, int steps, int s0, int w) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tm = min(mb * MM_T + (w >> 1) + 2 * j, m_tiles - 1);
-    p.xg[j] = act + (w & 1) * lo + ((size_t)tm * steps + s0) * 512 + lane * 8;
+  for (int j = 0; j < XT / 2; ++j) {
+    const int tm = min(mb * XT + (w >> 1) + 2 * j, m_tiles - 1);  // clamped to the last real tile
+    src.p[j] = act + (w & 1) * lo + ((size_t)tm * steps + s0) * 512;
   }
 }
 
-// Segment of a column block: each segment's units make ceil(units/4) blocks
-// (8 tiles of 16 output columns, or 4 SwiGLU feature tiles).
+// Weight tile (within the workgroup's WT) of this thread's load j >= XT/2.
+DEV int mm_w_tile(int j, int w) { return w + 4 * j - 2 * XT; }
+
+// Segment of a column block: each segment's units (2 output tiles each, or
+// one SwiGLU feature tile = a gate and an up tile) make ceil(2 units / WT) blocks.
 DEV int mm_segment(const WsArgs& a, int& nb) {
   int s = 0;
   while (s + 1 < a.nseg) {
-    const int blocks = (a.seg[s].units + 3) >> 2;
+    const int blocks = (2 * a.seg[s].units + WT - 1) / WT;
     if (nb < blocks) break;
     nb -= blocks;
     ++s;
@@ -160,71 +137,96 @@ DEV int mm_segment(const WsArgs& a, int& nb) {
 
 }  // namespace
 
+// SwiGLU blocks: weight tiles u < WT/2 are the gates of feature tiles
+// nb*WT/2 + u, the rest the ups of the same features, so wave (wm, 0) holds
+// gate and wave (wm, 1) up of the same rows and features.
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void mm_kernel(WsArgs a, int total, int MB) {
-  __shared__ u32x4 xs[2][kChunkBlocks * 64];
+  __shared__ u32x4 stages[2][kStageBlocks * 64];
   int nb, split, mb;
   if (!mm_place(total, MB, a.ks, nb, split, mb)) return;
   const int s = mm_segment(a, nb);
   const WsSeg sg = a.seg[s];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), wm = w & 1, wn = w >> 1;
   const int r16 = lane & 15, g4 = (lane >> 4) * 4;
   const int m_tiles = pad16(a.M) >> 4;
   const int steps = a.K >> 5;
   const int s0 = split * steps / a.ks;
-  MmLoop p;
-  p.steps = (split + 1) * steps / a.ks - s0;
-  mm_x_sources(p, sg.act, act_plane(a.M, a.K), mb, m_tiles, steps, s0);
-  int col_tile[4];  // PARTIAL: segment tile; SWIGLU: feature tile
-  if (MODE == WS_SWIGLU) {
+  MmSrc src;
+  src.steps = (split + 1) * steps / a.ks - s0;
+  mm_x_sources(src, sg.act, act_plane(a.M, a.K), mb, m_tiles, steps, s0, w);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      col_tile[t] = nb * 4 + wn * 2 + (t & 1);
-      const int f = min(col_tile[t], sg.units - 1);
-      p.pw[t] = (t < 2 ? sg.w0 : sg.w1) + ((size_t)f * steps + s0) * 512 + lane * 8;
+  for (int j = XT / 2; j < kLoads; ++j) {
+    const int u = mm_w_tile(j, w);
+    const uint16_t* base = sg.w0;
+    int tl;
+    if (MODE == WS_SWIGLU) {
+      if (u >= WT / 2) base = sg.w1;
+      tl = min(nb * (WT / 2) + u % (WT / 2), sg.units - 1);
+    } else {
+      tl = min(nb * WT + u, 2 * sg.units - 1);
     }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      col_tile[t] = nb * 8 + wn * 4 + t;
-      const int tl = min(col_tile[t], 2 * sg.units - 1);
-      p.pw[t] = sg.w0 + ((size_t)tl * steps + s0) * 512 + lane * 8;
-    }
+    src.p[j] = base + ((size_t)tl * steps + s0) * 512;
   }
-  f32x4 acc[4][4];
-  mm_ksteps(p, xs, wm, acc);
+  f32x4 acc[WW][XW];
+  mm_ksteps(src, stages, w, acc);
+
+  if (MODE == WS_PARTIAL) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tm = mb * MM_T + 4 * wm + i;
-    const int m = tm * 16 + r16;
-    if (tm >= m_tiles || m >= a.M) continue;
-    if (MODE == WS_PARTIAL) {
+    for (int i = 0; i < XW; ++i) {
+      const int tm = mb * XT + wm * XW + i;
+      const int m = tm * 16 + r16;
+      if (tm >= m_tiles || m >= a.M) continue;
       float* out = a.part + ((size_t)split * a.M + m) * a.n_cols + sg.col0;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (col_tile[t] < 2 * sg.units) *reinterpret_cast<f32x4*>(out + col_tile[t] * 16 + g4) = acc[t][i];
-    } else if (a.ks > 1) {
-      float* out = a.part + ((size_t)split * a.M + m) * 2 * a.n_cols + sg.col0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (col_tile[t] < sg.units)
-          *reinterpret_cast<f32x4*>(out + (t >= 2 ? a.n_cols : 0) + col_tile[t] * 16 + g4) = acc[t][i];
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if (col_tile[t] >= sg.units) continue;
-        f32x4 y;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float gt = acc[t][i][j];
-          y[j] = gt / (1.0f + __expf(-gt)) * acc[t + 2][i][j];
-        }
-        u16x4 hi, lo;
-        split4(y, hi, lo);
-        uint16_t* dst = a.out + pk_index(m, sg.col0 + col_tile[t] * 16 + g4, a.n_cols);
-        *reinterpret_cast<u16x4*>(dst) = hi;
-        *reinterpret_cast<u16x4*>(dst + act_plane(a.M, a.n_cols)) = lo;
+      for (int t = 0; t < WW; ++t) {
+        const int tile = nb * WT + wn * WW + t;
+        if (tile < 2 * sg.units) *reinterpret_cast<f32x4*>(out + tile * 16 + g4) = acc[t][i];
       }
+    }
+    return;
+  }
+
+  // SwiGLU: the up wave parks its accumulators in LDS (the stage buffers
+  // are free after the k loop's last barrier; row half wm uses stage wm)
+  // and the gate wave combines.
+  f32x4* park = reinterpret_cast<f32x4*>(stages[wm]);  // [t][i][lane]
+  static_assert(WW * XW <= kStageBlocks, "park fits a stage buffer");
+  if (wn == 1) {
+#pragma unroll
+    for (int t = 0; t < WW; ++t)
+#pragma unroll
+      for (int i = 0; i < XW; ++i) park[(t * XW + i) * 64 + lane] = acc[t][i];
+  }
+  __syncthreads();
+  if (wn == 1) return;
+#pragma unroll
+  for (int i = 0; i < XW; ++i) {
+    const int tm = mb * XT + wm * XW + i;
+    const int m = tm * 16 + r16;
+    if (tm >= m_tiles || m >= a.M) continue;
+#pragma unroll
+    for (int t = 0; t < WW; ++t) {
+      const int f = nb * (WT / 2) + t;  // feature tile
+      if (f >= sg.units) continue;
+      const f32x4 up = park[(t * XW + i) * 64 + lane];
+      if (a.ks > 1) {
+        float* out = a.part + ((size_t)split * a.M + m) * 2 * a.n_cols + sg.col0 + f * 16 + g4;
+        *reinterpret_cast<f32x4*>(out) = acc[t][i];
+        *reinterpret_cast<f32x4*>(out + a.n_cols) = up;
+        continue;
+      }
+      f32x4 y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gt = acc[t][i][j];
+        y[j] = gt / (1.0f + __expf(-gt)) * up[j];
+      }
+      u16x4 hi, lo;
+      split4(y, hi, lo);
+      uint16_t* dst = a.out + pk_index(m, sg.col0 + f * 16 + g4, a.n_cols);
+      *reinterpret_cast<u16x4*>(dst) = hi;
+      *reinterpret_cast<u16x4*>(dst + act_plane(a.M, a.n_cols)) = lo;
     }
   }
 }
@@ -252,51 +254,52 @@ __global__ __launch_bounds__(256) void swiglu_finish_kernel(WsArgs a) {
 }
 
 // LM head for many rows: the same tile loop over vocabulary tiles, then a
-// top-2 (value, lowest index) per row over the workgroup's 128 vocabulary
+// top-2 (value, lowest index) per row over the workgroup's WT*16 vocabulary
 // rows, written to part[column block][M]; argmax_reduce_kernel merges them.
 __global__ __launch_bounds__(256, 2) void mm_lmhead_kernel(LmArgs a, int total, int MB) {
-  __shared__ u32x4 xs[2][kChunkBlocks * 64];
-  __shared__ Top2 red[2][MM_T * 16];
+  __shared__ u32x4 stages[2][kStageBlocks * 64];
+  __shared__ Top2 red[2][XT * 16];
   int nb, split, mb;
   if (!mm_place(total, MB, 1, nb, split, mb)) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), wm = w & 1, wn = w >> 1;
   const int r16 = lane & 15, g4 = (lane >> 4) * 4;
   const int m_tiles = pad16(a.M) >> 4;
   const int v_tiles = a.V >> 4;
-  MmLoop p;
-  p.steps = a.K >> 5;
-  mm_x_sources(p, a.act, act_plane(a.M, a.K), mb, m_tiles, p.steps, 0);
-  int vt[4];
+  MmSrc src;
+  src.steps = a.K >> 5;
+  mm_x_sources(src, a.act, act_plane(a.M, a.K), mb, m_tiles, src.steps, 0, w);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    vt[t] = nb * 8 + wn * 4 + t;
-    p.pw[t] = a.w + (size_t)min(vt[t], v_tiles - 1) * p.steps * 512 + lane * 8;
-  }
-  f32x4 acc[4][4];
-  mm_ksteps(p, xs, wm, acc);
+  for (int j = XT / 2; j < kLoads; ++j)
+    src.p[j] = a.w + (size_t)min(nb * WT + mm_w_tile(j, w), v_tiles - 1) * src.steps * 512;
+  f32x4 acc[WW][XW];
+  mm_ksteps(src, stages, w, acc);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < XW; ++i) {
     Top2 t2 = top2_empty();
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      if (vt[t] < v_tiles)
+    for (int t = 0; t < WW; ++t) {
+      const int vt = nb * WT + wn * WW + t;
+      if (vt < v_tiles)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) t2 = top2_push(t2, acc[t][i][j], vt[t] * 16 + g4 + j);
+        for (int j = 0; j < 4; ++j) t2 = top2_push(t2, acc[t][i][j], vt * 16 + g4 + j);
+    }
     t2 = top2_shfl_xor(t2, 16);
     t2 = top2_shfl_xor(t2, 32);
-    if (lane < 16) red[wn][(4 * wm + i) * 16 + lane] = t2;
-    const int tm = mb * MM_T + 4 * wm + i;
+    if (lane < 16) red[wn][(wm * XW + i) * 16 + lane] = t2;
+    const int tm = mb * XT + wm * XW + i;
     const int m = tm * 16 + r16;
     if (a.dbg_logits && tm < m_tiles && m < a.M && (m % a.N) != 0) {
       float* dst = a.dbg_logits + ((size_t)(m / a.N) * (a.N - 1) + (m % a.N) - 1) * a.V;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (vt[t] < v_tiles) *reinterpret_cast<f32x4*>(dst + vt[t] * 16 + g4) = acc[t][i];
+      for (int t = 0; t < WW; ++t) {
+        const int vt = nb * WT + wn * WW + t;
+        if (vt < v_tiles) *reinterpret_cast<f32x4*>(dst + vt * 16 + g4) = acc[t][i];
+      }
     }
   }
   __syncthreads();
-  if (threadIdx.x < MM_T * 16) {
-    const int m = mb * MM_T * 16 + threadIdx.x;
+  if (threadIdx.x < XT * 16) {
+    const int m = mb * XT * 16 + threadIdx.x;
     if (m < a.M) a.part[(size_t)nb * a.M + m] = top2_merge(red[0][threadIdx.x], red[1][threadIdx.x]);
   }
 }
@@ -307,8 +310,8 @@ int round8(int n) { return (n + 7) & ~7; }
 
 extern "C" hipError_t dflash_launch_mm(const WsArgs* a, int mode, hipStream_t st) {
   int total_nb = 0;
-  for (int s = 0; s < a->nseg; ++s) total_nb += (a->seg[s].units + 3) / 4;
-  const int MB = ((pad16(a->M) >> 4) + MM_T - 1) / MM_T;
+  for (int s = 0; s < a->nseg; ++s) total_nb += (2 * a->seg[s].units + WT - 1) / WT;
+  const int MB = ((pad16(a->M) >> 4) + XT - 1) / XT;
   const int total = total_nb * a->ks * MB;
   const dim3 grid(round8(total)), block(256);
   if (mode == WS_SWIGLU) launch_kernel(mm_kernel<WS_SWIGLU>, grid, block, 0, st, *a, total, MB);
@@ -323,8 +326,8 @@ extern "C" hipError_t dflash_launch_swiglu_finish(const WsArgs* a, hipStream_t s
 }
 
 extern "C" hipError_t dflash_launch_lmhead_mm(const LmArgs* a, hipStream_t st) {
-  const int NB = ((a->V >> 4) + MM_T - 1) / MM_T;
-  const int MB = ((pad16(a->M) >> 4) + MM_T - 1) / MM_T;
+  const int NB = ((a->V >> 4) + WT - 1) / WT;
+  const int MB = ((pad16(a->M) >> 4) + XT - 1) / XT;
   const int total = NB * MB;
   launch_kernel(mm_lmhead_kernel, dim3(round8(total)), dim3(256), 0, st, *a, total, MB);
   return hipGetLastError();

@@ -2,13 +2,18 @@
 // (greedy, or temperature-1 rejection sampling).
 //
 // verify_rows_kernel streams every logit once: work item = (vocabulary chunk
-// of up to 32768 logits, block row, sequence). Greedy keeps (max, lowest index); temperature 1 keeps
-// (max, sum of exp(z - max)). The last workgroup of a sequence to finish
-// (device-scope counter, reset by that workgroup) merges the chunks in chunk
-// order and runs the accept scan. Temperature 1 then needs one more pass over
-// the single row it samples from (verify_sample_kernel): Gumbel-max with a
-// counter-based Philox4x64-10 draw per vocabulary entry, which gives the same
-// sample whatever the summation order.
+// of up to 32768 logits, block row, sequence). Greedy keeps (max, lowest
+// index); temperature 1 keeps (max, sum of exp(z - max)). A second kernel
+// merges each row's chunks in chunk order and runs the accept scan
+// (verify_greedy_kernel, one workgroup per sequence). Temperature 1 also
+// samples from one row: verify_sample_kernel repeats the scan in every
+// work item (vocabulary chunk of 8192, sequence) -- it is a few dozen
+// loads -- and takes a Gumbel-max over its chunk with a counter-based
+// Philox4x64-10 draw per vocabulary entry, which gives the same sample
+// whatever the order; verify_pick_kernel merges the chunks. Kernel
+// boundaries order the passes: a device-scope hand-off inside a kernel
+// costs an L2 write-back per workgroup, which thousands of workgroups (32
+// sequences x 16 rows x 5 chunks) cannot afford.
 #include "common.h"
 #include "dflash.h"
 
@@ -99,10 +104,6 @@ __global__ __launch_bounds__(VERIFY_THREADS) LATENCY_BOUND void verify_rows_kern
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int NW = VERIFY_THREADS / 64;
   __shared__ float2 red[NW];
-  __shared__ int last;
-  __shared__ float2 rowres[32];
-  __shared__ float prob[32], unif[32];
-  __shared__ float2 parts[VERIFY_MAX_PARTS];
   float2 res = make_float2(0.f, 0.f);
   if (!a.temp1) {
     ArgMax t{-INFINITY, 0x7FFFFFFF};
@@ -167,30 +168,36 @@ __global__ __launch_bounds__(VERIFY_THREADS) LATENCY_BOUND void verify_rows_kern
       res = u;
     }
   }
-  if (threadIdx.x == 0) {
-    *reinterpret_cast<float2*>(a.part + ((((size_t)b * a.N + r) * a.n_chunks + c) * 2)) = res;
-    __threadfence();
-    const int done = atomicAdd(&a.counters[b], 1);
-    last = (done == a.N * a.n_chunks - 1);
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+  if (threadIdx.x == 0) *reinterpret_cast<float2*>(a.part + ((((size_t)b * a.N + r) * a.n_chunks + c) * 2)) = res;
+}
 
-  // Last workgroup of this sequence: every (row, chunk) result is loaded
-  // in one batch into LDS, thread `row` merges its row's chunks in chunk
-  // order, then thread 0 runs the accept scan.
+namespace {
+// Accept scan of sequence b from the rows pass: every (row, chunk) result
+// is loaded in one batch into LDS, thread `row` merges its row's chunks in
+// chunk order, then every thread reads the scan's outcome. Greedy: acc and
+// the target's argmax of row acc (next token). Temperature 1: acc, and the
+// token excluded when sampling row acc (the rejected draft token, or -1).
+struct Scan {
+  int acc, next, excl;
+};
+
+template <int NT>
+DEV Scan verify_scan(const VerifyArgs& a, int b) {
+  __shared__ float2 parts[VERIFY_MAX_PARTS];
+  __shared__ float2 rowres[32];
+  __shared__ float prob[32], unif[32];
+  __shared__ Scan out;
   const int seq = a.seq_ids[b];
   const int* d = a.draft + (size_t)b * (a.N - 1);
   const int n_parts = a.N * a.n_chunks;  // <= VERIFY_MAX_PARTS (host check)
   const float2* src = reinterpret_cast<const float2*>(a.part) + (size_t)b * n_parts;
-  for (int p0 = 0; p0 < n_parts; p0 += VERIFY_THREADS * 8) {
+  for (int p0 = 0; p0 < n_parts; p0 += NT * 8) {
     float2 v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = src[min(p0 + j * VERIFY_THREADS + (int)threadIdx.x, n_parts - 1)];
+    for (int j = 0; j < 8; ++j) v[j] = src[min(p0 + j * NT + (int)threadIdx.x, n_parts - 1)];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (p0 + j * VERIFY_THREADS + (int)threadIdx.x < n_parts) parts[p0 + j * VERIFY_THREADS + threadIdx.x] = v[j];
+      if (p0 + j * NT + (int)threadIdx.x < n_parts) parts[p0 + j * NT + threadIdx.x] = v[j];
   }
   __syncthreads();
   const int row = threadIdx.x;
@@ -211,39 +218,56 @@ __global__ __launch_bounds__(VERIFY_THREADS) LATENCY_BOUND void verify_rows_kern
         set_error(a.err, DFLASH_DEV_BAD_TOKEN);
         tok = clampi(tok, 0, a.V - 1);
       }
-      float zt = load_logit(a, ((size_t)b * a.N + row) * a.V + tok);
+      const float zt = load_logit(a, ((size_t)b * a.N + row) * a.V + tok);
       prob[row] = expf(zt - lse);
       unif[row] = (float)(rng_word(a, seq, row, 0, 0) >> 40) * 5.9604644775390625e-08f;
     }
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  a.counters[b] = 0;
-  int acc = 0;
-  if (!a.temp1) {
-    while (acc < a.N - 1 && d[acc] == __float_as_int(rowres[acc].y)) ++acc;
-    a.accept_len[b] = acc;
-    a.next_token[b] = __float_as_int(rowres[acc].y);
-    if (a.commit_len) a.commit_len[b] = acc + 1;
-  } else {
-    while (acc < a.N - 1 && unif[acc] < prob[acc]) ++acc;
-    a.accept_len[b] = acc;
-    if (a.commit_len) a.commit_len[b] = acc + 1;
-    a.state[2 * b + 0] = acc;
-    a.state[2 * b + 1] = acc < a.N - 1 ? d[acc] : -1;
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    Scan r;
+    if (!a.temp1) {
+      while (acc < a.N - 1 && d[acc] == __float_as_int(rowres[acc].y)) ++acc;
+      r = Scan{acc, __float_as_int(rowres[acc].y), -1};
+    } else {
+      while (acc < a.N - 1 && unif[acc] < prob[acc]) ++acc;
+      r = Scan{acc, -1, acc < a.N - 1 ? d[acc] : -1};
+    }
+    out = r;
   }
+  __syncthreads();
+  return out;
+}
+}  // namespace
+
+#define SCAN_THREADS 256
+
+__global__ __launch_bounds__(SCAN_THREADS) LATENCY_BOUND void verify_greedy_kernel(VerifyArgs a) {
+  const int b = blockIdx.x;
+  const Scan r = verify_scan<SCAN_THREADS>(a, b);
+  if (threadIdx.x != 0) return;
+  a.accept_len[b] = r.acc;
+  a.next_token[b] = r.next;
+  if (a.commit_len) a.commit_len[b] = r.acc + 1;
 }
 
-// Gumbel-max sample of row state[b][0] with token state[b][1] excluded.
-__global__ __launch_bounds__(256) LATENCY_BOUND void verify_sample_kernel(VerifyArgs a) {
+// Gumbel-max sample over vocabulary chunk c of row acc, the excluded token
+// skipped; the chunk's (value, index) goes to spart[b][c].
+__global__ __launch_bounds__(SCAN_THREADS) LATENCY_BOUND void verify_sample_kernel(VerifyArgs a) {
   const int c = blockIdx.x, b = blockIdx.y;
-  const int row = a.state[2 * b + 0], excl = a.state[2 * b + 1];
+  const Scan r = verify_scan<SCAN_THREADS>(a, b);
+  if (c == 0 && threadIdx.x == 0) {
+    a.accept_len[b] = r.acc;
+    if (a.commit_len) a.commit_len[b] = r.acc + 1;
+  }
+  const int row = r.acc, excl = r.excl;
   const int seq = a.seq_ids[b];
   const size_t row_off = ((size_t)b * a.N + row) * a.V;
   const int k0 = c * a.s_chunk, k1 = min(a.V, k0 + a.s_chunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   ArgMax t{-INFINITY, 0x7FFFFFFF};
-  for (int k = k0 + threadIdx.x; k < k1; k += 256) {
+  for (int k = k0 + threadIdx.x; k < k1; k += SCAN_THREADS) {
     if (k == excl) continue;
     const unsigned long long w = rng_word(a, seq, row, k, 1);
     const float u = ((float)(w >> 41) + 0.5f) * 1.1920928955078125e-07f;
@@ -252,28 +276,30 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void verify_sample_kernel(Verify
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) t = am_shfl(t, o);
-  __shared__ ArgMax red[4];
-  __shared__ int last;
+  __shared__ ArgMax red[SCAN_THREADS / 64];
   if (lane == 0) red[wave] = t;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    ArgMax u = red[0];
-    for (int w = 1; w < 4; ++w) u = am_merge(u, red[w]);
-    *reinterpret_cast<float2*>(a.part + (((size_t)b * a.s_n_chunks + c) * 2)) = make_float2(u.v, __int_as_float(u.i));
-    __threadfence();
-    const int done = atomicAdd(&a.counters[a.B + b], 1);
-    last = (done == a.s_n_chunks - 1);
+  if (threadIdx.x != 0) return;
+  ArgMax u = red[0];
+  for (int w = 1; w < SCAN_THREADS / 64; ++w) u = am_merge(u, red[w]);
+  *reinterpret_cast<float2*>(a.spart + (((size_t)b * a.s_n_chunks + c) * 2)) = make_float2(u.v, __int_as_float(u.i));
+}
+
+// Next token of sequence b (temperature 1): merge of the sampling chunks in
+// chunk order (one wave per sequence, loads in one batch).
+__global__ __launch_bounds__(64) void verify_pick_kernel(VerifyArgs a) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  ArgMax t{-INFINITY, 0x7FFFFFFF};
+  for (int c0 = 0; c0 < a.s_n_chunks; c0 += 64) {
+    const int c = c0 + lane;
+    if (c < a.s_n_chunks) {
+      const float2 p = *reinterpret_cast<const float2*>(a.spart + (((size_t)b * a.s_n_chunks + c) * 2));
+      t = am_merge(t, ArgMax{p.x, __float_as_int(p.y)});
+    }
   }
-  __syncthreads();
-  if (!last || threadIdx.x != 0) return;
-  __threadfence();
-  a.counters[a.B + b] = 0;
-  ArgMax u{-INFINITY, 0x7FFFFFFF};
-  for (int cc = 0; cc < a.s_n_chunks; ++cc) {
-    const float2 p = *reinterpret_cast<const float2*>(a.part + (((size_t)b * a.s_n_chunks + cc) * 2));
-    u = am_merge(u, ArgMax{p.x, __float_as_int(p.y)});
-  }
-  a.next_token[b] = u.i;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) t = am_shfl(t, o);
+  if (lane == 0) a.next_token[b] = t.i;
 }
 
 extern "C" hipError_t dflash_launch_verify(const VerifyArgs* a, hipStream_t st) {
@@ -281,6 +307,9 @@ extern "C" hipError_t dflash_launch_verify(const VerifyArgs* a, hipStream_t st) 
   hipError_t e;
   if (a->dtype == DFLASH_DTYPE_F32) e = launch_kernel(verify_rows_kernel<DFLASH_DTYPE_F32>, grid, block, 0, st, *a);
   else e = launch_kernel(verify_rows_kernel<DFLASH_DTYPE_BF16>, grid, block, 0, st, *a);
-  if (e != hipSuccess || !a->temp1) return e;
-  return launch_kernel(verify_sample_kernel, dim3(a->s_n_chunks, a->B), dim3(256), 0, st, *a);
+  if (e != hipSuccess) return e;
+  if (!a->temp1) return launch_kernel(verify_greedy_kernel, dim3(a->B), dim3(SCAN_THREADS), 0, st, *a);
+  e = launch_kernel(verify_sample_kernel, dim3(a->s_n_chunks, a->B), dim3(SCAN_THREADS), 0, st, *a);
+  if (e != hipSuccess) return e;
+  return launch_kernel(verify_pick_kernel, dim3(a->B), dim3(64), 0, st, *a);
 }

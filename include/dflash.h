@@ -138,8 +138,8 @@ size_t dflash_workspace_bytes(const dflash_config* cfg);
 
 /* Validate shapes, compute alpha = softmax(w_fuse) rows [DFLARE 2.1] and the
  * RoPE cos/sin table (float64 angles rounded to fp32) on the host, copy them
- * into the workspace, pack the streamed weights into it and clear its
- * counters (synchronous, null stream; the weights must be ready).
+ * into the workspace and pack the streamed weights into it (synchronous,
+ * null stream; the weights must be ready).
  * workspace: device memory of at least dflash_workspace_bytes(cfg) bytes,
  * owned by the caller, exclusively used by this handle until destroy. */
 int dflash_create(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv,
@@ -208,7 +208,7 @@ int dflash_read_error(dflash_ctx* ctx, hipStream_t stream, int32_t* out);
 #define DFLASH_K_ATTN 4      /* split-context block attention */
 #define DFLASH_K_ATTN_MERGE 5
 #define DFLASH_K_OPROJ 6
-#define DFLASH_K_GATE_UP 7   /* gate/up projection + SwiGLU */
+#define DFLASH_K_GATE_UP 7   /* gate/up projection + SwiGLU (a second launch applies SwiGLU after a k split) */
 #define DFLASH_K_DOWN 8
 #define DFLASH_K_LM_HEAD 9   /* LM head + per-tile top-2 */
 #define DFLASH_K_ARGMAX 10
@@ -221,7 +221,8 @@ int dflash_read_error(dflash_ctx* ctx, hipStream_t stream, int32_t* out);
  * the totals. Capacity: 4096 launches between reads. A timed launch of a
  * single-kernel kind records the kernel's own start and end (the events of
  * hipExtLaunchKernel); DFLASH_K_VERIFY is timed between event records on
- * the stream around its one or two kernels. Timing adds a few microseconds
+ * the stream around its two (greedy) or three (temperature 1) kernels.
+ * Timing adds a few microseconds
  * of stream idle time around each timed launch; it is meant for eager
  * launches, not for graph capture. */
 int dflash_kernel_timer(dflash_ctx* ctx, int32_t kind, int32_t enable);

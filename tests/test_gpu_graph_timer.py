@@ -1,7 +1,8 @@
 """A decode step captured as a HIP graph and replayed gives, on every replay,
 bit-identical results to the same step launched eagerly (the library puts
-no memset nodes in a capture: counters reset themselves in-kernel); and the
-kernel timer reports launch durations for the kinds a step runs."""
+no memset nodes in a capture and keeps no counters across launches: its
+passes are separated by kernel boundaries); and the kernel timer reports
+launch durations for the kinds a step runs."""
 import numpy as np
 import pytest
 import torch

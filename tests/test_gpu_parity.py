@@ -148,8 +148,8 @@ def test_many_rows_tiled_gemm_tails():
     # of 250 tiles; the 24-row prefill chunks take the same kernels for the
     # context K/V. Hidden 352 (11 k steps) keeps every product in one k
     # split except the down projection (23 steps, 2 splits); hidden 544 (17
-    # steps) also splits the gate/up projection, whose SwiGLU then runs in
-    # the last workgroup of each tile.
+    # steps) also splits the QKV and gate/up projections; the SwiGLU then
+    # runs in its own kernel over the summed splits.
     for hidden, inter, seed in ((352, 736, 41), (544, 608, 43)):
         cfg = small_cfg(hidden=hidden, n_q_heads=4, n_kv_heads=2, head_dim=64, intermediate=inter, vocab=4000,
                         block_size=8)
