@@ -26,11 +26,11 @@
 // K and V are bf16 storage. Unnormalised O, the chunk's max and sum go to a
 // partial buffer, and attn_merge_kernel combines the chunks.
 //
-// Large batches have far more chunks than the chip holds at once. There
-// (d_h 64) a work item is cpi > 1 consecutive chunks, taken one after the
-// other by the same workgroup (stage, compute, stage, ...) with the running
-// max, sum and O rescaled per chunk as in any online softmax, and one
-// partial per item goes to the merge: cpi times fewer partial bytes.
+// Large batches have far more chunks than the chip holds at once. There a
+// work item is cpi > 1 consecutive chunks, taken one after the other by the
+// same workgroup (stage, compute, stage, ...) with the running max, sum and
+// O rescaled per half chunk as in any online softmax, and one partial per
+// item goes to the merge: cpi times fewer partial bytes.
 #include <algorithm>
 
 #include "common.h"
@@ -138,13 +138,14 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
     // covers the chunk.
     constexpr int UNITS_PER_PAGE = 4 * D;
     constexpr int TOTAL_UNITS = PAGES * UNITS_PER_PAGE;
-    for (int base = 0; base < TOTAL_UNITS; base += 8 * nthreads) {
-      int uu[8];
+    constexpr int UB = MULTI ? 4 : 8;  // loads per thread and batch (registers: O is live across chunks)
+    for (int base = 0; base < TOTAL_UNITS; base += UB * nthreads) {
+      int uu[UB];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) uu[j] = min(base + j * nthreads + tid, TOTAL_UNITS - 1);
-      u32x4 buf[8];
+      for (int j = 0; j < UB; ++j) uu[j] = min(base + j * nthreads + tid, TOTAL_UNITS - 1);
+      u32x4 buf[UB];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < UB; ++j) {
         const int p = uu[j] / UNITS_PER_PAGE, w = uu[j] % UNITS_PER_PAGE;
         const int pgv = cpg[p];
         const uint16_t* kb = pgv < 0 ? blk_k : a.pages + pgv * page_elems + (size_t)kvh * 16 * D;
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
         buf[j] = *reinterpret_cast<const u32x4*>(src);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < UB; ++j) {
         // a clamped duplicate rewrites the last unit with the same value
         const int p = uu[j] / UNITS_PER_PAGE, w = uu[j] % UNITS_PER_PAGE;
         const bool isk = w < 2 * D;
@@ -172,80 +173,91 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
     if (!computing) continue;
 
     // Key tile j = LDS rows 16j .. 16j+15; the lane holds S for keys
-    // tile_key(j, g, 0..3) of its query.
-    f32x4 s[NT];
-    {
-      f32x4 sa[NACC][NT];
+    // tile_key(j, g, 0..3) of its query. Multi-chunk items take a chunk as
+    // HV = 2 halves of 64 keys, each with its own online-softmax update, so
+    // that the O accumulators kept across chunks fit the registers.
+    constexpr int HV = MULTI ? 2 : 1, NTH = NT / HV;
 #pragma unroll
-      for (int h = 0; h < NACC; ++h)
+    for (int hv = 0; hv < HV; ++hv) {
+      f32x4 s[NTH];
+      {
+        f32x4 sa[NACC][NTH];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) sa[h][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < NACC; ++h)
 #pragma unroll
-      for (int kd = 0; kd < KD; ++kd) {
-        bf16x8 kf[NT];
+          for (int j = 0; j < NTH; ++j) sa[h][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-          kf[j] = *reinterpret_cast<const bf16x8*>(&lds[(16 * j + r16) * KP + kd * 32 + 8 * g]);
+        for (int kd = 0; kd < KD; ++kd) {
+          bf16x8 kf[NTH];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          sa[0][j] = mfma16(kf[j], qh[kd], sa[0][j]);
-          sa[NACC - 1][j] = mfma16(kf[j], ql[kd], sa[NACC - 1][j]);
+          for (int j = 0; j < NTH; ++j)
+            kf[j] = *reinterpret_cast<const bf16x8*>(&lds[(16 * (hv * NTH + j) + r16) * KP + kd * 32 + 8 * g]);
+#pragma unroll
+          for (int j = 0; j < NTH; ++j) {
+            sa[0][j] = mfma16(kf[j], qh[kd], sa[0][j]);
+            sa[NACC - 1][j] = mfma16(kf[j], ql[kd], sa[NACC - 1][j]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NTH; ++j) s[j] = NACC == 2 ? sa[0][j] + sa[NACC - 1][j] : sa[0][j];
+      }
+      if (v_begin < 16 || nv < CH) {  // edge chunk: mask invalid keys
+#pragma unroll
+        for (int j = 0; j < NTH; ++j) {
+          const int k0 = tile_key(hv * NTH + j, g, 0);  // 4 keys k0 .. k0+3 of one page
+          const int nj = ccnt[k0 >> 4] - (k0 & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[j][i] = i < nj ? s[j][i] : -INFINITY;
         }
       }
+      float cm = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) s[j] = NACC == 2 ? sa[0][j] + sa[NACC - 1][j] : sa[0][j];
-    }
-    if (v_begin < 16 || nv < CH) {  // edge chunk: mask invalid keys
+      for (int j = 0; j < NTH; ++j)
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int k0 = tile_key(j, g, 0);  // 4 keys k0 .. k0+3 of one page
-        const int nj = ccnt[k0 >> 4] - (k0 & 15);
+        for (int i = 0; i < 4; ++i) cm = fmaxf(cm, s[j][i]);
+      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));  // -inf for a half with no valid key
+      // finite: the first half of an item's first chunk always holds a valid key
+      const float mn = fmaxf(mx, cm);
+      const float scale = exp2f(mx - mn);  // 0 at the first chunk
+      mx = mn;
+      float cs = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[j][i] = i < nj ? s[j][i] : -INFINITY;
+      for (int j = 0; j < NTH; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s[j][i] = exp2f(s[j][i] - mx);
+          cs += s[j][i];
+        }
+      cs += __shfl_xor(cs, 16, 64);
+      cs += __shfl_xor(cs, 32, 64);
+      l = l * scale + cs;
+      if (MULTI) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t) acc[t] *= scale;
       }
-    }
-    float cm = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cm = fmaxf(cm, s[j][i]);
-    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));  // finite: every chunk has a valid key
-    const float mn = fmaxf(mx, cm);
-    const float scale = exp2f(mx - mn);  // 0 at the first chunk
-    mx = mn;
-    float cs = 0.f;
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[j][i] = exp2f(s[j][i] - mx);
-        cs += s[j][i];
-      }
-    cs += __shfl_xor(cs, 16, 64);
-    cs += __shfl_xor(cs, 32, 64);
-    l = l * scale + cs;
-    if (MULTI) {
-#pragma unroll
-      for (int t = 0; t < DT; ++t) acc[t] *= scale;
-    }
 
 #pragma unroll
-    for (int j = 0; j < NT; j += 2) {  // k-step: key tiles j and j+1 (32 keys, 2 pages)
-      // lane's keys: slots 8*(g&1) .. +7 of the step's page g>>1
-      bf16x8 vf[DT];
-      const uint16_t* vp = &lds[K_ELEMS + (j + (g >> 1)) * D * 16 + (g & 1) * D * 8 + r16 * 8];
+      for (int j = 0; j < NTH; j += 2) {  // k-step: key tiles j and j+1 (32 keys, 2 pages)
+        // lane's keys: slots 8*(g&1) .. +7 of the step's page g>>1
+        const uint16_t* vp = &lds[K_ELEMS + (hv * NTH + j + (g >> 1)) * D * 16 + (g & 1) * D * 8 + r16 * 8];
+        u16x4 h0, l0, h1, l1;
+        split4(s[j], h0, l0);
+        split4(s[j + 1], h1, l1);
+        const bf16x8 ph = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 pl = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
+        constexpr int TB = MULTI ? DT / 2 : DT;  // V fragments read at once
 #pragma unroll
-      for (int t = 0; t < DT; ++t) vf[t] = *reinterpret_cast<const bf16x8*>(vp + t * 128);
-      u16x4 h0, l0, h1, l1;
-      split4(s[j], h0, l0);
-      split4(s[j + 1], h1, l1);
-      const bf16x8 ph = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
-      const bf16x8 pl = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int t0 = 0; t0 < DT; t0 += TB) {
+          bf16x8 vf[TB];
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        acc[t] = mfma16(vf[t], ph, acc[t]);
-        acc[t] = mfma16(vf[t], pl, acc[t]);
+          for (int t = 0; t < TB; ++t) vf[t] = *reinterpret_cast<const bf16x8*>(vp + (t0 + t) * 128);
+#pragma unroll
+          for (int t = 0; t < TB; ++t) {
+            acc[t0 + t] = mfma16(vf[t], ph, acc[t0 + t]);
+            acc[t0 + t] = mfma16(vf[t], pl, acc[t0 + t]);
+          }
+        }
       }
     }
   }
@@ -330,11 +342,12 @@ extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim,
   const int G = a->n_q / a->n_kv, n_wr = G * a->N / 16;
   const int waves = std::max(n_wr, MIN_WAVES);
   const dim3 grid((a->n_ck + a->cpi - 1) / a->cpi, a->n_kv, B), block(64 * waves);
-  if (head_dim == 128) {  // cpi == 1 (the host's choice for d_h 128)
-    if (waves <= 8) launch_kernel(attn_chunk_kernel<128, 2, false>, grid, block, 0, st, *a);
+  if (head_dim == 128) {
+    if (a->cpi > 1) launch_kernel(attn_chunk_kernel<128, 1, true>, grid, block, 0, st, *a);
+    else if (waves <= 8) launch_kernel(attn_chunk_kernel<128, 2, false>, grid, block, 0, st, *a);
     else launch_kernel(attn_chunk_kernel<128, 1, false>, grid, block, 0, st, *a);
   } else if (a->cpi > 1) {
-    launch_kernel(attn_chunk_kernel<64, 1, true>, grid, block, 0, st, *a);
+    launch_kernel(attn_chunk_kernel<64, 2, true>, grid, block, 0, st, *a);
   } else {
     if (waves <= 8) launch_kernel(attn_chunk_kernel<64, 2, false>, grid, block, 0, st, *a);
     else launch_kernel(attn_chunk_kernel<64, 1, false>, grid, block, 0, st, *a);

@@ -505,9 +505,6 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   {  // chunks per work item, from the largest grid the batch can have
     const long long chunks = (long long)B * c.n_kv_heads * L.n_ck;
     aa.cpi = (int)std::min<long long>(8, std::max<long long>(1, (chunks + kAttnItems - 1) / kAttnItems));
-    // d_h 128: O accumulators kept across chunks would not fit the
-    // registers of two co-resident workgroups per CU; one chunk per item.
-    if (c.head_dim != 64) aa.cpi = 1;
   }
   aa.max_pages_per_seq = c.max_pages_per_seq;
   aa.n_pages = c.n_pages;
