@@ -66,8 +66,8 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   constexpr int K_ELEMS = CH * KP, V_ELEMS = PAGES * D * 16;
   constexpr int SLOTS = (MULTI ? CPI_MAX : 1) * PAGES;
   __shared__ __attribute__((aligned(16))) uint16_t lds[K_ELEMS + V_ELEMS];
-  __shared__ int pg[SLOTS];   // page of each page slot of the item (-1: the block)
-  __shared__ int cnt[SLOTS];  // valid key slots of each page slot
+  __shared__ long long poff[SLOTS];  // element offset in `pages` of each page slot's K block (this kv head); -1: block
+  __shared__ int cnt[SLOTS];         // valid key slots of each page slot
 
   const int item = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int cpi = MULTI ? a.cpi : 1;
@@ -80,18 +80,23 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   const int tid = threadIdx.x, nthreads = blockDim.x;
   const size_t page_elems = (size_t)2 * a.n_kv * 16 * D;
 
+  // Page slots of the item (virtual page 0 is the block; slots past the
+  // context point at the block and hold 0 valid keys).
+  const uint16_t* blk_k = a.kblk + ((size_t)b * a.n_kv + kvh) * 16 * D;
+  const uint16_t* blk_v = a.vblk + ((size_t)b * a.n_kv + kvh) * D * 16;
   for (int t = tid; t < n_chunks * PAGES; t += nthreads) {
-    int p = -1, n_ok = 0;
+    long long off = -1;
+    int n_ok = 0;
     if (16 * t < item_nv) {
       const int vp = item_begin / 16 + t;
       if (vp > 0) {
         const int raw = a.page_table[(size_t)seq * a.max_pages_per_seq + vp - 1];
         if (raw < 0 || raw >= a.n_pages) set_error(a.err, DFLASH_DEV_BAD_PAGE);
-        p = clampi(raw, 0, a.n_pages - 1);
+        off = (long long)clampi(raw, 0, a.n_pages - 1) * page_elems + (long long)kvh * 16 * D;
       }
       n_ok = vp == 0 ? a.N : min(16, item_nv - 16 * t);
     }
-    pg[t] = p;
+    poff[t] = off;
     cnt[t] = n_ok;
   }
 
@@ -99,6 +104,8 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   const int g = lane >> 4, r16 = lane & 15;
   const int G = a.n_q / a.n_kv, R = G * a.N, n_wr = R / 16;
   const bool computing = wave < n_wr;
+  // staging: thread t moves unit t % (4D) of its page slots, K units first
+  const bool isk_wave = __builtin_amdgcn_readfirstlane((int)(tid % (4 * D) < 2 * D));
   const int r = min(wave, n_wr - 1) * 16 + r16;
   const int hq = kvh * G + r / a.N, n = r % a.N;
   constexpr int KD = D / 32, DT = D / 16, NT = CH / 16;
@@ -119,54 +126,59 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mx = -INFINITY, l = 0.f;
-  const uint16_t* blk_k = a.kblk + ((size_t)b * a.n_kv + kvh) * 16 * D;
-  const uint16_t* blk_v = a.vblk + ((size_t)b * a.n_kv + kvh) * D * 16;
-
   for (int ci = 0; ci < n_chunks; ++ci) {
     const int v_begin = item_begin + ci * CH;
     const int nv = min(item_nv - ci * CH, CH);  // virtual keys in this chunk
-    const int* cpg = pg + ci * PAGES;
+    const long long* cpo = poff + ci * PAGES;
     const int* ccnt = cnt + ci * PAGES;
     __syncthreads();  // page slots written; the previous chunk's LDS reads done
 
     // Stage K (slot-major rows) and V (dim-major) of all PAGES page slots
-    // in LDS: per page, 2*D*16 bf16 = 4*D 16-byte units (K units first,
-    // then V units). Slots past the chunk's pages read the block (valid
-    // memory) and count 0 valid keys, so every V value of an invalid key is
-    // stored as 0 and the MFMAs never meet stale values; K of invalid keys
-    // is masked in S. One batch of 8 loads per thread when nthreads * 8
-    // covers the chunk.
-    constexpr int UNITS_PER_PAGE = 4 * D;
-    constexpr int TOTAL_UNITS = PAGES * UNITS_PER_PAGE;
-    constexpr int UB = MULTI ? 4 : 8;  // loads per thread and batch (registers: O is live across chunks)
-    for (int base = 0; base < TOTAL_UNITS; base += UB * nthreads) {
-      int uu[UB];
+    // in LDS: per page, 2*D*16 bf16 = UPP = 4*D 16-byte units, K units
+    // first. Thread t moves unit t % UPP of page slots t / UPP + SP*i, so
+    // the unit -- K or V, its source offset, its LDS place -- is fixed per
+    // thread and a whole wave works on one page slot (UPP is a multiple of
+    // 64): page lookups and the K/V choice are wave-uniform. Slots past the
+    // chunk's pages read the block (valid memory) and count 0 valid keys,
+    // so every V value of an invalid key is stored as 0 and the MFMAs never
+    // meet stale values; K of invalid keys is masked in S.
+    {
+      constexpr int UPP = 4 * D;
+      constexpr int UB = MULTI ? 4 : 8;  // loads per thread and batch (registers: O is live across chunks)
+      const int SP = nthreads / UPP;     // page slots per pass (nthreads >= 512 >= UPP)
+      const int passes = (PAGES + SP - 1) / SP;
+      const int w = tid % UPP;
+      const int p0 = __builtin_amdgcn_readfirstlane(tid / UPP);
+      const bool isk = isk_wave;
+      const int e = w - 2 * D;  // V unit: dim e/2, slots 8*(e&1) .. +7
+      const int src_off = isk ? (w / (D / 8)) * D + (w % (D / 8)) * 8 : e * 8;
+      const int lds_off = isk ? (w % (D / 8)) * 8 : K_ELEMS + (e & 1) * D * 8 + (e >> 1) * 8;
+      const uint16_t* blk = (isk ? blk_k : blk_v) + src_off;
+      const uint16_t* pgs = a.pages + (isk ? 0 : (size_t)a.n_kv * 16 * D) + src_off;
+      if (p0 < SP) {
+        for (int i0 = 0; i0 < passes; i0 += UB) {
+          u32x4 buf[UB];
 #pragma unroll
-      for (int j = 0; j < UB; ++j) uu[j] = min(base + j * nthreads + tid, TOTAL_UNITS - 1);
-      u32x4 buf[UB];
+          for (int u = 0; u < UB; ++u) {  // clamped slots: duplicate loads, not stored
+            const long long o = cpo[min((i0 + u) * SP + p0, PAGES - 1)];
+            buf[u] = *reinterpret_cast<const u32x4*>(o < 0 ? blk : pgs + o);
+          }
 #pragma unroll
-      for (int j = 0; j < UB; ++j) {
-        const int p = uu[j] / UNITS_PER_PAGE, w = uu[j] % UNITS_PER_PAGE;
-        const int pgv = cpg[p];
-        const uint16_t* kb = pgv < 0 ? blk_k : a.pages + pgv * page_elems + (size_t)kvh * 16 * D;
-        const uint16_t* vb = pgv < 0 ? blk_v : kb + (size_t)a.n_kv * 16 * D;
-        const uint16_t* src = (w < 2 * D) ? kb + (w / (D / 8)) * D + (w % (D / 8)) * 8 : vb + (w - 2 * D) * 8;
-        buf[j] = *reinterpret_cast<const u32x4*>(src);
-      }
+          for (int u = 0; u < UB; ++u) {
+            const int pi = (i0 + u) * SP + p0;
+            if (i0 + u >= passes || pi >= PAGES) break;
+            if (isk) {
+              *reinterpret_cast<u32x4*>(&lds[krow(pi * 16 + w / (D / 8)) * KP + lds_off]) = buf[u];
+            } else {
+              const int valid = ccnt[pi] - (e & 1) * 8;
+              u32x4 m;
 #pragma unroll
-      for (int j = 0; j < UB; ++j) {
-        // a clamped duplicate rewrites the last unit with the same value
-        const int p = uu[j] / UNITS_PER_PAGE, w = uu[j] % UNITS_PER_PAGE;
-        const bool isk = w < 2 * D;
-        const int valid = isk ? 8 : ccnt[p] - ((w - 2 * D) & 1) * 8;  // V unit: slots 8*(w&1) .. +7
-        u32x4 m;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) m[e] = (2 * e < valid ? 0xFFFFu : 0u) | (2 * e + 1 < valid ? 0xFFFF0000u : 0u);
-        const int key = p * 16 + w / (D / 8);  // K unit: chunk key, 8 dims
-        const int e = w - 2 * D;               // V unit: dim e/2, slots 8*(e&1) .. +7
-        const int off = isk ? krow(key) * KP + (w % (D / 8)) * 8
-                            : K_ELEMS + p * D * 16 + (e & 1) * D * 8 + (e >> 1) * 8;
-        *reinterpret_cast<u32x4*>(&lds[off]) = buf[j] & m;
+              for (int q = 0; q < 4; ++q)
+                m[q] = (2 * q < valid ? 0xFFFFu : 0u) | (2 * q + 1 < valid ? 0xFFFF0000u : 0u);
+              *reinterpret_cast<u32x4*>(&lds[pi * D * 16 + lds_off]) = buf[u] & m;
+            }
+          }
+        }
       }
     }
     __syncthreads();
@@ -226,7 +238,7 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
       for (int j = 0; j < NTH; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s[j][i] = exp2f(s[j][i] - mx);
+          s[j][i] = __builtin_amdgcn_exp2f(s[j][i] - mx);  // <= 1; results under 2^-126 flush to 0
           cs += s[j][i];
         }
       cs += __shfl_xor(cs, 16, 64);
