@@ -14,6 +14,13 @@ events on its launch stream over a second run of the same steps, since a
 timed launch idles the stream for a few microseconds), the whole step
 against the HBM roofline, and the oracle's CPU throughput on a bounded
 sample.
+
+`--workload qwen3_8b_batched` (32 sequences, ragged contexts from 512 to
+8192, ragged appends, temperature-1 verify) and `--workload gpt_oss_20b`
+(8 sequences at context 8192, greedy) time the batched shapes the same way;
+their dominant kernel is the block attention (HBM-bound on the context KV),
+and the step is set against a roofline that adds, per phase, the larger of
+the HBM time and the dense-bf16 MFMA time.
 """
 import argparse
 import json
@@ -88,6 +95,136 @@ def cpu_baseline(cfg, w, hidden_pre, hidden_step, anchor, logits_bits):
             "seconds": dt}
 
 
+MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def batched_roofline(cfg, ctx, n_new):
+    """Per-phase algorithmic bytes and flops of one batched step, and
+    t_roof = sum over phases of max(bytes / 8 TB/s, flops / 2.5 PF)."""
+    D, H, I, V, T, N = (cfg[k] for k in ("n_layers", "hidden", "intermediate", "vocab", "n_target_layers",
+                                         "block_size"))
+    d, nq, nkv = cfg["head_dim"], cfg["n_q_heads"], cfg["n_kv_heads"]
+    qd, kvd = nq * d, nkv * d
+    B = len(ctx)
+    M, rows = B * N, int(np.sum(n_new))
+    layer_w = qd * H + 2 * kvd * H + H * qd + 2 * I * H + H * I
+    wt = 0 if cfg.get("tied_kv") else D * 2 * kvd * H
+    gemm_bytes = (D * layer_w + V * H + wt) * 2
+    gemm_flops = 2.0 * M * (D * layer_w + V * H) + 2.0 * rows * D * 2 * kvd * H
+    keys = int(np.sum(ctx)) + B * N
+    attn_bytes = D * keys * 2 * kvd * 2
+    attn_flops = 4.0 * D * nq * N * keys * d
+    rest_bytes = rows * T * H * 2 + D * rows * 2 * kvd * 2 + M * V * 2
+    phases = {"gemm": (gemm_bytes, gemm_flops), "attention": (attn_bytes, attn_flops), "rest": (rest_bytes, 0.0)}
+    t = {k: max(b / (HBM_PEAK_GBS * 1e9), f / (MFMA_PEAK_TFS * 1e12)) for k, (b, f) in phases.items()}
+    return {"phases": {k: {"bytes": int(b), "flops": f, "t_us": round(t[k] * 1e6, 1)} for k, (b, f) in phases.items()},
+            "t_roof_us": round(sum(t.values()) * 1e6, 1), "attn_bytes_per_layer": attn_bytes // D}
+
+
+def run_batched(args, name):
+    """A batched workload: prefill (device-generated hidden states; their
+    values do not change the work), then timed steps as in the default
+    workload, then the attention kernel's launches timed in a second pass."""
+    import torch
+    from block_diffusion_drafter_softmax_amd import synth
+    from block_diffusion_drafter_softmax_amd import _binding as B
+    from block_diffusion_drafter_softmax_amd.drafter import Drafter
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    cfg = synth.config(name)
+    Bn, N, T, H, V = cfg["batch"], cfg["block_size"], cfg["n_target_layers"], cfg["hidden"], cfg["vocab"]
+    ctx = synth.context_lengths(cfg, 0)
+    n_new = synth.appended_rows(cfg, 0)
+    temp = 1.0 if cfg["verify"] == "temp1" else 0.0
+    dev = torch.device("cuda")
+    w = synth.make_weights(cfg, 0)
+    chunk = 512
+    dr = Drafter(cfg, w, max_batch=Bn, max_new=chunk, max_seqs=Bn,
+                 pages_per_seq=(int(ctx.max()) + N + 15) // 16 + 1, page_order="shuffled")
+    seq = torch.arange(Bn, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    hid = torch.randn((Bn, chunk, T, H), generator=gen, device=dev).to(torch.bfloat16)
+    pre, done = ctx - n_new, np.zeros(Bn, dtype=np.int64)
+    while (done < pre).any():
+        n = np.minimum(pre - done, chunk).astype(np.int32)
+        dr.ctx_append(seq, torch.from_numpy(n).to(dev), hid, chunk)
+        done += n
+    del hid
+    torch.cuda.synchronize()
+    assert dr.read_error() == 0
+    log(f"prefill done: {Bn} sequences, contexts {ctx.min()}..{ctx.max()}, appends {int(n_new.sum())} rows")
+
+    max_new = int(n_new.max())
+    step_hid = torch.randn((Bn, max_new, T, H), generator=gen, device=dev).to(torch.bfloat16)
+    n_new_t = torch.from_numpy(n_new.astype(np.int32)).to(dev)
+    anchor = torch.from_numpy(synth.make_anchor(cfg, Bn, 0)).to(dev)
+    draft = torch.zeros((Bn, N - 1), dtype=torch.int32, device=dev)
+    acc = torch.zeros(Bn, dtype=torch.int32, device=dev)
+    nxt = torch.zeros(Bn, dtype=torch.int32, device=dev)
+    com = torch.zeros(Bn, dtype=torch.int32, device=dev)
+    ctx0 = dr.ctx_len.clone()
+    dr.ctx_append(seq, n_new_t, step_hid, max_new)
+    dr.draft_block(seq, anchor, draft)
+    torch.cuda.synchronize()
+    logits_bits = synth.make_logits(cfg, draft.cpu().numpy(), 0)
+    logits = torch.from_numpy(logits_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def step():
+        dr.ctx_len.copy_(ctx0)
+        dr.ctx_append(seq, n_new_t, step_hid, max_new)
+        dr.draft_block(seq, anchor, draft)
+        dr.verify(seq, draft, logits, acc, nxt, com, temperature=temp, seed=1, step=0)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert dr.read_error() == 0
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    B.check(B.dflash_kernel_timer(dr.handle, B.K_ATTN, 1), "timer")
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    rc, at_ms, at_n = B.dflash_kernel_timer_read(dr.handle, B.K_ATTN)
+    B.check(rc, "timer read")
+    B.dflash_kernel_timer(dr.handle, B.K_ATTN, 0)
+    assert dr.read_error() == 0
+
+    rl = batched_roofline(cfg, ctx, n_new)
+    at_s = at_ms / at_n / 1e3
+    achieved = rl["attn_bytes_per_layer"] / at_s / 1e9
+    accepted = float(acc.float().mean())
+    res = {
+        "metric": "draft tokens/sec per GPU (block=16, batched drafter+verify); % roofline",
+        "value": round(Bn * (N - 1) / (ms_step / 1e3), 1), "unit": "draft tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{name}: {Bn} sequences x block {N}, contexts {int(ctx.min())}..{int(ctx.max())} "
+                               f"(sum {int(ctx.sum())}), {int(n_new.sum())} rows appended, "
+                               f"{'temperature-1' if temp else 'greedy'} verify; D {cfg['n_layers']}, H {H}, "
+                               f"{cfg['n_q_heads']}/{cfg['n_kv_heads']} heads of {cfg['head_dim']}, "
+                               f"I {cfg['intermediate']}, V {V}",
+                   "global_batch": Bn, "block": N, "launch": "eager"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "block attention (context + block K/V of one layer)",
+                     "bytes_per_launch": rl["attn_bytes_per_layer"], "avg_launch_us": round(at_s * 1e6, 2),
+                     "launches_timed": at_n},
+        "step_roofline": {"bound": "mixed", "t_roof_us": rl["t_roof_us"], "phases": rl["phases"],
+                          "frac": round(rl["t_roof_us"] / (ms_step * 1e3), 4)},
+        "mean_accept": round(accepted, 3),
+        "cpu_baseline": None,
+    }
+    log(f"{ms_step:.3f} ms/step, {res['value']:.0f} draft tok/s, step roofline {res['step_roofline']['frac']:.3f}")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,11 +232,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "qwen3_8b_batched", "gpt_oss_20b"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the drafter's hot path runs on a single MI355X here; "
               "--gpus must be 1", file=sys.stderr)
         sys.exit(2)
+    if args.workload != WORKLOAD:
+        return run_batched(args, args.workload)
 
     import torch
     from block_diffusion_drafter_softmax_amd import synth

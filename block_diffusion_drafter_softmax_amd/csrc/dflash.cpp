@@ -45,7 +45,8 @@ constexpr int kTargetWaves = 1536;  // streaming waves to aim for (~6 per CU)
 constexpr int kMmMinRows = 64;      // from this many activation rows on, GEMMs use the tiled MFMA kernels
 constexpr int kMmCols = MM_COL_TILES * 16;  // output columns (vocabulary rows) per tiled-GEMM workgroup
 constexpr int kMmRows = MM_ROW_TILES * 16;  // activation rows per tiled-GEMM workgroup
-constexpr int kMmTargetWgs = 512;   // tiled-GEMM workgroups to aim for (2 resident per CU)
+constexpr int kMmTargetWgs = 256;   // tiled-GEMM workgroups to aim for before splitting k (one per CU; more splits cost
+                                    // partial-sum traffic in the GEMM and its consumer)
 // Partial-sum floats a tiled GEMM may need: a k split is only taken while
 // the grid is under 2 * kMmTargetWgs workgroup tiles.
 constexpr size_t kMmPartFloats = (size_t)2 * kMmTargetWgs * kMmRows * kMmCols;

@@ -13,31 +13,43 @@ DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); 
 
 // ------------------------------------------------------------ fusion
 
-#define FUSE_MAXV 2   // float4 groups per thread: H <= 1024 * 4 * 2
 #define FUSE_TMAX 16  // target layers
+#define FUSE_DMAX 64  // draft layers (the host accepts up to 64)
 
-// One workgroup per (appended row m = b*max_new + t, draft layer i), one
-// float4 group of the row per thread. While the row's T target states are
-// in flight, thread 0 plans the row: sequence b's checks (sequence id,
-// n_new, position capacity; its page-table entries are checked by the first
-// threads) give position ctx_len + t, or -1 if t >= n_new or a check fails
-// (the whole sequence is then skipped and its error bits set once, by row
-// t = 0 of layer 0). Layer 0 records the positions for the context
-// finisher, which advances ctx_len. Then s = sum_j alpha[i][j] * h_j
-// (ascending j), f = s / sqrt(mean(s^2) + eps) * g, written as the packed
-// split activation of the context K/V projection.
+// One workgroup per (appended row m = b*max_new + t, group of DG draft
+// layers), MAXV float4 groups of the row per thread: DG = 1 (a workgroup
+// per layer) while rows are few, all layers of a row in one workgroup when
+// there are enough rows to fill the chip. While the row's T target states are in flight,
+// thread 0 plans the row: sequence b's checks (sequence id, n_new, position
+// capacity; its page-table entries are checked by the first threads) give
+// position ctx_len + t, or -1 if t >= n_new or a check fails (the whole
+// sequence is then skipped and its error bits set once, by row t = 0). The
+// positions are recorded for the context finisher, which advances ctx_len.
+// The T states stay in registers while, for every draft layer i of the
+// group (one workgroup reduction for the group), s = sum_j alpha[i][j] * h_j
+// (ascending j) and f = s / sqrt(mean(s^2) + eps) * g are formed and written
+// as the packed split activation of the context K/V projection.
+template <int MAXV, int DG>
 __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
-  const int m = blockIdx.x, i = blockIdx.y;
+  const int m = blockIdx.x, i0 = blockIdx.y * DG;
   const int b = m / a.max_new, t = m % a.max_new;
-  __shared__ float red[16];
+  __shared__ float red[16][DG];
+  __shared__ float al_s[FUSE_DMAX * FUSE_TMAX];  // alpha, [layer][j], zero past T
   __shared__ int plan[4];  // seq, L, n, bad
-  // the row's first 8 target states (this thread's first float4 group) are
-  // requested before the plan, which takes three dependent reads
+  // the row's target states are requested before the plan, which takes
+  // three dependent reads
   const uint16_t* h = a.hidden + (size_t)m * a.T * a.H;
-  const int kq = min((int)threadIdx.x * 4, a.H - 4);  // clamped: no branch around loads
-  u16x4 pre[8];
+  u16x4 x[MAXV][FUSE_TMAX];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) pre[j] = *reinterpret_cast<const u16x4*>(h + (size_t)min(j, a.T - 1) * a.H + kq);
+  for (int v = 0; v < MAXV; ++v) {
+    const int k = min((v * (int)blockDim.x + (int)threadIdx.x) * 4, a.H - 4);  // clamped: no branch around loads
+#pragma unroll
+    for (int j = 0; j < FUSE_TMAX; ++j) x[v][j] = *reinterpret_cast<const u16x4*>(h + (size_t)min(j, a.T - 1) * a.H + k);
+  }
+  for (int q = threadIdx.x; q < FUSE_DMAX * FUSE_TMAX; q += blockDim.x) {
+    const int i = q / FUSE_TMAX, j = q % FUSE_TMAX;
+    al_s[q] = (i < a.D && j < a.T) ? a.alpha[(size_t)i * a.T + j] : 0.f;  // weights past T are 0
+  }
   if (threadIdx.x == 0) {
     int bad = 0;
     const int s_raw = a.seq_ids[b];
@@ -66,66 +78,81 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
   __syncthreads();
   const int bad = plan[3];
   const int pos = (!bad && t < plan[2]) ? plan[1] + t : -1;
-  if (i == 0 && threadIdx.x == 0) {
+  if (blockIdx.y == 0 && threadIdx.x == 0) {
     a.row_pos[m] = pos;
     a.row_seq[m] = plan[0];
     if (t == 0 && bad) set_error(a.err, bad);
   }
   if (pos < 0) return;
-  const float* al = a.alpha + (size_t)i * a.T;
-  const int nv = (a.H / 4 + blockDim.x - 1) / blockDim.x;
-  float s[FUSE_MAXV][4];
-  float ss = 0.f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const size_t plane = act_plane(a.rows, a.H);
+  {
+    float s[DG][MAXV][4];
+    float ss[DG];
 #pragma unroll
-  for (int v = 0; v < FUSE_MAXV; ++v) {
-    const int k = min((v * (int)blockDim.x + (int)threadIdx.x) * 4, a.H - 4);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int di = 0; di < DG; ++di) {
+      ss[di] = 0.f;
+      const float* al = al_s + min(i0 + di, FUSE_DMAX - 1) * FUSE_TMAX;
 #pragma unroll
-    for (int j0 = 0; j0 < FUSE_TMAX; j0 += 8) {  // T <= FUSE_TMAX: at most two batches
-      if (j0 >= a.T) break;
-      u16x4 x[8];
+      for (int v = 0; v < MAXV; ++v) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        x[j] = (v == 0 && j0 == 0) ? pre[j]
-                                   : *reinterpret_cast<const u16x4*>(h + (size_t)min(j0 + j, a.T - 1) * a.H + k);
+        for (int j = 0; j < FUSE_TMAX; ++j) {  // ascending j; the clamped states past T weigh 0
+          const float w = al[j];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j0 + j >= a.T) break;
-        const float w = al[j0 + j];
+          for (int e = 0; e < 4; ++e) acc[e] += w * bf2f(x[v][j][e]);
+        }
+        const bool mine = (v * (int)blockDim.x + (int)threadIdx.x) * 4 < a.H;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += w * bf2f(x[j][e]);
+        for (int e = 0; e < 4; ++e) {
+          s[di][v][e] = acc[e];
+          if (mine) ss[di] += acc[e] * acc[e];
+        }
       }
     }
-    const bool mine = v < nv && (v * (int)blockDim.x + (int)threadIdx.x) * 4 < a.H;
+    // one reduction for the group's layers (fixed order: waves, then sum)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s[v][e] = acc[e];
-      if (mine) ss += acc[e] * acc[e];
+    for (int di = 0; di < DG; ++di) ss[di] = wave_sum(ss[di]);
+    if (lane == 0)
+#pragma unroll
+      for (int di = 0; di < DG; ++di) red[wave][di] = ss[di];
+    __syncthreads();
+#pragma unroll
+    for (int di = 0; di < DG; ++di) {
+      const int i = i0 + di;
+      if (i >= a.D) break;
+      float tot = 0.f;
+      for (int w = 0; w < nw; ++w) tot += red[w][di];
+      const float rstd = 1.0f / sqrtf(tot / a.H + a.eps);
+      uint16_t* out = a.f + (size_t)i * 2 * plane;
+      const uint16_t* g = a.g_fuse + (size_t)i * a.H;
+#pragma unroll
+      for (int v = 0; v < MAXV; ++v) {
+        const int k = (v * blockDim.x + threadIdx.x) * 4;
+        if (k >= a.H) continue;
+        const u16x4 gv = *reinterpret_cast<const u16x4*>(g + k);
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = s[di][v][e] * rstd * bf2f(gv[e]);
+        u16x4 hi, lo;
+        split4(y, hi, lo);
+        *reinterpret_cast<u16x4*>(out + pk_index(m, k, a.H)) = hi;
+        *reinterpret_cast<u16x4*>(out + plane + pk_index(m, k, a.H)) = lo;
+      }
     }
-  }
-  const float tot = block_sum(ss, red);
-  const float rstd = 1.0f / sqrtf(tot / a.H + a.eps);
-  const size_t plane = act_plane(a.rows, a.H);
-  uint16_t* out = a.f + (size_t)i * 2 * plane;
-  const uint16_t* g = a.g_fuse + (size_t)i * a.H;
-#pragma unroll
-  for (int v = 0; v < FUSE_MAXV; ++v) {
-    const int k = (v * blockDim.x + threadIdx.x) * 4;
-    if (v >= nv || k >= a.H) continue;
-    const u16x4 gv = *reinterpret_cast<const u16x4*>(g + k);
-    f32x4 y;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = s[v][e] * rstd * bf2f(gv[e]);
-    u16x4 hi, lo;
-    split4(y, hi, lo);
-    *reinterpret_cast<u16x4*>(out + pk_index(m, k, a.H)) = hi;
-    *reinterpret_cast<u16x4*>(out + plane + pk_index(m, k, a.H)) = lo;
   }
 }
 
 extern "C" hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st) {
   const int threads = std::min(1024, ((a->H / 4 + 63) / 64) * 64);
-  launch_kernel(fuse_kernel, dim3(a->rows, a->D), dim3(threads), 0, st, *a);
+  constexpr int DG = 8;
+  if (a->H > 4 * threads) {  // H > 4096: two float4 groups per thread, one layer per workgroup
+    launch_kernel((fuse_kernel<2, 1>), dim3(a->rows, a->D), dim3(threads), 0, st, *a);
+  } else if (a->rows < 128) {  // few rows: a workgroup per (row, layer)
+    launch_kernel((fuse_kernel<1, 1>), dim3(a->rows, a->D), dim3(threads), 0, st, *a);
+  } else {
+    launch_kernel((fuse_kernel<1, DG>), dim3(a->rows, (a->D + DG - 1) / DG), dim3(threads), 0, st, *a);
+  }
   return hipGetLastError();
 }
 
