@@ -21,6 +21,11 @@ What it follows (the pages are three web summaries; sections, not lines):
     by the target's own token. Key contributions: the result is lossless.
   * DFlash page, Methodology step 4: the window advances by the number of
     accepted tokens.
+  * "D^2SD: Accelerating Speculative Decoding with Dual Diffusion Draft
+    Models" (euno.news), Methodology steps 1-4: per-position confidence of
+    the first draft, K prefixes cut where a rejection is most likely, a
+    second batched drafting pass re-anchored on each prefix, and one
+    verification of all candidates that keeps the longest accepted prefix.
 
 Where the pages are silent the readings are (each also listed in the
 design notes): one pass, no noise; mask positions are an embedding row
@@ -60,7 +65,8 @@ __all__ = [
     "fuse_context", "attention", "silu", "argmax_first", "top2_gap",
     "OracleModel", "OracleCache", "ctx_append", "draft_block",
     "verify_greedy", "verify_temp1", "philox4x64_10", "philox4x64_10_vec",
-    "rng_uniform", "rng_gumbel_row",
+    "rng_uniform", "rng_gumbel_row", "draft_confidence", "d2sd_cut_points",
+    "d2sd_candidate_tokens", "d2sd_candidates", "verify_greedy_multi",
 ]
 
 
@@ -343,6 +349,73 @@ def verify_greedy(draft, z):
     while a < n_draft and int(draft[a]) == int(t[a]):
         a += 1
     return a, int(t[a]), a + 1
+
+
+# ------------------------------------------------- dual-pass drafting (D2SD)
+def draft_confidence(z):
+    """Confidence of each draft position: the drafter's largest softmax
+    probability, max_k softmax(z[r])_k = 1 / sum_k exp(z[r,k] - max z[r])
+    (D2SD page, Methodology step 1: a score per position for how likely the
+    target accepts it; reading: the drafter's own top probability).
+    z [R, V] -> [R] float64."""
+    z = np.asarray(z, dtype=np.float64)
+    m = z.max(axis=1, keepdims=True)
+    return 1.0 / np.exp(z - m).sum(axis=1)
+
+
+def d2sd_cut_points(conf, K):
+    """Where to cut the first draft (D2SD page, Methodology step 2: the
+    likeliest rejection points). conf[j-1] is the confidence of draft
+    position j = 1 .. N-1. Reading: the min(K, N-1) positions of lowest
+    confidence, ties to the lower position, returned in ascending position
+    order (the order of the candidates)."""
+    ranked = sorted(range(len(conf)), key=lambda j: (float(conf[j]), j))
+    return sorted(j + 1 for j in ranked[:min(K, len(conf))])
+
+
+def d2sd_candidate_tokens(anchor, draft, c, N, mask_id):
+    """Input block of the candidate re-anchored at cut point c (D2SD page,
+    Methodology step 3): the anchor, the first draft's d_1 .. d_{c-1} kept
+    as real tokens, masks from position c on."""
+    return [int(anchor)] + [int(t) for t in draft[:c - 1]] + [int(mask_id)] * (N - c)
+
+
+def d2sd_candidates(model, cache, seq, anchor, K, storage=True):
+    """First draft, its confidences and cut points, and the K re-anchored
+    candidates (the second pass uses the same weights and the same context
+    cache; D2SD page, Methodology steps 1-3). Candidate 0 is the first
+    draft; candidate k >= 1 keeps d_1 .. d_{c_k - 1} and takes the second
+    pass's argmax tokens from position c_k on.
+    Returns dict: first (draft_block output), conf [N-1], cuts [K'],
+    drafts [K'+1, N-1], second (draft_block outputs of the second pass)."""
+    c = model.cfg
+    N = c["block_size"]
+    first = draft_block(model, cache, seq, anchor, storage)
+    conf = draft_confidence(first["logits"])
+    cuts = d2sd_cut_points(conf, K)
+    drafts = [np.asarray(first["draft"])]
+    second = []
+    for cp in cuts:
+        toks = d2sd_candidate_tokens(anchor, first["draft"], cp, N, c["mask_token_id"])
+        out = draft_block(model, cache, seq, anchor, storage, tokens=toks)
+        drafts.append(np.concatenate([np.asarray(first["draft"])[:cp - 1], np.asarray(out["draft"])[cp - 1:]]))
+        second.append(out)
+    return {"first": first, "conf": conf, "cuts": cuts, "drafts": np.stack(drafts), "second": second}
+
+
+def verify_greedy_multi(drafts, z):
+    """Greedy verification of C candidate blocks of one sequence (D2SD page,
+    Methodology step 4: the longest prefix the target agrees with is kept,
+    the rest discarded). drafts [C, N-1]; z [C, N, V]: the target's logits
+    for each candidate block. Each candidate is verified as in
+    ``verify_greedy``; the longest accept wins, the lowest candidate index
+    on ties. Returns (accept_len, next_token, commit_len, chosen)."""
+    best = None
+    for ci in range(len(drafts)):
+        a, nxt, cm = verify_greedy(drafts[ci], z[ci])
+        if best is None or a > best[0]:
+            best = (a, nxt, cm, ci)
+    return best
 
 
 # Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as

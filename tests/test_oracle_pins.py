@@ -499,4 +499,81 @@ def test_temp1_first_token_is_lossless_chi_square():
     assert abs(accepted / n - pd) < 5 * math.sqrt(pd * (1 - pd) / n)
 
 
+# ---------------------------------------------- dual-pass drafting (D2SD)
+def test_confidence_is_the_softmax_maximum():
+    """Confidence = the largest softmax probability: scipy's softmax on random
+    rows; 1/V on a flat row; 1 when one logit dominates by far."""
+    r = np.random.default_rng(50)
+    z = r.standard_normal((7, 33)) * 3
+    assert np.allclose(O.draft_confidence(z), scipy.special.softmax(z, axis=1).max(axis=1), rtol=1e-12)
+    assert np.allclose(O.draft_confidence(np.zeros((2, 40))), 1 / 40, rtol=1e-14)
+    big = np.zeros((1, 10))
+    big[0, 3] = 800.0
+    assert O.draft_confidence(big)[0] == 1.0
+
+
+def test_cut_points_brute_force_and_ties():
+    # worked example: the three lowest confidences are 0.1 (position 5) and the
+    # tie 0.2 at positions 2 and 3; returned in position order
+    assert O.d2sd_cut_points([0.5, 0.2, 0.2, 0.9, 0.1], 3) == [2, 3, 5]
+    # a tie at the boundary goes to the lower position
+    assert O.d2sd_cut_points([0.3, 0.1, 0.3, 0.3], 2) == [1, 2]
+    assert O.d2sd_cut_points([0.3, 0.1], 5) == [1, 2]
+    r = np.random.default_rng(51)
+    for _ in range(300):
+        n = int(r.integers(1, 9))
+        conf = r.integers(0, 4, size=n) / 4.0                      # many ties
+        K = int(r.integers(0, 6))
+        got = O.d2sd_cut_points(conf, K)
+        k = min(K, n)
+        # brute force: the chosen set has the smallest (conf, position) keys
+        keys = sorted((conf[j], j + 1) for j in range(n))
+        assert got == sorted(p for _, p in keys[:k])
+        assert all(conf[g - 1] <= conf[j] for g in got for j in range(n) if j + 1 not in got)
+
+
+def test_candidate_tokens_layout():
+    # N = 8, cut at 3: anchor, d_1, d_2 kept, masks from position 3 on
+    assert O.d2sd_candidate_tokens(7, [11, 12, 13, 14, 15, 16, 17], 3, 8, 99) == [7, 11, 12, 99, 99, 99, 99, 99]
+    assert O.d2sd_candidate_tokens(7, [11, 12, 13], 1, 4, 99) == [7, 99, 99, 99]
+    assert O.d2sd_candidate_tokens(7, [11, 12, 13], 4, 4, 99) == [7, 11, 12, 13]
+
+
+def test_candidates_keep_the_prefix_and_cut_at_one_reproduces_the_first_draft():
+    c = tiny_cfg(block_size=6)
+    m = _model(c, tiny_weights(c, seed=52))
+    cache, _ = _prefill(m, c, 7)
+    out = O.d2sd_candidates(m, cache, 0, 5, K=5, storage=False)
+    first = out["first"]["draft"]
+    assert out["cuts"] == [1, 2, 3, 4, 5]                       # K >= N-1: every position
+    assert np.array_equal(out["drafts"][0], first)
+    for k, cp in enumerate(out["cuts"]):
+        d = out["drafts"][k + 1]
+        assert np.array_equal(d[:cp - 1], first[:cp - 1])        # the kept prefix
+        assert np.array_equal(d[cp - 1:], out["second"][k]["draft"][cp - 1:])
+    # cut at 1 re-drafts from [anchor, mask...]: the first pass itself
+    assert np.array_equal(out["drafts"][1], first)
+    assert np.array_equal(out["second"][0]["logits"], out["first"]["logits"])
+    # a longer kept prefix changes what the second pass sees: its hidden
+    # states differ from the first pass's from the first real token on
+    assert not np.allclose(out["second"][2]["hidden"][-1][1:], out["first"]["hidden"][-1][1:])
+
+
+def test_verify_multi_brute_force_and_ties():
+    r = np.random.default_rng(53)
+    for _ in range(300):
+        C, N, V = int(r.integers(1, 5)), 5, 4
+        z = r.integers(0, 3, size=(C, N, V)).astype(np.float64)
+        t = [[int(np.argmax(row)) for row in zc] for zc in z]
+        drafts = np.array([[t[ci][j] if r.random() < 0.7 else int(r.integers(0, V)) for j in range(N - 1)]
+                           for ci in range(C)])
+        a, nxt, commit, chosen = O.verify_greedy_multi(drafts, z)
+        acc = [_brute_accept(list(drafts[ci]), t[ci]) for ci in range(C)]
+        assert a == max(acc) and chosen == acc.index(max(acc))      # lowest index on ties
+        assert nxt == t[chosen][a] and commit == a + 1
+    # one candidate: plain greedy verification
+    z = np.eye(5)[[1, 2, 3, 4, 0]] * 3.0
+    assert O.verify_greedy_multi(np.array([[1, 2, 0, 4]]), z[None])[:3] == O.verify_greedy(np.array([1, 2, 0, 4]), z)
+
+
 import scipy.stats  # noqa: E402  (used above)
