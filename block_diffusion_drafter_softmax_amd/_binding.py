@@ -27,15 +27,15 @@ DTYPE_BF16 = 0
 DTYPE_F32 = 1
 
 K_FUSE, K_CTX_KV, K_NORM, K_QKV, K_ATTN, K_ATTN_MERGE, K_OPROJ, K_GATE_UP, K_DOWN, \
-    K_LM_HEAD, K_ARGMAX, K_VERIFY, K_QKV_FINISH, K_CTX_FINISH = range(14)
-K_COUNT = 14
+    K_LM_HEAD, K_ARGMAX, K_VERIFY, K_QKV_FINISH, K_CTX_FINISH, K_D2SD = range(15)
+K_COUNT = 15
 KERNEL_NAMES = ["fuse", "ctx_kv", "norm", "qkv", "attn", "attn_merge", "o_proj", "gate_up",
-                "down", "lm_head", "argmax", "verify", "plan", "qkv_finish", "ctx_finish"]
+                "down", "lm_head", "argmax", "verify", "qkv_finish", "ctx_finish", "d2sd"]
 
 EXPORTS = [
     "dflash_workspace_bytes", "dflash_create", "dflash_destroy", "dflash_ctx_append",
-    "dflash_draft_block", "dflash_verify", "dflash_last_error", "dflash_read_error",
-    "dflash_kernel_timer", "dflash_kernel_timer_read",
+    "dflash_draft_block", "dflash_verify", "dflash_d2sd_draft", "dflash_verify_multi",
+    "dflash_last_error", "dflash_read_error", "dflash_kernel_timer", "dflash_kernel_timer_read",
 ]
 
 
@@ -78,6 +78,8 @@ def _load():
         "dflash_ctx_append": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, vp]),
         "dflash_draft_block": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
         "dflash_verify": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, ctypes.c_float, u64, u64, vp, vp, vp, vp]),
+        "dflash_d2sd_draft": (ctypes.c_int, [vp, i32, vp, vp, i32, vp, vp, vp, vp]),
+        "dflash_verify_multi": (ctypes.c_int, [vp, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
         "dflash_last_error": (ctypes.c_char_p, []),
         "dflash_read_error": (ctypes.c_int, [vp, vp, ctypes.POINTER(i32)]),
         "dflash_kernel_timer": (ctypes.c_int, [vp, i32, i32]),
@@ -131,6 +133,16 @@ def dflash_verify(ctx, B, seq_ids, draft, target_logits, logits_dtype, temperatu
                   accept_len, next_token, commit_len, stream):
     return lib.dflash_verify(ctx, B, seq_ids, draft, target_logits, logits_dtype, float(temperature),
                              seed, step, accept_len, next_token, commit_len, stream)
+
+
+def dflash_d2sd_draft(ctx, B, seq_ids, anchor, K, drafts, conf, cuts, stream):
+    return lib.dflash_d2sd_draft(ctx, B, seq_ids, anchor, K, drafts, conf, cuts, stream)
+
+
+def dflash_verify_multi(ctx, B, C, seq_ids, drafts, target_logits, logits_dtype, accept_len, next_token,
+                        commit_len, chosen, stream):
+    return lib.dflash_verify_multi(ctx, B, C, seq_ids, drafts, target_logits, logits_dtype, accept_len,
+                                   next_token, commit_len, chosen, stream)
 
 
 def dflash_read_error(ctx, stream):

@@ -24,7 +24,7 @@ FLAGS = [
     "-Wno-unused-result",
 ]
 
-SOURCES = ["gemm.hip", "mm.hip", "finish.hip", "attention.hip", "small.hip", "lmhead.hip", "verify.hip", "dflash.cpp"]
+SOURCES = ["gemm.hip", "mm.hip", "finish.hip", "attention.hip", "small.hip", "lmhead.hip", "verify.hip", "d2sd.hip", "dflash.cpp"]
 
 
 def _compile(src):

@@ -140,27 +140,32 @@ DEV f32x4 split_sum4(const float* part, int ks, size_t stride, size_t off) {
 }
 
 
-DEV Top2 top2_empty() { return {-INFINITY, 0x7FFFFFFF, -INFINITY}; }
+DEV Top2 top2_empty() { return {-INFINITY, 0x7FFFFFFF, -INFINITY, 0.f}; }
 
 DEV bool better(float va, int ia, float vb, int ib) { return va > vb || (va == vb && ia < ib); }
+
+// exp of the loser's maximum against the winner's, 0 for an empty loser
+DEV float top2_rescale(float s, float v, float v1) { return s > 0.f ? s * __expf(v - v1) : 0.f; }
 
 DEV Top2 top2_merge(Top2 a, Top2 b) {
   Top2 r;
   if (better(a.v1, a.i1, b.v1, b.i1)) {
     r.v1 = a.v1; r.i1 = a.i1; r.v2 = fmaxf(a.v2, b.v1);
+    r.s = a.s + top2_rescale(b.s, b.v1, a.v1);
   } else {
     r.v1 = b.v1; r.i1 = b.i1; r.v2 = fmaxf(b.v2, a.v1);
+    r.s = b.s + top2_rescale(a.s, a.v1, b.v1);
   }
   return r;
 }
 
-DEV Top2 top2_push(Top2 a, float v, int i) { return top2_merge(a, Top2{v, i, -INFINITY}); }
+DEV Top2 top2_push(Top2 a, float v, int i) { return top2_merge(a, Top2{v, i, -INFINITY, 1.f}); }
 
 DEV Top2 top2_shfl_xor(Top2 a, int o) {
   Top2 b;
   b.v1 = __shfl_xor(a.v1, o, 64);
   b.i1 = __shfl_xor(a.i1, o, 64);
   b.v2 = __shfl_xor(a.v2, o, 64);
+  b.s = __shfl_xor(a.s, o, 64);
   return top2_merge(a, b);
 }
-

@@ -63,6 +63,9 @@ struct Layout {
   // per-call buffers
   size_t rowpos_a, rowseq_a, f, x, h, q, o, kblk, vblk, mm, gpart, cpart;
   size_t apo, aml, lmpart, vpart, spart, total;
+  // dual-pass drafting: second-pass sequences and input blocks, first and
+  // second drafts, confidence, cut points; multi-candidate verification
+  size_t d_seq, d_tok, d_draft1, d_draft2, d_conf, d_cuts, v_acc, v_next;
   size_t gpart_floats, cpart_floats;
   int n_ck, n_vchunks, n_schunks, m_max, rows_a_max;
 };
@@ -119,6 +122,14 @@ Layout make_layout(const dflash_config& c) {
   L.lmpart = take((size_t)std::max(lm_parts(c.vocab, 1), lm_parts(c.vocab, kMmMinRows)) * L.m_max * sizeof(Top2));
   L.vpart = take(Bm * N * L.n_vchunks * 2 * 4);
   L.spart = take(Bm * L.n_schunks * 2 * 4);
+  L.d_seq = take(Bm * 4);
+  L.d_tok = take(Bm * N * 4);
+  L.d_draft1 = take(Bm * N * 4);
+  L.d_draft2 = take(Bm * N * 4);
+  L.d_conf = take(Bm * N * 4);
+  L.d_cuts = take(Bm * N * 4);
+  L.v_acc = take(Bm * 4);
+  L.v_next = take(Bm * 4);
   L.total = off;
   return L;
 }
@@ -432,12 +443,16 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
   return ctx->launch(DFLASH_K_CTX_FINISH, stream, [&] { return dflash_launch_ctx_finish(&ca, stream); });
 }
 
-int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor, int32_t* draft,
-                       float* top2_gap, float* dbg_hidden, float* dbg_logits, hipStream_t stream) {
-  if (!ctx) return fail(DFLASH_ERR_INVALID_ARG, "ctx is null");
+}  // extern "C"
+
+namespace {
+
+// One drafting pass over B blocks: the block input is the anchor and masks,
+// or `tokens` [B][N] when given (the dual-pass drafter's second pass).
+int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor, const int32_t* tokens,
+               int32_t* draft, float* top2_gap, float* conf, float* dbg_hidden, float* dbg_logits,
+               hipStream_t stream) {
   const dflash_config& c = ctx->c;
-  if (B < 1 || B > c.max_batch) return fail(DFLASH_ERR_INVALID_ARG, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
-  if (!seq_ids || !anchor || !draft) return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
   const Layout& L = ctx->L;
   const int N = c.block_size, M = B * N;
   const int H = c.hidden, I = c.intermediate, D = c.n_layers;
@@ -452,6 +467,7 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   na.mode = 0;
   na.embed = ctx->w.embed;
   na.anchor = anchor;
+  na.tokens = tokens;
   na.mask_id = c.mask_token_id;
   na.N = N;
   na.V = c.vocab;
@@ -596,8 +612,60 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   ma.V = c.vocab;
   ma.draft = draft;
   ma.gap = top2_gap;
+  ma.conf = conf;
   ma.err = ctx->kv.error_word;
   return ctx->launch(DFLASH_K_ARGMAX, stream, [&] { return dflash_launch_argmax(&ma, stream); });
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor, int32_t* draft,
+                       float* top2_gap, float* dbg_hidden, float* dbg_logits, hipStream_t stream) {
+  if (!ctx) return fail(DFLASH_ERR_INVALID_ARG, "ctx is null");
+  const dflash_config& c = ctx->c;
+  if (B < 1 || B > c.max_batch) return fail(DFLASH_ERR_INVALID_ARG, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
+  if (!seq_ids || !anchor || !draft) return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
+  return draft_impl(ctx, B, seq_ids, anchor, nullptr, draft, top2_gap, nullptr, dbg_hidden, dbg_logits, stream);
+}
+
+int dflash_d2sd_draft(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor, int32_t K,
+                      int32_t* drafts, float* conf, int32_t* cuts, hipStream_t stream) {
+  if (!ctx) return fail(DFLASH_ERR_INVALID_ARG, "ctx is null");
+  const dflash_config& c = ctx->c;
+  const Layout& L = ctx->L;
+  const int N = c.block_size;
+  if (B < 1 || B > c.max_batch) return fail(DFLASH_ERR_INVALID_ARG, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
+  if (K < 1 || K > N - 1) return fail(DFLASH_ERR_INVALID_ARG, "K=%d outside [1, block_size-1=%d]", K, N - 1);
+  if ((long long)B * K > c.max_batch)
+    return fail(DFLASH_ERR_CAPACITY, "B*K=%lld second-pass blocks > max_batch=%d", (long long)B * K, c.max_batch);
+  if (!seq_ids || !anchor || !drafts) return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
+  D2sdArgs da{};
+  da.B = B;
+  da.N = N;
+  da.K = K;
+  da.V = c.vocab;
+  da.mask_id = c.mask_token_id;
+  da.seq_ids = seq_ids;
+  da.anchor = anchor;
+  da.conf = ctx->at<float>(L.d_conf);
+  da.draft1 = ctx->at<int>(L.d_draft1);
+  da.draft2 = ctx->at<int>(L.d_draft2);
+  da.cuts = ctx->at<int>(L.d_cuts);
+  da.seq2 = ctx->at<int>(L.d_seq);
+  da.tokens = ctx->at<int>(L.d_tok);
+  da.drafts = drafts;
+  da.cuts_out = cuts;
+  da.conf_out = conf;
+  int rc = draft_impl(ctx, B, seq_ids, anchor, nullptr, ctx->at<int>(L.d_draft1), nullptr, ctx->at<float>(L.d_conf),
+                      nullptr, nullptr, stream);
+  if (rc) return rc;
+  if ((rc = ctx->launch(DFLASH_K_D2SD, stream, [&] { return dflash_launch_d2sd_select(&da, stream); }))) return rc;
+  if ((rc = draft_impl(ctx, B * K, da.seq2, nullptr, da.tokens, ctx->at<int>(L.d_draft2), nullptr, nullptr, nullptr,
+                       nullptr, stream)))
+    return rc;
+  return ctx->launch(DFLASH_K_D2SD, stream, [&] { return dflash_launch_d2sd_assemble(&da, stream); });
 }
 
 int dflash_verify(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* draft, const void* target_logits,
@@ -635,6 +703,54 @@ int dflash_verify(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int3
   va.step = step;
   va.err = ctx->kv.error_word;
   return ctx->launch(DFLASH_K_VERIFY, stream, [&] { return dflash_launch_verify(&va, stream); });
+}
+
+int dflash_verify_multi(dflash_ctx* ctx, int32_t B, int32_t C, const int32_t* seq_ids, const int32_t* drafts,
+                        const void* target_logits, int32_t logits_dtype, int32_t* accept_len, int32_t* next_token,
+                        int32_t* commit_len, int32_t* chosen, hipStream_t stream) {
+  if (!ctx) return fail(DFLASH_ERR_INVALID_ARG, "ctx is null");
+  const dflash_config& c = ctx->c;
+  if (B < 1 || C < 1) return fail(DFLASH_ERR_INVALID_ARG, "B=%d and C=%d must be >= 1", B, C);
+  if ((long long)B * C > c.max_batch)
+    return fail(DFLASH_ERR_CAPACITY, "B*C=%lld candidate blocks > max_batch=%d", (long long)B * C, c.max_batch);
+  if (!seq_ids || !drafts || !target_logits || !accept_len || !next_token)
+    return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
+  if (logits_dtype != DFLASH_DTYPE_BF16 && logits_dtype != DFLASH_DTYPE_F32)
+    return fail(DFLASH_ERR_INVALID_ARG, "logits_dtype must be DFLASH_DTYPE_BF16 or DFLASH_DTYPE_F32");
+  const Layout& L = ctx->L;
+  // every candidate block verified greedily as one more sequence (the
+  // greedy passes do not read sequence ids), then the longest accept
+  VerifyArgs va{};
+  va.logits = target_logits;
+  va.dtype = logits_dtype;
+  va.B = B * C;
+  va.N = c.block_size;
+  va.V = c.vocab;
+  va.chunk = kVerifyChunk;
+  va.n_chunks = L.n_vchunks;
+  va.s_chunk = kSampleChunk;
+  va.s_n_chunks = L.n_schunks;
+  va.seq_ids = seq_ids;
+  va.draft = drafts;
+  va.part = ctx->at<float>(L.vpart);
+  va.spart = ctx->at<float>(L.spart);
+  va.accept_len = ctx->at<int>(L.v_acc);
+  va.next_token = ctx->at<int>(L.v_next);
+  va.commit_len = nullptr;
+  va.temp1 = 0;
+  va.err = ctx->kv.error_word;
+  int rc = ctx->launch(DFLASH_K_VERIFY, stream, [&] { return dflash_launch_verify(&va, stream); });
+  if (rc) return rc;
+  PickArgs pa{};
+  pa.B = B;
+  pa.C = C;
+  pa.acc = va.accept_len;
+  pa.next = va.next_token;
+  pa.accept_len = accept_len;
+  pa.next_token = next_token;
+  pa.commit_len = commit_len;
+  pa.chosen = chosen;
+  return ctx->launch(DFLASH_K_D2SD, stream, [&] { return dflash_launch_pick(&pa, stream); });
 }
 
 int dflash_read_error(dflash_ctx* ctx, hipStream_t stream, int32_t* out) {

@@ -6,11 +6,13 @@
 #include <stdint.h>
 
 // Top-2 with index: (v1, i1) is the maximum, lowest index on ties; v2 is
-// the largest value among the remaining entries.
+// the largest value among the remaining entries; s = sum of exp(v - v1)
+// over all entries merged (so the softmax maximum is 1 / s).
 struct Top2 {
   float v1;
   int i1;
   float v2;
+  float s;
 };
 
 // MFMA-operand packed layout, used for every weight matrix the GEMMs stream
@@ -143,6 +145,7 @@ struct NormArgs {
   int mode;                // 0: x = embedding rows, 1: x += sum of split partials
   const uint16_t* embed;   // [V][H]
   const int* anchor;       // [B]
+  const int* tokens;       // mode 0, nullable: [B][N] block input tokens (else anchor, then masks)
   int mask_id, N, V;
   const int* seq_ids;      // mode 0: checks of the draft call (error word)
   const int* ctx_len;
@@ -171,7 +174,36 @@ struct ArgmaxArgs {
   int n_parts, M, N, V;
   int* draft;        // [B][N-1]
   float* gap;        // nullable [B][N-1]
+  float* conf;       // nullable [B][N-1]: largest softmax probability of the drafter's row
   int32_t* err;
+};
+
+// Dual-pass drafting (D2SD): cut points of the first draft and the second
+// pass's input blocks; then the candidates' drafts.
+struct D2sdArgs {
+  int B, N, K, V, mask_id;
+  const int* seq_ids;   // [B]
+  const int* anchor;    // [B]
+  const float* conf;    // [B][N-1] first-pass confidence
+  const int* draft1;    // [B][N-1] first draft
+  const int* draft2;    // [B*K][N-1] second-pass drafts
+  int* cuts;            // [B][K] cut positions (1-based, ascending)
+  int* seq2;            // [B*K] sequence of each second-pass block
+  int* tokens;          // [B*K][N] second-pass input blocks
+  int* drafts;          // [B][K+1][N-1] candidates
+  int* cuts_out;        // nullable [B][K]
+  float* conf_out;      // nullable [B][N-1]
+};
+
+// Longest accept over C candidates of each sequence (lowest index on ties).
+struct PickArgs {
+  int B, C;
+  const int* acc;       // [B*C]
+  const int* next;      // [B*C]
+  int* accept_len;
+  int* next_token;
+  int* commit_len;      // nullable
+  int* chosen;          // nullable
 };
 
 #define VERIFY_MAX_PARTS 2048  // block rows * vocabulary chunks of one sequence
@@ -219,4 +251,7 @@ hipError_t dflash_launch_lmhead(const LmArgs* a, hipStream_t st);
 hipError_t dflash_launch_lmhead_mm(const LmArgs* a, hipStream_t st);
 hipError_t dflash_launch_argmax(const ArgmaxArgs* a, hipStream_t st);
 hipError_t dflash_launch_verify(const VerifyArgs* a, hipStream_t st);
+hipError_t dflash_launch_d2sd_select(const D2sdArgs* a, hipStream_t st);
+hipError_t dflash_launch_d2sd_assemble(const D2sdArgs* a, hipStream_t st);
+hipError_t dflash_launch_pick(const PickArgs* a, hipStream_t st);
 }

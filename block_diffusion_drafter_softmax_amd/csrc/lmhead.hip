@@ -108,6 +108,7 @@ __global__ __launch_bounds__(ARGMAX_THREADS) LATENCY_BOUND void argmax_reduce_ke
     }
     a.draft[b * (a.N - 1) + j] = tok;
     if (a.gap) a.gap[b * (a.N - 1) + j] = t.v1 - t.v2;
+    if (a.conf) a.conf[b * (a.N - 1) + j] = 1.0f / t.s;
   }
 }
 

@@ -163,8 +163,10 @@ extern "C" hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st) {
 // One workgroup per row, one float4 of the row per thread: build the
 // residual row (embedding gather, or x + the k-split partials of the last
 // projection, summed in split order), then h = x / sqrt(mean(x^2) + eps) * g
-// as the packed split activation the next projection streams. Mode 0 (first kernel of a draft call) also checks the call's
-// sequence ids, anchors and position capacity.
+// as the packed split activation the next projection streams. Mode 0 (first
+// kernel of a draft call) embeds the block's tokens (the anchor and masks,
+// or given input tokens) and also checks the call's sequence ids, tokens
+// and position capacity.
 __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
   const int m = blockIdx.x;
   __shared__ float red[16];
@@ -174,14 +176,15 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
   int tok = 0;
   if (a.mode == 0) {
     const int b = m / a.N;
-    tok = (m % a.N == 0) ? a.anchor[b] : a.mask_id;
-    if (threadIdx.x == 0 && m % a.N == 0) {
-      int bad = 0;
-      const int s_raw = a.seq_ids[b];
-      if (s_raw < 0 || s_raw >= a.max_seqs) bad |= DFLASH_DEV_BAD_SEQ;
-      if (tok < 0 || tok >= a.V) bad |= DFLASH_DEV_BAD_TOKEN;
-      const int L = a.ctx_len[clampi(s_raw, 0, a.max_seqs - 1)];
-      if (L < 0 || L + a.N > a.max_pos) bad |= DFLASH_DEV_NO_PAGES;
+    tok = a.tokens ? a.tokens[m] : (m % a.N == 0) ? a.anchor[b] : a.mask_id;
+    if (threadIdx.x == 0) {
+      int bad = (tok < 0 || tok >= a.V) ? DFLASH_DEV_BAD_TOKEN : 0;
+      if (m % a.N == 0) {
+        const int s_raw = a.seq_ids[b];
+        if (s_raw < 0 || s_raw >= a.max_seqs) bad |= DFLASH_DEV_BAD_SEQ;
+        const int L = a.ctx_len[clampi(s_raw, 0, a.max_seqs - 1)];
+        if (L < 0 || L + a.N > a.max_pos) bad |= DFLASH_DEV_NO_PAGES;
+      }
       if (bad) set_error(a.err, bad);
     }
     tok = clampi(tok, 0, a.V - 1);

@@ -187,7 +187,6 @@ DEV Scan verify_scan(const VerifyArgs& a, int b) {
   __shared__ float2 rowres[32];
   __shared__ float prob[32], unif[32];
   __shared__ Scan out;
-  const int seq = a.seq_ids[b];
   const int* d = a.draft + (size_t)b * (a.N - 1);
   const int n_parts = a.N * a.n_chunks;  // <= VERIFY_MAX_PARTS (host check)
   const float2* src = reinterpret_cast<const float2*>(a.part) + (size_t)b * n_parts;
@@ -220,7 +219,7 @@ DEV Scan verify_scan(const VerifyArgs& a, int b) {
       }
       const float zt = load_logit(a, ((size_t)b * a.N + row) * a.V + tok);
       prob[row] = expf(zt - lse);
-      unif[row] = (float)(rng_word(a, seq, row, 0, 0) >> 40) * 5.9604644775390625e-08f;
+      unif[row] = (float)(rng_word(a, a.seq_ids[b], row, 0, 0) >> 40) * 5.9604644775390625e-08f;
     }
   }
   __syncthreads();

@@ -124,6 +124,27 @@ class Drafter:
                              commit_len.data_ptr() if commit_len is not None else None, _stream(stream))
         return B.check(rc, "dflash_verify")
 
+    def d2sd_draft(self, seq_ids, anchor, K, drafts, conf=None, cuts=None, stream=None):
+        """Dual-pass drafting: drafts int32 [B, K+1, N-1] (candidate 0 = the
+        first draft); conf fp32 [B, N-1] and cuts int32 [B, K] optional."""
+        Bn = seq_ids.numel()
+        p = lambda t: t.data_ptr() if t is not None else None
+        rc = B.dflash_d2sd_draft(self.handle, Bn, seq_ids.data_ptr(), anchor.data_ptr(), K, drafts.data_ptr(),
+                                 p(conf), p(cuts), _stream(stream))
+        return B.check(rc, "dflash_d2sd_draft")
+
+    def verify_multi(self, seq_ids, drafts, logits, accept_len, next_token, commit_len=None, chosen=None,
+                     stream=None):
+        """Greedy verification of C candidates per sequence: drafts [B, C, N-1],
+        logits [B, C, N, V]; the longest accept wins (lowest index on ties)."""
+        Bn, C = drafts.shape[0], drafts.shape[1]
+        dt = B.DTYPE_F32 if logits.dtype == torch.float32 else B.DTYPE_BF16
+        p = lambda t: t.data_ptr() if t is not None else None
+        rc = B.dflash_verify_multi(self.handle, Bn, C, seq_ids.data_ptr(), drafts.data_ptr(), logits.data_ptr(), dt,
+                                   accept_len.data_ptr(), next_token.data_ptr(), p(commit_len), p(chosen),
+                                   _stream(stream))
+        return B.check(rc, "dflash_verify_multi")
+
     def read_error(self, stream=None):
         rc, v = B.dflash_read_error(self.handle, _stream(stream))
         B.check(rc, "dflash_read_error")

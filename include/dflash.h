@@ -191,6 +191,34 @@ int dflash_verify(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int3
                   uint64_t seed, uint64_t step, int32_t* accept_len, int32_t* next_token,
                   int32_t* commit_len, hipStream_t stream);
 
+/* Dual-pass drafting [D2SD Methodology 1-3]. First pass as
+ * dflash_draft_block; confidence of draft position j = the drafter's
+ * largest softmax probability of block row j, 1 / sum_v exp(z_v - max z);
+ * cut points = the K positions of lowest confidence (ties to the lower
+ * position), ascending; for each cut point c a second-pass block
+ * [anchor, d_1 .. d_{c-1}, mask ...] at the same positions and over the
+ * same context (same weights and cache), all B*K blocks in one pass;
+ * candidate 0 is the first draft, candidate k keeps d_1 .. d_{c_k - 1} and
+ * takes the second pass's argmax from position c_k on.
+ *   K         1 .. N-1; B*K <= cfg.max_batch (DFLASH_ERR_CAPACITY)
+ *   drafts    device int32 [B, K+1, N-1]      (out) candidates
+ *   conf      device fp32 [B, N-1], nullable   (out) first-pass confidence
+ *   cuts      device int32 [B, K], nullable    (out) cut positions, 1-based
+ * Workspace buffers hold the intermediate blocks; no host synchronisation. */
+int dflash_d2sd_draft(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor,
+                      int32_t K, int32_t* drafts, float* conf, int32_t* cuts, hipStream_t stream);
+
+/* Greedy verification of C candidate blocks per sequence [D2SD Methodology
+ * 4]: drafts device int32 [B, C, N-1], target_logits [B, C, N, V] (bf16 or
+ * fp32), each candidate's own logits. Every candidate is verified as in
+ * dflash_verify (temperature 0); the longest accept wins, the lowest
+ * candidate index on ties. B*C <= cfg.max_batch (DFLASH_ERR_CAPACITY).
+ * Outputs, device int32 [B]: accept_len, next_token, commit_len (nullable),
+ * chosen candidate (nullable). */
+int dflash_verify_multi(dflash_ctx* ctx, int32_t B, int32_t C, const int32_t* seq_ids, const int32_t* drafts,
+                        const void* target_logits, int32_t logits_dtype, int32_t* accept_len,
+                        int32_t* next_token, int32_t* commit_len, int32_t* chosen, hipStream_t stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* dflash_last_error(void);
 
@@ -215,7 +243,8 @@ int dflash_read_error(dflash_ctx* ctx, hipStream_t stream, int32_t* out);
 #define DFLASH_K_VERIFY 11
 #define DFLASH_K_QKV_FINISH 12 /* split-k sum + RoPE + layout of Q and block K/V */
 #define DFLASH_K_CTX_FINISH 13 /* split-k sum + RoPE + page scatter of context K/V; advances ctx_len */
-#define DFLASH_K_COUNT 14
+#define DFLASH_K_D2SD 14     /* dual-pass drafting: cut points + second-pass blocks, candidates; multi-verify pick */
+#define DFLASH_K_COUNT 15
 
 /* Start (enable != 0) or stop timing kernel kind `kind`; starting clears
  * the totals. Capacity: 4096 launches between reads. A timed launch of a

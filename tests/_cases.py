@@ -43,7 +43,7 @@ class Case:
     """
 
     def __init__(self, cfg, ctx, n_new, seed=0, page_order="contiguous", seq_offset=1,
-                 prefill_chunk=64, extra_pages=1, oracle_seqs=None, oracle_chunk=1024):
+                 prefill_chunk=64, extra_pages=1, oracle_seqs=None, oracle_chunk=1024, max_batch=None):
         self.cfg = cfg
         self.B = len(ctx)
         self.ctx = [int(x) for x in ctx]
@@ -58,7 +58,7 @@ class Case:
         self.cache = O.OracleCache(cfg["n_layers"])
         self.max_new = max(prefill_chunk, max(self.n_new))
         pps = (max(self.ctx) + N + 15) // 16 + extra_pages
-        self.dr = Drafter(cfg, self.w, max_batch=self.B, max_new=self.max_new,
+        self.dr = Drafter(cfg, self.w, max_batch=max_batch or self.B, max_new=self.max_new,
                           max_seqs=self.B + seq_offset, pages_per_seq=pps, page_order=page_order,
                           seed=seed, fill_workspace=NAN_FILL)
         self.dev = self.dr.device

@@ -101,7 +101,7 @@ def test_kernel_timer_reports_every_kind_of_a_step():
     h = case.dr.handle
     kinds = [B.K_FUSE, B.K_CTX_KV, B.K_CTX_FINISH, B.K_NORM, B.K_QKV, B.K_QKV_FINISH, B.K_ATTN,
              B.K_ATTN_MERGE, B.K_OPROJ, B.K_GATE_UP, B.K_DOWN, B.K_LM_HEAD, B.K_ARGMAX, B.K_VERIFY]
-    assert len(kinds) == B.K_COUNT
+    assert len(kinds) == B.K_COUNT - 1  # all but the dual-pass drafter's (tests/test_gpu_d2sd.py)
     for k in kinds:
         B.check(B.dflash_kernel_timer(h, k, 1), "timer")
     for _ in range(3):
