@@ -98,9 +98,12 @@ def cpu_baseline(cfg, w, hidden_pre, hidden_step, anchor, logits_bits):
 MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 
-def batched_roofline(cfg, ctx, n_new):
+def batched_roofline(cfg, ctx, n_new, K=0):
     """Per-phase algorithmic bytes and flops of one batched step, and
-    t_roof = sum over phases of max(bytes / 8 TB/s, flops / 2.5 PF)."""
+    t_roof = sum over phases of max(bytes / 8 TB/s, flops / 2.5 PF).
+    K > 0 adds the dual-pass drafter's second pass (B*K blocks of N against
+    each sequence's shared context: the context counts once per sequence,
+    the weights once more) and the verification of K+1 candidates."""
     D, H, I, V, T, N = (cfg[k] for k in ("n_layers", "hidden", "intermediate", "vocab", "n_target_layers",
                                          "block_size"))
     d, nq, nkv = cfg["head_dim"], cfg["n_q_heads"], cfg["n_kv_heads"]
@@ -116,6 +119,12 @@ def batched_roofline(cfg, ctx, n_new):
     attn_flops = 4.0 * D * nq * N * keys * d
     rest_bytes = rows * T * H * 2 + D * rows * 2 * kvd * 2 + M * V * 2
     phases = {"gemm": (gemm_bytes, gemm_flops), "attention": (attn_bytes, attn_flops), "rest": (rest_bytes, 0.0)}
+    if K:
+        M2 = B * K * N
+        phases["gemm_pass2"] = ((D * layer_w + V * H) * 2, 2.0 * M2 * (D * layer_w + V * H))
+        phases["attention_pass2"] = (D * (int(np.sum(ctx)) + B * K * N) * 2 * kvd * 2,
+                                     4.0 * D * nq * K * N * (int(np.sum(ctx)) + B * N) * d)
+        phases["verify_candidates"] = (B * (K + 1) * N * V * 2 - M * V * 2, 0.0)
     t = {k: max(b / (HBM_PEAK_GBS * 1e9), f / (MFMA_PEAK_TFS * 1e12)) for k, (b, f) in phases.items()}
     return {"phases": {k: {"bytes": int(b), "flops": f, "t_us": round(t[k] * 1e6, 1)} for k, (b, f) in phases.items()},
             "t_roof_us": round(sum(t.values()) * 1e6, 1), "attn_bytes_per_layer": attn_bytes // D}
@@ -139,9 +148,10 @@ def run_batched(args, name):
     n_new = synth.appended_rows(cfg, 0)
     temp = 1.0 if cfg["verify"] == "temp1" else 0.0
     dev = torch.device("cuda")
+    K = int(cfg.get("d2sd_k", 0))
     w = synth.make_weights(cfg, 0)
     chunk = 512
-    dr = Drafter(cfg, w, max_batch=Bn, max_new=chunk, max_seqs=Bn,
+    dr = Drafter(cfg, w, max_batch=Bn * (K + 1), max_new=chunk, max_seqs=Bn,
                  pages_per_seq=(int(ctx.max()) + N + 15) // 16 + 1, page_order="shuffled")
     seq = torch.arange(Bn, dtype=torch.int32, device=dev)
     gen = torch.Generator(device=dev).manual_seed(0)
@@ -171,32 +181,59 @@ def run_batched(args, name):
     logits_bits = synth.make_logits(cfg, draft.cpu().numpy(), 0)
     logits = torch.from_numpy(logits_bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
-    def step():
+    def step_first():
         dr.ctx_len.copy_(ctx0)
         dr.ctx_append(seq, n_new_t, step_hid, max_new)
         dr.draft_block(seq, anchor, draft)
         dr.verify(seq, draft, logits, acc, nxt, com, temperature=temp, seed=1, step=0)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    assert dr.read_error() == 0
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        assert dr.read_error() == 0
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    step, first_ms = step_first, None
+    if K:
+        # dual-pass step: first draft, K lowest-confidence cut points, one
+        # batched second pass, greedy verification of all K+1 candidates
+        # (target logits built around the GPU's own candidates)
+        C = K + 1
+        drafts = torch.zeros((Bn, C, N - 1), dtype=torch.int32, device=dev)
+        chosen = torch.zeros(Bn, dtype=torch.int32, device=dev)
+        dr.ctx_len.copy_(ctx0)
+        dr.ctx_append(seq, n_new_t, step_hid, max_new)
+        dr.d2sd_draft(seq, anchor, K, drafts)
+        torch.cuda.synchronize()
+        z = synth.make_logits(cfg, drafts.cpu().numpy().reshape(Bn * C, N - 1), 0)
+        logits_c = torch.from_numpy(z.view(np.int16)).to(dev).view(torch.bfloat16).view(Bn, C, N, V)
+        del z
+        first_ms = timed(step_first)
+
+        def step():
+            dr.ctx_len.copy_(ctx0)
+            dr.ctx_append(seq, n_new_t, step_hid, max_new)
+            dr.d2sd_draft(seq, anchor, K, drafts)
+            dr.verify_multi(seq, drafts, logits_c, acc, nxt, com, chosen)
+
+    ms_step = timed(step)
 
     B.check(B.dflash_kernel_timer(dr.handle, B.K_ATTN, 1), "timer")
     for _ in range(args.steps):
-        step()
+        step_first()  # the first pass's attention: the bytes per launch below
     torch.cuda.synchronize()
     rc, at_ms, at_n = B.dflash_kernel_timer_read(dr.handle, B.K_ATTN)
     B.check(rc, "timer read")
     B.dflash_kernel_timer(dr.handle, B.K_ATTN, 0)
     assert dr.read_error() == 0
 
-    rl = batched_roofline(cfg, ctx, n_new)
+    rl = batched_roofline(cfg, ctx, n_new, K)
+    rl1 = batched_roofline(cfg, ctx, n_new) if K else rl
     at_s = at_ms / at_n / 1e3
     achieved = rl["attn_bytes_per_layer"] / at_s / 1e9
     accepted = float(acc.float().mean())
@@ -207,7 +244,9 @@ def run_batched(args, name):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{name}: {Bn} sequences x block {N}, contexts {int(ctx.min())}..{int(ctx.max())} "
                                f"(sum {int(ctx.sum())}), {int(n_new.sum())} rows appended, "
-                               f"{'temperature-1' if temp else 'greedy'} verify; D {cfg['n_layers']}, H {H}, "
+                               f"{'temperature-1' if temp else 'greedy'} verify"
+                               f"{f' of {K + 1} dual-pass candidates (K={K} cut points, one batched second pass)' if K else ''}"
+                               f"; D {cfg['n_layers']}, H {H}, "
                                f"{cfg['n_q_heads']}/{cfg['n_kv_heads']} heads of {cfg['head_dim']}, "
                                f"I {cfg['intermediate']}, V {V}",
                    "global_batch": Bn, "block": N, "launch": "eager"},
@@ -219,6 +258,9 @@ def run_batched(args, name):
         "step_roofline": {"bound": "mixed", "t_roof_us": rl["t_roof_us"], "phases": rl["phases"],
                           "frac": round(rl["t_roof_us"] / (ms_step * 1e3), 4)},
         "mean_accept": round(accepted, 3),
+        "first_pass_only": None if not K else {
+            "ms_per_step": round(first_ms, 4), "draft_tok_s": round(Bn * (N - 1) / (first_ms / 1e3), 1),
+            "t_roof_us": rl1["t_roof_us"], "frac": round(rl1["t_roof_us"] / (first_ms * 1e3), 4)},
         "cpu_baseline": None,
     }
     log(f"{ms_step:.3f} ms/step, {res['value']:.0f} draft tok/s, step roofline {res['step_roofline']['frac']:.3f}")

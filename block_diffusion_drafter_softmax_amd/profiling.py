@@ -86,7 +86,9 @@ def write_stats(stats_csv, out_md, command, trace_csv=None, skip_last=0, top=24)
 def step_breakdown(trace_csv, last_kernel="verify_rows", steps=10, skip_last=0):
     """Per-kernel time of one decode step, averaged over `steps` steps of a
     kernel trace (a step ends with the verification kernel), leaving out the
-    final `skip_last` steps (e.g. a pass run with a kernel timer attached)."""
+    final `skip_last` steps (e.g. a pass run with a kernel timer attached).
+    Kernels between the dual-pass drafter's selection and assembly kernels
+    are listed as its second pass."""
     rows = _rows(trace_csv)
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     ends = [i for i, r in enumerate(rows) if r["Kernel_Name"].startswith("void " + last_kernel)]
@@ -97,8 +99,15 @@ def step_breakdown(trace_csv, last_kernel="verify_rows", steps=10, skip_last=0):
     for a, b in zip(ends[-steps - 1:-1], ends[-steps:]):
         seg = rows[a + 1: b + 1]
         span += (int(seg[-1]["End_Timestamp"]) - int(seg[0]["Start_Timestamp"])) / 1e3
+        second = False
         for r in seg:
             k = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            if k.startswith("d2sd_select"):
+                second = True
+            elif k.startswith("d2sd_assemble"):
+                second = False
+            elif second:
+                k += " (second pass)"
             dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             n, t = agg.get(k, (0, 0.0))
             agg[k] = (n + 1, t + dt)

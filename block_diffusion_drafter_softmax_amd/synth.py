@@ -44,11 +44,12 @@ CONFIGS = {
                              intermediate=12288, vocab=151936, n_target_layers=9, block_size=16,
                              tied_kv=0, context=(512, 8192), batch=32, n_new=16, verify="temp1",
                              logits_dtype="bf16", agreement=0.75, logit_model="accept_p"),
-    # GPT-OSS-20B-shaped drafter, batch 8, context 8192
+    # GPT-OSS-20B-shaped drafter, batch 8, context 8192, with the dual-pass
+    # drafter's second pass over K = 4 cut points and multi-candidate verify
     "gpt_oss_20b": dict(_BASE, hidden=2880, n_layers=5, n_q_heads=64, n_kv_heads=8, head_dim=64,
                         intermediate=2880, vocab=201088, n_target_layers=9, block_size=16, tied_kv=0,
                         context=8192, batch=8, n_new=8, verify="greedy", logits_dtype="bf16",
-                        agreement=0.8, logit_model="top_plus1"),
+                        agreement=0.8, logit_model="top_plus1", d2sd_k=4),
 }
 
 
