@@ -34,6 +34,12 @@ CONFIGS = {
                      intermediate=9728, vocab=151936, n_target_layers=5, block_size=16, tied_kv=1,
                      context=2048, batch=1, n_new=8, verify="greedy", logits_dtype="bf16",
                      agreement=0.8, logit_model="top_plus1"),
+    # the same shape with DFlash's own conditioning: one FC layer fuses the
+    # T states into a single context shared by all layers
+    "qwen3_4b_fc": dict(_BASE, hidden=2560, n_layers=5, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                        intermediate=9728, vocab=151936, n_target_layers=5, block_size=16, tied_kv=1,
+                        context=2048, batch=1, n_new=8, verify="greedy", logits_dtype="bf16",
+                        agreement=0.8, logit_model="top_plus1", fusion="fc"),
     # Qwen3-8B-shaped drafter with DFLARE fusion over T=9 and separate W^t / W^d
     "qwen3_8b": dict(_BASE, hidden=4096, n_layers=7, n_q_heads=32, n_kv_heads=8, head_dim=128,
                      intermediate=12288, vocab=151936, n_target_layers=9, block_size=16, tied_kv=0,
@@ -117,6 +123,9 @@ def make_weights(cfg, seed=0, std=0.02):
     for k, s in dict(g_fuse=(D, H), g_attn=(D, H), g_mlp=(D, H), g_final=(H,)).items():
         w[k] = np.full(s, one, dtype=np.uint16)
     w["w_fuse"] = _rng(seed, "w_fuse").standard_normal((D, T), dtype=np.float32)
+    if cfg.get("fusion", "softmax") == "fc":  # DFlash's FC fusion: W_fc [H, T*H], gain [H]
+        w["w_fc"] = normal_bf16((H, T * H), std, seed, "w_fc")
+        w["g_fc"] = np.full(H, one, dtype=np.uint16)
     return w
 
 

@@ -9,6 +9,9 @@ What it follows (the pages are three web summaries; sections, not lines):
     (gist.science technical summary), section 2.1 "Adaptive layer fusion":
     per-draft-layer softmax weights alpha^(i) over the T target layers, a
     weighted sum of the T target hidden states, then RMSNorm.
+  * same page, section 1 (first limitation): DFlash's own conditioning, one
+    fully-connected layer fusing the T target states into a single context
+    shared by every draft layer (the ``fusion == "fc"`` variant).
   * same page, section 2.2 "Heterogeneous KV projections": the fused
     context goes through its own W^t_K / W^t_V, the draft block (the
     target-decoded token plus mask positions) through W^d_K / W^d_V.
@@ -62,7 +65,7 @@ import numpy as np
 
 __all__ = [
     "bf16_round", "bf16_bits_to_f64", "fusion_weights", "rmsnorm", "rope",
-    "fuse_context", "attention", "silu", "argmax_first", "top2_gap",
+    "fuse_context", "fuse_context_fc", "attention", "silu", "argmax_first", "top2_gap",
     "OracleModel", "OracleCache", "ctx_append", "draft_block",
     "verify_greedy", "verify_temp1", "philox4x64_10", "philox4x64_10_vec",
     "rng_uniform", "rng_gumbel_row", "draft_confidence", "d2sd_cut_points",
@@ -125,6 +128,22 @@ def fuse_context(alpha_i, h, g, eps):
     for j in range(h.shape[1]):
         s = s + alpha_i[j] * h[:, j, :]
     return rmsnorm(s, g, eps)
+
+
+def fuse_context_fc(w_fc, h, g, eps):
+    """c_t = RMSNorm(W_fc [h^(0)_t; ...; h^(T-1)_t]) * g_fc.
+
+    DFlash's conditioning as the DFLARE summary describes it (section 1,
+    first limitation): one fully-connected layer merges the hidden states of
+    the selected target layers into a single shared representation, and that
+    same signal feeds every draft layer. ``h`` is [n, T, H]; the T states of
+    a token are concatenated along the feature axis in layer order; W_fc is
+    [H, T*H] (nn.Linear, no bias). The RMSNorm with gain after the layer is
+    the reading taken here, as in DFLARE's own fusion (section 2.1).
+    """
+    h = np.asarray(h, dtype=np.float64)
+    n, T, H = h.shape
+    return rmsnorm(h.reshape(n, T * H) @ np.asarray(w_fc, dtype=np.float64).T, g, eps)
 
 
 # ------------------------------------------------------------------- RoPE
@@ -197,6 +216,8 @@ class OracleModel:
     wg, wu [D, I, H]; wd [D, H, I]; embed, lm_head [V, H]; g_fuse, g_attn,
     g_mlp [D, H]; g_final [H]; w_fuse [D, T] float32. With ``tied_kv`` the
     context projections are the block ones (DFlash's shared projection).
+    With ``fusion == "fc"`` the context is DFlash's FC fusion instead, from
+    w_fc [H, T*H] and g_fc [H].
     """
     cfg: dict
     w: dict
@@ -238,8 +259,9 @@ def ctx_append(model, cache, seq, hidden, storage=True):
     hidden [n, T, H]: the T target-layer states of each appended token.
     Per layer i: f = fuse_context(alpha^(i), ...); K = RoPE(f W^t_K^T) at
     positions ctx_len .. ctx_len+n-1; V = f W^t_V^T (DFLARE summary,
-    section 2.2: the target context gets its own W^t_K, W^t_V). Then
-    ctx_len += n.
+    section 2.2: the target context gets its own W^t_K, W^t_V). With
+    ``fusion == "fc"`` every layer takes the one shared f = fuse_context_fc
+    (DFlash, as in section 1 of that summary). Then ctx_len += n.
     """
     c = model.cfg
     n_kv, d = c["n_kv_heads"], c["head_dim"]
@@ -247,8 +269,14 @@ def ctx_append(model, cache, seq, hidden, storage=True):
     n = hidden.shape[0]
     p0 = cache.length(seq)
     pos = p0 + np.arange(n)
+    shared = None
+    if c.get("fusion", "softmax") == "fc":
+        shared = fuse_context_fc(model.f64("w_fc"), hidden, model.f64("g_fc"), c["rms_eps"])
     for i in range(c["n_layers"]):
-        f = fuse_context(model.alpha[i], hidden, model.f64("g_fuse", i), c["rms_eps"])
+        if shared is not None:
+            f = shared
+        else:
+            f = fuse_context(model.alpha[i], hidden, model.f64("g_fuse", i), c["rms_eps"])
         k = (f @ model.f64("wk_t", i).T).reshape(n, n_kv, d)
         v = (f @ model.f64("wv_t", i).T).reshape(n, n_kv, d)
         if c.get("use_rope", 1):

@@ -345,6 +345,88 @@ def test_untied_context_uses_its_own_projection():
     assert not np.allclose(cache.v[0][0], v_d, atol=1e-3)
 
 
+# ----------------------------------------- DFlash FC fusion (shared context)
+def _selector(T, H, j, scale=1.0):
+    """W_fc [H, T*H] that reads layer j's state times `scale`."""
+    w = np.zeros((H, T * H))
+    w[:, j * H:(j + 1) * H] = np.eye(H) * scale
+    return w
+
+
+def test_fc_fusion_selector_is_one_hot_layer_fusion():
+    r = np.random.default_rng(40)
+    T, H, eps = 4, 32, 1e-6
+    h = r.standard_normal((7, T, H))
+    g = 1 + 0.1 * r.standard_normal(H)
+    for j in range(T):
+        fc = O.fuse_context_fc(_selector(T, H, j), h, g, eps)
+        alpha = np.where(np.arange(T) == j, 1.0, 0.0)
+        assert np.allclose(fc, O.fuse_context(alpha, h, g, eps), rtol=1e-15, atol=0)
+        ref = F.rms_norm(torch.from_numpy(h[:, j]), (H,), weight=torch.from_numpy(g), eps=eps).numpy()
+        assert np.allclose(fc, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_fc_fusion_with_scaled_identities_is_the_weighted_sum_fusion():
+    r = np.random.default_rng(41)
+    T, H, eps = 5, 24, 1e-6
+    h = r.standard_normal((6, T, H))
+    g = 1 + 0.1 * r.standard_normal(H)
+    alpha = O.fusion_weights(r.standard_normal((1, T)))[0]
+    w_fc = sum(_selector(T, H, j, alpha[j]) for j in range(T))
+    assert np.allclose(O.fuse_context_fc(w_fc, h, g, eps), O.fuse_context(alpha, h, g, eps), rtol=1e-12, atol=1e-12)
+
+
+def test_fc_fusion_matches_torch_linear_then_rmsnorm():
+    r = np.random.default_rng(42)
+    T, H, eps = 3, 40, 1e-6
+    h = r.standard_normal((5, T, H))
+    w_fc = r.standard_normal((H, T * H)) * 0.1
+    g = 1 + 0.1 * r.standard_normal(H)
+    cat = torch.cat([torch.from_numpy(h[:, j]) for j in range(T)], dim=1)  # [n, T*H], layer order
+    ref = F.rms_norm(F.linear(cat, torch.from_numpy(w_fc)), (H,), weight=torch.from_numpy(g), eps=eps)
+    assert np.allclose(O.fuse_context_fc(w_fc, h, g, eps), ref.numpy(), rtol=1e-12, atol=1e-12)
+    # the norm comes after the layer: scaling W_fc leaves the context unchanged (up to eps)
+    assert np.allclose(O.fuse_context_fc(3.0 * w_fc, h, g, eps), O.fuse_context_fc(w_fc, h, g, eps), rtol=1e-5)
+
+
+def _fc_model(c, w, r):
+    H, T = c["hidden"], c["n_target_layers"]
+    w = dict(w, w_fc=r.standard_normal((H, T * H)) * 0.1, g_fc=1 + 0.1 * r.standard_normal(H))
+    return O.OracleModel(dict(c, fusion="fc"), w), w
+
+
+def test_fc_append_feeds_one_shared_context_to_every_layer():
+    c = tiny_cfg(n_layers=3)
+    r = np.random.default_rng(43)
+    w = tiny_weights(c, seed=43)
+    for k in ("wk_t", "wv_t"):
+        w[k] = np.repeat(w[k][:1], 3, axis=0)  # the same context projection in every layer
+    m, w = _fc_model(c, w, r)
+    cache, h = _prefill(m, c, 6)
+    for i in (1, 2):
+        assert np.array_equal(cache.k[i][0], cache.k[0][0]) and np.array_equal(cache.v[i][0], cache.v[0][0])
+    f = O.fuse_context_fc(w["w_fc"], h, w["g_fc"], c["rms_eps"])
+    v = (f @ w["wv_t"][0].T).reshape(6, c["n_kv_heads"], -1)
+    assert np.allclose(cache.v[0][0], v, rtol=1e-12, atol=1e-12)
+
+
+def test_fc_append_with_a_selector_equals_one_hot_softmax_fusion():
+    c = tiny_cfg(n_layers=2)
+    r = np.random.default_rng(44)
+    w = tiny_weights(c, seed=44)
+    T, H, j = c["n_target_layers"], c["hidden"], 1
+    g = 1 + 0.1 * r.standard_normal(H)
+    w_fc = dict(w, w_fc=_selector(T, H, j), g_fc=g)
+    w_sm = dict(w, w_fuse=np.where(np.arange(T) == j, 0.0, -np.inf)[None].repeat(2, 0), g_fuse=np.stack([g, g]))
+    h = r.standard_normal((5, T, H))
+    a, b = O.OracleCache(2), O.OracleCache(2)
+    O.ctx_append(O.OracleModel(dict(c, fusion="fc"), w_fc), a, 0, h, storage=False)
+    O.ctx_append(O.OracleModel(c, w_sm), b, 0, h, storage=False)
+    for i in range(2):
+        assert np.allclose(a.k[i][0], b.k[i][0], rtol=1e-13, atol=1e-13)
+        assert np.allclose(a.v[i][0], b.v[i][0], rtol=1e-13, atol=1e-13)
+
+
 def test_append_in_chunks_equals_one_append():
     c = tiny_cfg()
     m = _model(c, tiny_weights(c, seed=24))
