@@ -112,8 +112,9 @@ def batched_roofline(cfg, ctx, n_new, K=0):
     M, rows = B * N, int(np.sum(n_new))
     layer_w = qd * H + 2 * kvd * H + H * qd + 2 * I * H + H * I
     wt = 0 if cfg.get("tied_kv") else D * 2 * kvd * H
-    gemm_bytes = (D * layer_w + V * H + wt) * 2
-    gemm_flops = 2.0 * M * (D * layer_w + V * H) + 2.0 * rows * D * 2 * kvd * H
+    wfc = T * H * H if cfg.get("fusion") == "fc" else 0  # DFlash's FC fusion layer
+    gemm_bytes = (D * layer_w + V * H + wt + wfc) * 2
+    gemm_flops = 2.0 * M * (D * layer_w + V * H) + 2.0 * rows * (D * 2 * kvd * H + wfc)
     keys = int(np.sum(ctx)) + B * N
     attn_bytes = D * keys * 2 * kvd * 2
     attn_flops = 4.0 * D * nq * N * keys * d
@@ -274,7 +275,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
-    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "qwen3_8b_batched", "gpt_oss_20b"])
+    ap.add_argument("--workload", default=WORKLOAD,
+                    choices=[WORKLOAD, "qwen3_8b_batched", "gpt_oss_20b", "qwen3_4b", "qwen3_4b_fc"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the drafter's hot path runs on a single MI355X here; "

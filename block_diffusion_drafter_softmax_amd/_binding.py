@@ -44,13 +44,15 @@ class Config(ctypes.Structure):
         "hidden", "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "intermediate", "vocab",
         "n_target_layers", "block_size", "page_size", "max_seqs", "max_pages_per_seq", "n_pages",
         "max_pos", "mask_token_id", "tied_kv", "use_rope", "max_batch", "max_new")] + [
-        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("fusion", ctypes.c_int32)]
+
+FUSION = {"softmax": 0, "fc": 1}
 
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_fuse", "g_fuse", "g_attn", "g_mlp", "g_final", "wq", "wk_d", "wv_d", "wk_t", "wv_t",
-        "wo", "wg", "wu", "wd", "embed", "lm_head")]
+        "wo", "wg", "wu", "wd", "embed", "lm_head", "w_fc", "g_fc")]
 
 
 class KV(ctypes.Structure):

@@ -31,6 +31,13 @@
 // same workgroup (stage, compute, stage, ...) with the running max, sum and
 // O rescaled per half chunk as in any online softmax, and one partial per
 // item goes to the merge: cpi times fewer partial bytes.
+//
+// Blocks that share a sequence (the dual-pass drafter's candidates: grp
+// consecutive blocks) share its context: a workgroup takes `cand` of them
+// for a context-only item, with cand * R / 16 computing waves, so each
+// context chunk is read from HBM once for all of them. Item 0 holds
+// the block page, which differs per candidate: it gets one workgroup per
+// candidate.
 #include <algorithm>
 
 #include "common.h"
@@ -69,9 +76,23 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   __shared__ long long poff[SLOTS];  // element offset in `pages` of each page slot's K block (this kv head); -1: block
   __shared__ int cnt[SLOTS];         // valid key slots of each page slot
 
-  const int item = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int splits = (a.grp + a.cand - 1) / a.cand;  // workgroups per group along z
+  int c0 = (blockIdx.z % splits) * a.cand;           // first candidate of this split
+  int n_cand = min(a.cand, a.grp - c0);              // candidates of this split
+  // x < cand: item 0 (holds the block page) for candidate c0 + x alone;
+  // x >= cand: context-only item x - cand + 1 for all n_cand candidates
+  int item = 0;
+  if ((int)blockIdx.x < a.cand) {
+    if ((int)blockIdx.x >= n_cand) return;
+    c0 += blockIdx.x;
+    n_cand = 1;
+  } else {
+    item = blockIdx.x - a.cand + 1;
+  }
+  const int b0 = blockIdx.z / splits * a.grp + c0;   // the workgroup's first block
   const int cpi = MULTI ? a.cpi : 1;
-  const int seq = clampi(a.seq_ids[b], 0, a.max_seqs - 1);
+  const int seq = clampi(a.seq_ids[b0], 0, a.max_seqs - 1);
   const int L = clampi(a.ctx_len[seq], 0, a.max_pages_per_seq * 16);
   const int item_begin = item * cpi * CH;
   const int item_nv = min(16 + L, item_begin + cpi * CH) - item_begin;  // virtual keys in this item
@@ -82,8 +103,8 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
 
   // Page slots of the item (virtual page 0 is the block; slots past the
   // context point at the block and hold 0 valid keys).
-  const uint16_t* blk_k = a.kblk + ((size_t)b * a.n_kv + kvh) * 16 * D;
-  const uint16_t* blk_v = a.vblk + ((size_t)b * a.n_kv + kvh) * D * 16;
+  const uint16_t* blk_k = a.kblk + ((size_t)b0 * a.n_kv + kvh) * 16 * D;
+  const uint16_t* blk_v = a.vblk + ((size_t)b0 * a.n_kv + kvh) * D * 16;
   for (int t = tid; t < n_chunks * PAGES; t += nthreads) {
     long long off = -1;
     int n_ok = 0;
@@ -103,10 +124,12 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int G = a.n_q / a.n_kv, R = G * a.N, n_wr = R / 16;
-  const bool computing = wave < n_wr;
+  const bool computing = wave < n_cand * n_wr;
   // staging: thread t moves unit t % (4D) of its page slots, K units first
   const bool isk_wave = __builtin_amdgcn_readfirstlane((int)(tid % (4 * D) < 2 * D));
-  const int r = min(wave, n_wr - 1) * 16 + r16;
+  const int wc = min(wave, n_cand * n_wr - 1);
+  const int cand = wc / n_wr, b = b0 + cand;  // the wave's block
+  const int r = (wc % n_wr) * 16 + r16;
   const int hq = kvh * G + r / a.N, n = r % a.N;
   constexpr int KD = D / 32, DT = D / 16, NT = CH / 16;
 
@@ -114,7 +137,7 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   bf16x8 qh[KD], ql[KD];
   {
     const uint16_t* qp = a.q + ((size_t)(b * a.N + n) * a.n_q + hq) * D + 8 * g;
-    const size_t q_lo = (size_t)gridDim.z * a.N * a.n_q * D;
+    const size_t q_lo = (size_t)(gridDim.z / splits * a.grp) * a.N * a.n_q * D;
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd) {
       qh[kd] = ld8(qp + kd * 32);
@@ -352,8 +375,9 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
 
 extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
   const int G = a->n_q / a->n_kv, n_wr = G * a->N / 16;
-  const int waves = std::max(n_wr, MIN_WAVES);
-  const dim3 grid((a->n_ck + a->cpi - 1) / a->cpi, a->n_kv, B), block(64 * waves);
+  const int waves = std::max(a->cand * n_wr, MIN_WAVES);
+  const int wgs_z = B / a->grp * ((a->grp + a->cand - 1) / a->cand);
+  const dim3 grid((a->n_ck + a->cpi - 1) / a->cpi + a->cand - 1, a->n_kv, wgs_z), block(64 * waves);
   if (head_dim == 128) {
     if (a->cpi > 1) launch_kernel(attn_chunk_kernel<128, 1, true>, grid, block, 0, st, *a);
     else if (waves <= 8) launch_kernel(attn_chunk_kernel<128, 2, false>, grid, block, 0, st, *a);

@@ -38,6 +38,9 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int kAttnChunk = 128;     // virtual keys (16 block slots + context) per attention chunk
 constexpr int kAttnItems = 4096;    // attention work items to aim for; larger batches take several chunks per item
+constexpr int kAttnMaxWaves = 8;    // computing waves of an attention workgroup that takes several blocks of one
+                                    // sequence: only the staging-only waves of an 8-wave workgroup are filled (larger
+                                    // workgroups were slower: the attention is bound by its compute phase)
 constexpr int kVerifyChunk = 32768;       // logits per verification work item (rows pass)
 constexpr int kSampleChunk = 8192;        // logits per work item of the temperature-1 sampling pass
 constexpr int kKsMax = 8;           // largest k split of a streaming GEMM (KS_MAX in common.h)
@@ -59,9 +62,9 @@ int lm_parts(int vocab, int M) { return M >= kMmMinRows ? (vocab + kMmCols - 1) 
 // Byte offsets of everything the library keeps in the caller's workspace.
 struct Layout {
   // set-up tables and packed weights
-  size_t alpha, rope, wq, wk_d, wv_d, wk_t, wv_t, wo, wg, wu, wd, lm;
+  size_t alpha, rope, wq, wk_d, wv_d, wk_t, wv_t, wo, wg, wu, wd, lm, wfc;
   // per-call buffers
-  size_t rowpos_a, rowseq_a, f, x, h, q, o, kblk, vblk, mm, gpart, cpart;
+  size_t rowpos_a, rowseq_a, f, fraw, x, h, q, o, kblk, vblk, mm, gpart, cpart;
   size_t apo, aml, lmpart, vpart, spart, total;
   // dual-pass drafting: second-pass sequences and input blocks, first and
   // second drafts, confidence, cut points; multi-candidate verification
@@ -85,6 +88,9 @@ Layout make_layout(const dflash_config& c) {
   const size_t ncol_d = std::max(qd + 2 * kvd, H), ncol_c = D * 2 * kvd;
   L.gpart_floats = std::max(ncol_d * std::max<size_t>(256, 2 * (size_t)L.m_max), kMmPartFloats);
   L.cpart_floats = std::max(ncol_c * std::max<size_t>(256, 2 * (size_t)L.rows_a_max), kMmPartFloats);
+  const bool fc = c.fusion == DFLASH_FUSION_FC;
+  if (fc)  // the FC fusion layer's partials [ks][rows][H] share this buffer
+    L.cpart_floats = std::max(L.cpart_floats, H * std::max<size_t>(256, 2 * (size_t)L.rows_a_max));
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -104,10 +110,13 @@ Layout make_layout(const dflash_config& c) {
   L.wu = take(D * I * H * 2);
   L.wd = take(D * H * I * 2);
   L.lm = take((size_t)c.vocab * H * 2);
+  L.wfc = fc ? take(H * T * H * 2) : 0;
   L.rowpos_a = take(L.rows_a_max * 4);
   L.rowseq_a = take(L.rows_a_max * 4);
-  // activations are split hi/lo bf16 pairs: two planes each
-  L.f = take(D * 2 * rp * H * 2);
+  // activations are split hi/lo bf16 pairs: two planes each (FC fusion: one
+  // shared context instead of D, and the FC layer's [rows][T*H] input)
+  L.f = take((fc ? 1 : D) * 2 * rp * H * 2);
+  L.fraw = fc ? take(2 * rp * T * H * 2) : 0;
   L.x = take(L.m_max * H * 4);
   L.h = take(2 * mp * H * 2);
   L.q = take(2 * L.m_max * qd * 2);
@@ -159,6 +168,8 @@ int check_config(const dflash_config* c) {
   if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab)
     return fail(DFLASH_ERR_INVALID_ARG, "mask_token_id out of range");
   if (c->max_pos < c->block_size) return fail(DFLASH_ERR_INVALID_ARG, "max_pos too small");
+  if (c->fusion != DFLASH_FUSION_SOFTMAX && c->fusion != DFLASH_FUSION_FC)
+    return fail(DFLASH_ERR_INVALID_ARG, "fusion must be DFLASH_FUSION_SOFTMAX or DFLASH_FUSION_FC");
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f))
     return fail(DFLASH_ERR_INVALID_ARG, "rms_eps > 0 and rope_theta > 1 required");
   return DFLASH_OK;
@@ -291,18 +302,22 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, const dflas
   if (rc) return rc;
   if (!w || !kv || !workspace) return fail(DFLASH_ERR_INVALID_ARG, "weights, kv and workspace are required");
   const dflash_config& c = *cfg;
-  if (!w->w_fuse || !w->g_fuse || !w->g_attn || !w->g_mlp || !w->g_final || !w->wq || !w->wk_d || !w->wv_d ||
-      !w->wo || !w->wg || !w->wu || !w->wd || !w->embed || !w->lm_head)
+  const bool fc = c.fusion == DFLASH_FUSION_FC;
+  if (!w->g_attn || !w->g_mlp || !w->g_final || !w->wq || !w->wk_d || !w->wv_d || !w->wo || !w->wg || !w->wu ||
+      !w->wd || !w->embed || !w->lm_head)
     return fail(DFLASH_ERR_INVALID_ARG, "a weight pointer is null");
+  if (fc ? (!w->w_fc || !w->g_fc) : (!w->w_fuse || !w->g_fuse))
+    return fail(DFLASH_ERR_INVALID_ARG, fc ? "w_fc and g_fc required for FC fusion" : "w_fuse and g_fuse required");
   if (!c.tied_kv && (!w->wk_t || !w->wv_t)) return fail(DFLASH_ERR_INVALID_ARG, "wk_t/wv_t required unless tied_kv");
   if (!kv->kv_pages || !kv->page_table || !kv->ctx_len || !kv->error_word)
     return fail(DFLASH_ERR_INVALID_ARG, "a kv pointer is null");
   const Layout L = make_layout(c);
   if (ws_bytes < L.total) return fail(DFLASH_ERR_CAPACITY, "workspace %zu bytes < required %zu", ws_bytes, L.total);
 
-  // alpha^(i) = softmax over the T entries of w_fuse[i] (float64 on the host).
-  std::vector<float> wf((size_t)c.n_layers * c.n_target_layers);
-  HIP_OK(hipMemcpy(wf.data(), w->w_fuse, wf.size() * 4, hipMemcpyDeviceToHost));
+  // alpha^(i) = softmax over the T entries of w_fuse[i] (float64 on the host;
+  // unused, all zero, with FC fusion).
+  std::vector<float> wf((size_t)c.n_layers * c.n_target_layers, 0.f);
+  if (!fc) HIP_OK(hipMemcpy(wf.data(), w->w_fuse, wf.size() * 4, hipMemcpyDeviceToHost));
   std::vector<float> alpha(wf.size());
   for (int i = 0; i < c.n_layers; ++i) {
     const float* row = &wf[(size_t)i * c.n_target_layers];
@@ -343,6 +358,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, const dflas
     jobs.push_back({w->wk_t, L.wk_t, D * kvd, H});
     jobs.push_back({w->wv_t, L.wv_t, D * kvd, H});
   }
+  if (fc) jobs.push_back({w->w_fc, L.wfc, H, c.n_target_layers * H});
   for (const Job& j : jobs) {
     PackArgs pa{j.src, reinterpret_cast<uint16_t*>(ws + j.dst), j.R, j.K};
     HIP_OK(dflash_launch_pack(&pa, nullptr));
@@ -402,7 +418,31 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
   fa.H = H;
   fa.D = D;
   fa.eps = c.rms_eps;
+  const bool fc = c.fusion == DFLASH_FUSION_FC;
+  if (fc) {
+    fa.raw = 1;
+    fa.f = ctx->at<uint16_t>(L.fraw);
+  }
   if ((rc = ctx->launch(DFLASH_K_FUSE, stream, [&] { return dflash_launch_fuse(&fa, stream); }))) return rc;
+
+  if (fc) {  // DFlash's FC fusion: c = RMSNorm(W_fc [h^(0); ...; h^(T-1)]) * g_fc, one context for all layers
+    const int TH = c.n_target_layers * H;
+    WsArgs g = ws_base(rows, TH, H);
+    g.part = ctx->at<float>(L.cpart);
+    add_seg(g, ctx->at<uint16_t>(L.wfc), nullptr, fa.f, H / 32, 0);
+    g.ks = gemm_ks(g, WS_PARTIAL, L.cpart_floats);
+    if ((rc = ctx->launch(DFLASH_K_CTX_KV, stream, [&] { return launch_gemm(g, WS_PARTIAL, stream); }))) return rc;
+    NormArgs na{};
+    na.mode = 2;
+    na.part = g.part;
+    na.ks = g.ks;
+    na.g = ctx->w.g_fc;
+    na.h = ctx->at<uint16_t>(L.f);
+    na.H = H;
+    na.M = rows;
+    na.eps = c.rms_eps;
+    if ((rc = ctx->launch(DFLASH_K_FUSE, stream, [&] { return dflash_launch_norm(&na, stream); }))) return rc;
+  }
 
   // Context K and V of every layer: fp32 split partials, columns
   // [layer][K | V], then one finisher (RoPE, bf16, page scatter).
@@ -412,7 +452,7 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
     WsArgs g = ws_base(rows, H, n_cols);
     g.part = ctx->at<float>(L.cpart);
     for (int i = l0; i < D && i < l0 + WS_MAX_SEG / 2; ++i) {
-      const uint16_t* act = ctx->at<uint16_t>(L.f) + (size_t)i * 2 * act_plane(rows, H);
+      const uint16_t* act = ctx->at<uint16_t>(L.f) + (fc ? 0 : (size_t)i * 2 * act_plane(rows, H));
       add_seg(g, ctx->at<uint16_t>(L.wk_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd);
       add_seg(g, ctx->at<uint16_t>(L.wv_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd + kvd);
     }
@@ -448,10 +488,12 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
 namespace {
 
 // One drafting pass over B blocks: the block input is the anchor and masks,
-// or `tokens` [B][N] when given (the dual-pass drafter's second pass).
+// or `tokens` [B][N] when given (the dual-pass drafter's second pass). Each
+// run of `grp` consecutive blocks belongs to one sequence (B % grp == 0), so
+// the attention reads that sequence's context once for several blocks.
 int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor, const int32_t* tokens,
                int32_t* draft, float* top2_gap, float* conf, float* dbg_hidden, float* dbg_logits,
-               hipStream_t stream) {
+               hipStream_t stream, int grp = 1) {
   const dflash_config& c = ctx->c;
   const Layout& L = ctx->L;
   const int N = c.block_size, M = B * N;
@@ -519,8 +561,13 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
   aa.n_kv = c.n_kv_heads;
   aa.chunk = kAttnChunk;
   aa.n_ck = L.n_ck;
-  {  // chunks per work item, from the largest grid the batch can have
-    const long long chunks = (long long)B * c.n_kv_heads * L.n_ck;
+  {  // blocks per workgroup, then chunks per work item from the largest grid
+     // the batch can have
+    const int n_wr = c.n_q_heads / c.n_kv_heads * N / 16;
+    aa.grp = grp;
+    aa.cand = std::max(1, std::min(grp, kAttnMaxWaves / n_wr));
+    const long long wgs_z = (long long)(B / grp) * ((grp + aa.cand - 1) / aa.cand);
+    const long long chunks = wgs_z * c.n_kv_heads * L.n_ck;
     aa.cpi = (int)std::min<long long>(8, std::max<long long>(1, (chunks + kAttnItems - 1) / kAttnItems));
   }
   aa.max_pages_per_seq = c.max_pages_per_seq;
@@ -663,7 +710,7 @@ int dflash_d2sd_draft(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
   if (rc) return rc;
   if ((rc = ctx->launch(DFLASH_K_D2SD, stream, [&] { return dflash_launch_d2sd_select(&da, stream); }))) return rc;
   if ((rc = draft_impl(ctx, B * K, da.seq2, nullptr, da.tokens, ctx->at<int>(L.d_draft2), nullptr, nullptr, nullptr,
-                       nullptr, stream)))
+                       nullptr, stream, K)))
     return rc;
   return ctx->launch(DFLASH_K_D2SD, stream, [&] { return dflash_launch_d2sd_assemble(&da, stream); });
 }

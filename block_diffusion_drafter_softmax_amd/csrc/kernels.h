@@ -118,6 +118,8 @@ struct AttnArgs {
   int32_t* err;
   int N, n_q, n_kv, chunk, n_ck, max_pages_per_seq, n_pages, max_seqs;
   int cpi;                 // chunks of `chunk` virtual keys per work item (1 .. 8)
+  int grp;                 // consecutive blocks that share one sequence's context (B % grp == 0)
+  int cand;                // blocks of a group one workgroup takes (1 .. grp): a context chunk is read once for them
 };
 
 // ------------------------------------------------------------ small kernels
@@ -139,10 +141,13 @@ struct FuseArgs {
   int32_t* err;
   int rows, T, H, D;
   float eps;
+  int raw;                 // FC fusion: f is instead the FC layer's input, each row's T*H states as a packed
+                           // split activation [rows][T*H] (lo plane 0); no fusion, no norm
 };
 
 struct NormArgs {
-  int mode;                // 0: x = embedding rows, 1: x += sum of split partials
+  int mode;                // 0: x = embedding rows, 1: x += sum of split partials,
+                           // 2: x = sum of split partials (no residual; x not written)
   const uint16_t* embed;   // [V][H]
   const int* anchor;       // [B]
   const int* tokens;       // mode 0, nullable: [B][N] block input tokens (else anchor, then masks)

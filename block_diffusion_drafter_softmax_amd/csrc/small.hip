@@ -84,6 +84,24 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
     if (t == 0 && bad) set_error(a.err, bad);
   }
   if (pos < 0) return;
+  if (a.raw) {  // FC fusion: the row's T states, in layer order, are the FC layer's input row
+    const int K = a.T * a.H;
+    const size_t plane_k = act_plane(a.rows, K);
+    const u16x4 zero = {0, 0, 0, 0};
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+      const int k = (v * blockDim.x + threadIdx.x) * 4;
+      if (k >= a.H) continue;
+#pragma unroll
+      for (int j = 0; j < FUSE_TMAX; ++j) {
+        if (j >= a.T) break;
+        uint16_t* dst = a.f + pk_index(m, j * a.H + k, K);
+        *reinterpret_cast<u16x4*>(dst) = x[v][j];
+        *reinterpret_cast<u16x4*>(dst + plane_k) = zero;
+      }
+    }
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const size_t plane = act_plane(a.rows, a.H);
   {
@@ -146,10 +164,11 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
 extern "C" hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st) {
   const int threads = std::min(1024, ((a->H / 4 + 63) / 64) * 64);
   constexpr int DG = 8;
+  const int gy = a->raw ? 1 : a->D;  // the FC layer's input: one workgroup per row
   if (a->H > 4 * threads) {  // H > 4096: two float4 groups per thread, one layer per workgroup
-    launch_kernel((fuse_kernel<2, 1>), dim3(a->rows, a->D), dim3(threads), 0, st, *a);
-  } else if (a->rows < 128) {  // few rows: a workgroup per (row, layer)
-    launch_kernel((fuse_kernel<1, 1>), dim3(a->rows, a->D), dim3(threads), 0, st, *a);
+    launch_kernel((fuse_kernel<2, 1>), dim3(a->rows, gy), dim3(threads), 0, st, *a);
+  } else if (a->rows < 128 || a->raw) {  // few rows: a workgroup per (row, layer)
+    launch_kernel((fuse_kernel<1, 1>), dim3(a->rows, gy), dim3(threads), 0, st, *a);
   } else {
     launch_kernel((fuse_kernel<1, DG>), dim3(a->rows, (a->D + DG - 1) / DG), dim3(threads), 0, st, *a);
   }
@@ -163,7 +182,8 @@ extern "C" hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st) {
 // One workgroup per row, one float4 of the row per thread: build the
 // residual row (embedding gather, or x + the k-split partials of the last
 // projection, summed in split order), then h = x / sqrt(mean(x^2) + eps) * g
-// as the packed split activation the next projection streams. Mode 0 (first
+// as the packed split activation the next projection streams. Mode 2 norms
+// the FC fusion layer's output (its partials alone; no residual). Mode 0 (first
 // kernel of a draft call) embeds the block's tokens (the anchor and masks,
 // or given input tokens) and also checks the call's sequence ids, tokens
 // and position capacity.
@@ -199,11 +219,13 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
       const u16x4 e = *reinterpret_cast<const u16x4*>(a.embed + (size_t)tok * a.H + k);
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = bf2f(e[i]);
-    } else {
+    } else if (a.mode == 1) {
       x = *reinterpret_cast<const f32x4*>(a.x + (size_t)m * a.H + k);
       x += split_sum4(a.part, a.ks, split_stride, (size_t)m * a.H + k);
+    } else {
+      x = split_sum4(a.part, a.ks, split_stride, (size_t)m * a.H + k);
     }
-    *reinterpret_cast<f32x4*>(a.x + (size_t)m * a.H + k) = x;
+    if (a.mode != 2) *reinterpret_cast<f32x4*>(a.x + (size_t)m * a.H + k) = x;
     if (a.dbg) *reinterpret_cast<f32x4*>(a.dbg + (size_t)m * a.H + k) = x;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -64,8 +64,9 @@ class Drafter:
 
         c = B.Config()
         for f, _ in B.Config._fields_:
-            if f in cfg:
+            if f in cfg and f != "fusion":
                 setattr(c, f, cfg[f])
+        c.fusion = B.FUSION[cfg.get("fusion", "softmax")]
         c.page_size = 16
         c.max_seqs = max_seqs
         c.max_pages_per_seq = pages_per_seq
@@ -96,7 +97,7 @@ class Drafter:
         B.check(rc, "dflash_create")
         self.handle = h
         # the library keeps its own packed copies of the streamed matrices
-        for k in ("wq", "wk_d", "wv_d", "wk_t", "wv_t", "wo", "wg", "wu", "wd", "lm_head"):
+        for k in ("wq", "wk_d", "wv_d", "wk_t", "wv_t", "wo", "wg", "wu", "wd", "lm_head", "w_fc"):
             self.w.pop(k, None)
 
     # ---------------------------------------------------------------- calls

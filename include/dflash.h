@@ -93,25 +93,36 @@ typedef struct dflash_config {
   int32_t max_new;         /* largest rows appended per sequence per call (workspace sizing) */
   float rope_theta;        /* RoPE base, e.g. 1e6 */
   float rms_eps;           /* RMSNorm epsilon, e.g. 1e-6 */
+  int32_t fusion;          /* DFLASH_FUSION_SOFTMAX (0): per-layer weighted sum [DFLARE 2.1];
+                              DFLASH_FUSION_FC (1): one FC layer, one context for every layer
+                              [DFLARE 1: DFlash's conditioning] */
 } dflash_config;
+
+#define DFLASH_FUSION_SOFTMAX 0
+#define DFLASH_FUSION_FC 1
 
 /* Device pointers to drafter weights, all bf16 except w_fuse (fp32).
  * Stacked over the D draft layers:
  *   wq [D, n_q*d_h, H]          wk_d, wv_d [D, n_kv*d_h, H]  block K/V  [DFLARE 2.2]
  *   wk_t, wv_t [D, n_kv*d_h, H] context K/V [DFLARE 2.2]; ignored when tied_kv
  *   wo [D, H, n_q*d_h]          wg, wu [D, I, H]             wd [D, H, I]
- *   embed, lm_head [V, H]       g_fuse, g_attn, g_mlp [D, H] g_final [H]
- *   w_fuse [D, T] fp32: alpha^(i) = softmax(w_fuse[i, :])    [DFLARE 2.1]
- * dflash_create copies every projection matrix and lm_head into the
- * workspace in the layout the kernels stream (16x32 MFMA operand blocks, 1 KB
- * contiguous each); after it returns only embed, the gains and w_fuse are
- * read again and must stay valid and unchanged until dflash_destroy; the
- * other weight buffers may be freed. */
+ *   embed, lm_head [V, H]       g_attn, g_mlp [D, H]         g_final [H]
+ *   softmax fusion: w_fuse [D, T] fp32, alpha^(i) = softmax(w_fuse[i, :]),
+ *                   and g_fuse [D, H]                          [DFLARE 2.1]
+ *   FC fusion:      w_fc [H, T*H] (the T states of a token concatenated in
+ *                   layer order) and g_fc [H]                  [DFLARE 1]
+ * The pointers of the fusion not configured may be null.
+ * dflash_create copies every projection matrix (w_fc included) and lm_head
+ * into the workspace in the layout the kernels stream (16x32 MFMA operand
+ * blocks, 1 KB contiguous each); after it returns only embed and the gains
+ * are read again and must stay valid and unchanged until dflash_destroy;
+ * the other weight buffers may be freed. */
 typedef struct dflash_weights {
   const float* w_fuse;
   const uint16_t *g_fuse, *g_attn, *g_mlp, *g_final;
   const uint16_t *wq, *wk_d, *wv_d, *wk_t, *wv_t, *wo, *wg, *wu, *wd;
   const uint16_t *embed, *lm_head;
+  const uint16_t *w_fc, *g_fc;
 } dflash_weights;
 
 /* Paged per-sequence context cache, one set of pages per draft layer.
@@ -152,8 +163,9 @@ void dflash_destroy(dflash_ctx* ctx);
  * target_hidden: bf16 [B, max_new, T, H]; row t < n_new[b] of batch entry b
  * holds the T selected target-layer states of the token at position
  * ctx_len[seq] + t. For every draft layer i: f = RMSNorm(sum_j alpha^(i)_j
- * h^(j)) * g_fuse[i]; K = RoPE(f W^t_K[i]^T) and V = f W^t_V[i]^T go to
- * the cache; then ctx_len[seq] += n_new[b]. seq_ids, n_new: device int32
+ * h^(j)) * g_fuse[i] (FC fusion: f = RMSNorm(W_fc [h^(0); ...; h^(T-1)])
+ * * g_fc, the same for every layer); K = RoPE(f W^t_K[i]^T) and
+ * V = f W^t_V[i]^T go to the cache; then ctx_len[seq] += n_new[b]. seq_ids, n_new: device int32
  * [B]; the B sequences must be distinct. max_new <= cfg.max_new. */
 int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* n_new,
                       const uint16_t* target_hidden, int32_t max_new, hipStream_t stream);

@@ -37,8 +37,9 @@ def make_cfg(name="qwen3_8b", **kw):
     cfg = synth.config(name)
     c = B.Config()
     for f, _ in B.Config._fields_:
-        if f in cfg:
+        if f in cfg and f != "fusion":
             setattr(c, f, cfg[f])
+    c.fusion = B.FUSION[cfg.get("fusion", "softmax")]
     c.page_size, c.max_seqs, c.max_pages_per_seq, c.n_pages = 16, 4, 260, 1040
     c.max_pos, c.max_batch, c.max_new = 4200, 4, 16
     c.mask_token_id = cfg["mask_token_id"]
@@ -66,6 +67,7 @@ def test_workspace_sizes_every_config(name):
     ("n_kv_heads", 5, "multiple"),
     ("mask_token_id", 10 ** 6, "mask_token_id"),
     ("max_batch", 0, "positive"),
+    ("fusion", 2, "fusion"),
 ])
 def test_bad_config_is_rejected_with_message(field, value, msg):
     c = make_cfg(**{field: value})

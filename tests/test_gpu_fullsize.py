@@ -4,7 +4,7 @@ benchmark times (one decode step after a prefill), against the oracle.
 * Qwen3-8B-shaped DFLARE drafter (T=9, 7 layers, context 4096, block 16,
   batch 1, 8 appended rows, greedy verify): every output.
 * Qwen3-4B-shaped DFlash-style drafter (tied context/block K/V, T=5,
-  context 2048): every output.
+  context 2048): every output; the same with DFlash's FC fusion.
 * GPT-OSS-20B-shaped drafter (d_h 64, GQA 8:1, V 201088, batch 8, context
   8192): the whole batch runs on the GPU, the oracle reproduces two of the
   eight sequences (sequences never interact).
@@ -57,6 +57,13 @@ def test_qwen3_8b_full_step():
 def test_qwen3_4b_tied_full_step():
     cfg = synth.config("qwen3_4b")
     assert cfg["tied_kv"] == 1
+    full_step(Case(cfg, ctx=[cfg["context"]], n_new=[cfg["n_new"]], prefill_chunk=512, seq_offset=0))
+
+
+@pytest.mark.timeout(1200)
+def test_qwen3_4b_fc_fusion_full_step():
+    cfg = synth.config("qwen3_4b_fc")
+    assert cfg["fusion"] == "fc" and cfg["tied_kv"] == 1
     full_step(Case(cfg, ctx=[cfg["context"]], n_new=[cfg["n_new"]], prefill_chunk=512, seq_offset=0))
 
 

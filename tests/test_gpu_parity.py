@@ -134,6 +134,21 @@ def test_attention_multi_chunk_items():
                   extra_pages=2100 - pps_min))
 
 
+def test_fc_fusion_ragged_batch():
+    # DFlash's FC fusion: one shared context from W_fc [H, T*H] for every
+    # layer; ragged appends (one entry appends nothing), shuffled pages
+    cfg = small_cfg(fusion="fc")
+    run_step(Case(cfg, ctx=[70, 9, 131], n_new=[8, 0, 5], seed=71, page_order="shuffled", prefill_chunk=40))
+
+
+def test_fc_fusion_tied_many_rows():
+    # FC fusion with tied context/block K/V (DFlash's shared projection),
+    # T = 5, appends of 2 x 80 rows: the FC layer and the context K/V run on
+    # the tiled GEMM, with a partial last row tile
+    cfg = small_cfg(fusion="fc", tied_kv=1, n_target_layers=5, block_size=16, n_q_heads=8, n_kv_heads=2)
+    run_step(Case(cfg, ctx=[200, 97], n_new=[16, 3], seed=73, prefill_chunk=80))
+
+
 def test_wide_batch_multi_group_rows():
     # M = 5 * 16 = 80 rows -> several 64-row groups in the projection kernels
     cfg = small_cfg(hidden=256, block_size=16, n_q_heads=4, n_kv_heads=4)
