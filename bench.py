@@ -268,6 +268,82 @@ def run_batched(args, name):
     print(json.dumps(res), flush=True)
 
 
+def run_rollout(args):
+    """S decode steps of the Qwen3-8B-shaped workload captured as one graph:
+    each step appends the previous step's committed rows and drafts from its
+    next token (device-resident, no host round trip); synthetic target
+    logits by the agreement model (p = 0.8) are built on the device around
+    each step's draft. Timed over replays of the whole graph."""
+    import torch
+    from block_diffusion_drafter_softmax_amd import synth
+    from block_diffusion_drafter_softmax_amd.drafter import Drafter
+    from block_diffusion_drafter_softmax_amd.rollout import Rollout
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    cfg = synth.config(WORKLOAD)
+    S = args.rollout
+    N, L, n_new, T, H, V = (cfg[k] for k in ("block_size", "context", "n_new", "n_target_layers", "hidden", "vocab"))
+    dev = torch.device("cuda")
+    w = synth.make_weights(cfg, 0)
+    chunk = 512
+    dr = Drafter(cfg, w, max_batch=1, max_new=chunk, max_seqs=1, pages_per_seq=(L + S * N + N + 15) // 16 + 1)
+    seq = torch.zeros(1, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    hid = torch.randn((1, chunk, T, H), generator=gen, device=dev).to(torch.bfloat16)
+    done = 0
+    while done < L - n_new:
+        n = min(chunk, L - n_new - done)
+        dr.ctx_append(seq, torch.tensor([n], dtype=torch.int32, device=dev), hid, chunk)
+        done += n
+    del hid
+    # per-step target stand-in: hidden rows, noise logits, agreement coins
+    hidden = torch.randn((S, 1, N, T, H), generator=gen, device=dev).to(torch.bfloat16)
+    noise = torch.randn((S, 1, N, V), generator=gen, device=dev).to(torch.bfloat16)
+    top1 = (noise[:, :, : N - 1].float().amax(-1) + 1.0).to(torch.bfloat16)
+    agree = torch.rand((S, 1, N - 1), generator=gen, device=dev) < cfg["agreement"]
+    anchor = torch.from_numpy(synth.make_anchor(cfg, 1, 0)).to(dev)
+    rl = Rollout(dr, seq, anchor, torch.tensor([n_new], dtype=torch.int32, device=dev), hidden, noise, agree, top1)
+    rl.run()
+    torch.cuda.synchronize()
+    assert dr.read_error() == 0
+    graph = rl.capture()
+    reps = max(1, args.steps // S)
+    for _ in range(max(1, args.warmup // S)):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert dr.read_error() == 0
+    com = rl.commit.cpu().numpy()[:, 0]
+    acc = rl.accept.cpu().numpy()[:, 0]
+    ms_step = elapsed * 1e3 / (reps * S)
+    ctx_steps = L + np.concatenate([[0], np.cumsum(com[:-1])])  # context of each step (after its append)
+    appended = np.concatenate([[n_new], com[:-1]])
+    t_roof = float(np.mean([step_bytes(cfg, int(c), int(a))["total"] for c, a in zip(ctx_steps, appended)])) \
+        / (HBM_PEAK_GBS * 1e9) * 1e6
+    res = {
+        "metric": METRIC, "value": round((N - 1) / (ms_step / 1e3), 1), "unit": "draft tokens/s", "n_gpus": 1,
+        "steps": reps * S, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"Qwen3-8B-shaped roll-out: {S} device-resident decode steps in one graph "
+                               f"(append the previous commit, draft, target stand-in, greedy verify), context "
+                               f"{int(ctx_steps[0])}..{int(ctx_steps[-1])}",
+                   "global_batch": 1, "block": N, "launch": "graph", "rollout_steps": S},
+        "committed_tok_s": round(float(com.sum()) / (ms_step * S / 1e3), 1),
+        "mean_accept": round(float(acc.mean()), 3),
+        "step_roofline": {"bound": "hbm", "t_roof_us": round(t_roof, 1), "frac": round(t_roof / (ms_step * 1e3), 4)},
+        "roofline": None, "cpu_baseline": None,
+    }
+    log(f"roll-out: {ms_step:.3f} ms/step over {S} steps, {res['value']:.0f} draft tok/s, "
+        f"{res['committed_tok_s']:.0f} committed tok/s, mean accept {res['mean_accept']}")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,11 +353,15 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=[WORKLOAD, "qwen3_8b_batched", "gpt_oss_20b", "qwen3_4b", "qwen3_4b_fc"])
+    ap.add_argument("--rollout", type=int, default=0,
+                    help="S > 0: S device-resident steps of the default workload captured as one graph")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the drafter's hot path runs on a single MI355X here; "
               "--gpus must be 1", file=sys.stderr)
         sys.exit(2)
+    if args.rollout > 0:
+        return run_rollout(args)
     if args.workload != WORKLOAD:
         return run_batched(args, args.workload)
 
