@@ -24,6 +24,9 @@ What it follows (the pages are three web summaries; sections, not lines):
     by the target's own token. Key contributions: the result is lossless.
   * DFlash page, Methodology step 4: the window advances by the number of
     accepted tokens.
+  * DFlash page, Methodology step 3 with a sampled draft: the same standard
+    acceptance test with a general drafter distribution (accept with
+    probability min(1, p/q), resample from max(0, p - q)).
   * "D^2SD: Accelerating Speculative Decoding with Dual Diffusion Draft
     Models" (euno.news), Methodology steps 1-4: per-position confidence of
     the first draft, K prefixes cut where a rejection is most likely, a
@@ -70,6 +73,7 @@ __all__ = [
     "verify_greedy", "verify_temp1", "philox4x64_10", "philox4x64_10_vec",
     "rng_uniform", "rng_gumbel_row", "draft_confidence", "d2sd_cut_points",
     "d2sd_candidate_tokens", "d2sd_candidates", "verify_greedy_multi",
+    "draft_sample", "verify_sampled",
 ]
 
 
@@ -515,14 +519,15 @@ def rng_uniform(seed, step, seq, row, k=0, stream=0):
     return float(w0 >> 40) * 2.0 ** -24
 
 
-def rng_gumbel_row(seed, step, seq, row, vocab):
+def rng_gumbel_row(seed, step, seq, row, vocab, stream=1):
     """Standard Gumbel noise for every k < vocab of one row, float32.
 
     u' = (top 23 bits of Philox word 0 + 1/2) * 2^-23 lies strictly in
     (0, 1) and is exact in float32; G = -log(-log u'), evaluated in float32.
+    Stream 1 serves the verification's samples, stream 2 the sampled draft.
     """
     k = np.arange(vocab, dtype=np.uint64)
-    c1 = np.uint64((int(row) & 0xFFFFFFFF) | (1 << 32))
+    c1 = np.uint64((int(row) & 0xFFFFFFFF) | (int(stream) << 32))
     w0, _, _, _ = philox4x64_10_vec(k, c1, np.uint64(seq), np.uint64(step), seed, 0)
     u = ((w0 >> np.uint64(41)).astype(np.float64) + 0.5) * 2.0 ** -23
     u = u.astype(np.float32)
@@ -567,4 +572,81 @@ def verify_temp1(draft, z, seed, step, seq):
     nxt = int(argmax_first(key))
     finite = key[np.isfinite(key)].astype(np.float64)
     info = {"p": ps, "u": us, "gumbel_gap": float(top2_gap(finite)), "row": row}
+    return a, nxt, a + 1, info
+
+
+# ------------------------------------------ sampled drafts (temperature tau)
+def _row_lse(z):
+    z = np.asarray(z, dtype=np.float64)
+    m = np.max(z, axis=-1, keepdims=True)
+    return (m + np.log(np.sum(np.exp(z - m), axis=-1, keepdims=True)))[..., 0]
+
+
+def draft_sample(z, tau, seed, step, seq):
+    """Draft tokens sampled from the drafter at temperature tau > 0.
+
+    z [N-1, V]: the drafter's logits of block rows 1 .. N-1 (LM-head row r
+    gives draft position r + 1). Its proposal for that position is
+    q_r = softmax(z[r] / tau); the token is drawn by Gumbel-max,
+    argmax_k (z[r, k] / tau + G_k), in float32 with Gumbel noise of stream 2,
+    lowest index on ties. Returns (draft [N-1], key top-2 gap per row).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    n_rows, vocab = z.shape
+    draft = np.zeros(n_rows, dtype=np.int64)
+    gaps = np.zeros(n_rows)
+    for r in range(n_rows):
+        key = z[r].astype(np.float32) / np.float32(tau) + rng_gumbel_row(seed, step, seq, r, vocab, stream=2)
+        draft[r] = int(argmax_first(key))
+        gaps[r] = float(top2_gap(key.astype(np.float64)))
+    return draft, gaps
+
+
+def verify_sampled(draft, zq, tau, z, seed, step, seq):
+    """Lossless verification of a sampled draft at target temperature 1.
+
+    The standard speculative acceptance test (DFlash page, Methodology step
+    3; lossless per its key contributions) with a general proposal: target
+    p_r = softmax(z[r]) and drafter q_r = softmax(zq[r] / tau) for the token
+    d_{r+1} proposed at row r. Accept d_{a+1} iff u_a * q_a(d) < p_a(d),
+    i.e. with probability min(1, p/q), u_a the stream-0 uniform of row a; at
+    the first rejection draw from the residual max(0, p_a - q_a)
+    renormalised, by Gumbel-max over log(p_k - q_k) + G_k (stream 1) on the
+    entries with p_k > q_k; if all N-1 are accepted, draw the bonus token
+    from p_{N-1} (argmax of z + G, as for the one-hot draft). The keys are
+    float32, lowest index on ties.
+
+    Returns (a, next_token, commit_len, info): info holds per tested row p,
+    q, u, and the Gumbel top-2 gap of the sampled row (exclusion rule).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    zq = np.asarray(zq, dtype=np.float64) / float(tau)
+    n_rows, vocab = z.shape
+    lse_p, lse_q = _row_lse(z), _row_lse(zq)
+    a = 0
+    ps, qs, us = [], [], []
+    while a < n_rows - 1:
+        d = int(draft[a])
+        u = rng_uniform(seed, step, seq, a, 0, 0)
+        p = math.exp(z[a, d] - lse_p[a])
+        q = math.exp(zq[a, d] - lse_q[a])
+        ps.append(p)
+        qs.append(q)
+        us.append(u)
+        if u * q < p:
+            a += 1
+        else:
+            break
+    g = rng_gumbel_row(seed, step, seq, a, vocab, stream=1)
+    if a < n_rows - 1:
+        w = np.exp(z[a] - lse_p[a]) - np.exp(zq[a] - lse_q[a])
+        key = np.full(vocab, -np.inf, dtype=np.float32)
+        pos = w > 0
+        key[pos] = np.log(w[pos]).astype(np.float32) + g[pos]
+    else:
+        key = z[a].astype(np.float32) + g
+    nxt = int(argmax_first(key))
+    finite = key[np.isfinite(key)].astype(np.float64)
+    info = {"p": ps, "q": qs, "u": us, "row": a,
+            "gumbel_gap": float(top2_gap(finite)) if finite.size > 1 else float("inf")}
     return a, nxt, a + 1, info

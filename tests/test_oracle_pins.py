@@ -581,6 +581,96 @@ def test_temp1_first_token_is_lossless_chi_square():
     assert abs(accepted / n - pd) < 5 * math.sqrt(pd * (1 - pd) / n)
 
 
+# ----------------------------------- sampled drafts, general verification
+def test_sampled_draft_follows_softmax_over_tau_chi_square():
+    r = np.random.default_rng(50)
+    V, n, tau = 6, 20000, 0.7
+    z = r.standard_normal((1, V)).astype(np.float32).astype(np.float64)
+    counts = np.zeros(V)
+    for sd in range(n):
+        d, _ = O.draft_sample(z, tau, seed=sd, step=3, seq=1)
+        counts[d[0]] += 1
+    q = scipy.special.softmax(z[0] / tau)
+    chi2 = float(np.sum((counts - n * q) ** 2 / (n * q)))
+    assert scipy.stats.chi2.sf(chi2, V - 1) > 1e-4
+
+
+def test_sampled_draft_uses_its_own_noise_stream():
+    # the draft's Gumbel noise (stream 2) is not the verification's (stream 1)
+    g1 = O.rng_gumbel_row(7, 0, 0, 0, 64, stream=1)
+    g2 = O.rng_gumbel_row(7, 0, 0, 0, 64, stream=2)
+    assert not np.array_equal(g1, g2)
+    z = np.zeros((1, 64))
+    d, _ = O.draft_sample(z, 1.0, seed=7, step=0, seq=0)
+    assert d[0] == int(np.argmax(g2))
+
+
+def test_sampled_verify_with_one_hot_proposal_is_the_temp1_rule():
+    r = np.random.default_rng(51)
+    N, V = 5, 16
+    for sd in range(300):
+        z = r.standard_normal((N, V))
+        draft = r.integers(0, V, N - 1)
+        zq = np.zeros((N - 1, V))
+        zq[np.arange(N - 1), draft] = 10.0   # q one-hot at tau = 1e-2: exp(-1000) == 0
+        got = O.verify_sampled(draft, zq, 1e-2, z, seed=sd, step=2, seq=3)
+        ref = O.verify_temp1(draft, z, seed=sd, step=2, seq=3)
+        assert got[:3] == ref[:3], (sd, got[:3], ref[:3])
+
+
+def test_sampled_verify_proposal_equal_to_target_accepts_everything():
+    r = np.random.default_rng(52)
+    N, V = 6, 12
+    for sd in range(200):
+        z = r.standard_normal((N, V))
+        draft = r.integers(0, V, N - 1)
+        a, nxt, com, _ = O.verify_sampled(draft, z[: N - 1], 1.0, z, seed=sd, step=0, seq=0)
+        assert a == N - 1 and com == N
+        key = z[N - 1].astype(np.float32) + O.rng_gumbel_row(sd, 0, 0, N - 1, V)
+        assert nxt == int(np.argmax(key))
+
+
+def test_sampled_verify_residual_only_where_target_exceeds_proposal():
+    r = np.random.default_rng(53)
+    N, V = 3, 10
+    seen = 0
+    for sd in range(400):
+        z = r.standard_normal((N, V))
+        zq = r.standard_normal((N - 1, V)) * 2.0
+        draft = np.array([int(np.argmax(zq[0])), 0])
+        a, nxt, _, info = O.verify_sampled(draft, zq, 1.0, z, seed=sd, step=0, seq=0)
+        if a == 0:
+            p = scipy.special.softmax(z[0])
+            q = scipy.special.softmax(zq[0])
+            assert p[nxt] > q[nxt]
+            assert info["u"][0] * info["q"][0] >= info["p"][0]
+            seen += 1
+    assert seen > 50
+
+
+def test_sampled_draft_and_verify_are_lossless_chi_square():
+    """Draft d ~ q = softmax(zq / tau), verify against p = softmax(z[0]):
+    the first committed token follows p whatever q (the lossless guarantee,
+    DFlash page, key contributions), and P(accept) = sum_k min(p_k, q_k)."""
+    r = np.random.default_rng(54)
+    V, n, tau = 8, 20000, 0.8
+    z = r.standard_normal((2, V)) * 1.2
+    zq = (z[:1] + r.standard_normal((1, V))).astype(np.float32).astype(np.float64)
+    counts = np.zeros(V)
+    accepted = 0
+    for sd in range(n):
+        d, _ = O.draft_sample(zq, tau, seed=sd, step=1, seq=0)
+        a, nxt, _, _ = O.verify_sampled(d, zq, tau, z, seed=sd, step=1, seq=0)
+        counts[d[0] if a >= 1 else nxt] += 1
+        accepted += a >= 1
+    p = scipy.special.softmax(z[0])
+    chi2 = float(np.sum((counts - n * p) ** 2 / (n * p)))
+    assert scipy.stats.chi2.sf(chi2, V - 1) > 1e-4
+    q = scipy.special.softmax(zq[0] / tau)
+    pa = float(np.minimum(p, q).sum())
+    assert abs(accepted / n - pa) < 5 * math.sqrt(pa * (1 - pa) / n)
+
+
 # ---------------------------------------------- dual-pass drafting (D2SD)
 def test_confidence_is_the_softmax_maximum():
     """Confidence = the largest softmax probability: scipy's softmax on random
