@@ -353,6 +353,8 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=[WORKLOAD, "qwen3_8b_batched", "gpt_oss_20b", "qwen3_4b", "qwen3_4b_fc"])
+    ap.add_argument("--sampled", type=float, default=0.0,
+                    help="tau > 0: drafts sampled at temperature tau, lossless verification at temperature 1")
     ap.add_argument("--rollout", type=int, default=0,
                     help="S > 0: S device-resident steps of the default workload captured as one graph")
     args = ap.parse_args()
@@ -420,6 +422,16 @@ def main():
         dr.draft_block(seq, anchor_t, draft)
         dr.verify(seq, draft, logits, acc, nxt, com)
 
+    tau = args.sampled
+    if tau > 0:  # sampled drafts; the drafter's logits go to HBM for the verification
+        draft_logits = torch.zeros((1, N - 1, cfg["vocab"]), dtype=torch.float32, device=dev)
+
+        def step():
+            dr.ctx_len.copy_(ctx0)
+            dr.ctx_append(seq, n_new_t, step_hidden, n_new)
+            dr.draft_sample(seq, anchor_t, tau, draft, draft_logits, seed=1, step=0)
+            dr.verify_sample(seq, draft, draft_logits, tau, logits, acc, nxt, com, seed=1, step=0)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -461,6 +473,8 @@ def main():
     ms_step = elapsed * 1e3 / args.steps
     tok_s = (N - 1) / (ms_step / 1e3)
     sb = step_bytes(cfg, L, n_new)
+    if tau > 0:  # the drafter's fp32 logits, written once and read by the verification
+        sb["total"] += 2 * (N - 1) * cfg["vocab"] * 4
     M = N
     roof = None
     if gu_n:
@@ -480,7 +494,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "Qwen3-8B-shaped DFLARE drafter decode step: append 8 context rows "
                                "(T=9 fusion), draft block 16 over ctx 4096 (7 layers, H 4096, 32/8 heads, "
-                               "I 12288, V 151936), greedy verify; batch 1",
+                               "I 12288, V 151936), "
+                               + (f"drafts sampled at temperature {tau}, lossless temperature-1 verify"
+                                  if tau > 0 else "greedy verify") + "; batch 1",
                    "global_batch": 1, "seq_len": L, "block": N, "launch": "graph" if graph else "eager"},
         "roofline": roof,
         "step_roofline": {"bound": "hbm", "bytes": sb["total"], "t_roof_us": round(t_roof_us, 1),

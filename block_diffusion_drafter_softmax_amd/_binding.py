@@ -35,6 +35,7 @@ KERNEL_NAMES = ["fuse", "ctx_kv", "norm", "qkv", "attn", "attn_merge", "o_proj",
 EXPORTS = [
     "dflash_workspace_bytes", "dflash_create", "dflash_destroy", "dflash_ctx_append",
     "dflash_draft_block", "dflash_verify", "dflash_d2sd_draft", "dflash_verify_multi",
+    "dflash_draft_sample", "dflash_verify_sample",
     "dflash_last_error", "dflash_read_error", "dflash_kernel_timer", "dflash_kernel_timer_read",
 ]
 
@@ -82,6 +83,9 @@ def _load():
         "dflash_verify": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, ctypes.c_float, u64, u64, vp, vp, vp, vp]),
         "dflash_d2sd_draft": (ctypes.c_int, [vp, i32, vp, vp, i32, vp, vp, vp, vp]),
         "dflash_verify_multi": (ctypes.c_int, [vp, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
+        "dflash_draft_sample": (ctypes.c_int, [vp, i32, vp, vp, ctypes.c_float, u64, u64, vp, vp, vp]),
+        "dflash_verify_sample": (ctypes.c_int, [vp, i32, vp, vp, vp, ctypes.c_float, vp, i32, u64, u64,
+                                                vp, vp, vp, vp]),
         "dflash_last_error": (ctypes.c_char_p, []),
         "dflash_read_error": (ctypes.c_int, [vp, vp, ctypes.POINTER(i32)]),
         "dflash_kernel_timer": (ctypes.c_int, [vp, i32, i32]),
@@ -145,6 +149,17 @@ def dflash_verify_multi(ctx, B, C, seq_ids, drafts, target_logits, logits_dtype,
                         commit_len, chosen, stream):
     return lib.dflash_verify_multi(ctx, B, C, seq_ids, drafts, target_logits, logits_dtype, accept_len,
                                    next_token, commit_len, chosen, stream)
+
+
+def dflash_draft_sample(ctx, B, seq_ids, anchor, temperature, seed, step, draft, draft_logits, stream):
+    return lib.dflash_draft_sample(ctx, B, seq_ids, anchor, float(temperature), seed, step, draft, draft_logits,
+                                   stream)
+
+
+def dflash_verify_sample(ctx, B, seq_ids, draft, draft_logits, draft_temperature, target_logits, logits_dtype,
+                         seed, step, accept_len, next_token, commit_len, stream):
+    return lib.dflash_verify_sample(ctx, B, seq_ids, draft, draft_logits, float(draft_temperature), target_logits,
+                                    logits_dtype, seed, step, accept_len, next_token, commit_len, stream)
 
 
 def dflash_read_error(ctx, stream):

@@ -69,6 +69,8 @@ struct Layout {
   // dual-pass drafting: second-pass sequences and input blocks, first and
   // second drafts, confidence, cut points; multi-candidate verification
   size_t d_seq, d_tok, d_draft1, d_draft2, d_conf, d_cuts, v_acc, v_next;
+  // sampled drafts: drafter rows pass, draft sampling partials
+  size_t qpart, dpart;
   size_t gpart_floats, cpart_floats;
   int n_ck, n_vchunks, n_schunks, m_max, rows_a_max;
 };
@@ -139,6 +141,8 @@ Layout make_layout(const dflash_config& c) {
   L.d_cuts = take(Bm * N * 4);
   L.v_acc = take(Bm * 4);
   L.v_next = take(Bm * 4);
+  L.qpart = take(Bm * N * L.n_vchunks * 2 * 4);
+  L.dpart = take(Bm * N * L.n_schunks * 2 * 4);
   L.total = off;
   return L;
 }
@@ -749,6 +753,80 @@ int dflash_verify(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int3
   va.seed = seed;
   va.step = step;
   va.err = ctx->kv.error_word;
+  va.inv_scale = 1.f;
+  return ctx->launch(DFLASH_K_VERIFY, stream, [&] { return dflash_launch_verify(&va, stream); });
+}
+
+int dflash_draft_sample(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor, float temperature,
+                        uint64_t seed, uint64_t step, int32_t* draft, float* draft_logits, hipStream_t stream) {
+  if (!ctx) return fail(DFLASH_ERR_INVALID_ARG, "ctx is null");
+  const dflash_config& c = ctx->c;
+  if (B < 1 || B > c.max_batch) return fail(DFLASH_ERR_INVALID_ARG, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
+  if (!seq_ids || !anchor || !draft || !draft_logits) return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(DFLASH_ERR_INVALID_ARG, "temperature must be finite and > 0");
+  const Layout& L = ctx->L;
+  int rc = draft_impl(ctx, B, seq_ids, anchor, nullptr, ctx->at<int>(L.d_draft1), nullptr, nullptr, nullptr,
+                      draft_logits, stream);
+  if (rc) return rc;
+  VerifyArgs va{};
+  va.B = B;
+  va.N = c.block_size;
+  va.V = c.vocab;
+  va.s_chunk = kSampleChunk;
+  va.s_n_chunks = L.n_schunks;
+  va.seq_ids = seq_ids;
+  va.seed = seed;
+  va.step = step;
+  va.err = ctx->kv.error_word;
+  va.inv_scale = 1.f;
+  va.qlogits = draft_logits;
+  va.inv_tau = 1.f / temperature;
+  va.dpart = ctx->at<float>(L.dpart);
+  va.draft_out = draft;
+  return ctx->launch(DFLASH_K_ARGMAX, stream, [&] { return dflash_launch_draft_sample(&va, stream); });
+}
+
+int dflash_verify_sample(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* draft,
+                         const float* draft_logits, float draft_temperature, const void* target_logits,
+                         int32_t logits_dtype, uint64_t seed, uint64_t step, int32_t* accept_len, int32_t* next_token,
+                         int32_t* commit_len, hipStream_t stream) {
+  if (!ctx) return fail(DFLASH_ERR_INVALID_ARG, "ctx is null");
+  const dflash_config& c = ctx->c;
+  if (B < 1 || B > c.max_batch) return fail(DFLASH_ERR_INVALID_ARG, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
+  if (!seq_ids || !draft || !draft_logits || !target_logits || !accept_len || !next_token)
+    return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
+  if (logits_dtype != DFLASH_DTYPE_BF16 && logits_dtype != DFLASH_DTYPE_F32)
+    return fail(DFLASH_ERR_INVALID_ARG, "logits_dtype must be DFLASH_DTYPE_BF16 or DFLASH_DTYPE_F32");
+  if (!(draft_temperature > 0.f) || !std::isfinite(draft_temperature))
+    return fail(DFLASH_ERR_INVALID_ARG, "draft_temperature must be finite and > 0");
+  const Layout& L = ctx->L;
+  VerifyArgs va{};
+  va.logits = target_logits;
+  va.dtype = logits_dtype;
+  va.B = B;
+  va.N = c.block_size;
+  va.V = c.vocab;
+  va.chunk = kVerifyChunk;
+  va.n_chunks = L.n_vchunks;
+  va.s_chunk = kSampleChunk;
+  va.s_n_chunks = L.n_schunks;
+  va.seq_ids = seq_ids;
+  va.draft = draft;
+  va.part = ctx->at<float>(L.vpart);
+  va.spart = ctx->at<float>(L.spart);
+  va.accept_len = accept_len;
+  va.next_token = next_token;
+  va.commit_len = commit_len;
+  va.temp1 = 1;
+  va.seed = seed;
+  va.step = step;
+  va.err = ctx->kv.error_word;
+  va.inv_scale = 1.f;
+  va.sampled = 1;
+  va.qlogits = draft_logits;
+  va.qpart = ctx->at<float>(L.qpart);
+  va.inv_tau = 1.f / draft_temperature;
   return ctx->launch(DFLASH_K_VERIFY, stream, [&] { return dflash_launch_verify(&va, stream); });
 }
 
@@ -786,6 +864,7 @@ int dflash_verify_multi(dflash_ctx* ctx, int32_t B, int32_t C, const int32_t* se
   va.commit_len = nullptr;
   va.temp1 = 0;
   va.err = ctx->kv.error_word;
+  va.inv_scale = 1.f;
   int rc = ctx->launch(DFLASH_K_VERIFY, stream, [&] { return dflash_launch_verify(&va, stream); });
   if (rc) return rc;
   PickArgs pa{};

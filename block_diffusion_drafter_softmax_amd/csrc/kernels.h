@@ -228,6 +228,14 @@ struct VerifyArgs {
   int temp1;
   unsigned long long seed, step;
   int32_t* err;
+  // sampled drafts (a general proposal q = softmax(z / tau) per draft row)
+  float inv_scale;         // rows pass: logits times this (1 for the target, 1/tau for the drafter)
+  int sampled;             // temperature-1 verification against the drafter's q
+  const float* qlogits;    // the drafter's logits [B][N-1][V] (fp32)
+  const float* qpart;      // rows pass over qlogits / tau: [B][N-1][n_chunks][2]
+  float inv_tau;
+  float* dpart;            // draft sampling: [B][N-1][s_n_chunks][2]
+  int* draft_out;          // draft sampling: [B][N-1]
 };
 
 // Kernel timer hook: while `start` is non-null, every single-kernel launcher
@@ -256,6 +264,7 @@ hipError_t dflash_launch_lmhead(const LmArgs* a, hipStream_t st);
 hipError_t dflash_launch_lmhead_mm(const LmArgs* a, hipStream_t st);
 hipError_t dflash_launch_argmax(const ArgmaxArgs* a, hipStream_t st);
 hipError_t dflash_launch_verify(const VerifyArgs* a, hipStream_t st);
+hipError_t dflash_launch_draft_sample(const VerifyArgs* a, hipStream_t st);
 hipError_t dflash_launch_d2sd_select(const D2sdArgs* a, hipStream_t st);
 hipError_t dflash_launch_d2sd_assemble(const D2sdArgs* a, hipStream_t st);
 hipError_t dflash_launch_pick(const PickArgs* a, hipStream_t st);

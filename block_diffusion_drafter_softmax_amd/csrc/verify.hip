@@ -1,5 +1,6 @@
 // Parallel verification of the drafted blocks against the target's logits
-// (greedy, or temperature-1 rejection sampling).
+// (greedy, or temperature-1 rejection sampling of an argmax draft or of a
+// draft sampled at temperature tau), and the sampling of such drafts.
 //
 // verify_rows_kernel streams every logit once: work item = (vocabulary chunk
 // of up to 32768 logits, block row, sequence). Greedy keeps (max, lowest
@@ -141,6 +142,10 @@ __global__ __launch_bounds__(VERIFY_THREADS) LATENCY_BOUND void verify_rows_kern
         const int k = min(base + (int)(threadIdx.x + VERIFY_THREADS * j) * 8, k1 - 8);
         load8<DTYPE>(a, row_off + k, zs[j]);
       }
+#pragma unroll
+      for (int j = 0; j < VG; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zs[j][e] *= a.inv_scale;  // 1 for the target; 1/tau for the drafter
       float m = -INFINITY;
 #pragma unroll
       for (int j = 0; j < VG; ++j) {
@@ -179,13 +184,14 @@ namespace {
 // token excluded when sampling row acc (the rejected draft token, or -1).
 struct Scan {
   int acc, next, excl;
+  float lse_p, lse_q;  // sampled drafts: log-normalisers of row acc (target, drafter / tau)
 };
 
 template <int NT>
 DEV Scan verify_scan(const VerifyArgs& a, int b) {
   __shared__ float2 parts[VERIFY_MAX_PARTS];
   __shared__ float2 rowres[32];
-  __shared__ float prob[32], unif[32];
+  __shared__ float prob[32], unif[32], qprob[32], lsep[32], lseq[32];
   __shared__ Scan out;
   const int* d = a.draft + (size_t)b * (a.N - 1);
   const int n_parts = a.N * a.n_chunks;  // <= VERIFY_MAX_PARTS (host check)
@@ -220,6 +226,15 @@ DEV Scan verify_scan(const VerifyArgs& a, int b) {
       const float zt = load_logit(a, ((size_t)b * a.N + row) * a.V + tok);
       prob[row] = expf(zt - lse);
       unif[row] = (float)(rng_word(a, a.seq_ids[b], row, 0, 0) >> 40) * 5.9604644775390625e-08f;
+      if (a.sampled) {  // the drafter's probability of its own token: q = softmax(z / tau)
+        float2 mq = make_float2(-INFINITY, 0.f);
+        const float2* qp = reinterpret_cast<const float2*>(a.qpart) + ((size_t)b * (a.N - 1) + row) * a.n_chunks;
+        for (int cc = 0; cc < a.n_chunks; ++cc) mq = ms_merge(mq, qp[cc]);
+        const float lq = mq.x + __logf(mq.y);
+        qprob[row] = expf(a.qlogits[((size_t)b * (a.N - 1) + row) * a.V + tok] * a.inv_tau - lq);
+        lsep[row] = lse;
+        lseq[row] = lq;
+      }
     }
   }
   __syncthreads();
@@ -228,10 +243,13 @@ DEV Scan verify_scan(const VerifyArgs& a, int b) {
     Scan r;
     if (!a.temp1) {
       while (acc < a.N - 1 && d[acc] == __float_as_int(rowres[acc].y)) ++acc;
-      r = Scan{acc, __float_as_int(rowres[acc].y), -1};
-    } else {
+      r = Scan{acc, __float_as_int(rowres[acc].y), -1, 0.f, 0.f};
+    } else if (!a.sampled) {
       while (acc < a.N - 1 && unif[acc] < prob[acc]) ++acc;
       r = Scan{acc, -1, acc < a.N - 1 ? d[acc] : -1};
+    } else {  // accept with probability min(1, p/q)
+      while (acc < a.N - 1 && unif[acc] * qprob[acc] < prob[acc]) ++acc;
+      r = Scan{acc, -1, -1, acc < a.N - 1 ? lsep[acc] : 0.f, acc < a.N - 1 ? lseq[acc] : 0.f};
     }
     out = r;
   }
@@ -266,12 +284,19 @@ __global__ __launch_bounds__(SCAN_THREADS) LATENCY_BOUND void verify_sample_kern
   const int k0 = c * a.s_chunk, k1 = min(a.V, k0 + a.s_chunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   ArgMax t{-INFINITY, 0x7FFFFFFF};
+  const bool residual = a.sampled && row < a.N - 1;  // max(0, p - q) of a sampled draft
+  const float* qrow = residual ? a.qlogits + ((size_t)b * (a.N - 1) + row) * a.V : nullptr;
   for (int k = k0 + threadIdx.x; k < k1; k += SCAN_THREADS) {
     if (k == excl) continue;
     const unsigned long long w = rng_word(a, seq, row, k, 1);
     const float u = ((float)(w >> 41) + 0.5f) * 1.1920928955078125e-07f;
     const float gmb = -logf(-logf(u));
-    t = am_merge(t, ArgMax{load_logit(a, row_off + k) + gmb, k});
+    float key = load_logit(a, row_off + k) + gmb;
+    if (residual) {
+      const float rw = expf(load_logit(a, row_off + k) - r.lse_p) - expf(qrow[k] * a.inv_tau - r.lse_q);
+      key = rw > 0.f ? logf(rw) + gmb : -INFINITY;
+    }
+    t = am_merge(t, ArgMax{key, k});
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) t = am_shfl(t, o);
@@ -301,12 +326,66 @@ __global__ __launch_bounds__(64) void verify_pick_kernel(VerifyArgs a) {
   if (lane == 0) a.next_token[b] = t.i;
 }
 
+// Sampled drafts: Gumbel-max over vocabulary chunk c of draft row r,
+// argmax_k (z[r, k] / tau + G_k) with noise of stream 2; the chunk's
+// (value, index) goes to dpart[b][r][c].
+__global__ __launch_bounds__(SCAN_THREADS) LATENCY_BOUND void draft_sample_kernel(VerifyArgs a) {
+  const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const int seq = a.seq_ids[b];
+  const float* zr = a.qlogits + ((size_t)b * (a.N - 1) + r) * a.V;
+  const int k0 = c * a.s_chunk, k1 = min(a.V, k0 + a.s_chunk);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  ArgMax t{-INFINITY, 0x7FFFFFFF};
+  for (int k = k0 + threadIdx.x; k < k1; k += SCAN_THREADS) {
+    const unsigned long long w = rng_word(a, seq, r, k, 2);
+    const float u = ((float)(w >> 41) + 0.5f) * 1.1920928955078125e-07f;
+    t = am_merge(t, ArgMax{zr[k] * a.inv_tau - logf(-logf(u)), k});
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) t = am_shfl(t, o);
+  __shared__ ArgMax red[SCAN_THREADS / 64];
+  if (lane == 0) red[wave] = t;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  ArgMax u = red[0];
+  for (int w = 1; w < SCAN_THREADS / 64; ++w) u = am_merge(u, red[w]);
+  *reinterpret_cast<float2*>(a.dpart + ((((size_t)b * (a.N - 1) + r) * a.s_n_chunks + c) * 2)) =
+      make_float2(u.v, __int_as_float(u.i));
+}
+
+// Draft token of (row r, sequence b): merge of the row's chunks in chunk order.
+__global__ __launch_bounds__(64) void draft_pick_kernel(VerifyArgs a) {
+  const int r = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const float2* src = reinterpret_cast<const float2*>(a.dpart) + ((size_t)b * (a.N - 1) + r) * a.s_n_chunks;
+  ArgMax t{-INFINITY, 0x7FFFFFFF};
+  for (int c = lane; c < a.s_n_chunks; c += 64) t = am_merge(t, ArgMax{src[c].x, __float_as_int(src[c].y)});
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) t = am_shfl(t, o);
+  if (lane == 0) a.draft_out[(size_t)b * (a.N - 1) + r] = t.i;
+}
+
+extern "C" hipError_t dflash_launch_draft_sample(const VerifyArgs* a, hipStream_t st) {
+  hipError_t e = launch_kernel(draft_sample_kernel, dim3(a->s_n_chunks, a->N - 1, a->B), dim3(SCAN_THREADS), 0, st, *a);
+  if (e != hipSuccess) return e;
+  return launch_kernel(draft_pick_kernel, dim3(a->N - 1, a->B), dim3(64), 0, st, *a);
+}
+
 extern "C" hipError_t dflash_launch_verify(const VerifyArgs* a, hipStream_t st) {
   const dim3 grid(a->n_chunks, a->N, a->B), block(VERIFY_THREADS);
   hipError_t e;
   if (a->dtype == DFLASH_DTYPE_F32) e = launch_kernel(verify_rows_kernel<DFLASH_DTYPE_F32>, grid, block, 0, st, *a);
   else e = launch_kernel(verify_rows_kernel<DFLASH_DTYPE_BF16>, grid, block, 0, st, *a);
   if (e != hipSuccess) return e;
+  if (a->sampled) {  // rows pass over the drafter's logits / tau: (max, sum) per row chunk into qpart
+    VerifyArgs q = *a;
+    q.logits = a->qlogits;
+    q.dtype = DFLASH_DTYPE_F32;
+    q.N = a->N - 1;
+    q.part = const_cast<float*>(a->qpart);
+    q.inv_scale = a->inv_tau;
+    e = launch_kernel(verify_rows_kernel<DFLASH_DTYPE_F32>, dim3(a->n_chunks, a->N - 1, a->B), block, 0, st, q);
+    if (e != hipSuccess) return e;
+  }
   if (!a->temp1) return launch_kernel(verify_greedy_kernel, dim3(a->B), dim3(SCAN_THREADS), 0, st, *a);
   e = launch_kernel(verify_sample_kernel, dim3(a->s_n_chunks, a->B), dim3(SCAN_THREADS), 0, st, *a);
   if (e != hipSuccess) return e;

@@ -125,6 +125,25 @@ class Drafter:
                              commit_len.data_ptr() if commit_len is not None else None, _stream(stream))
         return B.check(rc, "dflash_verify")
 
+    def draft_sample(self, seq_ids, anchor, temperature, draft, draft_logits, seed=0, step=0, stream=None):
+        """Sampled draft at `temperature`: draft int32 [B, N-1] and the
+        drafter's logits fp32 [B, N-1, V] (out; verify_sample reads them)."""
+        Bn = seq_ids.numel()
+        rc = B.dflash_draft_sample(self.handle, Bn, seq_ids.data_ptr(), anchor.data_ptr(), temperature, seed, step,
+                                   draft.data_ptr(), draft_logits.data_ptr(), _stream(stream))
+        return B.check(rc, "dflash_draft_sample")
+
+    def verify_sample(self, seq_ids, draft, draft_logits, draft_temperature, logits, accept_len, next_token,
+                      commit_len=None, seed=0, step=0, stream=None):
+        """Lossless verification of a sampled draft at target temperature 1."""
+        Bn = seq_ids.numel()
+        dt = B.DTYPE_F32 if logits.dtype == torch.float32 else B.DTYPE_BF16
+        rc = B.dflash_verify_sample(self.handle, Bn, seq_ids.data_ptr(), draft.data_ptr(), draft_logits.data_ptr(),
+                                    draft_temperature, logits.data_ptr(), dt, seed, step, accept_len.data_ptr(),
+                                    next_token.data_ptr(),
+                                    commit_len.data_ptr() if commit_len is not None else None, _stream(stream))
+        return B.check(rc, "dflash_verify_sample")
+
     def d2sd_draft(self, seq_ids, anchor, K, drafts, conf=None, cuts=None, stream=None):
         """Dual-pass drafting: drafts int32 [B, K+1, N-1] (candidate 0 = the
         first draft); conf fp32 [B, N-1] and cuts int32 [B, K] optional."""

@@ -203,6 +203,30 @@ int dflash_verify(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int3
                   uint64_t seed, uint64_t step, int32_t* accept_len, int32_t* next_token,
                   int32_t* commit_len, hipStream_t stream);
 
+/* Sampled drafting at temperature > 0 [DFLASH Methodology 2-3, with a
+ * sampled proposal]. The forward pass of dflash_draft_block, then for each
+ * draft row r (position r + 1) the token d = argmax_k (z[r,k] / temperature
+ * + G_k): a draw from q_r = softmax(z[r] / temperature), G_k Gumbel noise from
+ * Philox4x64-10 keyed by (seed; counter k, r | 2 << 32, seq, step).
+ *   draft        device int32 [B, N-1]   (out)
+ *   draft_logits device fp32 [B, N-1, V] (out, required): the drafter's
+ *                logits z, which dflash_verify_sample needs. */
+int dflash_draft_sample(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor,
+                        float temperature, uint64_t seed, uint64_t step, int32_t* draft, float* draft_logits,
+                        hipStream_t stream);
+
+/* Lossless verification of sampled drafts at target temperature 1 [DFLASH
+ * Methodology 3, key contributions]. p_r = softmax(target_logits[b, r]),
+ * q_r = softmax(draft_logits[b, r] / draft_temperature). Accept draft[a]
+ * while u_a * q_a(draft[a]) < p_a(draft[a]) (u_a as in dflash_verify); at the
+ * first rejection sample max(0, p_a - q_a) renormalised, by Gumbel-max over
+ * log(p_k - q_k) + G_k (stream 1) on the entries with p_k > q_k; if all N-1
+ * are accepted sample the bonus row N-1 from p. Outputs as dflash_verify. */
+int dflash_verify_sample(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* draft,
+                         const float* draft_logits, float draft_temperature, const void* target_logits,
+                         int32_t logits_dtype, uint64_t seed, uint64_t step, int32_t* accept_len,
+                         int32_t* next_token, int32_t* commit_len, hipStream_t stream);
+
 /* Dual-pass drafting [D2SD Methodology 1-3]. First pass as
  * dflash_draft_block; confidence of draft position j = the drafter's
  * largest softmax probability of block row j, 1 / sum_v exp(z_v - max z);
