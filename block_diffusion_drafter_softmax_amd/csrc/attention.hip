@@ -45,6 +45,7 @@
 
 namespace {
 DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
 constexpr int CH = 128;  // virtual keys per work item
 constexpr int PAGES = CH / 16;
 constexpr int MIN_WAVES = 8;  // staging waves per workgroup
@@ -92,8 +93,9 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   }
   const int b0 = blockIdx.z / splits * a.grp + c0;   // the workgroup's first block
   const int cpi = MULTI ? a.cpi : 1;
-  const int seq = clampi(a.seq_ids[b0], 0, a.max_seqs - 1);
-  const int L = clampi(a.ctx_len[seq], 0, a.max_pages_per_seq * 16);
+  const int2 pl = *reinterpret_cast<const int2*>(a.plan + 2 * b0);  // (sequence, context length)
+  const int seq = clampi(pl.x, 0, a.max_seqs - 1);
+  const int L = clampi(pl.y, 0, a.max_pages_per_seq * 16);
   const int item_begin = item * cpi * CH;
   const int item_nv = min(16 + L, item_begin + cpi * CH) - item_begin;  // virtual keys in this item
   if (item_nv <= 0) return;
@@ -323,8 +325,7 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
   const int kvh = (blockIdx.x / R) % a.n_kv;
   const int b = blockIdx.x / R / a.n_kv;
   const int dq = threadIdx.x % TPR, cg = threadIdx.x / TPR;
-  const int seq = clampi(a.seq_ids[b], 0, a.max_seqs - 1);
-  const int L = clampi(a.ctx_len[seq], 0, a.max_pages_per_seq * 16);
+  const int L = clampi(a.plan[2 * b + 1], 0, a.max_pages_per_seq * 16);
   const int nc = min(a.n_ck, (16 + L + a.cpi * CH - 1) / (a.cpi * CH));  // work items of the sequence
   const size_t unit0 = ((size_t)b * a.n_kv + kvh) * a.n_ck;
   float M = -INFINITY, den = 0.f;

@@ -71,6 +71,8 @@ struct Layout {
   size_t d_seq, d_tok, d_draft1, d_draft2, d_conf, d_cuts, v_acc, v_next;
   // sampled drafts: drafter rows pass, draft sampling partials
   size_t qpart, dpart;
+  // a draft call's plan: per block (sequence, context length), per row RoPE cos/sin
+  size_t plan, plan_rope;
   size_t gpart_floats, cpart_floats;
   int n_ck, n_vchunks, n_schunks, m_max, rows_a_max;
 };
@@ -143,6 +145,8 @@ Layout make_layout(const dflash_config& c) {
   L.v_next = take(Bm * 4);
   L.qpart = take(Bm * N * L.n_vchunks * 2 * 4);
   L.dpart = take(Bm * N * L.n_schunks * 2 * 4);
+  L.plan = take(Bm * 2 * 4);
+  L.plan_rope = take(Bm * N * (c.head_dim / 2) * 2 * 4);
   L.total = off;
   return L;
 }
@@ -525,6 +529,10 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
   na.dbg = dbg_hidden;
   na.seq_ids = seq_ids;
   na.ctx_len = ctx->kv.ctx_len;
+  na.plan = ctx->at<int>(L.plan);
+  na.plan_rope = ctx->at<float>(L.plan_rope);
+  na.rope = c.use_rope ? ctx->at<float>(L.rope) : nullptr;
+  na.half = c.head_dim / 2;
   na.max_seqs = c.max_seqs;
   na.max_pos = c.max_pos;
   na.err = ctx->kv.error_word;
@@ -540,11 +548,7 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
   qa.n_kv = c.n_kv_heads;
   qa.d = c.head_dim;
   qa.N = N;
-  qa.seq_ids = seq_ids;
-  qa.ctx_len = ctx->kv.ctx_len;
-  qa.max_seqs = c.max_seqs;
-  qa.max_pos = c.max_pos;
-  qa.rope = c.use_rope ? ctx->at<float>(L.rope) : nullptr;
+  qa.rope = c.use_rope ? na.plan_rope : nullptr;
   qa.q = ctx->at<uint16_t>(L.q);
   qa.kblk = ctx->at<uint16_t>(L.kblk);
   qa.vblk = ctx->at<uint16_t>(L.vblk);
@@ -556,6 +560,7 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
   aa.page_table = ctx->kv.page_table;
   aa.ctx_len = ctx->kv.ctx_len;
   aa.seq_ids = seq_ids;
+  aa.plan = na.plan;
   aa.part_o = ctx->at<float>(L.apo);
   aa.part_ml = ctx->at<float>(L.aml);
   aa.o = ctx->at<uint16_t>(L.o);

@@ -42,8 +42,7 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void qkv_finish_kernel(QkvFinish
     const int col = (isq ? 0 : a.n_q * d) + head * d + i;
     float x1 = split_sum(a.part, a.ks, a.M, n_cols, m, col);
     float x2 = split_sum(a.part, a.ks, a.M, n_cols, m, col + half);
-    rotate(x1, x2, a.rope, clampi(a.ctx_len[clampi(a.seq_ids[b], 0, a.max_seqs - 1)] + n, 0, a.max_pos - 1),
-           half, i);
+    rotate(x1, x2, a.rope, m, half, i);  // the call's plan holds row m's cos/sin
     if (isq) {  // query, scaled for a log2-domain softmax: split activation of the attention
       uint16_t* dst = a.q + ((size_t)m * a.n_q + head) * d;
       const size_t lo = (size_t)a.M * a.n_q * d;

@@ -78,10 +78,7 @@ struct PackArgs {
 struct QkvFinishArgs {
   const float* part;  // [ks][M][n_q*d + 2*n_kv*d]: Q columns, then block K, then block V
   int ks, M, n_q, n_kv, d, N;
-  const int* seq_ids;  // row m = b*N + n sits at position ctx_len[seq_ids[b]] + n
-  const int* ctx_len;
-  int max_seqs, max_pos;
-  const float* rope;  // [max_pos][d/2][2] or null (no rotation)
+  const float* rope;  // the call's plan: cos/sin of every row's position [M][d/2][2], or null (no rotation)
   float q_scale;      // applied to rotated queries: log2(e) / sqrt(d) (attention works in log2 units)
   uint16_t* q;        // split: hi [M][n_q][d], lo at + M*n_q*d
   uint16_t* kblk;     // [B][n_kv][16][d]
@@ -118,6 +115,7 @@ struct AttnArgs {
   int32_t* err;
   int N, n_q, n_kv, chunk, n_ck, max_pages_per_seq, n_pages, max_seqs;
   int cpi;                 // chunks of `chunk` virtual keys per work item (1 .. 8)
+  const int* plan;         // the call's plan [B][2]: sequence (clamped), context length
   int grp;                 // consecutive blocks that share one sequence's context (B % grp == 0)
   int cand;                // blocks of a group one workgroup takes (1 .. grp): a context chunk is read once for them
 };
@@ -164,6 +162,12 @@ struct NormArgs {
   float* dbg;              // nullable [M][H]
   int H, M;
   float eps;
+  // mode 0 also writes the draft call's plan, read by the later kernels in
+  // one load instead of a sequence id -> context length -> table chain
+  int* plan;               // [B][2]: sequence (clamped), context length
+  float* plan_rope;        // [M][d/2][2]: cos/sin at row m's position (when rope is set)
+  const float* rope;       // [max_pos][d/2][2] or null
+  int half;                // d/2
 };
 
 struct LmArgs {

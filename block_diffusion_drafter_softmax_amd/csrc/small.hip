@@ -195,21 +195,35 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
   float ss = 0.f;
   int tok = 0;
   if (a.mode == 0) {
-    const int b = m / a.N;
-    tok = a.tokens ? a.tokens[m] : (m % a.N == 0) ? a.anchor[b] : a.mask_id;
+    const int b = m / a.N, n = m % a.N;
+    tok = a.tokens ? a.tokens[m] : (n == 0) ? a.anchor[b] : a.mask_id;
+    const int s_raw = a.seq_ids[b];
+    const int seq = clampi(s_raw, 0, a.max_seqs - 1);
+    const int L = a.ctx_len[seq];
     if (threadIdx.x == 0) {
       int bad = (tok < 0 || tok >= a.V) ? DFLASH_DEV_BAD_TOKEN : 0;
-      if (m % a.N == 0) {
-        const int s_raw = a.seq_ids[b];
+      if (n == 0) {
         if (s_raw < 0 || s_raw >= a.max_seqs) bad |= DFLASH_DEV_BAD_SEQ;
-        const int L = a.ctx_len[clampi(s_raw, 0, a.max_seqs - 1)];
         if (L < 0 || L + a.N > a.max_pos) bad |= DFLASH_DEV_NO_PAGES;
+        a.plan[2 * b] = seq;
+        a.plan[2 * b + 1] = L;
       }
       if (bad) set_error(a.err, bad);
+    }
+    if (a.rope && (int)threadIdx.x < a.half) {  // this row's RoPE cos/sin (position L + n)
+      const int pos = clampi(L + n, 0, a.max_pos - 1);
+      const float2 cs = *reinterpret_cast<const float2*>(a.rope + ((size_t)pos * a.half + threadIdx.x) * 2);
+      *reinterpret_cast<float2*>(a.plan_rope + ((size_t)m * a.half + threadIdx.x) * 2) = cs;
     }
     tok = clampi(tok, 0, a.V - 1);
   }
   const size_t split_stride = (size_t)a.M * a.H;
+  u16x4 gv[NORM_MAXV];  // the gain, requested with the row (not after the reduction's barriers)
+#pragma unroll
+  for (int v = 0; v < NORM_MAXV; ++v) {
+    const int k = min((v * (int)blockDim.x + (int)threadIdx.x) * 4, a.H - 4);
+    gv[v] = *reinterpret_cast<const u16x4*>(a.g + k);
+  }
 #pragma unroll
   for (int v = 0; v < NORM_MAXV; ++v) {
     const int k = (v * blockDim.x + threadIdx.x) * 4;
@@ -239,10 +253,9 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
   for (int v = 0; v < NORM_MAXV; ++v) {
     const int k = (v * blockDim.x + threadIdx.x) * 4;
     if (v >= nv || k >= a.H) continue;
-    const u16x4 gv = *reinterpret_cast<const u16x4*>(a.g + k);
     f32x4 y;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = xv[v][i] * rstd * bf2f(gv[i]);
+    for (int i = 0; i < 4; ++i) y[i] = xv[v][i] * rstd * bf2f(gv[v][i]);
     u16x4 hi, lo;
     split4(y, hi, lo);
     *reinterpret_cast<u16x4*>(a.h + pk_index(m, k, a.H)) = hi;
