@@ -93,11 +93,12 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
       const int k = (v * blockDim.x + threadIdx.x) * 4;
       if (k >= a.H) continue;
 #pragma unroll
-      for (int j = 0; j < FUSE_TMAX; ++j) {
-        if (j >= a.T) break;
-        uint16_t* dst = a.f + pk_index(m, j * a.H + k, K);
-        *reinterpret_cast<u16x4*>(dst) = x[v][j];
-        *reinterpret_cast<u16x4*>(dst + plane_k) = zero;
+      for (int j = 0; j < FUSE_TMAX; ++j) {  // guarded, not `break`: the loop unrolls, x stays in registers
+        if (j < a.T) {
+          uint16_t* dst = a.f + pk_index(m, j * a.H + k, K);
+          *reinterpret_cast<u16x4*>(dst) = x[v][j];
+          *reinterpret_cast<u16x4*>(dst + plane_k) = zero;
+        }
       }
     }
     return;
