@@ -42,7 +42,8 @@ constexpr int kAttnMaxWaves = 8;    // computing waves of an attention workgroup
                                     // sequence: only the staging-only waves of an 8-wave workgroup are filled (larger
                                     // workgroups were slower: the attention is bound by its compute phase)
 constexpr int kVerifyChunk = 32768;       // logits per verification work item (rows pass)
-constexpr int kSampleChunk = 8192;        // logits per work item of the temperature-1 sampling pass
+constexpr int kSampleChunkMin = 1024;     // logits per work item of a sampling pass, at least (and a multiple of)
+constexpr int kSampleWgs = 512;           // sampling work items to aim for (a batch-1 row still fills the chip)
 constexpr int kKsMax = 8;           // largest k split of a streaming GEMM (KS_MAX in common.h)
 constexpr int kTargetWaves = 1536;  // streaming waves to aim for (~6 per CU)
 constexpr int kMmMinRows = 64;      // from this many activation rows on, GEMMs use the tiled MFMA kernels
@@ -55,6 +56,15 @@ constexpr int kMmTargetWgs = 256;   // tiled-GEMM workgroups to aim for before s
 constexpr size_t kMmPartFloats = (size_t)2 * kMmTargetWgs * kMmRows * kMmCols;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Logits per work item of a sampling pass over `rows` vocabulary rows: about
+// kSampleWgs work items, chunks a multiple of kSampleChunkMin.
+int sample_chunk(int vocab, long long rows) {
+  long long c = (long long)vocab * rows / kSampleWgs;
+  c = (c + kSampleChunkMin - 1) / kSampleChunkMin * kSampleChunkMin;
+  return (int)std::max<long long>(kSampleChunkMin, std::min<long long>(c, ((long long)vocab + kSampleChunkMin - 1) /
+                                                                            kSampleChunkMin * kSampleChunkMin));
+}
 
 // Partial top-2 per row that the LM head leaves for the argmax reduction.
 int lm_parts(int vocab, int M) { return M >= kMmMinRows ? (vocab + kMmCols - 1) / kMmCols : (vocab / 32 + 1) / 2; }
@@ -88,7 +98,7 @@ Layout make_layout(const dflash_config& c) {
   const size_t mp = pad16(L.m_max), rp = pad16(L.rows_a_max);
   L.n_ck = (16 + c.max_pages_per_seq * 16 + kAttnChunk - 1) / kAttnChunk;
   L.n_vchunks = (c.vocab + kVerifyChunk - 1) / kVerifyChunk;
-  L.n_schunks = (c.vocab + kSampleChunk - 1) / kSampleChunk;
+  L.n_schunks = (c.vocab + kSampleChunkMin - 1) / kSampleChunkMin;  // the most chunks a sampling pass uses
   const size_t ncol_d = std::max(qd + 2 * kvd, H), ncol_c = D * 2 * kvd;
   L.gpart_floats = std::max(ncol_d * std::max<size_t>(256, 2 * (size_t)L.m_max), kMmPartFloats);
   L.cpart_floats = std::max(ncol_c * std::max<size_t>(256, 2 * (size_t)L.rows_a_max), kMmPartFloats);
@@ -745,8 +755,8 @@ int dflash_verify(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int3
   va.V = c.vocab;
   va.chunk = kVerifyChunk;
   va.n_chunks = L.n_vchunks;
-  va.s_chunk = kSampleChunk;
-  va.s_n_chunks = L.n_schunks;
+  va.s_chunk = sample_chunk(c.vocab, (long long)B);
+  va.s_n_chunks = (c.vocab + va.s_chunk - 1) / va.s_chunk;
   va.seq_ids = seq_ids;
   va.draft = draft;
   va.part = ctx->at<float>(L.vpart);
@@ -778,8 +788,8 @@ int dflash_draft_sample(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, cons
   va.B = B;
   va.N = c.block_size;
   va.V = c.vocab;
-  va.s_chunk = kSampleChunk;
-  va.s_n_chunks = L.n_schunks;
+  va.s_chunk = sample_chunk(c.vocab, (long long)B * (c.block_size - 1));
+  va.s_n_chunks = (c.vocab + va.s_chunk - 1) / va.s_chunk;
   va.seq_ids = seq_ids;
   va.seed = seed;
   va.step = step;
@@ -814,8 +824,8 @@ int dflash_verify_sample(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, con
   va.V = c.vocab;
   va.chunk = kVerifyChunk;
   va.n_chunks = L.n_vchunks;
-  va.s_chunk = kSampleChunk;
-  va.s_n_chunks = L.n_schunks;
+  va.s_chunk = sample_chunk(c.vocab, (long long)B);
+  va.s_n_chunks = (c.vocab + va.s_chunk - 1) / va.s_chunk;
   va.seq_ids = seq_ids;
   va.draft = draft;
   va.part = ctx->at<float>(L.vpart);
@@ -858,8 +868,8 @@ int dflash_verify_multi(dflash_ctx* ctx, int32_t B, int32_t C, const int32_t* se
   va.V = c.vocab;
   va.chunk = kVerifyChunk;
   va.n_chunks = L.n_vchunks;
-  va.s_chunk = kSampleChunk;
-  va.s_n_chunks = L.n_schunks;
+  va.s_chunk = sample_chunk(c.vocab, (long long)B * C);
+  va.s_n_chunks = (c.vocab + va.s_chunk - 1) / va.s_chunk;
   va.seq_ids = seq_ids;
   va.draft = drafts;
   va.part = ctx->at<float>(L.vpart);

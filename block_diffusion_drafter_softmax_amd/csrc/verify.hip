@@ -327,19 +327,27 @@ __global__ __launch_bounds__(64) void verify_pick_kernel(VerifyArgs a) {
 }
 
 // Sampled drafts: Gumbel-max over vocabulary chunk c of draft row r,
-// argmax_k (z[r, k] / tau + G_k) with noise of stream 2; the chunk's
-// (value, index) goes to dpart[b][r][c].
+// argmax_k (z[r, k] / tau + G_k) with noise of stream 2: one Philox block
+// at counter (k / 4, r | 2 << 32, seq, step) serves entries k .. k+3, word
+// j for entry k + j. The chunk's (value, index) goes to dpart[b][r][c].
 __global__ __launch_bounds__(SCAN_THREADS) LATENCY_BOUND void draft_sample_kernel(VerifyArgs a) {
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const int seq = a.seq_ids[b];
   const float* zr = a.qlogits + ((size_t)b * (a.N - 1) + r) * a.V;
-  const int k0 = c * a.s_chunk, k1 = min(a.V, k0 + a.s_chunk);
+  const int k0 = c * a.s_chunk, k1 = min(a.V, k0 + a.s_chunk);  // multiples of 4
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   ArgMax t{-INFINITY, 0x7FFFFFFF};
-  for (int k = k0 + threadIdx.x; k < k1; k += SCAN_THREADS) {
-    const unsigned long long w = rng_word(a, seq, r, k, 2);
-    const float u = ((float)(w >> 41) + 0.5f) * 1.1920928955078125e-07f;
-    t = am_merge(t, ArgMax{zr[k] * a.inv_tau - logf(-logf(u)), k});
+  for (int k = k0 + 4 * (int)threadIdx.x; k < k1; k += 4 * SCAN_THREADS) {
+    unsigned long long w[4] = {(unsigned long long)(unsigned)(k >> 2),
+                               (unsigned long long)(unsigned)r | (2ull << 32),
+                               (unsigned long long)(unsigned)seq, a.step};
+    philox4x64_10(w, a.seed, 0ull);
+    const f32x4 z = *reinterpret_cast<const f32x4*>(zr + k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float u = ((float)(w[e] >> 41) + 0.5f) * 1.1920928955078125e-07f;
+      t = am_merge(t, ArgMax{z[e] * a.inv_tau - logf(-logf(u)), k + e});
+    }
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) t = am_shfl(t, o);

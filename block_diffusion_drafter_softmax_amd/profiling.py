@@ -4,7 +4,7 @@
 device-to-device copy of 256 MiB three times: the reference workload whose
 FETCH_SIZE / WRITE_SIZE readings calibrate the HBM traffic counters.
 
-``... profiling stats <kernel_stats.csv> <out.md> <command> [<kernel_trace.csv> [<skip_last>]]`` and
+``... profiling stats <kernel_stats.csv> <out.md> <command> [<kernel_trace.csv> [<skip_last> [<step-end kernel>]]]`` and
 ``... profiling traffic <kernel regex> <fetch.csv> <write.csv> <copy_fetch.csv>
 <copy_write.csv> <out.json> <out.md> <commands...>`` turn rocprofv3 CSV output
 into the short text summaries kept with the sources.
@@ -65,7 +65,7 @@ def copy_factor(path, counter):
     return (COPY_BYTES / 1024) / counted_kib, counted_kib
 
 
-def write_stats(stats_csv, out_md, command, trace_csv=None, skip_last=0, top=24):
+def write_stats(stats_csv, out_md, command, trace_csv=None, skip_last=0, last_kernel="verify_rows", top=24):
     rows = _rows(stats_csv)
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     lines = ["# Kernel time, rocprofv3 --kernel-trace --stats", "", "Command:", "", "```", command, "```", "",
@@ -78,7 +78,8 @@ def write_stats(stats_csv, out_md, command, trace_csv=None, skip_last=0, top=24)
                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
     if trace_csv:
-        lines += ["", "## One decode step", ""] + step_breakdown(trace_csv, skip_last=skip_last)
+        lines += ["", "## One decode step", ""] + step_breakdown(trace_csv, last_kernel=last_kernel,
+                                                                 skip_last=skip_last)
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -91,7 +92,7 @@ def step_breakdown(trace_csv, last_kernel="verify_rows", steps=10, skip_last=0):
     are listed as its second pass."""
     rows = _rows(trace_csv)
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    ends = [i for i, r in enumerate(rows) if r["Kernel_Name"].startswith("void " + last_kernel)]
+    ends = [i for i, r in enumerate(rows) if r["Kernel_Name"].replace("void ", "", 1).startswith(last_kernel)]
     if skip_last:
         ends = ends[:-skip_last]
     steps = min(steps, len(ends) - 1)
@@ -157,7 +158,7 @@ def main(argv):
         copy_probe()
     elif argv[0] == "stats":
         write_stats(argv[1], argv[2], argv[3], argv[4] if len(argv) > 4 else None,
-                    int(argv[5]) if len(argv) > 5 else 0)
+                    int(argv[5]) if len(argv) > 5 else 0, argv[6] if len(argv) > 6 else "verify_rows")
     elif argv[0] == "traffic":
         print(json.dumps(write_traffic(*argv[1:8], argv[8:])))
     else:

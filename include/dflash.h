@@ -207,7 +207,8 @@ int dflash_verify(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int3
  * sampled proposal]. The forward pass of dflash_draft_block, then for each
  * draft row r (position r + 1) the token d = argmax_k (z[r,k] / temperature
  * + G_k): a draw from q_r = softmax(z[r] / temperature), G_k Gumbel noise from
- * Philox4x64-10 keyed by (seed; counter k, r | 2 << 32, seq, step).
+ * Philox4x64-10 keyed by (seed; counter k / 4, r | 2 << 32, seq, step),
+ * word k % 4.
  *   draft        device int32 [B, N-1]   (out)
  *   draft_logits device fp32 [B, N-1, V] (out, required): the drafter's
  *                logits z, which dflash_verify_sample needs. */

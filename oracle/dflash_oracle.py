@@ -73,7 +73,7 @@ __all__ = [
     "verify_greedy", "verify_temp1", "philox4x64_10", "philox4x64_10_vec",
     "rng_uniform", "rng_gumbel_row", "draft_confidence", "d2sd_cut_points",
     "d2sd_candidate_tokens", "d2sd_candidates", "verify_greedy_multi",
-    "draft_sample", "verify_sampled",
+    "draft_sample", "verify_sampled", "rng_gumbel_row_words",
 ]
 
 
@@ -575,6 +575,21 @@ def verify_temp1(draft, z, seed, step, seq):
     return a, nxt, a + 1, info
 
 
+def rng_gumbel_row_words(seed, step, seq, row, vocab, stream=2):
+    """Standard Gumbel noise for every k < vocab of one row, float32, from all
+    four Philox words: entry k takes word k % 4 of the block at counter
+    (k // 4, row | stream << 32, seq, step); u' and G as in rng_gumbel_row.
+    The sampled draft's noise (stream 2)."""
+    n4 = (vocab + 3) // 4
+    k4 = np.arange(n4, dtype=np.uint64)
+    c1 = np.uint64((int(row) & 0xFFFFFFFF) | (int(stream) << 32))
+    words = philox4x64_10_vec(k4, c1, np.uint64(seq), np.uint64(step), seed, 0)
+    w = np.stack(words, axis=1).reshape(-1)[:vocab]  # entry 4i + j <- word j of block i
+    u = ((w >> np.uint64(41)).astype(np.float64) + 0.5) * 2.0 ** -23
+    u = u.astype(np.float32)
+    return (-np.log(-np.log(u))).astype(np.float32)
+
+
 # ------------------------------------------ sampled drafts (temperature tau)
 def _row_lse(z):
     z = np.asarray(z, dtype=np.float64)
@@ -588,15 +603,16 @@ def draft_sample(z, tau, seed, step, seq):
     z [N-1, V]: the drafter's logits of block rows 1 .. N-1 (LM-head row r
     gives draft position r + 1). Its proposal for that position is
     q_r = softmax(z[r] / tau); the token is drawn by Gumbel-max,
-    argmax_k (z[r, k] / tau + G_k), in float32 with Gumbel noise of stream 2,
-    lowest index on ties. Returns (draft [N-1], key top-2 gap per row).
+    argmax_k (z[r, k] / tau + G_k), in float32 with the Gumbel noise of
+    rng_gumbel_row_words (stream 2), lowest index on ties. Returns
+    (draft [N-1], key top-2 gap per row).
     """
     z = np.asarray(z, dtype=np.float64)
     n_rows, vocab = z.shape
     draft = np.zeros(n_rows, dtype=np.int64)
     gaps = np.zeros(n_rows)
     for r in range(n_rows):
-        key = z[r].astype(np.float32) / np.float32(tau) + rng_gumbel_row(seed, step, seq, r, vocab, stream=2)
+        key = z[r].astype(np.float32) / np.float32(tau) + rng_gumbel_row_words(seed, step, seq, r, vocab, stream=2)
         draft[r] = int(argmax_first(key))
         gaps[r] = float(top2_gap(key.astype(np.float64)))
     return draft, gaps

@@ -596,13 +596,24 @@ def test_sampled_draft_follows_softmax_over_tau_chi_square():
 
 
 def test_sampled_draft_uses_its_own_noise_stream():
-    # the draft's Gumbel noise (stream 2) is not the verification's (stream 1)
+    # the draft's Gumbel noise (stream 2, all four words of each Philox block)
+    # is not the verification's (stream 1, word 0 of one block per entry)
     g1 = O.rng_gumbel_row(7, 0, 0, 0, 64, stream=1)
-    g2 = O.rng_gumbel_row(7, 0, 0, 0, 64, stream=2)
+    g2 = O.rng_gumbel_row_words(7, 0, 0, 0, 64, stream=2)
     assert not np.array_equal(g1, g2)
     z = np.zeros((1, 64))
     d, _ = O.draft_sample(z, 1.0, seed=7, step=0, seq=0)
     assert d[0] == int(np.argmax(g2))
+
+
+def test_four_word_gumbel_noise_against_scalar_philox():
+    # entry k is word k % 4 of the scalar generator's block at counter k // 4
+    seed, step, seq, row, V = 11, 3, 5, 2, 22
+    g = O.rng_gumbel_row_words(seed, step, seq, row, V, stream=2)
+    for k in range(V):
+        w = O.philox4x64_10((k // 4, row | (2 << 32), seq, step), (seed, 0))[k % 4]
+        u = np.float32((float(w >> 41) + 0.5) * 2.0 ** -23)
+        assert g[k] == np.float32(-np.log(-np.log(u))), k
 
 
 def test_sampled_verify_with_one_hot_proposal_is_the_temp1_rule():
