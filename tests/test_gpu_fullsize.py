@@ -2,7 +2,8 @@
 benchmark times (one decode step after a prefill), against the oracle.
 
 * Qwen3-8B-shaped DFLARE drafter (T=9, 7 layers, context 4096, block 16,
-  batch 1, 8 appended rows, greedy verify): every output.
+  batch 1, 8 appended rows, greedy verify): every output; then drafts
+  sampled at temperature 1 and their lossless verification.
 * Qwen3-4B-shaped DFlash-style drafter (tied context/block K/V, T=5,
   context 2048): every output; the same with DFlash's FC fusion.
 * GPT-OSS-20B-shaped drafter (d_h 64, GQA 8:1, V 201088, batch 8, context
@@ -16,6 +17,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle as O
 from _cases import Case, FLOAT_TOL, say, nan_free
 from block_diffusion_drafter_softmax_amd import synth
 from test_gpu_parity import check_verify_greedy
@@ -50,7 +52,20 @@ def full_step(case, verify=True):
 @pytest.mark.timeout(1200)
 def test_qwen3_8b_full_step():
     cfg = synth.config("qwen3_8b")
-    full_step(Case(cfg, ctx=[cfg["context"]], n_new=[cfg["n_new"]], prefill_chunk=512, seq_offset=0))
+    case = Case(cfg, ctx=[cfg["context"]], n_new=[cfg["n_new"]], prefill_chunk=512, seq_offset=0)
+    _, orc = full_step(case)
+    # the same step with drafts sampled at temperature 1 and the lossless
+    # verification, on the oracle's logits of this step
+    from test_gpu_sampled import check_sampled_draft, check_sampled_verify
+    check_sampled_draft(case, 1.0, seed=5, step=9, orc=orc)
+    zq = np.stack([o["logits"] for o in orc])
+    draft = np.stack([O.draft_sample(o["logits"], 1.0, 5, 9, case.seq_ids[b])[0] for b, o in enumerate(orc)])
+    bits = synth.make_logits(cfg, draft, 7)
+    logits_dev = torch.from_numpy(bits.view(np.int16)).to(case.dev).view(torch.bfloat16)
+    comp, exc = check_sampled_verify(case, draft, zq, 1.0, O.bf16_bits_to_f64(bits), logits_dev,
+                                     [(s, 9) for s in range(8)])
+    say(f"  sampled verify: compared {comp}, excluded {exc}")
+    assert comp >= 4
 
 
 @pytest.mark.timeout(1200)
