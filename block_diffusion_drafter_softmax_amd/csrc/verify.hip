@@ -8,7 +8,8 @@
 // merges each row's chunks in chunk order and runs the accept scan
 // (verify_greedy_kernel, one workgroup per sequence). Temperature 1 also
 // samples from one row: verify_sample_kernel repeats the scan in every
-// work item (vocabulary chunk of 8192, sequence) -- it is a few dozen
+// work item (vocabulary chunk, sequence; chunks sized per call so that a
+// batch-1 row still spreads over ~512 work items) -- it is a few dozen
 // loads -- and takes a Gumbel-max over its chunk with a counter-based
 // Philox4x64-10 draw per vocabulary entry, which gives the same sample
 // whatever the order; verify_pick_kernel merges the chunks. Kernel
