@@ -16,6 +16,28 @@ def _stream(stream):
     return s.cuda_stream
 
 
+def _need(name, t, shape, dtypes, optional=False):
+    """The library cannot see a buffer's size: a tensor handed to it must be a
+    contiguous device tensor of exactly the documented shape and dtype.
+    `shape` entries of None match any extent (at least 1)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if t.dim() != len(shape) or any(e is not None and e != g for e, g in zip(shape, t.shape)) or \
+            any(g < 1 for g in t.shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+I32, F32, BF16, LOGITS = (torch.int32,), (torch.float32,), (torch.bfloat16,), (torch.float32, torch.bfloat16)
+
+
 def _bits_to_bf16(a, device):
     """uint16 bf16 bit patterns (numpy) -> torch.bfloat16 device tensor."""
     t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
@@ -101,16 +123,31 @@ class Drafter:
             self.w.pop(k, None)
 
     # ---------------------------------------------------------------- calls
+    def _dims(self):
+        c = self.cfg
+        return c["block_size"], c["vocab"], c["hidden"], c["n_layers"], c["n_target_layers"]
+
     def ctx_append(self, seq_ids, n_new, hidden, max_new=None, stream=None):
         """hidden: bf16 tensor [B, max_new, T, H]; seq_ids, n_new: int32 [B]."""
         Bn = seq_ids.numel()
         max_new = max_new or hidden.shape[1]
+        N, V, H, D, T = self._dims()
+        _need("seq_ids", seq_ids, (Bn,), I32)
+        _need("n_new", n_new, (Bn,), I32)
+        _need("hidden", hidden, (Bn, max_new, T, H), BF16)
         rc = B.dflash_ctx_append(self.handle, Bn, seq_ids.data_ptr(), n_new.data_ptr(), hidden.data_ptr(),
                                  max_new, _stream(stream))
         return B.check(rc, "dflash_ctx_append")
 
     def draft_block(self, seq_ids, anchor, draft, gap=None, dbg_hidden=None, dbg_logits=None, stream=None):
         Bn = seq_ids.numel()
+        N, V, H, D, T = self._dims()
+        _need("seq_ids", seq_ids, (Bn,), I32)
+        _need("anchor", anchor, (Bn,), I32)
+        _need("draft", draft, (Bn, N - 1), I32)
+        _need("gap", gap, (Bn, N - 1), F32, optional=True)
+        _need("dbg_hidden", dbg_hidden, (D + 1, Bn, N, H), F32, optional=True)
+        _need("dbg_logits", dbg_logits, (Bn, N - 1, V), F32, optional=True)
         p = lambda t: t.data_ptr() if t is not None else None
         rc = B.dflash_draft_block(self.handle, Bn, seq_ids.data_ptr(), anchor.data_ptr(), draft.data_ptr(),
                                   p(gap), p(dbg_hidden), p(dbg_logits), _stream(stream))
@@ -119,6 +156,13 @@ class Drafter:
     def verify(self, seq_ids, draft, logits, accept_len, next_token, commit_len=None, temperature=0.0,
                seed=0, step=0, stream=None):
         Bn = seq_ids.numel()
+        N, V, H, D, T = self._dims()
+        _need("seq_ids", seq_ids, (Bn,), I32)
+        _need("draft", draft, (Bn, N - 1), I32)
+        _need("logits", logits, (Bn, N, V), LOGITS)
+        for name, t in (("accept_len", accept_len), ("next_token", next_token)):
+            _need(name, t, (Bn,), I32)
+        _need("commit_len", commit_len, (Bn,), I32, optional=True)
         dt = B.DTYPE_F32 if logits.dtype == torch.float32 else B.DTYPE_BF16
         rc = B.dflash_verify(self.handle, Bn, seq_ids.data_ptr(), draft.data_ptr(), logits.data_ptr(), dt,
                              temperature, seed, step, accept_len.data_ptr(), next_token.data_ptr(),
@@ -129,6 +173,11 @@ class Drafter:
         """Sampled draft at `temperature`: draft int32 [B, N-1] and the
         drafter's logits fp32 [B, N-1, V] (out; verify_sample reads them)."""
         Bn = seq_ids.numel()
+        N, V, H, D, T = self._dims()
+        _need("seq_ids", seq_ids, (Bn,), I32)
+        _need("anchor", anchor, (Bn,), I32)
+        _need("draft", draft, (Bn, N - 1), I32)
+        _need("draft_logits", draft_logits, (Bn, N - 1, V), F32)
         rc = B.dflash_draft_sample(self.handle, Bn, seq_ids.data_ptr(), anchor.data_ptr(), temperature, seed, step,
                                    draft.data_ptr(), draft_logits.data_ptr(), _stream(stream))
         return B.check(rc, "dflash_draft_sample")
@@ -137,6 +186,14 @@ class Drafter:
                       commit_len=None, seed=0, step=0, stream=None):
         """Lossless verification of a sampled draft at target temperature 1."""
         Bn = seq_ids.numel()
+        N, V, H, D, T = self._dims()
+        _need("seq_ids", seq_ids, (Bn,), I32)
+        _need("draft", draft, (Bn, N - 1), I32)
+        _need("draft_logits", draft_logits, (Bn, N - 1, V), F32)
+        _need("logits", logits, (Bn, N, V), LOGITS)
+        for name, t in (("accept_len", accept_len), ("next_token", next_token)):
+            _need(name, t, (Bn,), I32)
+        _need("commit_len", commit_len, (Bn,), I32, optional=True)
         dt = B.DTYPE_F32 if logits.dtype == torch.float32 else B.DTYPE_BF16
         rc = B.dflash_verify_sample(self.handle, Bn, seq_ids.data_ptr(), draft.data_ptr(), draft_logits.data_ptr(),
                                     draft_temperature, logits.data_ptr(), dt, seed, step, accept_len.data_ptr(),
@@ -148,6 +205,12 @@ class Drafter:
         """Dual-pass drafting: drafts int32 [B, K+1, N-1] (candidate 0 = the
         first draft); conf fp32 [B, N-1] and cuts int32 [B, K] optional."""
         Bn = seq_ids.numel()
+        N, V, H, D, T = self._dims()
+        _need("seq_ids", seq_ids, (Bn,), I32)
+        _need("anchor", anchor, (Bn,), I32)
+        _need("drafts", drafts, (Bn, K + 1, N - 1), I32)
+        _need("conf", conf, (Bn, N - 1), F32, optional=True)
+        _need("cuts", cuts, (Bn, K), I32, optional=True)
         p = lambda t: t.data_ptr() if t is not None else None
         rc = B.dflash_d2sd_draft(self.handle, Bn, seq_ids.data_ptr(), anchor.data_ptr(), K, drafts.data_ptr(),
                                  p(conf), p(cuts), _stream(stream))
@@ -158,6 +221,14 @@ class Drafter:
         """Greedy verification of C candidates per sequence: drafts [B, C, N-1],
         logits [B, C, N, V]; the longest accept wins (lowest index on ties)."""
         Bn, C = drafts.shape[0], drafts.shape[1]
+        N, V, H, D, T = self._dims()
+        _need("seq_ids", seq_ids, (Bn,), I32)
+        _need("drafts", drafts, (Bn, C, N - 1), I32)
+        _need("logits", logits, (Bn, C, N, V), LOGITS)
+        for name, t in (("accept_len", accept_len), ("next_token", next_token)):
+            _need(name, t, (Bn,), I32)
+        for name, t in (("commit_len", commit_len), ("chosen", chosen)):
+            _need(name, t, (Bn,), I32, optional=True)
         dt = B.DTYPE_F32 if logits.dtype == torch.float32 else B.DTYPE_BF16
         p = lambda t: t.data_ptr() if t is not None else None
         rc = B.dflash_verify_multi(self.handle, Bn, C, seq_ids.data_ptr(), drafts.data_ptr(), logits.data_ptr(), dt,

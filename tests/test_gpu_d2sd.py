@@ -95,6 +95,7 @@ def check_verify_multi(case, orc, K):
     else:
         zt = torch.from_numpy(z.view(np.int16)).to(dev).view(torch.bfloat16)
         zf = O.bf16_bits_to_f64(z)
+    zt = zt.view(Bn, C, cfg["block_size"], -1)                              # [B, C, N, V]
     acc, nxt, com, cho = (torch.full((Bn,), -1, dtype=torch.int32, device=dev) for _ in range(4))
     case.dr.verify_multi(case.t_i32(case.seq_ids), torch.from_numpy(d_or).to(dev), zt, acc, nxt, com, cho)
     torch.cuda.synchronize()
@@ -155,7 +156,7 @@ def test_d2sd_rejects_bad_arguments_and_times_its_kernels():
     with pytest.raises(B.DFlashError, match="max_batch"):
         case.dr.d2sd_draft(seq, anchor, 4, d)          # 4 second-pass blocks > max_batch 3
     with pytest.raises(B.DFlashError, match="K=0"):
-        case.dr.d2sd_draft(seq, anchor, 0, d)
+        case.dr.d2sd_draft(seq, anchor, 0, torch.zeros((1, 1, N - 1), dtype=torch.int32, device=dev))
     logits = torch.zeros((1, 4, N, cfg["vocab"]), dtype=torch.float32, device=dev)
     one = torch.zeros(1, dtype=torch.int32, device=dev)
     with pytest.raises(B.DFlashError, match="max_batch"):

@@ -292,6 +292,19 @@ def test_host_validation_enqueues_nothing():
                   case.t_i32([0]), case.t_i32([0]), temperature=0.5)
     assert "temperature" in B.last_error()
     hid = torch.zeros((1, 16, cfg["n_target_layers"], cfg["hidden"]), dtype=torch.bfloat16, device=case.dev)
-    with pytest.raises(B.DFlashError):
-        dr.ctx_append(case.t_i32([1]), case.t_i32([1]), hid, 10 ** 4)
+    # straight through the C ABI (the binding would refuse the buffer's shape first)
+    seq1, one = case.t_i32([1]), case.t_i32([1])
+    rc = B.dflash_ctx_append(dr.handle, 1, seq1.data_ptr(), one.data_ptr(), hid.data_ptr(), 10 ** 4,
+                             torch.cuda.current_stream().cuda_stream)
+    assert rc < 0 and "max_new" in B.last_error()
+    assert int(dr.ctx_len.sum()) == 0
+    # the binding refuses tensors whose shape, dtype or device the library cannot check
+    with pytest.raises(ValueError, match="hidden"):
+        dr.ctx_append(seq1, one, hid[:, :8], 16)
+    with pytest.raises(ValueError, match="draft"):
+        dr.draft_block(seq1, one, torch.zeros((1, 3), dtype=torch.int32, device=case.dev))
+    with pytest.raises(ValueError, match="logits"):
+        dr.verify(seq1, case.t_i32(np.zeros((1, 7))), torch.zeros((1, 8, 100), device=case.dev), one, one)
+    with pytest.raises(ValueError, match="device"):
+        dr.verify(seq1, case.t_i32(np.zeros((1, 7))), torch.zeros((1, 8, cfg["vocab"])), one, one)
     assert int(dr.ctx_len.sum()) == 0
