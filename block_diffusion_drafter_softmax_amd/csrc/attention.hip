@@ -327,32 +327,39 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
   const int dq = threadIdx.x % TPR, cg = threadIdx.x / TPR;
   const size_t unit0 = ((size_t)b * a.n_kv + kvh) * a.n_ck;
   constexpr int GRP = 8;  // loads in flight per thread (more costs time on gfx950)
-  // The first batch is requested before the sequence's item count is known
-  // (every slot below n_ck is in the buffer; slots past the sequence's items
-  // are dropped unread), so the plan load does not delay it.
+  // One chunk per item (small batches): the first batch is requested before
+  // the sequence's item count is known (every slot below n_ck is in the
+  // buffer; slots past the sequence's items are dropped unread), so the plan
+  // load does not delay it. With several chunks per item the sequence's
+  // items are far fewer than n_ck: there the batch waits for the count.
+  const bool spec = a.cpi == 1;
   float2 ml0[GRP];
   f32x4 ov0[GRP];
+  if (spec) {
 #pragma unroll
-  for (int j = 0; j < GRP; ++j) {
-    const size_t row = (unit0 + min(cg + j * CG, a.n_ck - 1)) * R + r;
-    ml0[j] = *reinterpret_cast<const float2*>(a.part_ml + row * 2);
-    ov0[j] = *reinterpret_cast<const f32x4*>(a.part_o + row * D + dq * 4);
+    for (int j = 0; j < GRP; ++j) {
+      const size_t row = (unit0 + min(cg + j * CG, a.n_ck - 1)) * R + r;
+      ml0[j] = *reinterpret_cast<const float2*>(a.part_ml + row * 2);
+      ov0[j] = *reinterpret_cast<const f32x4*>(a.part_o + row * D + dq * 4);
+    }
   }
   const int L = clampi(a.plan[2 * b + 1], 0, a.max_pages_per_seq * 16);
   const int nc = min(a.n_ck, (16 + L + a.cpi * CH - 1) / (a.cpi * CH));  // work items of the sequence
   float M = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  if (spec) {
 #pragma unroll
-  for (int j = 0; j < GRP; ++j) {
-    if (cg + j * CG < nc) {
-      const float Mn = fmaxf(M, ml0[j].x);
-      const float wo = exp2f(M - Mn), wn = exp2f(ml0[j].x - Mn);
-      den = den * wo + ml0[j].y * wn;
-      num = num * wo + ov0[j] * wn;
-      M = Mn;
+    for (int j = 0; j < GRP; ++j) {
+      if (cg + j * CG < nc) {
+        const float Mn = fmaxf(M, ml0[j].x);
+        const float wo = exp2f(M - Mn), wn = exp2f(ml0[j].x - Mn);
+        den = den * wo + ml0[j].y * wn;
+        num = num * wo + ov0[j] * wn;
+        M = Mn;
+      }
     }
   }
-  for (int c0 = cg + GRP * CG; c0 < nc; c0 += GRP * CG) {
+  for (int c0 = cg + (spec ? GRP * CG : 0); c0 < nc; c0 += GRP * CG) {
     float2 ml[GRP];
     f32x4 ov[GRP];
 #pragma unroll

@@ -83,6 +83,8 @@ struct Layout {
   size_t qpart, dpart;
   // a draft call's plan: per block (sequence, context length), per row RoPE cos/sin
   size_t plan, plan_rope;
+  // compacted LM-head rows of a dual-pass second pass: block row of each, count
+  size_t lm_inv, lm_count;
   size_t gpart_floats, cpart_floats;
   int n_ck, n_vchunks, n_schunks, m_max, rows_a_max;
 };
@@ -157,6 +159,8 @@ Layout make_layout(const dflash_config& c) {
   L.dpart = take(Bm * N * L.n_schunks * 2 * 4);
   L.plan = take(Bm * 2 * 4);
   L.plan_rope = take(Bm * N * (c.head_dim / 2) * 2 * 4);
+  L.lm_inv = take(Bm * N * 4);
+  L.lm_count = take(4);
   L.total = off;
   return L;
 }
@@ -509,9 +513,12 @@ namespace {
 // or `tokens` [B][N] when given (the dual-pass drafter's second pass). Each
 // run of `grp` consecutive blocks belongs to one sequence (B % grp == 0), so
 // the attention reads that sequence's context once for several blocks.
+// `row_cut` [B] (device, nullable): block b needs draft positions
+// row_cut[b] .. N-1 only (a dual-pass candidate keeps the first draft before
+// its cut), so the LM head runs on those rows alone, compacted.
 int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor, const int32_t* tokens,
                int32_t* draft, float* top2_gap, float* conf, float* dbg_hidden, float* dbg_logits,
-               hipStream_t stream, int grp = 1) {
+               hipStream_t stream, int grp = 1, const int32_t* row_cut = nullptr) {
   const dflash_config& c = ctx->c;
   const Layout& L = ctx->L;
   const int N = c.block_size, M = B * N;
@@ -653,6 +660,11 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
     na.mode = 1;
     na.g = (i + 1 < D) ? ctx->w.g_attn + (size_t)(i + 1) * H : ctx->w.g_final;
     na.dbg = dbg_hidden ? dbg_hidden + (size_t)(i + 1) * M * H : nullptr;
+    if (i + 1 == D && row_cut) {  // the LM head's input: the needed rows, compacted
+      na.row_cut = row_cut;
+      na.row_inv = ctx->at<int>(L.lm_inv);
+      na.row_count = ctx->at<int>(L.lm_count);
+    }
     if ((rc = ctx->launch(DFLASH_K_NORM, stream, [&] { return dflash_launch_norm(&na, stream); }))) return rc;
   }
 
@@ -664,7 +676,8 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
   la.V = c.vocab;
   la.N = N;
   la.part = ctx->at<Top2>(L.lmpart);
-  la.dbg_logits = dbg_logits;
+  la.dbg_logits = row_cut ? nullptr : dbg_logits;
+  la.row_count = row_cut ? na.row_count : nullptr;
   if ((rc = ctx->launch(DFLASH_K_LM_HEAD, stream, [&] {
          return M >= kMmMinRows ? dflash_launch_lmhead_mm(&la, stream) : dflash_launch_lmhead(&la, stream);
        })))
@@ -680,6 +693,8 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
   ma.gap = top2_gap;
   ma.conf = conf;
   ma.err = ctx->kv.error_word;
+  ma.row_inv = row_cut ? na.row_inv : nullptr;
+  ma.row_count = row_cut ? na.row_count : nullptr;
   return ctx->launch(DFLASH_K_ARGMAX, stream, [&] { return dflash_launch_argmax(&ma, stream); });
 }
 
@@ -729,7 +744,7 @@ int dflash_d2sd_draft(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
   if (rc) return rc;
   if ((rc = ctx->launch(DFLASH_K_D2SD, stream, [&] { return dflash_launch_d2sd_select(&da, stream); }))) return rc;
   if ((rc = draft_impl(ctx, B * K, da.seq2, nullptr, da.tokens, ctx->at<int>(L.d_draft2), nullptr, nullptr, nullptr,
-                       nullptr, stream, K)))
+                       nullptr, stream, K, da.cuts)))
     return rc;
   return ctx->launch(DFLASH_K_D2SD, stream, [&] { return dflash_launch_d2sd_assemble(&da, stream); });
 }

@@ -168,6 +168,12 @@ struct NormArgs {
   float* plan_rope;        // [M][d/2][2]: cos/sin at row m's position (when rope is set)
   const float* rope;       // [max_pos][d/2][2] or null
   int half;                // d/2
+  // Rows the LM head needs (the dual-pass drafter's second pass): block b
+  // keeps rows n >= row_cut[b]; those rows are written compacted, in block
+  // order, with row_inv[compact] = m and the number of rows in *row_count.
+  const int* row_cut;      // nullable [M/N]
+  int* row_inv;            // [M]
+  int* row_count;          // [1]
 };
 
 struct LmArgs {
@@ -176,6 +182,7 @@ struct LmArgs {
   int M, K, V, N;       // N = block rows per sequence
   Top2* part;           // [n_parts][M]: one top-2 per workgroup (64 or 128 vocabulary rows)
   float* dbg_logits;    // nullable [B][N-1][V]
+  const int* row_count; // nullable: rows 0 .. *row_count-1 of act are compacted rows; row blocks past it are skipped
 };
 
 struct ArgmaxArgs {
@@ -185,6 +192,8 @@ struct ArgmaxArgs {
   float* gap;        // nullable [B][N-1]
   float* conf;       // nullable [B][N-1]: largest softmax probability of the drafter's row
   int32_t* err;
+  const int* row_inv;    // nullable: compacted rows (row m of the partials is block row row_inv[m])
+  const int* row_count;  // with row_inv: rows present
 };
 
 // Dual-pass drafting (D2SD): cut points of the first draft and the second

@@ -80,8 +80,13 @@ extern "C" hipError_t dflash_launch_lmhead(const LmArgs* a, hipStream_t st) {
 // is order independent).
 #define ARGMAX_THREADS 1024
 __global__ __launch_bounds__(ARGMAX_THREADS) LATENCY_BOUND void argmax_reduce_kernel(ArgmaxArgs a) {
-  const int m = blockIdx.x;
-  if (m % a.N == 0) return;
+  const int m = blockIdx.x;  // row of the partials
+  int mo = m;                // block row it belongs to
+  if (a.row_inv) {
+    if (m >= *a.row_count) return;
+    mo = a.row_inv[m];
+  }
+  if (mo % a.N == 0) return;
   Top2 t = top2_empty();
   for (int j0 = 0; j0 < a.n_parts; j0 += ARGMAX_THREADS * 8) {
     Top2 v[8];
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(ARGMAX_THREADS) LATENCY_BOUND void argmax_reduce_ke
   if (threadIdx.x == 0) {
     t = red[0];
     for (int w = 1; w < ARGMAX_THREADS / 64; ++w) t = top2_merge(t, red[w]);
-    const int b = m / a.N, j = m % a.N - 1;
+    const int b = mo / a.N, j = mo % a.N - 1;
     int tok = t.i1;
     if (tok < 0 || tok >= a.V) {
       set_error(a.err, DFLASH_DEV_BAD_TOKEN);

@@ -261,6 +261,7 @@ __global__ __launch_bounds__(256, 2) void mm_lmhead_kernel(LmArgs a, int total, 
   __shared__ Top2 red[2][XT * 16];
   int nb, split, mb;
   if (!mm_place(total, MB, 1, nb, split, mb)) return;
+  if (a.row_count && mb * XT * 16 >= *a.row_count) return;  // compacted rows: nothing in this row block
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), wm = w & 1, wn = w >> 1;
   const int r16 = lane & 15, g4 = (lane >> 4) * 4;
   const int m_tiles = pad16(a.M) >> 4;

@@ -250,6 +250,20 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
   }
   const float tot = block_sum(ss, red);
   const float rstd = 1.0f / sqrtf(tot / a.H + a.eps);
+  int row = m;  // where the normed row goes
+  if (a.row_cut) {  // compacted: only rows n >= the block's cut, blocks in order
+    const int b = m / a.N, n = m % a.N;
+    float before = 0.f;  // rows kept by the earlier blocks (exact in fp32)
+    for (int t = threadIdx.x; t < b; t += blockDim.x) before += (float)(a.N - a.row_cut[t]);
+    before = block_sum(before, red);
+    const int c = a.row_cut[b];
+    row = n >= c ? (int)before + n - c : -1;
+    if (threadIdx.x == 0 && row >= 0) {
+      a.row_inv[row] = m;
+      if (m == a.M - 1) *a.row_count = row + 1;  // the last row of the last block is always kept
+    }
+    if (row < 0) return;
+  }
 #pragma unroll
   for (int v = 0; v < NORM_MAXV; ++v) {
     const int k = (v * blockDim.x + threadIdx.x) * 4;
@@ -259,8 +273,8 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
     for (int i = 0; i < 4; ++i) y[i] = xv[v][i] * rstd * bf2f(gv[v][i]);
     u16x4 hi, lo;
     split4(y, hi, lo);
-    *reinterpret_cast<u16x4*>(a.h + pk_index(m, k, a.H)) = hi;
-    *reinterpret_cast<u16x4*>(a.h + act_plane(a.M, a.H) + pk_index(m, k, a.H)) = lo;
+    *reinterpret_cast<u16x4*>(a.h + pk_index(row, k, a.H)) = hi;
+    *reinterpret_cast<u16x4*>(a.h + act_plane(a.M, a.H) + pk_index(row, k, a.H)) = lo;
   }
 }
 
