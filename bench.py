@@ -223,6 +223,7 @@ def run_batched(args, name):
             dr.verify_multi(seq, drafts, logits_c, acc, nxt, com, chosen)
 
     ms_step = timed(step)
+    acc_main, com_main = acc.clone(), com.clone()  # the timed step's outcome (the timer pass below reruns pass one)
 
     B.check(B.dflash_kernel_timer(dr.handle, B.K_ATTN, 1), "timer")
     for _ in range(args.steps):
@@ -237,7 +238,7 @@ def run_batched(args, name):
     rl1 = batched_roofline(cfg, ctx, n_new) if K else rl
     at_s = at_ms / at_n / 1e3
     achieved = rl["attn_bytes_per_layer"] / at_s / 1e9
-    accepted = float(acc.float().mean())
+    accepted = float(acc_main.float().mean())
     res = {
         "metric": "draft tokens/sec per GPU (block=16, batched drafter+verify); % roofline",
         "value": round(Bn * (N - 1) / (ms_step / 1e3), 1), "unit": "draft tokens/s", "n_gpus": 1,
@@ -259,6 +260,7 @@ def run_batched(args, name):
         "step_roofline": {"bound": "mixed", "t_roof_us": rl["t_roof_us"], "phases": rl["phases"],
                           "frac": round(rl["t_roof_us"] / (ms_step * 1e3), 4)},
         "mean_accept": round(accepted, 3),
+        "committed_tok_s": round(float(com_main.float().sum()) / (ms_step / 1e3), 1),
         "first_pass_only": None if not K else {
             "ms_per_step": round(first_ms, 4), "draft_tok_s": round(Bn * (N - 1) / (first_ms / 1e3), 1),
             "t_roof_us": rl1["t_roof_us"], "frac": round(rl1["t_roof_us"] / (first_ms * 1e3), 4)},
@@ -502,6 +504,8 @@ def main():
         "step_roofline": {"bound": "hbm", "bytes": sb["total"], "t_roof_us": round(t_roof_us, 1),
                           "achieved_GBs": round(sb["total"] / (ms_step / 1e3) / 1e9, 1),
                           "frac": round(t_roof_us / (ms_step * 1e3), 4)},
+        "mean_accept": int(acc[0]),
+        "committed_tok_s": round(int(com[0]) / (ms_step / 1e3), 1),
     }
     log(f"{ms_step:.3f} ms/step, {tok_s:.0f} draft tok/s, step roofline {res['step_roofline']['frac']:.3f}")
     if not args.no_cpu_baseline:
