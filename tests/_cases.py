@@ -9,8 +9,6 @@ Parity bar (stated once, used by every GPU test):
   * floating point (context K/V, the residual stream after every layer,
     logits): max |gpu - oracle| / max |oracle| <= 2e-2 per tensor.
 """
-import math
-
 import numpy as np
 import torch
 

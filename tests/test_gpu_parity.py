@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle as O
-from _cases import Case, FLOAT_TOL, rel_err, say, nan_free
+from _cases import Case, FLOAT_TOL, say, nan_free
 from block_diffusion_drafter_softmax_amd import synth
 from block_diffusion_drafter_softmax_amd import _binding as B
 

@@ -10,7 +10,6 @@ import math
 import os
 
 import numpy as np
-import pytest
 import scipy.special
 import torch
 import torch.nn.functional as F
