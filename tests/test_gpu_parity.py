@@ -118,6 +118,21 @@ def test_gqa_16_to_1_rows_256_both_head_dims():
         run_step(Case(cfg, ctx=ctx, n_new=n_new, seed=17 + d, page_order="shuffled", prefill_chunk=64))
 
 
+def test_context_fills_every_page():
+    # Page table exactly full: the step's 16 appended rows land in the last
+    # page of sequence 0 (368 = 23 pages), whose 16 + 368 virtual keys end
+    # exactly on the third 128-key chunk, the last slot of the attention's
+    # chunk grid; sequence 1's 112 context keys plus the block fill exactly
+    # one chunk.
+    cfg = small_cfg(hidden=384, n_q_heads=8, n_kv_heads=2, head_dim=128, intermediate=768,
+                    vocab=2048 + 32, n_target_layers=4, block_size=16)
+    case = Case(cfg, ctx=[368, 112], n_new=[16, 16], seed=61, page_order="shuffled", prefill_chunk=64,
+                extra_pages=-1)
+    assert case.dr.pages_per_seq * 16 == 368
+    run_step(case)
+    assert int(case.dr.ctx_len[case.seq_ids[0]]) == 368
+
+
 def test_attention_multi_chunk_items():
     # GPT-OSS attention geometry (d_h 64, 8 kv heads, 128 query rows per kv
     # head) with a page pool large enough (2100 pages per sequence) that the
