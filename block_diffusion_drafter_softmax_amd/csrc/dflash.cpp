@@ -793,8 +793,8 @@ int dflash_draft_sample(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, cons
   const dflash_config& c = ctx->c;
   if (B < 1 || B > c.max_batch) return fail(DFLASH_ERR_INVALID_ARG, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
   if (!seq_ids || !anchor || !draft || !draft_logits) return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
-  if (!(temperature > 0.f) || !std::isfinite(temperature))
-    return fail(DFLASH_ERR_INVALID_ARG, "temperature must be finite and > 0");
+  if (!(temperature > 0.f) || !std::isfinite(temperature) || !std::isfinite(1.f / temperature))
+    return fail(DFLASH_ERR_INVALID_ARG, "temperature must be finite and > 0, with a finite reciprocal");
   const Layout& L = ctx->L;
   int rc = draft_impl(ctx, B, seq_ids, anchor, nullptr, ctx->at<int>(L.d_draft1), nullptr, nullptr, nullptr,
                       draft_logits, stream);
@@ -828,8 +828,8 @@ int dflash_verify_sample(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, con
     return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
   if (logits_dtype != DFLASH_DTYPE_BF16 && logits_dtype != DFLASH_DTYPE_F32)
     return fail(DFLASH_ERR_INVALID_ARG, "logits_dtype must be DFLASH_DTYPE_BF16 or DFLASH_DTYPE_F32");
-  if (!(draft_temperature > 0.f) || !std::isfinite(draft_temperature))
-    return fail(DFLASH_ERR_INVALID_ARG, "draft_temperature must be finite and > 0");
+  if (!(draft_temperature > 0.f) || !std::isfinite(draft_temperature) || !std::isfinite(1.f / draft_temperature))
+    return fail(DFLASH_ERR_INVALID_ARG, "draft_temperature must be finite and > 0, with a finite reciprocal");
   const Layout& L = ctx->L;
   VerifyArgs va{};
   va.logits = target_logits;

@@ -209,6 +209,8 @@ int dflash_verify(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int3
  * + G_k): a draw from q_r = softmax(z[r] / temperature), G_k Gumbel noise from
  * Philox4x64-10 keyed by (seed; counter k / 4, r | 2 << 32, seq, step),
  * word k % 4.
+ * temperature: finite, > 0, with a finite fp32 reciprocal
+ * (DFLASH_ERR_INVALID_ARG otherwise; the same for draft_temperature below).
  *   draft        device int32 [B, N-1]   (out)
  *   draft_logits device fp32 [B, N-1, V] (out, required): the drafter's
  *                logits z, which dflash_verify_sample needs. */
@@ -259,7 +261,9 @@ int dflash_verify_multi(dflash_ctx* ctx, int32_t B, int32_t C, const int32_t* se
 /* Message of the last failed call on this thread ("" if none). */
 const char* dflash_last_error(void);
 
-/* Synchronise the stream, copy the device error word to *out and clear it. */
+/* Synchronise the stream, copy the device error word to *out and clear it.
+ * Bits that work on another stream sets between the copy and the clear are
+ * lost: call it while no other stream uses the context. */
 int dflash_read_error(dflash_ctx* ctx, hipStream_t stream, int32_t* out);
 
 /* ------------------------------------------------------ kernel timing

@@ -141,6 +141,8 @@ def test_sampled_rejects_bad_arguments():
     zl = torch.zeros((1, N - 1, V), dtype=torch.float32, device=dev)
     with pytest.raises(B.DFlashError, match="temperature"):
         case.dr.draft_sample(seq, anchor, 0.0, d, zl)
+    with pytest.raises(B.DFlashError, match="reciprocal"):  # subnormal: 1 / tau overflows fp32
+        case.dr.draft_sample(seq, anchor, 1e-40, d, zl)
     one = torch.zeros(1, dtype=torch.int32, device=dev)
     tl = torch.zeros((1, N, V), dtype=torch.float32, device=dev)
     with pytest.raises(B.DFlashError, match="draft_temperature"):
