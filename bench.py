@@ -16,11 +16,13 @@ against the HBM roofline, and the oracle's CPU throughput on a bounded
 sample.
 
 `--workload qwen3_8b_batched` (32 sequences, ragged contexts from 512 to
-8192, ragged appends, temperature-1 verify) and `--workload gpt_oss_20b`
-(8 sequences at context 8192, greedy) time the batched shapes the same way;
-their dominant kernel is the block attention (HBM-bound on the context KV),
-and the step is set against a roofline that adds, per phase, the larger of
-the HBM time and the dense-bf16 MFMA time.
+8192, ragged appends, temperature-1 verify), `--workload gpt_oss_20b`
+(8 sequences at context 8192, greedy) and the Qwen3-4B shapes time their
+steps the same way; their `roofline` is whichever of the block attention,
+the gate/up projection and the LM head has the largest roofline time per
+step (the attention for the 32-sequence batch, the LM head for GPT-OSS and
+Qwen3-4B), and the step is set against a roofline that adds, per phase, the
+larger of the HBM time and the dense-bf16 MFMA time.
 """
 import argparse
 import json
@@ -131,10 +133,42 @@ def batched_roofline(cfg, ctx, n_new, K=0):
             "t_roof_us": round(sum(t.values()) * 1e6, 1), "attn_bytes_per_layer": attn_bytes // D}
 
 
+def dominant_kernel(cfg, ctx):
+    """Among the first pass's block attention, gate/up projection (one
+    launch each per layer) and LM head, the one with the largest roofline
+    time per step: max(bytes / 8 TB/s, flops / 2.5 PF) times its units per
+    step (a layer, or the whole LM head). Algorithmic bytes: the weights or
+    the context and block K/V once, activations in (split, 4 bytes a
+    value) and out; flops: the method's 2 per multiply-add (not the split
+    activation's second product)."""
+    from block_diffusion_drafter_softmax_amd import _binding as B
+    D, H, I, V, N = (cfg[k] for k in ("n_layers", "hidden", "intermediate", "vocab", "block_size"))
+    d, nq, nkv = cfg["head_dim"], cfg["n_q_heads"], cfg["n_kv_heads"]
+    Bn = len(ctx)
+    M, keys = Bn * N, int(np.sum(ctx)) + Bn * N
+    cands = {
+        "attention": ("block attention (context + block K/V of one layer)", B.K_ATTN, D,
+                      keys * 2 * nkv * d * 2 + M * nq * d * 4, 4.0 * nq * N * keys * d),
+        "gate_up": ("gate/up projection + SwiGLU (one layer)", B.K_GATE_UP, D,
+                    2 * I * H * 2 + M * H * 4 + M * I * 4, 2.0 * M * 2 * I * H),
+        "lm_head": ("LM head + per-tile top-2 (draft rows)", B.K_LM_HEAD, 1,
+                    V * H * 2 + Bn * (N - 1) * H * 4, 2.0 * Bn * (N - 1) * V * H),
+    }
+
+    def t_unit(c):
+        return max(c[3] / (HBM_PEAK_GBS * 1e9), c[4] / (MFMA_PEAK_TFS * 1e12))
+
+    key = max(cands, key=lambda k: cands[k][2] * t_unit(cands[k]))
+    label, kind, units, nbytes, flops = cands[key]
+    bound = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_PEAK_TFS * 1e12) else "mfma"
+    return {"name": key, "label": label, "kind": kind, "units": units, "bytes": nbytes, "flops": flops,
+            "bound": bound}
+
+
 def run_batched(args, name):
     """A batched workload: prefill (device-generated hidden states; their
     values do not change the work), then timed steps as in the default
-    workload, then the attention kernel's launches timed in a second pass."""
+    workload, then the dominant kernel's launches timed in a second pass."""
     import torch
     from block_diffusion_drafter_softmax_amd import synth
     from block_diffusion_drafter_softmax_amd import _binding as B
@@ -225,19 +259,23 @@ def run_batched(args, name):
     ms_step = timed(step)
     acc_main, com_main = acc.clone(), com.clone()  # the timed step's outcome (the timer pass below reruns pass one)
 
-    B.check(B.dflash_kernel_timer(dr.handle, B.K_ATTN, 1), "timer")
+    dk = dominant_kernel(cfg, ctx)
+    B.check(B.dflash_kernel_timer(dr.handle, dk["kind"], 1), "timer")
     for _ in range(args.steps):
-        step_first()  # the first pass's attention: the bytes per launch below
+        step_first()  # the first pass's launches of the dominant kernel: the units below
     torch.cuda.synchronize()
-    rc, at_ms, at_n = B.dflash_kernel_timer_read(dr.handle, B.K_ATTN)
+    rc, k_ms, k_n = B.dflash_kernel_timer_read(dr.handle, dk["kind"])
     B.check(rc, "timer read")
-    B.dflash_kernel_timer(dr.handle, B.K_ATTN, 0)
+    B.dflash_kernel_timer(dr.handle, dk["kind"], 0)
     assert dr.read_error() == 0
 
     rl = batched_roofline(cfg, ctx, n_new, K)
     rl1 = batched_roofline(cfg, ctx, n_new) if K else rl
-    at_s = at_ms / at_n / 1e3
-    achieved = rl["attn_bytes_per_layer"] / at_s / 1e9
+    unit_s = k_ms / (args.steps * dk["units"]) / 1e3  # all launches of the kind per unit (a k split adds one)
+    if dk["bound"] == "hbm":
+        achieved, peak, unit = dk["bytes"] / unit_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = dk["flops"] / unit_s / 1e12, MFMA_PEAK_TFS, "TFLOP/s"
     accepted = float(acc_main.float().mean())
     res = {
         "metric": "draft tokens/sec per GPU (block=16, batched drafter+verify); % roofline",
@@ -252,11 +290,10 @@ def run_batched(args, name):
                                f"{cfg['n_q_heads']}/{cfg['n_kv_heads']} heads of {cfg['head_dim']}, "
                                f"I {cfg['intermediate']}, V {V}",
                    "global_batch": Bn, "block": N, "launch": "eager"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "block attention (context + block K/V of one layer)",
-                     "bytes_per_launch": rl["attn_bytes_per_layer"], "avg_launch_us": round(at_s * 1e6, 2),
-                     "launches_timed": at_n},
+        "roofline": {"bound": dk["bound"], "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": dk["label"],
+                     "bytes_per_unit": int(dk["bytes"]), "flops_per_unit": dk["flops"],
+                     "us_per_unit": round(unit_s * 1e6, 2), "launches_timed": k_n},
         "step_roofline": {"bound": "mixed", "t_roof_us": rl["t_roof_us"], "phases": rl["phases"],
                           "frac": round(rl["t_roof_us"] / (ms_step * 1e3), 4)},
         "mean_accept": round(accepted, 3),
