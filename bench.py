@@ -72,9 +72,11 @@ def traffic_from_profile():
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, w, hidden_pre, hidden_step, anchor, logits_bits):
-    """The oracle, as it stands, on a bounded sample: one decode step
-    (append 8 rows, draft, verify) after an untimed prefill."""
+def cpu_baseline(cfg, w, hidden_pre, hidden_step, anchor, logits_bits, min_seconds=10.0, max_steps=8):
+    """The oracle, as it stands, on a bounded sample: the same decode step
+    (append 8 rows, draft, verify) repeated after an untimed prefill until
+    `min_seconds` of CPU work (at most `max_steps` steps), the cache set
+    back to its pre-step state between steps outside the timed region."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -85,15 +87,22 @@ def cpu_baseline(cfg, w, hidden_pre, hidden_step, anchor, logits_bits):
     cache = O.OracleCache(cfg["n_layers"])
     for r0 in range(0, len(hidden_pre), 1024):  # untimed prefill, in row chunks
         O.ctx_append(model, cache, 0, O.bf16_bits_to_f64(hidden_pre[r0: r0 + 1024]))
-    t0 = time.perf_counter()
-    O.ctx_append(model, cache, 0, O.bf16_bits_to_f64(hidden_step))
-    out = O.draft_block(model, cache, 0, int(anchor))
-    O.verify_greedy(out["draft"], O.bf16_bits_to_f64(logits_bits))
-    dt = time.perf_counter() - t0
-    return {"value": (cfg["block_size"] - 1) / dt, "unit": "draft tokens/s", "cores": int(threads),
+    saved = ([dict(k) for k in cache.k], [dict(v) for v in cache.v], dict(cache.ctx_len))  # the append rebinds
+    dt, steps = 0.0, 0
+    while steps < max_steps and (steps == 0 or dt < min_seconds):
+        cache.k, cache.v = [dict(k) for k in saved[0]], [dict(v) for v in saved[1]]
+        cache.ctx_len = dict(saved[2])
+        t0 = time.perf_counter()
+        O.ctx_append(model, cache, 0, O.bf16_bits_to_f64(hidden_step))
+        out = O.draft_block(model, cache, 0, int(anchor))
+        O.verify_greedy(out["draft"], O.bf16_bits_to_f64(logits_bits))
+        dt += time.perf_counter() - t0
+        steps += 1
+    return {"value": (cfg["block_size"] - 1) * steps / dt, "unit": "draft tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": "one decode step of the same workload (append 8 rows, draft a 16-block over a "
-                      "4096-token context, greedy verify) after an untimed prefill; float64 numpy",
+            "sample": f"{steps} repeats of one decode step of the same workload (append 8 rows, draft a "
+                      "16-block over a 4096-token context, greedy verify) after an untimed prefill; "
+                      "float64 numpy",
             "seconds": dt}
 
 
