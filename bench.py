@@ -101,8 +101,8 @@ def cpu_baseline(cfg, w, hidden_pre, hidden_step, anchor, logits_bits, min_secon
     return {"value": (cfg["block_size"] - 1) * steps / dt, "unit": "draft tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{steps} repeats of one decode step of the same workload (append 8 rows, draft a "
-                      "16-block over a 4096-token context, greedy verify) after an untimed prefill; "
-                      "float64 numpy",
+                      f"16-block over a {len(hidden_pre) + len(hidden_step)}-token context, greedy verify) "
+                      "after an untimed prefill; float64 numpy",
             "seconds": dt}
 
 
@@ -403,6 +403,8 @@ def main():
                     choices=[WORKLOAD, "qwen3_8b_batched", "gpt_oss_20b", "qwen3_4b", "qwen3_4b_fc"])
     ap.add_argument("--sampled", type=float, default=0.0,
                     help="tau > 0: drafts sampled at temperature tau, lossless verification at temperature 1")
+    ap.add_argument("--context", type=int, default=0,
+                    help="L > 0: the default workload at context length L instead of 4096 (a sweep, not the headline)")
     ap.add_argument("--rollout", type=int, default=0,
                     help="S > 0: S device-resident steps of the default workload captured as one graph")
     args = ap.parse_args()
@@ -424,6 +426,10 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     cfg = synth.config(WORKLOAD)
+    if args.context:
+        if args.context < cfg["n_new"]:
+            raise SystemExit("--context must be at least the 8 appended rows")
+        cfg["context"] = args.context
     N, L, n_new, T, H = cfg["block_size"], cfg["context"], cfg["n_new"], cfg["n_target_layers"], cfg["hidden"]
     seed = 0
     t0 = time.perf_counter()
@@ -541,7 +547,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "Qwen3-8B-shaped DFLARE drafter decode step: append 8 context rows "
-                               "(T=9 fusion), draft block 16 over ctx 4096 (7 layers, H 4096, 32/8 heads, "
+                               f"(T=9 fusion), draft block 16 over ctx {L} (7 layers, H 4096, 32/8 heads, "
                                "I 12288, V 151936), "
                                + (f"drafts sampled at temperature {tau}, lossless temperature-1 verify"
                                   if tau > 0 else "greedy verify") + "; batch 1",
