@@ -37,7 +37,8 @@ int fail(int code, const char* fmt, ...) {
   } while (0)
 
 constexpr int kAttnChunk = 128;     // virtual keys (16 block slots + context) per attention chunk
-constexpr int kAttnItems = 4096;    // attention work items to aim for; larger batches take several chunks per item
+constexpr int kAttnItems = 512;     // attention work items to aim for (two 8-wave workgroups fit a CU: about one
+                                    // round of the chip); larger grids take several chunks per item
 constexpr int kAttnMaxWaves = 8;    // computing waves of an attention workgroup that takes several blocks of one
                                     // sequence: only the staging-only waves of an 8-wave workgroup are filled (larger
                                     // workgroups were slower: the attention is bound by its compute phase)

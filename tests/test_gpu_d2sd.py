@@ -130,17 +130,18 @@ def test_d2sd_gpt_oss_geometry_all_cuts():
 def test_d2sd_head_dim_128_shared_context_multi_chunk():
     # d_h 128, GQA 4:1, block 16: 64 query rows (4 computing waves) per kv
     # head, so one 8-wave attention workgroup takes 2 candidates of a
-    # sequence (K = 6: 3 splits). The page pool (1500 pages per sequence)
+    # sequence (K = 6: 3 splits). The page pool (120 pages per sequence)
     # makes the second pass's chunk grid (2 sequences x 3 splits x 8 kv heads
-    # x 188 chunks) exceed the work-item target, so the shared items take 2
-    # chunks each.
+    # x 16 chunks = 768) exceed the target of 512 work items, so items take 2
+    # chunks each: item 0 (block page) per candidate, then the 700-token
+    # context's shared items of 2 and 2 partial chunks.
     cfg = small_cfg(hidden=512, n_q_heads=32, n_kv_heads=8, head_dim=128, intermediate=512, vocab=4096,
                     n_target_layers=3, block_size=16)
     K = 6
     ctx = [700, 150]
     pps_min = (max(ctx) + 16 + 15) // 16
     case = Case(cfg, ctx=ctx, n_new=[8, 3], seed=67, page_order="shuffled", prefill_chunk=128,
-                extra_pages=1500 - pps_min, max_batch=2 * (K + 1))
+                extra_pages=120 - pps_min, max_batch=2 * (K + 1))
     _, orc = run_d2sd(case, K)
     check_verify_multi(case, orc, K)
 

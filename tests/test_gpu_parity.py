@@ -135,18 +135,18 @@ def test_context_fills_every_page():
 
 def test_attention_multi_chunk_items():
     # GPT-OSS attention geometry (d_h 64, 8 kv heads, 128 query rows per kv
-    # head) with a page pool large enough (2100 pages per sequence) that the
-    # batch's chunk grid (4 x 8 x 263) exceeds the attention's work-item
-    # target 3-fold: every work item then takes 3 chunks of 128 virtual keys
-    # in a row. Contexts end inside an item's first chunk (383: 399 virtual
-    # keys), hold only the block, and end with partial items of 1 and 3
-    # chunks.
+    # head) with a page pool (300 pages per sequence) whose chunk grid
+    # (4 x 8 x 38 = 1216) is between 2 and 3 times the attention's target of
+    # 512 work items: every work item then takes 3 chunks of 128 virtual
+    # keys in a row (384 keys). Virtual key counts 1216 (the last item holds
+    # one partial chunk), 399 (ends 15 keys into an item's first chunk), 16
+    # (the block alone) and 2333 (7 items, the last with 29 keys).
     cfg = small_cfg(hidden=512, n_q_heads=64, n_kv_heads=8, head_dim=64, intermediate=512, vocab=2048,
                     block_size=16)
     ctx, n_new = [1200, 383, 0, 2317], [8, 5, 0, 16]
     pps_min = (max(ctx) + 16 + 15) // 16
     run_step(Case(cfg, ctx=ctx, n_new=n_new, seed=51, page_order="shuffled", prefill_chunk=256,
-                  extra_pages=2100 - pps_min))
+                  extra_pages=300 - pps_min))
 
 
 def test_fc_fusion_ragged_batch():
