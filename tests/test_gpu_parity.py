@@ -149,6 +149,19 @@ def test_attention_multi_chunk_items():
                   extra_pages=300 - pps_min))
 
 
+def test_long_context_multi_chunk_head_dim_128():
+    # One sequence at 32000 tokens with the Qwen3 attention geometry (d_h
+    # 128, GQA 4:1, block 16) at a small width: the chunk grid (8 kv heads x
+    # 251 chunks) is about 4 times the attention's target of 512 work items,
+    # so every item streams 4 chunks (512 virtual keys) with the online
+    # softmax, 63 items, the last one 272 keys long.
+    cfg = small_cfg(hidden=512, n_q_heads=32, n_kv_heads=8, head_dim=128, intermediate=512, vocab=4096,
+                    n_target_layers=3, block_size=16)
+    case = Case(cfg, ctx=[32000], n_new=[8], seed=57, page_order="shuffled", prefill_chunk=1024)
+    assert case.dr.pages_per_seq == 2002
+    run_step(case)
+
+
 def test_fc_fusion_ragged_batch():
     # DFlash's FC fusion: one shared context from W_fc [H, T*H] for every
     # layer; ragged appends (one entry appends nothing), shuffled pages
