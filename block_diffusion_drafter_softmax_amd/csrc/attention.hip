@@ -26,8 +26,9 @@
 // K and V are bf16 storage. Unnormalised O, the chunk's max and sum go to a
 // partial buffer, and attn_merge_kernel combines the chunks.
 //
-// Large batches have far more chunks than the chip holds at once. There a
-// work item is cpi > 1 consecutive chunks, taken one after the other by the
+// Large batches and long contexts have far more chunks than the chip holds
+// at once (about 512 workgroups, two per CU). There a work item is cpi > 1
+// consecutive chunks, taken one after the other by the
 // same workgroup (stage, compute, stage, ...) with the running max, sum and
 // O rescaled per half chunk as in any online softmax, and one partial per
 // item goes to the merge: cpi times fewer partial bytes.
@@ -46,7 +47,7 @@
 namespace {
 DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-constexpr int CH = 128;  // virtual keys per work item
+constexpr int CH = 128;  // virtual keys per chunk (a work item takes cpi chunks)
 constexpr int PAGES = CH / 16;
 constexpr int MIN_WAVES = 8;  // staging waves per workgroup
 constexpr int CPI_MAX = 8;    // chunks per work item, at most
