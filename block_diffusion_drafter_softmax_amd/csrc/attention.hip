@@ -94,6 +94,13 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   }
   const int b0 = blockIdx.z / splits * a.grp + c0;   // the workgroup's first block
   const int cpi = MULTI ? a.cpi : 1;
+  const int tid = threadIdx.x, nthreads = blockDim.x;
+  // page-table entry of page slot tid (< SLOTS <= nthreads), requested with
+  // the plan from the call's per-block copy; clamped, used only if valid
+  int raw_slot = 0;
+  if (tid < cpi * PAGES)
+    raw_slot = a.blk_pages[(size_t)b0 * a.max_pages_per_seq +
+                           clampi(item * cpi * PAGES + tid - 1, 0, a.max_pages_per_seq - 1)];
   const int2 pl = *reinterpret_cast<const int2*>(a.plan + 2 * b0);  // (sequence, context length)
   const int seq = clampi(pl.x, 0, a.max_seqs - 1);
   const int L = clampi(pl.y, 0, a.max_pages_per_seq * 16);
@@ -101,20 +108,20 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   const int item_nv = min(16 + L, item_begin + cpi * CH) - item_begin;  // virtual keys in this item
   if (item_nv <= 0) return;
   const int n_chunks = MULTI ? (item_nv + CH - 1) / CH : 1;
-  const int tid = threadIdx.x, nthreads = blockDim.x;
   const size_t page_elems = (size_t)2 * a.n_kv * 16 * D;
 
   // Page slots of the item (virtual page 0 is the block; slots past the
   // context point at the block and hold 0 valid keys).
   const uint16_t* blk_k = a.kblk + ((size_t)b0 * a.n_kv + kvh) * 16 * D;
   const uint16_t* blk_v = a.vblk + ((size_t)b0 * a.n_kv + kvh) * D * 16;
-  for (int t = tid; t < n_chunks * PAGES; t += nthreads) {
+  if (tid < n_chunks * PAGES) {  // n_chunks * PAGES <= SLOTS <= nthreads: one slot per thread
+    const int t = tid;
     long long off = -1;
     int n_ok = 0;
     if (16 * t < item_nv) {
       const int vp = item_begin / 16 + t;
       if (vp > 0) {
-        const int raw = a.page_table[(size_t)seq * a.max_pages_per_seq + vp - 1];
+        const int raw = raw_slot;
         if (raw < 0 || raw >= a.n_pages) set_error(a.err, DFLASH_DEV_BAD_PAGE);
         off = (long long)clampi(raw, 0, a.n_pages - 1) * page_elems + (long long)kvh * 16 * D;
       }

@@ -84,6 +84,8 @@ struct Layout {
   size_t qpart, dpart;
   // a draft call's plan: per block (sequence, context length), per row RoPE cos/sin
   size_t plan, plan_rope;
+  // and each block's page-table row, read by the attention with the plan
+  size_t blk_pages;
   // compacted LM-head rows of a dual-pass second pass: block row of each, count
   size_t lm_inv, lm_count;
   size_t gpart_floats, cpart_floats;
@@ -160,6 +162,7 @@ Layout make_layout(const dflash_config& c) {
   L.dpart = take(Bm * N * L.n_schunks * 2 * 4);
   L.plan = take(Bm * 2 * 4);
   L.plan_rope = take(Bm * N * (c.head_dim / 2) * 2 * 4);
+  L.blk_pages = take((size_t)Bm * c.max_pages_per_seq * 4);
   L.lm_inv = take(Bm * N * 4);
   L.lm_count = take(4);
   L.total = off;
@@ -551,6 +554,9 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
   na.plan_rope = ctx->at<float>(L.plan_rope);
   na.rope = c.use_rope ? ctx->at<float>(L.rope) : nullptr;
   na.half = c.head_dim / 2;
+  na.page_table = ctx->kv.page_table;
+  na.blk_pages = ctx->at<int>(L.blk_pages);
+  na.max_pages_per_seq = c.max_pages_per_seq;
   na.max_seqs = c.max_seqs;
   na.max_pos = c.max_pos;
   na.err = ctx->kv.error_word;
@@ -579,6 +585,7 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
   aa.ctx_len = ctx->kv.ctx_len;
   aa.seq_ids = seq_ids;
   aa.plan = na.plan;
+  aa.blk_pages = na.blk_pages;
   aa.part_o = ctx->at<float>(L.apo);
   aa.part_ml = ctx->at<float>(L.aml);
   aa.o = ctx->at<uint16_t>(L.o);

@@ -116,6 +116,7 @@ struct AttnArgs {
   int N, n_q, n_kv, chunk, n_ck, max_pages_per_seq, n_pages, max_seqs;
   int cpi;                 // chunks of `chunk` virtual keys per work item (1 .. 8)
   const int* plan;         // the call's plan [B][2]: sequence (clamped), context length
+  const int* blk_pages;    // the call's page-table row of each block [B][max_pages_per_seq]
   int grp;                 // consecutive blocks that share one sequence's context (B % grp == 0)
   int cand;                // blocks of a group one workgroup takes (1 .. grp): a context chunk is read once for them
 };
@@ -168,6 +169,11 @@ struct NormArgs {
   float* plan_rope;        // [M][d/2][2]: cos/sin at row m's position (when rope is set)
   const float* rope;       // [max_pos][d/2][2] or null
   int half;                // d/2
+  // and block b's row of the page table, copied to blk_pages[b] so that the
+  // attention requests its pages together with the plan, not after it
+  const int* page_table;   // [max_seqs][max_pages_per_seq]
+  int* blk_pages;          // nullable [B][max_pages_per_seq]
+  int max_pages_per_seq;
   // Rows the LM head needs (the dual-pass drafter's second pass): block b
   // keeps rows n >= row_cut[b]; those rows are written compacted, in block
   // order, with row_inv[compact] = m and the number of rows in *row_count.

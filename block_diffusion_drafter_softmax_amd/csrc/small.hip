@@ -211,6 +211,9 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
       }
       if (bad) set_error(a.err, bad);
     }
+    if (n == 0 && a.blk_pages)
+      for (int p = threadIdx.x; p < a.max_pages_per_seq; p += blockDim.x)
+        a.blk_pages[(size_t)b * a.max_pages_per_seq + p] = a.page_table[(size_t)seq * a.max_pages_per_seq + p];
     if (a.rope && (int)threadIdx.x < a.half) {  // this row's RoPE cos/sin (position L + n)
       const int pos = clampi(L + n, 0, a.max_pos - 1);
       const float2 cs = *reinterpret_cast<const float2*>(a.rope + ((size_t)pos * a.half + threadIdx.x) * 2);
