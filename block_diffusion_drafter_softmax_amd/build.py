@@ -7,6 +7,7 @@ file and the shared library to this package directory.
 import argparse
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -36,6 +37,24 @@ def _compile(src):
     return obj, r.stderr
 
 
+def header_entry_points():
+    """Function names include/dflash.h declares (comments stripped)."""
+    text = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z0-9_]+)\s*\(", text)))
+
+
+def write_version_script():
+    """Linker version script: the library exports exactly the entry points
+    of include/dflash.h; every other symbol (kernel launchers, helpers,
+    the C++ runtime pieces linked in) stays local to libdflash.so."""
+    path = os.path.join(BUILD, "exports.map")
+    names = header_entry_points()
+    with open(path, "w") as f:
+        f.write("{\n  global:\n" + "".join(f"    {n};\n" for n in names) + "  local:\n    *;\n};\n")
+    return path
+
+
 def build(jobs=None, verbose=False):
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(8, len(SOURCES))
@@ -47,7 +66,8 @@ def build(jobs=None, verbose=False):
             if err.strip():
                 print(err, file=sys.stderr)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--version-script=" + write_version_script(),
+           "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -110,6 +110,15 @@ def make_weights(cfg, seed=0, std=0.02):
 
     Linear and embedding weights ~N(0, std^2); norm gains 1.0; W_fuse
     ~N(0, 1) in float32. With tied_kv the context projections are omitted.
+
+    ``cfg["qk_score_var"]`` (optional, parity inputs only) draws the query
+    and key projections (wq, wk_d, wk_t) with std sqrt(v / H) instead, so
+    that the attention logits q.k / sqrt(d_h) of unit-RMS rows have variance
+    about v whatever the width. At small widths std 0.02 makes the scores
+    nearly zero: the attention is uniform, every mask position of a block
+    then carries the same state and the whole block drafts one token. With
+    v ~ 2.5 (what std 0.02 gives at H = 4096) the RoPE positions separate
+    the rows and the drafted tokens differ from position to position.
     """
     D, H, I, V, T = cfg["n_layers"], cfg["hidden"], cfg["intermediate"], cfg["vocab"], cfg["n_target_layers"]
     qd = cfg["n_q_heads"] * cfg["head_dim"]
@@ -118,7 +127,8 @@ def make_weights(cfg, seed=0, std=0.02):
                   wg=(D, I, H), wu=(D, I, H), wd=(D, H, I), embed=(V, H), lm_head=(V, H))
     if not cfg.get("tied_kv"):
         shapes.update(wk_t=(D, kd, H), wv_t=(D, kd, H))
-    w = {k: normal_bf16(s, std, seed, k) for k, s in shapes.items()}
+    qk_std = float(np.sqrt(cfg["qk_score_var"] / H)) if cfg.get("qk_score_var") else std
+    w = {k: normal_bf16(s, qk_std if k in ("wq", "wk_d", "wk_t") else std, seed, k) for k, s in shapes.items()}
     one = np.uint16(0x3F80)
     for k, s in dict(g_fuse=(D, H), g_attn=(D, H), g_mlp=(D, H), g_final=(H,)).items():
         w[k] = np.full(s, one, dtype=np.uint16)
@@ -168,7 +178,9 @@ def make_logits(cfg, draft, seed, step=0):
     temperature 1 ("accept_p"): z ~ N(0,1) -> bf16; rows r < N-1 get
       z[r, d] = ln(p/(1-p)) + logsumexp_{k != d} z[r, k], so that d has
       probability p = `agreement` under softmax(z[r]) (before rounding).
-    Returns float32 (tiny) or bf16 bits (uint16).
+    Returns float32 (the "boost3" model, or any model with
+    ``cfg["logits_f32"]`` set: no bf16 rounding anywhere) or bf16 bits
+    (uint16).
     """
     draft = np.asarray(draft)
     B, N, V = draft.shape[0], cfg["block_size"], cfg["vocab"]
@@ -176,7 +188,8 @@ def make_logits(cfg, draft, seed, step=0):
     z = r.standard_normal((B, N, V), dtype=np.float32)
     coin = r.random((B, N - 1)) < cfg["agreement"]
     model = cfg["logit_model"]
-    if model != "boost3":
+    f32 = model == "boost3" or bool(cfg.get("logits_f32"))
+    if not f32:
         z = f32_to_bf16_bits(z).astype(np.uint32) << 16
         z = z.view(np.float32)
     for b in range(B):
@@ -193,6 +206,6 @@ def make_logits(cfg, draft, seed, step=0):
                 rest = np.delete(z[b, row].astype(np.float64), d)
                 m = rest.max()
                 z[b, row, d] = np.log(p / (1 - p)) + m + np.log(np.exp(rest - m).sum())
-    if model == "boost3":
+    if f32:
         return z
     return f32_to_bf16_bits(z)

@@ -1,6 +1,7 @@
-"""rocprofv3 helpers for the measurement summaries.
+"""rocprofv3 helpers for the measurement summaries (measurement tooling that
+sits beside bench.py; not part of the library).
 
-``python -m block_diffusion_drafter_softmax_amd.profiling copy`` runs a plain
+``python profiling.py copy`` runs a plain
 device-to-device copy of 256 MiB three times: the reference workload whose
 FETCH_SIZE / WRITE_SIZE readings calibrate the HBM traffic counters.
 
@@ -16,7 +17,7 @@ import os
 import re
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "block_diffusion_drafter_softmax_amd", "csrc")
 
 # Sources the streaming GEMM kernels are compiled from: a traffic summary is

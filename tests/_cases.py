@@ -168,5 +168,36 @@ class Case:
         return he, le, compared, excluded
 
 
+def check_positions(g, orc, oracle_seqs, min_distinct=3):
+    """Per-position checks of a draft whose positions differ.
+
+    * diversity: each sampled sequence's oracle draft holds at least
+      `min_distinct` distinct tokens at positions whose top-2 gap is >= 1e-2
+      (otherwise the exact token comparison decides only one argmax);
+    * row identity: every GPU logits row is closer (max abs difference over
+      the oracle row's max abs value) to its own oracle row than to any
+      other row of the block, and the margin is wider than the float bar,
+      so a block-row mix-up (a RoPE position, a page-table row, the
+      LM-head row -> draft position map) cannot pass.
+    Returns the smallest distinct count seen."""
+    fewest = None
+    for b, o in zip(oracle_seqs, orc):
+        ok = [int(t) for t, gp in zip(o["draft"], o["gap"]) if gp >= GAP_MIN]
+        n = len(set(ok))
+        fewest = n if fewest is None else min(fewest, n)
+        assert n >= min_distinct, f"seq {b}: oracle draft {list(o['draft'])} has {n} distinct decided tokens"
+        if g["logits"] is None:
+            continue
+        z, zo = g["logits"][b].astype(np.float64), o["logits"]
+        for j in range(zo.shape[0]):
+            errs = [float(np.max(np.abs(z[j] - zo[k]))) / max(float(np.max(np.abs(zo[k]))), 1e-30)
+                    for k in range(zo.shape[0])]
+            own = errs[j]
+            other = min(e for k, e in enumerate(errs) if k != j)
+            assert own < other and other > 2 * FLOAT_TOL, (
+                f"seq {b} row {j}: own-row error {own:.2e}, nearest other row {other:.2e}")
+    return fewest
+
+
 def nan_free(*arrays):
     return all(np.all(np.isfinite(a)) for a in arrays if a is not None)

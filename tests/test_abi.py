@@ -4,6 +4,7 @@ arguments before touching the device."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -31,6 +32,24 @@ def test_library_exports_every_declared_symbol():
     for n in header_functions():
         assert hasattr(lib, n), n
     assert sorted(B.EXPORTS) == header_functions()
+
+
+def exported_functions(path):
+    """Defined function symbols in the dynamic symbol table (readelf)."""
+    out = subprocess.run(["readelf", "--dyn-syms", "-W", path], capture_output=True, text=True, check=True).stdout
+    names = set()
+    for line in out.splitlines():
+        f = line.split()
+        # Num: Value Size Type Bind Vis Ndx Name
+        if len(f) >= 8 and f[3] == "FUNC" and f[4] in ("GLOBAL", "WEAK") and f[6] != "UND":
+            names.add(f[7].split("@")[0])
+    return names
+
+
+def test_library_exports_nothing_but_the_header():
+    """The dynamic symbol table holds exactly the header's entry points: the
+    kernel launchers and helpers stay internal to the library."""
+    assert exported_functions(B.LIB_PATH) == set(header_functions())
 
 
 def make_cfg(name="qwen3_8b", **kw):

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle as O
-from _cases import Case, FLOAT_TOL, say, nan_free
+from _cases import Case, FLOAT_TOL, say, nan_free, check_positions
 from block_diffusion_drafter_softmax_amd import synth
 from block_diffusion_drafter_softmax_amd import _binding as B
 
@@ -31,7 +31,10 @@ def small_cfg(**kw):
     return c
 
 
-def run_step(case, verify=True, check_cache=True):
+def run_step(case, verify=True, check_cache=True, positions=0):
+    """positions > 0: the oracle's drafts must hold at least that many
+    distinct decided tokens per sequence, and every GPU logits row must sit
+    closest to its own oracle row (check_positions)."""
     case.prefill()
     case.step_append()
     assert case.dr.read_error() == 0
@@ -44,6 +47,9 @@ def run_step(case, verify=True, check_cache=True):
     assert ce <= FLOAT_TOL and he <= FLOAT_TOL and le <= FLOAT_TOL
     assert n_cmp > 0
     assert case.dr.read_error() == 0
+    if positions:
+        fewest = check_positions(g, orc, case.oracle_seqs, positions)
+        say(f"  per-position drafts: {[list(map(int, o['draft'])) for o in orc]} (>= {fewest} distinct)")
     if verify:
         check_verify_greedy(case, orc)
     return g, orc
@@ -82,6 +88,49 @@ def test_tiny_ragged_batch_shuffled_pages():
     # appended rows, one with an empty context before the step, shuffled pages
     run_step(Case(synth.config("tiny"), ctx=[37, 133, 301, 5], n_new=[1, 8, 0, 5], seed=3,
                   page_order="shuffled", prefill_chunk=48))
+
+
+# Parity inputs whose drafts differ from position to position: the query and
+# key projections drawn so that attention logits have variance 2.5 (as std
+# 0.02 gives at H = 4096), see synth.make_weights. Every case asserts at
+# least 3 distinct decided tokens per sequence and row identity.
+SHARP = dict(qk_score_var=2.5)
+
+
+def test_tiny_diverse_drafts():
+    cfg = synth.config("tiny", **SHARP)
+    run_step(Case(cfg, ctx=[128], n_new=[8], prefill_chunk=40), positions=3)
+
+
+def test_diverse_ragged_batch_shuffled_pages():
+    cfg = synth.config("tiny", **SHARP)
+    run_step(Case(cfg, ctx=[37, 133, 301, 5], n_new=[1, 8, 0, 5], seed=3, page_order="shuffled",
+                  prefill_chunk=48), positions=3)
+
+
+def test_diverse_head_dim_128_block_16():
+    # the Qwen3 attention geometry (d_h 128, GQA 4:1, N 16) at a small width
+    cfg = small_cfg(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, intermediate=1024,
+                    vocab=8192, n_target_layers=5, block_size=16, **SHARP)
+    run_step(Case(cfg, ctx=[200, 257], n_new=[8, 3], seed=7, page_order="shuffled", prefill_chunk=64),
+             positions=3)
+
+
+def test_diverse_gqa_8_to_1_multi_chunk():
+    # GPT-OSS attention geometry (d_h 64, GQA 8:1) with multi-chunk work
+    # items (the page pool of test_attention_multi_chunk_items)
+    cfg = small_cfg(hidden=512, n_q_heads=64, n_kv_heads=8, head_dim=64, intermediate=512, vocab=2048,
+                    block_size=16, **SHARP)
+    ctx, n_new = [1200, 383], [8, 5]
+    pps_min = (max(ctx) + 16 + 15) // 16
+    run_step(Case(cfg, ctx=ctx, n_new=n_new, seed=51, page_order="shuffled", prefill_chunk=256,
+                  extra_pages=300 - pps_min), positions=3)
+
+
+def test_diverse_fc_fusion_tied():
+    cfg = small_cfg(fusion="fc", tied_kv=1, n_target_layers=5, block_size=16, n_q_heads=8, n_kv_heads=2,
+                    **SHARP)
+    run_step(Case(cfg, ctx=[200, 97], n_new=[16, 3], seed=73, prefill_chunk=80), positions=3)
 
 
 def test_tiny_tied_kv_without_rope():
@@ -219,8 +268,9 @@ def verify_only_drafter(V, N, batch):
     """A one-layer drafter with the given vocabulary and block: only its
     verify entry point is used (verification reads no weights)."""
     from block_diffusion_drafter_softmax_amd.drafter import Drafter
+    G = 16 // np.gcd(16, N)  # query rows per kv head, G * N, must fill 16-row tiles
     cfg = small_cfg(vocab=V, hidden=256, n_layers=1, intermediate=256, block_size=N,
-                    n_q_heads=2, n_kv_heads=2)
+                    n_q_heads=2 * G, n_kv_heads=2)
     return Drafter(cfg, synth.make_weights(cfg, 0), max_batch=batch, max_new=1, max_seqs=batch + 3,
                    pages_per_seq=2)
 
@@ -276,6 +326,43 @@ def test_verify_temperature_one_batched():
     assert compared_a >= B_ - 2 and compared_n >= B_ - 4
 
 
+def test_verify_temperature_one_fp32_logits():
+    """Temperature-1 verification of fp32 target logits (the tiny shape's
+    logits dtype) against the oracle: a 4096 vocabulary at block 8 and the
+    full 151936 vocabulary at block 16, logits with the draft token's
+    probability set to 0.75 (no bf16 rounding)."""
+    dev = torch.device("cuda")
+    for V, N, B_, seed in ((4096, 8, 16, 23), (151936, 16, 8, 24)):
+        cfg = small_cfg(vocab=V, block_size=N, logit_model="accept_p", agreement=0.75, logits_f32=True)
+        rng = np.random.default_rng(seed)
+        draft = rng.integers(0, V - 1, size=(B_, N - 1)).astype(np.int32)
+        z = synth.make_logits(cfg, draft, seed=seed)
+        assert z.dtype == np.float32
+        dr = verify_only_drafter(V, N, B_)
+        seq_np = np.arange(B_, dtype=np.int32) + 2
+        step = 7
+        acc, nxt, com = (torch.full((B_,), -1, dtype=torch.int32, device=dev) for _ in range(3))
+        dr.verify(torch.from_numpy(seq_np).to(dev), torch.from_numpy(draft).to(dev), torch.from_numpy(z).to(dev),
+                  acc, nxt, com, temperature=1.0, seed=seed, step=step)
+        torch.cuda.synchronize()
+        compared_a = compared_n = 0
+        for b in range(B_):
+            a, n, c, info = O.verify_temp1(draft[b], z[b].astype(np.float64), seed, step, int(seq_np[b]))
+            if any(abs(u - p) < 1e-5 for u, p in zip(info["u"], info["p"])):
+                continue
+            compared_a += 1
+            assert int(acc[b]) == a and int(com[b]) == c, (V, b, int(acc[b]), a)
+            if info["gumbel_gap"] >= 1e-2:
+                compared_n += 1
+                assert int(nxt[b]) == n, (V, b, int(nxt[b]), n)
+            if a < N - 1:
+                assert int(nxt[b]) != int(draft[b, a])
+        say(f"  V {V}: accept {acc.tolist()}  compared {compared_a}/{B_} accept, {compared_n} next")
+        assert compared_a >= B_ - 2 and compared_n >= B_ - 4
+        assert len(set(acc.tolist())) >= 2  # accept lengths differ across the batch
+        dr.close()
+
+
 # ------------------------------------------------------ error word (host-forced)
 def test_device_error_bits_and_skips():
     cfg = synth.config("tiny")
@@ -304,6 +391,25 @@ def test_device_error_bits_and_skips():
     dr.draft_block(case.t_i32([case.seq_ids[0], 10 ** 6]), case.t_i32([cfg["vocab"], 0]), draft)
     err = dr.read_error()
     assert err & B.DEV_BAD_TOKEN and err & B.DEV_BAD_SEQ
+    # a hole in an already appended context page, seen by the draft: the
+    # attention flags it and clamps the entry, so every access stays in
+    # bounds (the clamped page here is an unwritten, NaN-filled one: the
+    # affected sequence's results are unspecified); the other sequence's
+    # draft is untouched
+    gap = torch.zeros((2, cfg["block_size"] - 1), dtype=torch.float32, device=case.dev)
+    dr.draft_block(case.t_i32(case.seq_ids), case.t_i32([3, 4]), draft, gap)
+    assert dr.read_error() == 0
+    clean_draft, clean_gap = draft.clone(), gap.clone()
+    dr.page_table[case.seq_ids[0], 0] = -1
+    dr.draft_block(case.t_i32(case.seq_ids), case.t_i32([3, 4]), draft, gap)
+    assert dr.read_error() & B.DEV_BAD_PAGE
+    torch.cuda.synchronize()
+    assert torch.equal(draft[1], clean_draft[1]) and torch.equal(gap[1], clean_gap[1])
+    dr.page_table.copy_(pt)
+    dr.draft_block(case.t_i32(case.seq_ids), case.t_i32([3, 4]), draft, gap)
+    assert dr.read_error() == 0
+    torch.cuda.synchronize()
+    assert torch.equal(draft, clean_draft) and torch.equal(gap, clean_gap)
     # capacity: more rows than the sequence's pages hold
     dr.ctx_len[case.seq_ids[1]] = dr.pages_per_seq * 16 - 2
     dr.ctx_append(case.t_i32(case.seq_ids[1:]), case.t_i32([4]), hid[:1], 16)
