@@ -34,7 +34,7 @@ KERNEL_NAMES = ["fuse", "ctx_kv", "norm", "qkv", "attn", "attn_merge", "o_proj",
 
 EXPORTS = [
     "dflash_workspace_bytes", "dflash_create", "dflash_destroy", "dflash_ctx_append",
-    "dflash_draft_block", "dflash_verify", "dflash_d2sd_draft", "dflash_verify_multi",
+    "dflash_draft_block", "dflash_verify", "dflash_verify_noalloc", "dflash_d2sd_draft", "dflash_verify_multi",
     "dflash_draft_sample", "dflash_verify_sample",
     "dflash_last_error", "dflash_read_error", "dflash_kernel_timer", "dflash_kernel_timer_read",
 ]
@@ -81,6 +81,8 @@ def _load():
         "dflash_ctx_append": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, vp]),
         "dflash_draft_block": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
         "dflash_verify": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, ctypes.c_float, u64, u64, vp, vp, vp, vp]),
+        "dflash_verify_noalloc": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, ctypes.c_float, u64, u64, vp, vp, vp,
+                                                 vp]),
         "dflash_d2sd_draft": (ctypes.c_int, [vp, i32, vp, vp, i32, vp, vp, vp, vp]),
         "dflash_verify_multi": (ctypes.c_int, [vp, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
         "dflash_draft_sample": (ctypes.c_int, [vp, i32, vp, vp, ctypes.c_float, u64, u64, vp, vp, vp]),
@@ -139,6 +141,15 @@ def dflash_verify(ctx, B, seq_ids, draft, target_logits, logits_dtype, temperatu
                   accept_len, next_token, commit_len, stream):
     return lib.dflash_verify(ctx, B, seq_ids, draft, target_logits, logits_dtype, float(temperature),
                              seed, step, accept_len, next_token, commit_len, stream)
+
+
+def dflash_verify_noalloc(ctx, B, seq_ids, draft, target_logits, logits_dtype, temperature, seed, step,
+                          accept_len, next_token, commit_len, stream):
+    return lib.dflash_verify_noalloc(ctx, B, seq_ids, draft, target_logits, logits_dtype, float(temperature),
+                                     seed, step, accept_len, next_token, commit_len, stream)
+
+
+VERIFY_SCRATCH_BYTES = 1 << 20  # DFLASH_VERIFY_SCRATCH_BYTES
 
 
 def dflash_d2sd_draft(ctx, B, seq_ids, anchor, K, drafts, conf, cuts, stream):

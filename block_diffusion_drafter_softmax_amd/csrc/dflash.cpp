@@ -212,6 +212,7 @@ struct Timer {
 }  // namespace
 
 struct dflash_ctx {
+  int device;  // the GPU current at dflash_create
   dflash_config c;
   dflash_weights w;
   dflash_kv kv;
@@ -364,6 +365,9 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, const dflas
       rope[((size_t)p * half + j) * 2 + 0] = (float)std::cos(ang);
       rope[((size_t)p * half + j) * 2 + 1] = (float)std::sin(ang);
     }
+  int device = 0;
+  HIP_OK(hipGetDevice(&device));
+  HIP_OK(dflash_verify_scratch_setup(device));  // dflash_verify_noalloc's static scratch on this GPU
   char* ws = static_cast<char*>(workspace);
   HIP_OK(hipMemcpy(ws + L.alpha, alpha.data(), alpha.size() * 4, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(ws + L.rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
@@ -392,6 +396,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, const dflas
   HIP_OK(hipStreamSynchronize(nullptr));
 
   dflash_ctx* ctx = new dflash_ctx();
+  ctx->device = device;
   ctx->c = c;
   ctx->w = *w;
   ctx->kv = *kv;
@@ -706,6 +711,66 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
   return ctx->launch(DFLASH_K_ARGMAX, stream, [&] { return dflash_launch_argmax(&ma, stream); });
 }
 
+// Greedy or temperature-1 verification; the rows-pass and sampling-pass
+// partials go to the workspace, or (noalloc) to the static scratch array of
+// the handle's GPU.
+int verify_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* draft, const void* target_logits,
+                int32_t logits_dtype, float temperature, uint64_t seed, uint64_t step, int32_t* accept_len,
+                int32_t* next_token, int32_t* commit_len, hipStream_t stream, bool noalloc) {
+  if (!ctx) return fail(DFLASH_ERR_INVALID_ARG, "ctx is null");
+  const dflash_config& c = ctx->c;
+  if (B < 1 || B > c.max_batch) return fail(DFLASH_ERR_INVALID_ARG, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
+  if (!seq_ids || !draft || !target_logits || !accept_len || !next_token)
+    return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
+  if (logits_dtype != DFLASH_DTYPE_BF16 && logits_dtype != DFLASH_DTYPE_F32)
+    return fail(DFLASH_ERR_INVALID_ARG, "logits_dtype must be DFLASH_DTYPE_BF16 or DFLASH_DTYPE_F32");
+  if (temperature != 0.f && temperature != 1.f)
+    return fail(DFLASH_ERR_UNSUPPORTED, "temperature must be 0 (greedy) or 1");
+  const Layout& L = ctx->L;
+  VerifyArgs va{};
+  va.logits = target_logits;
+  va.dtype = logits_dtype;
+  va.B = B;
+  va.N = c.block_size;
+  va.V = c.vocab;
+  va.chunk = kVerifyChunk;
+  va.n_chunks = L.n_vchunks;
+  va.s_chunk = sample_chunk(c.vocab, (long long)B);
+  va.s_n_chunks = (c.vocab + va.s_chunk - 1) / va.s_chunk;
+  va.seq_ids = seq_ids;
+  va.draft = draft;
+  va.temp1 = temperature == 1.f;
+  if (noalloc) {  // partials in the static scratch: rows pass, then (temperature 1) sampling pass
+    const size_t part_b = align256((size_t)B * c.block_size * L.n_vchunks * 2 * sizeof(float));
+    const size_t spart_b = va.temp1 ? align256((size_t)B * va.s_n_chunks * 2 * sizeof(float)) : 0;
+    if (part_b + spart_b > DFLASH_VERIFY_SCRATCH_BYTES)
+      return fail(DFLASH_ERR_CAPACITY,
+                  "dflash_verify_noalloc: B=%d needs %zu bytes of scratch, the static scratch holds %u "
+                  "(dflash_verify takes its partials from the workspace)",
+                  B, part_b + spart_b, (unsigned)DFLASH_VERIFY_SCRATCH_BYTES);
+    char* scratch = reinterpret_cast<char*>(dflash_verify_scratch(ctx->device));
+    if (!scratch) return fail(DFLASH_ERR_HIP, "static scratch of device %d is not set up", ctx->device);
+    va.part = reinterpret_cast<float*>(scratch);
+    va.spart = reinterpret_cast<float*>(scratch + part_b);
+  } else {
+    va.part = ctx->at<float>(L.vpart);
+    va.spart = ctx->at<float>(L.spart);
+  }
+  va.accept_len = accept_len;
+  va.next_token = next_token;
+  va.commit_len = commit_len;
+  va.seed = seed;
+  va.step = step;
+  va.err = ctx->kv.error_word;
+  va.inv_scale = 1.f;
+  if (noalloc) {  // not routed through the kernel timer, whose events are created on demand
+    const hipError_t e = dflash_launch_verify(&va, stream);
+    if (e != hipSuccess) return fail(DFLASH_ERR_HIP, "verification launch: %s", hipGetErrorString(e));
+    return DFLASH_OK;
+  }
+  return ctx->launch(DFLASH_K_VERIFY, stream, [&] { return dflash_launch_verify(&va, stream); });
+}
+
 }  // namespace
 
 extern "C" {
@@ -760,39 +825,16 @@ int dflash_d2sd_draft(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
 int dflash_verify(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* draft, const void* target_logits,
                   int32_t logits_dtype, float temperature, uint64_t seed, uint64_t step, int32_t* accept_len,
                   int32_t* next_token, int32_t* commit_len, hipStream_t stream) {
-  if (!ctx) return fail(DFLASH_ERR_INVALID_ARG, "ctx is null");
-  const dflash_config& c = ctx->c;
-  if (B < 1 || B > c.max_batch) return fail(DFLASH_ERR_INVALID_ARG, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
-  if (!seq_ids || !draft || !target_logits || !accept_len || !next_token)
-    return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
-  if (logits_dtype != DFLASH_DTYPE_BF16 && logits_dtype != DFLASH_DTYPE_F32)
-    return fail(DFLASH_ERR_INVALID_ARG, "logits_dtype must be DFLASH_DTYPE_BF16 or DFLASH_DTYPE_F32");
-  if (temperature != 0.f && temperature != 1.f)
-    return fail(DFLASH_ERR_UNSUPPORTED, "temperature must be 0 (greedy) or 1");
-  const Layout& L = ctx->L;
-  VerifyArgs va{};
-  va.logits = target_logits;
-  va.dtype = logits_dtype;
-  va.B = B;
-  va.N = c.block_size;
-  va.V = c.vocab;
-  va.chunk = kVerifyChunk;
-  va.n_chunks = L.n_vchunks;
-  va.s_chunk = sample_chunk(c.vocab, (long long)B);
-  va.s_n_chunks = (c.vocab + va.s_chunk - 1) / va.s_chunk;
-  va.seq_ids = seq_ids;
-  va.draft = draft;
-  va.part = ctx->at<float>(L.vpart);
-  va.spart = ctx->at<float>(L.spart);
-  va.accept_len = accept_len;
-  va.next_token = next_token;
-  va.commit_len = commit_len;
-  va.temp1 = temperature == 1.f;
-  va.seed = seed;
-  va.step = step;
-  va.err = ctx->kv.error_word;
-  va.inv_scale = 1.f;
-  return ctx->launch(DFLASH_K_VERIFY, stream, [&] { return dflash_launch_verify(&va, stream); });
+  return verify_impl(ctx, B, seq_ids, draft, target_logits, logits_dtype, temperature, seed, step, accept_len,
+                     next_token, commit_len, stream, false);
+}
+
+int dflash_verify_noalloc(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* draft,
+                          const void* target_logits, int32_t logits_dtype, float temperature, uint64_t seed,
+                          uint64_t step, int32_t* accept_len, int32_t* next_token, int32_t* commit_len,
+                          hipStream_t stream) {
+  return verify_impl(ctx, B, seq_ids, draft, target_logits, logits_dtype, temperature, seed, step, accept_len,
+                     next_token, commit_len, stream, true);
 }
 
 int dflash_draft_sample(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor, float temperature,

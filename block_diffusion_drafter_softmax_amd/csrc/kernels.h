@@ -287,4 +287,6 @@ hipError_t dflash_launch_draft_sample(const VerifyArgs* a, hipStream_t st);
 hipError_t dflash_launch_d2sd_select(const D2sdArgs* a, hipStream_t st);
 hipError_t dflash_launch_d2sd_assemble(const D2sdArgs* a, hipStream_t st);
 hipError_t dflash_launch_pick(const PickArgs* a, hipStream_t st);
+hipError_t dflash_verify_scratch_setup(int device);
+float* dflash_verify_scratch(int device);
 }

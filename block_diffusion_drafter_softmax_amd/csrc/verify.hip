@@ -16,6 +16,8 @@
 // boundaries order the passes: a device-scope hand-off inside a kernel
 // costs an L2 write-back per workgroup, which thousands of workgroups (32
 // sequences x 16 rows x 5 chunks) cannot afford.
+#include <mutex>
+
 #include "common.h"
 #include "dflash.h"
 
@@ -399,4 +401,39 @@ extern "C" hipError_t dflash_launch_verify(const VerifyArgs* a, hipStream_t st) 
   e = launch_kernel(verify_sample_kernel, dim3(a->s_n_chunks, a->B), dim3(SCAN_THREADS), 0, st, *a);
   if (e != hipSuccess) return e;
   return launch_kernel(verify_pick_kernel, dim3(a->B), dim3(64), 0, st, *a);
+}
+
+// ------------------------------------------------------- static scratch
+// The partials of dflash_verify_noalloc, the verification for callers that
+// cannot allocate device memory: a file-scope array, one copy per GPU, held
+// until the process ends. On the host the array's name is only a stand-in
+// for the device variable, never a device address: the set-up below looks
+// up each device's address once (hipGetSymbolAddress) and the launches
+// take that pointer.
+static __device__ __align__(256) float scratch[DFLASH_VERIFY_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kScratchDevices];  // address of `scratch` on each device; null until set up
+}  // namespace
+
+// Called by dflash_create with `device` current; later calls on the same
+// device return at once.
+extern "C" hipError_t dflash_verify_scratch_setup(int device) {
+  if (device < 0 || device >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[device]) return hipSuccess;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch[device] = static_cast<float*>(p);
+  return hipSuccess;
+}
+
+// Device address of the scratch array on `device`, or null if not set up.
+extern "C" float* dflash_verify_scratch(int device) {
+  if (device < 0 || device >= kScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch[device];
 }

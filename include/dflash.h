@@ -203,6 +203,30 @@ int dflash_verify(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int3
                   uint64_t seed, uint64_t step, int32_t* accept_len, int32_t* next_token,
                   int32_t* commit_len, hipStream_t stream);
 
+/* Verification that allocates nothing, for callers that cannot allocate
+ * device memory or must not touch the handle's workspace (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * Arguments, outputs and results are exactly those of dflash_verify (the
+ * same kernels; bit-identical outputs). The kernels' partial results live
+ * in a static device array of DFLASH_VERIFY_SCRATCH_BYTES per GPU (held
+ * until the process ends, its address looked up once per device by
+ * dflash_create) instead of the workspace; the call needs
+ *   8 * B * N * ceil(V / 32768) bytes (greedy), plus about
+ *   8 * B * ceil(V / chunk) bytes at temperature 1 (chunk: 1024 .. V logits,
+ *   about 512 sampling work items per call),
+ * each part rounded up to 256 bytes; a call needing more returns
+ * DFLASH_ERR_CAPACITY with a message and enqueues nothing. No hipMalloc,
+ * hipFree or allocating library routine is called. Every call on a GPU
+ * shares that GPU's array (the last call's partials stay in it; every
+ * partial a call reads it wrote first): calls that overlap on one GPU --
+ * on different streams, or from several handles -- race and must be
+ * ordered by the caller. */
+#define DFLASH_VERIFY_SCRATCH_BYTES (1u << 20)
+int dflash_verify_noalloc(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* draft,
+                          const void* target_logits, int32_t logits_dtype, float temperature,
+                          uint64_t seed, uint64_t step, int32_t* accept_len, int32_t* next_token,
+                          int32_t* commit_len, hipStream_t stream);
+
 /* Sampled drafting at temperature > 0 [DFLASH Methodology 2-3, with a
  * sampled proposal]. The forward pass of dflash_draft_block, then for each
  * draft row r (position r + 1) the token d = argmax_k (z[r,k] / temperature
