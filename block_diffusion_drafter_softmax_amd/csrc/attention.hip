@@ -78,21 +78,39 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   __shared__ long long poff[SLOTS];  // element offset in `pages` of each page slot's K block (this kv head); -1: block
   __shared__ int cnt[SLOTS];         // valid key slots of each page slot
 
-  const int kvh = blockIdx.y;
+  // Grid position (x: item slot, y: kv head, z: sequence group * splits + split).
+  // With one block per workgroup (cand == 1) the grid is 1-D instead and
+  // numbered so that all workgroups of one (sequence group, kv head) -- every
+  // item of every candidate block -- are dealt to the same XCD (the hardware
+  // deals workgroups to the 8 XCDs round robin), one after the other: the
+  // head's query rows then come from memory once, not once per XCD, and a
+  // context chunk that several candidate blocks attend to once, then from
+  // that XCD's L2.
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  if (a.xcd_order) {
+    const int L = blockIdx.x, local = L >> 3, per = a.xcd_items * a.grp;
+    const int T = (local / per) * 8 + (L & 7);  // (sequence group, kv head), head fastest
+    if (T >= a.xcd_tuples) return;
+    const int rem = local % per;
+    bx = rem / a.grp;
+    by = T % a.n_kv;
+    bz = T / a.n_kv * a.grp + rem % a.grp;
+  }
+  const int kvh = by;
   const int splits = (a.grp + a.cand - 1) / a.cand;  // workgroups per group along z
-  int c0 = (blockIdx.z % splits) * a.cand;           // first candidate of this split
+  int c0 = (bz % splits) * a.cand;                   // first candidate of this split
   int n_cand = min(a.cand, a.grp - c0);              // candidates of this split
   // x < cand: item 0 (holds the block page) for candidate c0 + x alone;
   // x >= cand: context-only item x - cand + 1 for all n_cand candidates
   int item = 0;
-  if ((int)blockIdx.x < a.cand) {
-    if ((int)blockIdx.x >= n_cand) return;
-    c0 += blockIdx.x;
+  if (bx < a.cand) {
+    if (bx >= n_cand) return;
+    c0 += bx;
     n_cand = 1;
   } else {
-    item = blockIdx.x - a.cand + 1;
+    item = bx - a.cand + 1;
   }
-  const int b0 = blockIdx.z / splits * a.grp + c0;   // the workgroup's first block
+  const int b0 = bz / splits * a.grp + c0;   // the workgroup's first block
   const int cpi = MULTI ? a.cpi : 1;
   const int tid = threadIdx.x, nthreads = blockDim.x;
   // page-table entry of page slot tid (< SLOTS <= nthreads), requested with
@@ -147,7 +165,7 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   bf16x8 qh[KD], ql[KD];
   {
     const uint16_t* qp = a.q + ((size_t)(b * a.N + n) * a.n_q + hq) * D + 8 * g;
-    const size_t q_lo = (size_t)(gridDim.z / splits * a.grp) * a.N * a.n_q * D;
+    const size_t q_lo = (size_t)a.n_blocks * a.N * a.n_q * D;
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd) {
       qh[kd] = ld8(qp + kd * 32);
@@ -414,7 +432,10 @@ extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim,
   const int G = a->n_q / a->n_kv, n_wr = G * a->N / 16;
   const int waves = std::max(a->cand * n_wr, MIN_WAVES);
   const int wgs_z = B / a->grp * ((a->grp + a->cand - 1) / a->cand);
-  const dim3 grid((a->n_ck + a->cpi - 1) / a->cpi + a->cand - 1, a->n_kv, wgs_z), block(64 * waves);
+  const int items = (a->n_ck + a->cpi - 1) / a->cpi + a->cand - 1;
+  dim3 grid(items, a->n_kv, wgs_z);
+  if (a->xcd_order) grid = dim3((a->xcd_tuples + 7) / 8 * 8 * a->xcd_items * a->grp);  // whole XCD rounds
+  const dim3 block(64 * waves);
   if (head_dim == 128) {
     if (a->cpi > 1) launch_kernel(attn_chunk_kernel<128, 1, true>, grid, block, 0, st, *a);
     else if (waves <= 8) launch_kernel(attn_chunk_kernel<128, 2, false>, grid, block, 0, st, *a);

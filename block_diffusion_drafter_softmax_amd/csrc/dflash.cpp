@@ -608,6 +608,10 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
     const long long wgs_z = (long long)(B / grp) * ((grp + aa.cand - 1) / aa.cand);
     const long long chunks = wgs_z * c.n_kv_heads * L.n_ck;
     aa.cpi = (int)std::min<long long>(8, std::max<long long>(1, (chunks + kAttnItems - 1) / kAttnItems));
+    aa.n_blocks = B;
+    aa.xcd_order = aa.cand == 1;
+    aa.xcd_items = (L.n_ck + aa.cpi - 1) / aa.cpi;
+    aa.xcd_tuples = (B / grp) * c.n_kv_heads;
   }
   aa.max_pages_per_seq = c.max_pages_per_seq;
   aa.n_pages = c.n_pages;

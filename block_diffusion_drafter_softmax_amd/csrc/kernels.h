@@ -119,6 +119,9 @@ struct AttnArgs {
   const int* blk_pages;    // the call's page-table row of each block [B][max_pages_per_seq]
   int grp;                 // consecutive blocks that share one sequence's context (B % grp == 0)
   int cand;                // blocks of a group one workgroup takes (1 .. grp): a context chunk is read once for them
+  int n_blocks;            // B, the blocks of the call
+  int xcd_order;           // cand == 1: 1-D grid, all workgroups of a (sequence group, kv head) on one XCD
+  int xcd_items, xcd_tuples;  // items per (block, kv head); (B / grp) * n_kv (sequence groups x kv heads)
 };
 
 // ------------------------------------------------------------ small kernels
