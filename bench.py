@@ -58,17 +58,17 @@ def gate_up_bytes(cfg, M):
     return 2 * I * H * 2 + M * H * 4 + M * I * 4
 
 
-def traffic_from_profile():
-    """HBM bytes per launch of the gate/up kernel from the committed
-    rocprofv3 FETCH_SIZE/WRITE_SIZE summary, if it was taken on the current
-    kernel sources; else None."""
-    p = os.path.join(ROOT, "profiles", "gate_up_qwen3_8b_traffic.json")
+def traffic_from_profile(name="gate_up_qwen3_8b", kernel="gate_up"):
+    """HBM bytes per launch of a kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary profiles/<name>_traffic.json, if it was
+    taken on the kernel's current sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(p):
         return None
     sys.path.insert(0, ROOT)
-    from profiling import source_hash
+    from profiling import KERNEL_SOURCES, source_hash
     d = json.load(open(p))
-    if d.get("source_sha256_16") != source_hash():
+    if d.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return d.get("bytes_per_launch")
 
@@ -334,6 +334,14 @@ def run_batched(args, name):
     else:
         achieved, peak, unit = dk["flops"] / unit_s / 1e12, MFMA_PEAK_TFS, "TFLOP/s"
     accepted = float(acc_main.float().mean())
+    committed = float(com_main.float().sum())
+    accept_src = f"the timed step's verification over its {Bn} sequences (one agreement-model draw each)"
+    if not K:  # more agreement-model draws around the timed draft: at least --accept-draws sequence samples
+        n_draws = -(-args.accept_draws // Bn)
+        ma, mc = accept_model(dr, cfg, seq, draft, 0, n_draws, temperature=temp)
+        accepted, committed = ma, mc * Bn
+        accept_src = (f"{'temperature-1' if temp else 'greedy'} verify of the timed draft ({Bn} sequences) "
+                      f"against {n_draws} draws of the synthetic agreement model (p = {cfg['agreement']})")
     res = {
         "metric": "draft tokens/sec per GPU (block=16, batched drafter+verify); % roofline",
         "value": round(Bn * (N - 1) / (ms_step / 1e3), 1), "unit": "draft tokens/s", "n_gpus": 1,
@@ -348,14 +356,15 @@ def run_batched(args, name):
                                f"I {cfg['intermediate']}, V {V}",
                    "global_batch": Bn, "block": N, "launch": "eager"},
         "roofline": {"bound": dk["bound"], "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": dk["label"],
+                     "frac": round(achieved / peak, 4), "traffic": traffic_from_profile(f"{dk['name']}_{name}", dk["name"]),
+                     "kernel": dk["label"],
                      "bytes_per_unit": int(dk["bytes"]), "flops_per_unit": dk["flops"],
                      "us_per_unit": round(unit_s * 1e6, 2), "launches_timed": k_n},
         "step_roofline": {"bound": "mixed", "t_roof_us": rl["t_roof_us"], "phases": rl["phases"],
                           "frac": round(rl["t_roof_us"] / (ms_step * 1e3), 4)},
         "mean_accept": round(accepted, 3),
-        "committed_tok_s": round(float(com_main.float().sum()) / (ms_step / 1e3), 1),
-        "accept_source": f"the timed step's verification over its {Bn} sequences (one agreement-model draw each)",
+        "committed_tok_s": round(committed / (ms_step / 1e3), 1),
+        "accept_source": accept_src,
         "first_pass_only": None if not K else {
             "ms_per_step": round(first_ms, 4), "draft_tok_s": round(Bn * (N - 1) / (first_ms / 1e3), 1),
             "t_roof_us": rl1["t_roof_us"], "frac": round(rl1["t_roof_us"] / (first_ms * 1e3), 4)},

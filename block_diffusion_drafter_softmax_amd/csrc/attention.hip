@@ -347,9 +347,16 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
   __shared__ float sm[CG], sd[CG];
   __shared__ f32x4 sn[CG][TPR];
   const int G = a.n_q / a.n_kv, R = G * a.N;
-  const int r = blockIdx.x % R;
-  const int kvh = (blockIdx.x / R) % a.n_kv;
-  const int b = blockIdx.x / R / a.n_kv;
+  // The rows of one (block, kv head) are dealt to one XCD, the XCD whose
+  // attention workgroups wrote the head's partials when the attention grid
+  // is XCD-ordered (tuple (block, head) -> XCD tuple % 8 there too, with one
+  // block per sequence group): the partials are read from that XCD's L2.
+  const int local = blockIdx.x >> 3;
+  const int T = (local / R) * 8 + (blockIdx.x & 7);  // b * n_kv + kvh
+  if (T >= B * a.n_kv) return;
+  const int r = local % R;
+  const int kvh = T % a.n_kv;
+  const int b = T / a.n_kv;
   const int dq = threadIdx.x % TPR, cg = threadIdx.x / TPR;
   const size_t unit0 = ((size_t)b * a.n_kv + kvh) * a.n_ck;
   constexpr int GRP = 8;  // loads in flight per thread (more costs time on gfx950)
@@ -451,7 +458,7 @@ extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim,
 
 extern "C" hipError_t dflash_launch_attn_merge(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
   const int G = a->n_q / a->n_kv, R = G * a->N;
-  const dim3 grid(B * a->n_kv * R), block(256);
+  const dim3 grid((B * a->n_kv + 7) / 8 * 8 * R), block(256);  // whole XCD rounds of (block, kv head) tuples
   if (head_dim == 128) launch_kernel(attn_merge_kernel<128>, grid, block, 0, st, *a, B);
   else launch_kernel(attn_merge_kernel<64>, grid, block, 0, st, *a, B);
   return hipGetLastError();

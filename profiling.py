@@ -7,8 +7,11 @@ FETCH_SIZE / WRITE_SIZE readings calibrate the HBM traffic counters.
 
 ``... profiling stats <kernel_stats.csv> <out.md> <command> [<kernel_trace.csv> [<skip_last> [<step-end kernel>]]]`` and
 ``... profiling traffic <kernel regex> <fetch.csv> <write.csv> <copy_fetch.csv>
-<copy_write.csv> <out.json> <out.md> <commands...>`` turn rocprofv3 CSV output
-into the short text summaries kept with the sources.
+<copy_write.csv> <out.json> <out.md> <commands...>`` and
+``... profiling counters <workload> <dir> <out.md> <commands...>`` (per-kernel
+FETCH_SIZE / WRITE_SIZE and MFMA utilisation of one bench workload, from the
+runs under <dir>/pmc_{fetch,write,mfma,copy_fetch,copy_write}) turn rocprofv3
+CSV output into the short text summaries kept with the sources.
 """
 import csv
 import hashlib
@@ -20,9 +23,14 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "block_diffusion_drafter_softmax_amd", "csrc")
 
-# Sources the streaming GEMM kernels are compiled from: a traffic summary is
-# valid only for the sources it was taken on.
+# Sources each measured kernel is compiled from: a traffic summary is valid
+# only for the sources it was taken on.
 GEMM_SOURCES = [os.path.join(CSRC, f) for f in ("gemm.hip", "stream.h", "common.h", "kernels.h")]
+KERNEL_SOURCES = {
+    "gate_up": GEMM_SOURCES,
+    "attention": [os.path.join(CSRC, f) for f in ("attention.hip", "common.h", "kernels.h")],
+    "lm_head": [os.path.join(CSRC, f) for f in ("mm.hip", "lmhead.hip", "stream.h", "common.h", "kernels.h")],
+}
 COPY_BYTES = 256 << 20
 
 
@@ -50,9 +58,12 @@ def _rows(path):
 
 
 def counter_per_dispatch(path, name_re, counter):
-    """Mean counter value (KiB) over the dispatches whose kernel name matches."""
+    """Mean counter value (KiB) over the dispatches whose kernel name matches
+    (`regex#grid` also requires that grid size, in threads)."""
+    name_re, _, grid = name_re.partition("#")
     vals = [float(r["Counter_Value"]) for r in _rows(path)
-            if r["Counter_Name"] == counter and re.search(name_re, r["Kernel_Name"])]
+            if r["Counter_Name"] == counter and re.search(name_re, r["Kernel_Name"])
+            and (not grid or r["Grid_Size"] == grid)]
     if not vals:
         raise SystemExit(f"no {counter} rows for /{name_re}/ in {path}")
     return sum(vals) / len(vals), len(vals)
@@ -123,14 +134,15 @@ def step_breakdown(trace_csv, last_kernel="verify_rows", steps=10, skip_last=0):
     return out
 
 
-def write_traffic(name_re, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_json, out_md, commands):
+def write_traffic(name_re, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_json, out_md, commands,
+                  sources=GEMM_SOURCES):
     ff, ff_counted = copy_factor(copy_fetch_csv, "FETCH_SIZE")
     wf, wf_counted = copy_factor(copy_write_csv, "WRITE_SIZE")
     fetch_kib, n_f = counter_per_dispatch(fetch_csv, name_re, "FETCH_SIZE")
     write_kib, n_w = counter_per_dispatch(write_csv, name_re, "WRITE_SIZE")
     fetch_b = fetch_kib * 1024 * ff
     write_b = write_kib * 1024 * wf
-    d = {"kernel_regex": name_re, "source_sha256_16": source_hash(),
+    d = {"kernel_regex": name_re, "source_sha256_16": source_hash(sources),
          "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
          "dispatches": [n_f, n_w], "fetch_factor": ff, "write_factor": wf,
          "copy_counted_kib": {"FETCH_SIZE": ff_counted, "WRITE_SIZE": wf_counted},
@@ -139,7 +151,8 @@ def write_traffic(name_re, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
         json.dump(d, f, indent=1)
         f.write("\n")
     lines = ["# HBM traffic per launch, rocprofv3 --pmc", "",
-             f"Kernel: `{name_re}` ({n_f} dispatches), sources sha256[:16] {d['source_sha256_16']}.", "",
+             f"Kernel: `{name_re}` ({n_f} dispatches; `#n`: grid size n only), sources sha256[:16] "
+             f"{d['source_sha256_16']} ({', '.join(os.path.basename(p) for p in sources)}).", "",
              "Calibration: a plain 256 MiB device copy reads "
              f"FETCH_SIZE {ff_counted:.0f} KiB and WRITE_SIZE {wf_counted:.0f} KiB for 262144 KiB moved, "
              f"so FETCH_SIZE is scaled by {ff:.4f} and WRITE_SIZE by {wf:.4f}.", "",
@@ -152,6 +165,74 @@ def write_traffic(name_re, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
     return d
 
 
+def _dispatches(path):
+    """{dispatch id: (kernel label, grid size, {counter: value}, duration ns)} of a counter run."""
+    d = {}
+    for r in _rows(path):
+        k = int(r["Dispatch_Id"])
+        name = r["Kernel_Name"].replace("void ", "").split("(")[0]
+        e = d.setdefault(k, [name, int(r["Grid_Size"]), {}, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])])
+        e[2][r["Counter_Name"]] = float(r["Counter_Value"])
+    return d
+
+
+def _label(name, grid, last):
+    """Tell the streaming GEMM's launches of the Qwen3-8B-shaped step apart
+    by grid size (O and down share one: by their order); the tiled GEMM's by
+    grid size (threads)."""
+    if name.startswith("mm_kernel"):
+        return f"{name} (grid {grid})", last
+    if name != "ws_kernel<1, 4, 0>":
+        return name, last
+    n = {98304: "QKV", 114688: "append K/V"}.get(grid, "")
+    if grid == 65536:
+        n = "O" if last != "O" else "down"
+        last = n
+    return f"{name} ({n})" if n else name, last
+
+
+def write_counters(workload, d, out_md, commands):
+    """Per-kernel HBM bytes (FETCH_SIZE, WRITE_SIZE scaled by the copy probe's
+    factors) and MFMA utilisation (MfmaUtil: the summed SQ_VALU_MFMA_BUSY_CYCLES
+    over GRBM_GUI_ACTIVE of one XCC times the 1024 SIMDs) per dispatch."""
+    ff, _ = copy_factor(os.path.join(d, "pmc_copy_fetch", "run_counter_collection.csv"), "FETCH_SIZE")
+    wf, _ = copy_factor(os.path.join(d, "pmc_copy_write", "run_counter_collection.csv"), "WRITE_SIZE")
+    agg = {}
+    for kind in ("fetch", "write", "mfma"):
+        p = os.path.join(d, f"pmc_{kind}", "run_counter_collection.csv")
+        if not os.path.exists(p):
+            continue
+        last = None
+        for k, (name, grid, c, dur) in sorted(_dispatches(p).items()):
+            lab, last = _label(name, grid, last)
+            a = agg.setdefault(lab, {})
+            for cn, v in c.items():
+                a.setdefault(cn, []).append(v)
+            a.setdefault("dur_" + kind, []).append(dur)
+    mean = lambda v: sum(v) / len(v)
+    lines = [f"# Per-kernel counters, rocprofv3 --pmc: workload `{workload}`", "",
+             f"FETCH_SIZE scaled by {ff:.4f}, WRITE_SIZE by {wf:.4f} (a plain 256 MiB device copy); "
+             "MfmaUtil = sum of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE of one XCC x 1024 SIMDs), "
+             "the profiler's own formula (GRBM_GUI_ACTIVE is summed over the 8 XCCs in the CSV, so "
+             "divided by 8). Kernels with no MFMA work show 0.", "",
+             "| kernel | dispatches | FETCH bytes / dispatch | WRITE bytes / dispatch | MfmaUtil % |", "|---|---|---|---|---|"]
+    rows = []
+    for lab, a in agg.items():
+        f = mean(a["FETCH_SIZE"]) * 1024 * ff if "FETCH_SIZE" in a else float("nan")
+        w = mean(a["WRITE_SIZE"]) * 1024 * wf if "WRITE_SIZE" in a else float("nan")
+        busy, gui = a.get("SQ_VALU_MFMA_BUSY_CYCLES"), a.get("GRBM_GUI_ACTIVE")
+        util = 100 * sum(busy) / (sum(gui) / 8 * 1024) if busy and gui and sum(gui) else 0.0
+        n = len(a.get("FETCH_SIZE", a.get("SQ_VALU_MFMA_BUSY_CYCLES", [0])))
+        rows.append((f, lab, n, w, util))
+    for f, lab, n, w, util in sorted(rows, key=lambda r: -(r[0] if r[0] == r[0] else 0)):
+        if f != f or f < 1e5:
+            continue
+        lines.append(f"| `{lab}` | {n} | {f:,.0f} | {w:,.0f} | {util:.1f} |")
+    lines += ["", "Commands:", "", "```"] + list(commands) + ["```"]
+    with open(out_md, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+
+
 def main(argv):
     if not argv:
         raise SystemExit(__doc__)
@@ -160,8 +241,14 @@ def main(argv):
     elif argv[0] == "stats":
         write_stats(argv[1], argv[2], argv[3], argv[4] if len(argv) > 4 else None,
                     int(argv[5]) if len(argv) > 5 else 0, argv[6] if len(argv) > 6 else "verify_rows")
-    elif argv[0] == "traffic":
-        print(json.dumps(write_traffic(*argv[1:8], argv[8:])))
+    elif argv[0] == "traffic":  # traffic [--sources gate_up|attention|lm_head] <regex> <csvs...> <json> <md> <cmds>
+        srcs = GEMM_SOURCES
+        if argv[1] == "--sources":
+            srcs = KERNEL_SOURCES[argv[2]]
+            argv = argv[2:]
+        print(json.dumps(write_traffic(*argv[1:8], argv[8:], sources=srcs)))
+    elif argv[0] == "counters":
+        write_counters(argv[1], argv[2], argv[3], argv[4:])
     else:
         raise SystemExit(__doc__)
 
