@@ -195,16 +195,16 @@ def dominant_kernel(cfg, ctx):
     launch each per layer) and LM head, the one with the largest roofline
     time per step: max(bytes / 8 TB/s, flops / 2.5 PF) times its units per
     step (a layer, or the whole LM head). Algorithmic bytes: the weights or
-    the context and block K/V once, activations in (split, 4 bytes a
-    value) and out; flops: the method's 2 per multiply-add (not the split
+    the context K/V once, activations in (split, 4 bytes a value) and
+    out; flops: the method's 2 per multiply-add (not the split
     activation's second product)."""
     from block_diffusion_drafter_softmax_amd import _binding as B
     D, H, I, V, N = (cfg[k] for k in ("n_layers", "hidden", "intermediate", "vocab", "block_size"))
     d, nq, nkv = cfg["head_dim"], cfg["n_q_heads"], cfg["n_kv_heads"]
     Bn = len(ctx)
-    M, keys = Bn * N, int(np.sum(ctx)) + Bn * N
+    M, keys = Bn * N, int(np.sum(ctx))  # the chunk kernel takes the context keys (the merge the block's)
     cands = {
-        "attention": ("block attention (context + block K/V of one layer)", B.K_ATTN, D,
+        "attention": ("block attention over the context K/V (one layer)", B.K_ATTN, D,
                       keys * 2 * nkv * d * 2 + M * nq * d * 4, 4.0 * nq * N * keys * d),
         "gate_up": ("gate/up projection + SwiGLU (one layer)", B.K_GATE_UP, D,
                     2 * I * H * 2 + M * H * 4 + M * I * 4, 2.0 * M * 2 * I * H),

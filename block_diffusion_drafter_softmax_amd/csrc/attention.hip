@@ -3,10 +3,12 @@
 // is not autoregressive; the fused target context enters each draft layer
 // as keys/values only).
 //
-// Keys are numbered in a virtual order: slots 0..15 are the block's own K/V
-// (laid out like one cache page; slots >= N are invalid), then context key
-// j is virtual key 16 + j, so virtual page p >= 1 is context page p - 1.
-// Work item = (chunk of CH = 128 virtual keys, kv head, sequence). A
+// Work item = (key set, kv head, sequence). Item 0 is the block's own N
+// keys (laid out like one cache page; slots >= N are invalid): a short
+// item, two key tiles of compute. Item i >= 1 is the context chunk of CH =
+// 128 keys from 128 * (i - 1) (page p of the sequence holds keys 16p ..
+// 16p+15), so a context of 128 * n keys gives 1 + n items per kv head; the
+// one workgroup past a CU each (at 4096 keys) is a light block item. A
 // workgroup holds all R = (n_q/n_kv)*N query rows of one kv head (GQA: a
 // K/V tile is read from HBM once for the whole query group), one computing
 // wave per 16 rows, and at least 8 waves for staging. The chunk's page
@@ -35,10 +37,9 @@
 //
 // Blocks that share a sequence (the dual-pass drafter's candidates: grp
 // consecutive blocks) share its context: a workgroup takes `cand` of them
-// for a context-only item, with cand * R / 16 computing waves, so each
-// context chunk is read from HBM once for all of them. Item 0 holds
-// the block page, which differs per candidate: it gets one workgroup per
-// candidate.
+// for a context item, with cand * R / 16 computing waves, so each context
+// chunk is read from HBM once for all of them. Item 0, the block keys,
+// differs per candidate: it gets one workgroup per candidate.
 #include <algorithm>
 
 #include "common.h"
@@ -47,7 +48,7 @@
 namespace {
 DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-constexpr int CH = 128;  // virtual keys per chunk (a work item takes cpi chunks)
+constexpr int CH = 128;  // context keys per chunk (a context item takes cpi chunks)
 constexpr int PAGES = CH / 16;
 constexpr int MIN_WAVES = 8;  // staging waves per workgroup
 constexpr int CPI_MAX = 8;    // chunks per work item, at most
@@ -69,7 +70,12 @@ DEV int tile_key(int j, int g, int i) { return (j >> 1) * 32 + 8 * g + (j & 1) *
 // NACC: accumulator sets for the S products (2: hi and lo separately, more
 // independent MFMA chains; 1 where 1024-thread workgroups cap the registers).
 // MULTI: work items of up to CPI_MAX chunks.
-template <int D, int NACC, bool MULTI>
+// KS = 2 (multi-chunk items, where the workgroup's staging-only waves
+// allow it): twice as many computing waves as query row groups; the second
+// group takes the second half of every chunk's keys for the same rows,
+// with its own online softmax, and hands (max, sum, O) to its partner
+// through LDS at the end.
+template <int D, int NACC, bool MULTI, int KS>
 __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs a) {
   constexpr int KP = D + 8;  // padded LDS row of one key (bf16 elements)
   constexpr int K_ELEMS = CH * KP, V_ELEMS = PAGES * D * 16;
@@ -100,8 +106,8 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   const int splits = (a.grp + a.cand - 1) / a.cand;  // workgroups per group along z
   int c0 = (bz % splits) * a.cand;                   // first candidate of this split
   int n_cand = min(a.cand, a.grp - c0);              // candidates of this split
-  // x < cand: item 0 (holds the block page) for candidate c0 + x alone;
-  // x >= cand: context-only item x - cand + 1 for all n_cand candidates
+  // x < cand: item 0 (the block keys) for candidate c0 + x alone;
+  // x >= cand: context item x - cand + 1 for all n_cand candidates
   int item = 0;
   if (bx < a.cand) {
     if (bx >= n_cand) return;
@@ -111,39 +117,39 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
     item = bx - a.cand + 1;
   }
   const int b0 = bz / splits * a.grp + c0;   // the workgroup's first block
+  const bool blk_item = item == 0;
   const int cpi = MULTI ? a.cpi : 1;
   const int tid = threadIdx.x, nthreads = blockDim.x;
   // page-table entry of page slot tid (< SLOTS <= nthreads), requested with
   // the plan from the call's per-block copy; clamped, used only if valid
   int raw_slot = 0;
-  if (tid < cpi * PAGES)
+  if (!blk_item && tid < cpi * PAGES)
     raw_slot = a.blk_pages[(size_t)b0 * a.max_pages_per_seq +
-                           clampi(item * cpi * PAGES + tid - 1, 0, a.max_pages_per_seq - 1)];
+                           clampi((item - 1) * cpi * PAGES + tid, 0, a.max_pages_per_seq - 1)];
   const int2 pl = *reinterpret_cast<const int2*>(a.plan + 2 * b0);  // (sequence, context length)
   const int seq = clampi(pl.x, 0, a.max_seqs - 1);
   const int L = clampi(pl.y, 0, a.max_pages_per_seq * 16);
-  const int item_begin = item * cpi * CH;
-  const int item_nv = min(16 + L, item_begin + cpi * CH) - item_begin;  // virtual keys in this item
+  const int c_begin = (item - 1) * cpi * CH;  // context items: first key
+  const int item_nv = blk_item ? a.N : min(L, c_begin + cpi * CH) - c_begin;  // keys in this item
   if (item_nv <= 0) return;
-  const int n_chunks = MULTI ? (item_nv + CH - 1) / CH : 1;
+  const int n_chunks = MULTI && !blk_item ? (item_nv + CH - 1) / CH : 1;
   const size_t page_elems = (size_t)2 * a.n_kv * 16 * D;
 
-  // Page slots of the item (virtual page 0 is the block; slots past the
-  // context point at the block and hold 0 valid keys).
+  // Page slots of the item (the block item's slot 0 is the block; slots
+  // past the keys point at the block, valid memory, and hold 0 valid keys).
   const uint16_t* blk_k = a.kblk + ((size_t)b0 * a.n_kv + kvh) * 16 * D;
   const uint16_t* blk_v = a.vblk + ((size_t)b0 * a.n_kv + kvh) * D * 16;
   if (tid < n_chunks * PAGES) {  // n_chunks * PAGES <= SLOTS <= nthreads: one slot per thread
     const int t = tid;
     long long off = -1;
     int n_ok = 0;
-    if (16 * t < item_nv) {
-      const int vp = item_begin / 16 + t;
-      if (vp > 0) {
-        const int raw = raw_slot;
-        if (raw < 0 || raw >= a.n_pages) set_error(a.err, DFLASH_DEV_BAD_PAGE);
-        off = (long long)clampi(raw, 0, a.n_pages - 1) * page_elems + (long long)kvh * 16 * D;
-      }
-      n_ok = vp == 0 ? a.N : min(16, item_nv - 16 * t);
+    if (blk_item) {
+      n_ok = t == 0 ? a.N : 0;
+    } else if (16 * t < item_nv) {
+      const int raw = raw_slot;
+      if (raw < 0 || raw >= a.n_pages) set_error(a.err, DFLASH_DEV_BAD_PAGE);
+      off = (long long)clampi(raw, 0, a.n_pages - 1) * page_elems + (long long)kvh * 16 * D;
+      n_ok = min(16, item_nv - 16 * t);
     }
     poff[t] = off;
     cnt[t] = n_ok;
@@ -152,10 +158,12 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int G = a.n_q / a.n_kv, R = G * a.N, n_wr = R / 16;
-  const bool computing = wave < n_cand * n_wr;
+  const int n_comp = n_cand * n_wr;  // computing waves per key group
+  const bool computing = wave < KS * n_comp;
+  const int kh = KS == 2 && wave >= n_comp ? 1 : 0;  // the wave's key group (wave-uniform)
   // staging: thread t moves unit t % (4D) of its page slots, K units first
   const bool isk_wave = __builtin_amdgcn_readfirstlane((int)(tid % (4 * D) < 2 * D));
-  const int wc = min(wave, n_cand * n_wr - 1);
+  const int wc = min(wave - kh * n_comp, n_comp - 1);
   const int cand = wc / n_wr, b = b0 + cand;  // the wave's block
   const int r = (wc % n_wr) * 16 + r16;
   const int hq = kvh * G + r / a.N, n = r % a.N;
@@ -177,9 +185,11 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mx = -INFINITY, l = 0.f;
+  // the block item's compute takes two key tiles: its keys, then a masked
+  // page (V stored as zeros, K masked in S)
+  const int st_pages = 2;
   for (int ci = 0; ci < n_chunks; ++ci) {
-    const int v_begin = item_begin + ci * CH;
-    const int nv = min(item_nv - ci * CH, CH);  // virtual keys in this chunk
+    const int nv = min(item_nv - ci * CH, CH);  // keys in this chunk
     const long long* cpo = poff + ci * PAGES;
     const int* ccnt = cnt + ci * PAGES;
     __syncthreads();  // page slots written; the previous chunk's LDS reads done
@@ -206,7 +216,22 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
       const int lds_off = isk ? (w % (D / 8)) * 8 : K_ELEMS + (e & 1) * D * 8 + (e >> 1) * 8;
       const uint16_t* blk = (isk ? blk_k : blk_v) + src_off;
       const uint16_t* pgs = a.pages + (isk ? 0 : (size_t)a.n_kv * 16 * D) + src_off;
-      if (p0 < SP) {
+      if (blk_item) {  // the block page (one load per thread), and the masked page's V as zeros
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (p0 == 0) v = *reinterpret_cast<const u32x4*>(blk);
+        for (int pi = p0; pi < st_pages; pi += SP) {
+          if (isk) {
+            if (pi == 0) *reinterpret_cast<u32x4*>(&lds[krow(w / (D / 8)) * KP + lds_off]) = v;
+          } else {
+            const int valid = ccnt[pi] - (e & 1) * 8;
+            u32x4 m;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              m[q] = (2 * q < valid ? 0xFFFFu : 0u) | (2 * q + 1 < valid ? 0xFFFF0000u : 0u);
+            *reinterpret_cast<u32x4*>(&lds[pi * D * 16 + lds_off]) = v & m;
+          }
+        }
+      } else if (p0 < SP) {
         for (int i0 = 0; i0 < passes; i0 += UB) {
           u32x4 buf[UB];
 #pragma unroll
@@ -238,10 +263,16 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
     // Key tile j = LDS rows 16j .. 16j+15; the lane holds S for keys
     // tile_key(j, g, 0..3) of its query. Multi-chunk items take a chunk as
     // HV = 2 halves of 64 keys, each with its own online-softmax update, so
-    // that the O accumulators kept across chunks fit the registers.
-    constexpr int HV = MULTI ? 2 : 1, NTH = NT / HV;
+    // that the O accumulators kept across chunks fit the registers; with
+    // KS = 2 each key group takes its own half.
+    constexpr int HV = MULTI || KS == 2 ? 2 : 1, NTH = NT / HV;
+    // key tiles with work: the block item's two (its keys, then a masked
+    // page), all of a context chunk's (wave-uniform)
+    const int nt_act = blk_item ? 2 : NTH;
 #pragma unroll
-    for (int hv = 0; hv < HV; ++hv) {
+    for (int hh = 0; hh < (KS == 2 ? 1 : HV); ++hh) {
+      const int hv = KS == 2 ? kh : hh;  // the half: a key group's own one with KS = 2
+      if (blk_item && hv > 0) break;
       f32x4 s[NTH];
       {
         f32x4 sa[NACC][NTH];
@@ -257,14 +288,16 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
             kf[j] = *reinterpret_cast<const bf16x8*>(&lds[(16 * (hv * NTH + j) + r16) * KP + kd * 32 + 8 * g]);
 #pragma unroll
           for (int j = 0; j < NTH; ++j) {
-            sa[0][j] = mfma16(kf[j], qh[kd], sa[0][j]);
-            sa[NACC - 1][j] = mfma16(kf[j], ql[kd], sa[NACC - 1][j]);
+            if (true) {
+              sa[0][j] = mfma16(kf[j], qh[kd], sa[0][j]);
+              sa[NACC - 1][j] = mfma16(kf[j], ql[kd], sa[NACC - 1][j]);
+            }
           }
         }
 #pragma unroll
         for (int j = 0; j < NTH; ++j) s[j] = NACC == 2 ? sa[0][j] + sa[NACC - 1][j] : sa[0][j];
       }
-      if (v_begin < 16 || nv < CH) {  // edge chunk: mask invalid keys
+      if (blk_item || nv < CH) {  // block item, or the context's last chunk: mask invalid keys
 #pragma unroll
         for (int j = 0; j < NTH; ++j) {
           const int k0 = tile_key(hv * NTH + j, g, 0);  // 4 keys k0 .. k0+3 of one page
@@ -280,16 +313,18 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
         for (int i = 0; i < 4; ++i) cm = fmaxf(cm, s[j][i]);
       cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
       cm = fmaxf(cm, __shfl_xor(cm, 32, 64));  // -inf for a half with no valid key
-      // finite: the first half of an item's first chunk always holds a valid key
+      // mx stays -inf while a wave has met no valid key (the second key
+      // group can meet none); mref keeps the exponents defined then
       const float mn = fmaxf(mx, cm);
-      const float scale = exp2f(mx - mn);  // 0 at the first chunk
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      const float scale = exp2f(mx - mref);  // 0 at the first update
       mx = mn;
       float cs = 0.f;
 #pragma unroll
       for (int j = 0; j < NTH; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s[j][i] = __builtin_amdgcn_exp2f(s[j][i] - mx);  // <= 1; results under 2^-126 flush to 0
+          s[j][i] = __builtin_amdgcn_exp2f(s[j][i] - mref);  // <= 1; results under 2^-126 flush to 0
           cs += s[j][i];
         }
       cs += __shfl_xor(cs, 16, 64);
@@ -302,29 +337,51 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
 
 #pragma unroll
       for (int j = 0; j < NTH; j += 2) {  // k-step: key tiles j and j+1 (32 keys, 2 pages)
-        // lane's keys: slots 8*(g&1) .. +7 of the step's page g>>1
-        const uint16_t* vp = &lds[K_ELEMS + (hv * NTH + j + (g >> 1)) * D * 16 + (g & 1) * D * 8 + r16 * 8];
-        u16x4 h0, l0, h1, l1;
-        split4(s[j], h0, l0);
-        split4(s[j + 1], h1, l1);
-        const bf16x8 ph = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
-        const bf16x8 pl = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
-        constexpr int TB = MULTI ? DT / 2 : DT;  // V fragments read at once
+        if (j < nt_act) {
+          // lane's keys: slots 8*(g&1) .. +7 of the step's page g>>1
+          const uint16_t* vp = &lds[K_ELEMS + (hv * NTH + j + (g >> 1)) * D * 16 + (g & 1) * D * 8 + r16 * 8];
+          u16x4 h0, l0, h1, l1;
+          split4(s[j], h0, l0);
+          split4(s[j + 1], h1, l1);
+          const bf16x8 ph = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+          const bf16x8 pl = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
+          constexpr int TB = MULTI ? DT / 2 : DT;  // V fragments read at once
 #pragma unroll
-        for (int t0 = 0; t0 < DT; t0 += TB) {
-          bf16x8 vf[TB];
+          for (int t0 = 0; t0 < DT; t0 += TB) {
+            bf16x8 vf[TB];
 #pragma unroll
-          for (int t = 0; t < TB; ++t) vf[t] = *reinterpret_cast<const bf16x8*>(vp + (t0 + t) * 128);
+            for (int t = 0; t < TB; ++t) vf[t] = *reinterpret_cast<const bf16x8*>(vp + (t0 + t) * 128);
 #pragma unroll
-          for (int t = 0; t < TB; ++t) {
-            acc[t0 + t] = mfma16(vf[t], ph, acc[t0 + t]);
-            acc[t0 + t] = mfma16(vf[t], pl, acc[t0 + t]);
+            for (int t = 0; t < TB; ++t) {
+              acc[t0 + t] = mfma16(vf[t], ph, acc[t0 + t]);
+              acc[t0 + t] = mfma16(vf[t], pl, acc[t0 + t]);
+            }
           }
         }
       }
     }
   }
-  if (!computing) return;
+  if (KS == 2) {  // the second key group's (max, sum, O) to its partner, lane by lane
+    static_assert(4 * (DT + 1) * 64 * 16 <= (K_ELEMS + V_ELEMS) * 2, "hand-off area");
+    f32x4* xl = reinterpret_cast<f32x4*>(lds) + (size_t)wc * (DT + 1) * 64 + lane;  // wc < n_comp <= 4
+    __syncthreads();  // every LDS read of the last chunk done
+    if (computing && kh == 1) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) xl[t * 64] = acc[t];
+      xl[DT * 64] = f32x4{mx, l, 0.f, 0.f};
+    }
+    __syncthreads();
+    if (computing && kh == 0) {
+      const f32x4 ml1 = xl[DT * 64];
+      const float M = fmaxf(mx, ml1[0]);  // finite: the first group's first half holds a valid key
+      const float w0 = exp2f(mx - M), w1 = exp2f(ml1[0] - M);
+      l = l * w0 + ml1[1] * w1;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) acc[t] = acc[t] * w0 + xl[t * 64] * w1;
+      mx = M;
+    }
+  }
+  if (!computing || kh == 1) return;
 
   const size_t unit = ((size_t)b * a.n_kv + kvh) * a.n_ck + item;
   float* po = a.part_o + (unit * R + r) * D;
@@ -377,7 +434,7 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
     }
   }
   const int L = clampi(a.plan[2 * b + 1], 0, a.max_pages_per_seq * 16);
-  const int nc = min(a.n_ck, (16 + L + a.cpi * CH - 1) / (a.cpi * CH));  // work items of the sequence
+  const int nc = min(a.n_ck, 1 + (L + a.cpi * CH - 1) / (a.cpi * CH));  // work items of the block (item 0: its keys)
   float M = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   if (spec) {
@@ -438,20 +495,30 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
 extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
   const int G = a->n_q / a->n_kv, n_wr = G * a->N / 16;
   const int waves = std::max(a->cand * n_wr, MIN_WAVES);
+  // idle staging waves take the second half of the keys: where work items
+  // are chunk sequences (at one chunk per item the hand-off did not pay)
+  const bool ks2 = a->cpi > 1 && 2 * a->cand * n_wr <= waves;
   const int wgs_z = B / a->grp * ((a->grp + a->cand - 1) / a->cand);
-  const int items = (a->n_ck + a->cpi - 1) / a->cpi + a->cand - 1;
+  const int items = 1 + (a->n_ck - 1 + a->cpi - 1) / a->cpi + a->cand - 1;
   dim3 grid(items, a->n_kv, wgs_z);
   if (a->xcd_order) grid = dim3((a->xcd_tuples + 7) / 8 * 8 * a->xcd_items * a->grp);  // whole XCD rounds
   const dim3 block(64 * waves);
   if (head_dim == 128) {
-    if (a->cpi > 1) launch_kernel(attn_chunk_kernel<128, 1, true>, grid, block, 0, st, *a);
-    else if (waves <= 8) launch_kernel(attn_chunk_kernel<128, 2, false>, grid, block, 0, st, *a);
-    else launch_kernel(attn_chunk_kernel<128, 1, false>, grid, block, 0, st, *a);
+    if (a->cpi > 1) {
+      if (ks2) launch_kernel((attn_chunk_kernel<128, 1, true, 2>), grid, block, 0, st, *a);
+      else launch_kernel((attn_chunk_kernel<128, 1, true, 1>), grid, block, 0, st, *a);
+    } else if (waves <= 8) {
+      launch_kernel((attn_chunk_kernel<128, 2, false, 1>), grid, block, 0, st, *a);
+    } else {
+      launch_kernel((attn_chunk_kernel<128, 1, false, 1>), grid, block, 0, st, *a);
+    }
   } else if (a->cpi > 1) {
-    launch_kernel(attn_chunk_kernel<64, 2, true>, grid, block, 0, st, *a);
+    if (ks2) launch_kernel((attn_chunk_kernel<64, 2, true, 2>), grid, block, 0, st, *a);
+    else launch_kernel((attn_chunk_kernel<64, 2, true, 1>), grid, block, 0, st, *a);
+  } else if (waves <= 8) {
+    launch_kernel((attn_chunk_kernel<64, 2, false, 1>), grid, block, 0, st, *a);
   } else {
-    if (waves <= 8) launch_kernel(attn_chunk_kernel<64, 2, false>, grid, block, 0, st, *a);
-    else launch_kernel(attn_chunk_kernel<64, 1, false>, grid, block, 0, st, *a);
+    launch_kernel((attn_chunk_kernel<64, 1, false, 1>), grid, block, 0, st, *a);
   }
   return hipGetLastError();
 }

@@ -36,7 +36,7 @@ int fail(int code, const char* fmt, ...) {
     if (e_ != hipSuccess) return fail(DFLASH_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_));     \
   } while (0)
 
-constexpr int kAttnChunk = 128;     // virtual keys (16 block slots + context) per attention chunk
+constexpr int kAttnChunk = 128;     // context keys per attention chunk
 constexpr int kAttnItems = 512;     // attention work items to aim for (two 8-wave workgroups fit a CU: about one
                                     // round of the chip); larger grids take several chunks per item
 constexpr int kAttnMaxWaves = 8;    // computing waves of an attention workgroup that takes several blocks of one
@@ -101,7 +101,7 @@ Layout make_layout(const dflash_config& c) {
   L.m_max = (int)(Bm * N);
   L.rows_a_max = (int)(Bm * c.max_new);
   const size_t mp = pad16(L.m_max), rp = pad16(L.rows_a_max);
-  L.n_ck = (16 + c.max_pages_per_seq * 16 + kAttnChunk - 1) / kAttnChunk;
+  L.n_ck = 1 + (c.max_pages_per_seq * 16 + kAttnChunk - 1) / kAttnChunk;  // the block's keys, then context chunks
   L.n_vchunks = (c.vocab + kVerifyChunk - 1) / kVerifyChunk;
   L.n_schunks = (c.vocab + kSampleChunkMin - 1) / kSampleChunkMin;  // the most chunks a sampling pass uses
   const size_t ncol_d = std::max(qd + 2 * kvd, H), ncol_c = D * 2 * kvd;
@@ -610,7 +610,7 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
     aa.cpi = (int)std::min<long long>(8, std::max<long long>(1, (chunks + kAttnItems - 1) / kAttnItems));
     aa.n_blocks = B;
     aa.xcd_order = aa.cand == 1;
-    aa.xcd_items = (L.n_ck + aa.cpi - 1) / aa.cpi;
+    aa.xcd_items = 1 + (L.n_ck - 1 + aa.cpi - 1) / aa.cpi;
     aa.xcd_tuples = (B / grp) * c.n_kv_heads;
   }
   aa.max_pages_per_seq = c.max_pages_per_seq;

@@ -109,12 +109,13 @@ struct AttnArgs {
   const int* page_table;
   const int* ctx_len;
   const int* seq_ids;
-  float* part_o;           // [B][n_kv][n_ck][R][d]: one per work item (item < ceil(n_ck / cpi))
+  float* part_o;           // [B][n_kv][n_ck][R][d]: one per work item (item 0: the block's keys; then
+                           // context items, < 1 + ceil((n_ck - 1) / cpi))
   float* part_ml;          // [B][n_kv][n_ck][R][2]
   uint16_t* o;             // merge output, packed split activation (planes of act_plane(B*N, n_q*d))
   int32_t* err;
   int N, n_q, n_kv, chunk, n_ck, max_pages_per_seq, n_pages, max_seqs;
-  int cpi;                 // chunks of `chunk` virtual keys per work item (1 .. 8)
+  int cpi;                 // chunks of `chunk` context keys per context work item (1 .. 8)
   const int* plan;         // the call's plan [B][2]: sequence (clamped), context length
   const int* blk_pages;    // the call's page-table row of each block [B][max_pages_per_seq]
   int grp;                 // consecutive blocks that share one sequence's context (B % grp == 0)
