@@ -530,8 +530,15 @@ def main():
     logits = torch.from_numpy(logits_bits.view(np.int16)).to(dev).view(torch.bfloat16).unsqueeze(0)
     dr.ctx_len.copy_(ctx0)
 
+    # The same workload every step: the context goes back to L - 8 before the
+    # append. A fill kernel, not a copy: a copy is a memcpy node in a graph
+    # capture, which the runtime may run on a copy engine and synchronise
+    # with the kernels around it.
+    def rewind():
+        dr.ctx_len.fill_(L - n_new)
+
     def step():
-        dr.ctx_len.copy_(ctx0)  # the same workload every step: context back to L - 8 before the append
+        rewind()
         dr.ctx_append(seq, n_new_t, step_hidden, n_new)
         dr.draft_block(seq, anchor_t, draft)
         dr.verify(seq, draft, logits, acc, nxt, com)
@@ -541,7 +548,7 @@ def main():
         draft_logits = torch.zeros((1, N - 1, cfg["vocab"]), dtype=torch.float32, device=dev)
 
         def step():
-            dr.ctx_len.copy_(ctx0)
+            rewind()
             dr.ctx_append(seq, n_new_t, step_hidden, n_new)
             dr.draft_sample(seq, anchor_t, tau, draft, draft_logits, seed=1, step=0)
             dr.verify_sample(seq, draft, draft_logits, tau, logits, acc, nxt, com, seed=1, step=0)
