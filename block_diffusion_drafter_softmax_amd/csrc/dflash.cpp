@@ -289,15 +289,21 @@ int pick_ks(int units, int K, int M, int n_cols, size_t cap_floats) {
 }
 
 // Few rows: the weight-streaming GEMM with a k split (none for SwiGLU).
-// Many rows: the tiled MFMA GEMM, split in k only while its grid of
-// 128 x 128 output tiles is too small to fill the chip.
-int gemm_ks(const WsArgs& g, int mode, size_t cap_floats) {
+// Many rows: the tiled MFMA GEMM (sets g.mm_xt): 128-row workgroup tiles
+// while they give every CU two workgroups, else 64-row tiles (three fit a
+// CU, so a grid of 64-row tiles needs fewer k splits to fill the chip);
+// then a k split only while the grid is under its target.
+int gemm_ks(WsArgs& g, int mode, size_t cap_floats) {
   const int units = g.unit_start[g.nseg];
   if (g.M < kMmMinRows) return mode == WS_SWIGLU ? 1 : pick_ks(units, g.K, g.M, g.n_cols, cap_floats);
-  int blocks = 0;
-  for (int s = 0; s < g.nseg; ++s) blocks += (2 * g.seg[s].units + MM_COL_TILES - 1) / MM_COL_TILES;
-  blocks *= (g.M + kMmRows - 1) / kMmRows;
-  int ks = (kMmTargetWgs + blocks - 1) / blocks;
+  int cblocks = 0;
+  for (int s = 0; s < g.nseg; ++s) cblocks += (2 * g.seg[s].units + MM_COL_TILES - 1) / MM_COL_TILES;
+  const int m_tiles = pad16(g.M) / 16;
+  const int full = cblocks * ((m_tiles + MM_ROW_TILES - 1) / MM_ROW_TILES);
+  g.mm_xt = full >= 2 * kMmTargetWgs ? MM_ROW_TILES : MM_ROW_TILES / 2;
+  const int blocks = cblocks * ((m_tiles + g.mm_xt - 1) / g.mm_xt);
+  const int target = g.mm_xt == MM_ROW_TILES ? kMmTargetWgs : 2 * kMmTargetWgs;
+  int ks = (target + blocks - 1) / blocks;
   ks = std::min(ks, std::max(1, (g.K / 32) / 8));
   ks = std::min(ks, kKsMax);
   const size_t cols = (size_t)g.n_cols * (mode == WS_SWIGLU ? 2 : 1);
@@ -478,7 +484,7 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
   // Context K and V of every layer: fp32 split partials, columns
   // [layer][K | V], then one finisher (RoPE, bf16, page scatter).
   const int n_cols = D * 2 * kvd;
-  int ks = 1;
+  int ks = 1, mm_xt = MM_ROW_TILES;  // of the first launch: every launch writes the same partial layout
   for (int l0 = 0; l0 < D; l0 += WS_MAX_SEG / 2) {
     WsArgs g = ws_base(rows, H, n_cols);
     g.part = ctx->at<float>(L.cpart);
@@ -487,8 +493,12 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
       add_seg(g, ctx->at<uint16_t>(L.wk_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd);
       add_seg(g, ctx->at<uint16_t>(L.wv_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd + kvd);
     }
-    if (l0 == 0) ks = gemm_ks(g, WS_PARTIAL, L.cpart_floats);
+    if (l0 == 0) {
+      ks = gemm_ks(g, WS_PARTIAL, L.cpart_floats);
+      mm_xt = g.mm_xt;
+    }
     g.ks = ks;
+    g.mm_xt = mm_xt;
     if ((rc = ctx->launch(DFLASH_K_CTX_KV, stream, [&] { return launch_gemm(g, WS_PARTIAL, stream); })))
       return rc;
   }

@@ -66,6 +66,7 @@ struct WsArgs {
   int n_cols;   // row length of the partial buffer / SwiGLU features
   float* part;  // WS_PARTIAL: [ks][M][n_cols]; tiled WS_SWIGLU with ks > 1: [ks][M][2*n_cols] (gate | up)
   uint16_t* out;  // WS_SWIGLU: packed split activation, planes of act_plane(M, n_cols)
+  int mm_xt;      // tiled GEMM: activation tiles per workgroup (MM_ROW_TILES, or half of it)
 };
 
 struct PackArgs {

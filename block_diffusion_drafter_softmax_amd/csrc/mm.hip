@@ -25,12 +25,18 @@
 
 namespace {
 
-constexpr int XT = MM_ROW_TILES;           // activation tiles per workgroup
-constexpr int WT = MM_COL_TILES;           // weight tiles per workgroup
-constexpr int XW = XT / 2, WW = WT / 2;    // per wave (2 x 2 waves)
-constexpr int kStageBlocks = 2 * XT + WT;  // 1 KB blocks per stage: X tile t plane p at 2t+p, W tile u at 2XT+u
-constexpr int kLoads = kStageBlocks / 4;   // 16-byte loads per thread and stage (4 waves)
-static_assert(kStageBlocks % 4 == 0 && XT % 4 == 0, "stage blocks are dealt to 4 waves");
+// Workgroup tile geometry: XT activation tiles (MM_ROW_TILES, or half of it
+// where 128-row tiles would leave CUs without a second workgroup) by WT
+// weight tiles; 2 x 2 waves, each XW x WW tiles.
+template <int XT>
+struct Geo {
+  static constexpr int WT = MM_COL_TILES;
+  static constexpr int XW = XT / 2, WW = WT / 2;
+  static constexpr int kStageBlocks = 2 * XT + WT;  // 1 KB blocks per stage: X tile t plane p at 2t+p, W tile u at 2XT+u
+  static constexpr int kLoads = kStageBlocks / 4;   // 16-byte loads per thread and stage (4 waves)
+  static_assert(kStageBlocks % 4 == 0 && XT % 4 == 0, "stage blocks are dealt to 4 waves");
+};
+constexpr int WT = MM_COL_TILES;
 
 // Workgroup -> (column block, k split, row block). The grid is a multiple
 // of 8 and the hardware deals workgroups to the 8 XCDs round robin;
@@ -50,21 +56,24 @@ DEV bool mm_place(int total, int MB, int ks, int& nb, int& split, int& mb) {
 // the split's first k step; k step s adds s*512 and lane l reads the 16
 // bytes at l*8. Wave w moves stage blocks w + 4j: for j < XT/2 activation
 // tile (w>>1) + 2j, plane w&1; after that weight tile w + 4j - 2XT.
+template <int XT>
 struct MmSrc {
-  const uint16_t* p[kLoads];
+  const uint16_t* p[Geo<XT>::kLoads];
   int steps;  // k steps of the split
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// 16 bytes per lane from global memory straight into LDS (one 1 KB block per wave instruction).
+DEV void dma16(const uint16_t* src, u32x4* dst) { __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 16, 0, 0); }
+
 // Stage k step s into `stage` (kStageBlocks blocks of 1 KB): each wave
 // instruction writes one whole block, lane l at byte 16 l.
-DEV void mm_dma(u32x4* stage, const MmSrc& src, int s, int w) {
+template <int XT>
+DEV void mm_dma(u32x4* stage, const MmSrc<XT>& src, int s, int w) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j)
-    __builtin_amdgcn_global_load_lds(src.p[j] + (size_t)s * 512 + lane * 8, (lds_ptr)(stage + (w + 4 * j) * 64), 16, 0,
-                                     0);
+  for (int j = 0; j < Geo<XT>::kLoads; ++j) dma16(src.p[j] + (size_t)s * 512 + lane * 8, stage + (w + 4 * j) * 64);
 }
 
 DEV void mm_wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -74,7 +83,10 @@ DEV void mm_wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // ordered before those writes, and whatever the compiler waits for before
 // the next LDS read has already been waited for at the step's barrier),
 // then acc[t][i] += W tile (wn*WW + t) x X tile (wm*XW + i), hi and lo.
-DEV void mm_step(const u32x4* cur, u32x4* nxt, const MmSrc& src, int s, int w, f32x4 (&acc)[WW][XW]) {
+template <int XT>
+DEV void mm_step(const u32x4* cur, u32x4* nxt, const MmSrc<XT>& src, int s, int w,
+                 f32x4 (&acc)[Geo<XT>::WW][Geo<XT>::XW]) {
+  constexpr int XW = Geo<XT>::XW, WW = Geo<XT>::WW;
   const int lane = threadIdx.x & 63, wm = w & 1, wn = w >> 1;
   bf16x8 xh[XW], xl[XW], wf[WW];
 #pragma unroll
@@ -84,7 +96,7 @@ DEV void mm_step(const u32x4* cur, u32x4* nxt, const MmSrc& src, int s, int w, f
   }
 #pragma unroll
   for (int t = 0; t < WW; ++t) wf[t] = __builtin_bit_cast(bf16x8, cur[(2 * XT + wn * WW + t) * 64 + lane]);
-  if (s + 1 < src.steps) mm_dma(nxt, src, s + 1, w);
+  if (s + 1 < src.steps) mm_dma<XT>(nxt, src, s + 1, w);
 #pragma unroll
   for (int t = 0; t < WW; ++t)
 #pragma unroll
@@ -94,23 +106,27 @@ DEV void mm_step(const u32x4* cur, u32x4* nxt, const MmSrc& src, int s, int w, f
     }
 }
 
-DEV void mm_ksteps(const MmSrc& src, u32x4 (*stages)[kStageBlocks * 64], int w, f32x4 (&acc)[WW][XW]) {
+template <int XT>
+DEV void mm_ksteps(const MmSrc<XT>& src, u32x4 (*stages)[Geo<XT>::kStageBlocks * 64], int w,
+                   f32x4 (&acc)[Geo<XT>::WW][Geo<XT>::XW]) {
+  constexpr int XW = Geo<XT>::XW, WW = Geo<XT>::WW;
 #pragma unroll
   for (int t = 0; t < WW; ++t)
 #pragma unroll
     for (int i = 0; i < XW; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mm_dma(stages[0], src, 0, w);
+  mm_dma<XT>(stages[0], src, 0, w);
   for (int s = 0; s < src.steps; ++s) {
     // the wait sits at the top of the trip, so the MFMAs of step s-1 (which
     // touch no memory and could otherwise sink below it) are issued first
     mm_wait_dma();
     __syncthreads();
-    mm_step(stages[s & 1], stages[(s + 1) & 1], src, s, w, acc);
+    mm_step<XT>(stages[s & 1], stages[(s + 1) & 1], src, s, w, acc);
   }
   __syncthreads();  // every wave's last LDS reads are done before the epilogue reuses LDS
 }
 
-DEV void mm_x_sources(MmSrc& src, const uint16_t* act, size_t lo, int mb, int m_tiles, int steps, int s0, int w) {
+template <int XT>
+DEV void mm_x_sources(MmSrc<XT>& src, const uint16_t* act, size_t lo, int mb, int m_tiles, int steps, int s0, int w) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < XT / 2; ++j) {
@@ -120,6 +136,7 @@ DEV void mm_x_sources(MmSrc& src, const uint16_t* act, size_t lo, int mb, int m_
 }
 
 // Weight tile (within the workgroup's WT) of this thread's load j >= XT/2.
+template <int XT>
 DEV int mm_w_tile(int j, int w) { return w + 4 * j - 2 * XT; }
 
 // Segment of a column block: each segment's units (2 output tiles each, or
@@ -140,8 +157,10 @@ DEV int mm_segment(const WsArgs& a, int& nb) {
 // SwiGLU blocks: weight tiles u < WT/2 are the gates of feature tiles
 // nb*WT/2 + u, the rest the ups of the same features, so wave (wm, 0) holds
 // gate and wave (wm, 1) up of the same rows and features.
-template <int MODE>
-__global__ __launch_bounds__(256, 2) void mm_kernel(WsArgs a, int total, int MB) {
+template <int MODE, int XT>
+__global__ __launch_bounds__(256, XT == 4 ? 3 : 2) void mm_kernel(WsArgs a, int total, int MB) {
+  using Gm = Geo<XT>;
+  constexpr int XW = Gm::XW, WW = Gm::WW, kStageBlocks = Gm::kStageBlocks, kLoads = Gm::kLoads;
   __shared__ u32x4 stages[2][kStageBlocks * 64];
   int nb, split, mb;
   if (!mm_place(total, MB, a.ks, nb, split, mb)) return;
@@ -152,12 +171,12 @@ __global__ __launch_bounds__(256, 2) void mm_kernel(WsArgs a, int total, int MB)
   const int m_tiles = pad16(a.M) >> 4;
   const int steps = a.K >> 5;
   const int s0 = split * steps / a.ks;
-  MmSrc src;
+  MmSrc<XT> src;
   src.steps = (split + 1) * steps / a.ks - s0;
-  mm_x_sources(src, sg.act, act_plane(a.M, a.K), mb, m_tiles, steps, s0, w);
+  mm_x_sources<XT>(src, sg.act, act_plane(a.M, a.K), mb, m_tiles, steps, s0, w);
 #pragma unroll
   for (int j = XT / 2; j < kLoads; ++j) {
-    const int u = mm_w_tile(j, w);
+    const int u = mm_w_tile<XT>(j, w);
     const uint16_t* base = sg.w0;
     int tl;
     if (MODE == WS_SWIGLU) {
@@ -169,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void mm_kernel(WsArgs a, int total, int MB)
     src.p[j] = base + ((size_t)tl * steps + s0) * 512;
   }
   f32x4 acc[WW][XW];
-  mm_ksteps(src, stages, w, acc);
+  mm_ksteps<XT>(src, stages, w, acc);
 
   if (MODE == WS_PARTIAL) {
 #pragma unroll
@@ -257,6 +276,9 @@ __global__ __launch_bounds__(256) void swiglu_finish_kernel(WsArgs a) {
 // top-2 (value, lowest index) per row over the workgroup's WT*16 vocabulary
 // rows, written to part[column block][M]; argmax_reduce_kernel merges them.
 __global__ __launch_bounds__(256, 2) void mm_lmhead_kernel(LmArgs a, int total, int MB) {
+  constexpr int XT = MM_ROW_TILES;  // the vocabulary gives plenty of column blocks
+  using Gm = Geo<XT>;
+  constexpr int XW = Gm::XW, WW = Gm::WW, kStageBlocks = Gm::kStageBlocks, kLoads = Gm::kLoads;
   __shared__ u32x4 stages[2][kStageBlocks * 64];
   __shared__ Top2 red[2][XT * 16];
   int nb, split, mb;
@@ -266,14 +288,14 @@ __global__ __launch_bounds__(256, 2) void mm_lmhead_kernel(LmArgs a, int total, 
   const int r16 = lane & 15, g4 = (lane >> 4) * 4;
   const int m_tiles = pad16(a.M) >> 4;
   const int v_tiles = a.V >> 4;
-  MmSrc src;
+  MmSrc<XT> src;
   src.steps = a.K >> 5;
-  mm_x_sources(src, a.act, act_plane(a.M, a.K), mb, m_tiles, src.steps, 0, w);
+  mm_x_sources<XT>(src, a.act, act_plane(a.M, a.K), mb, m_tiles, src.steps, 0, w);
 #pragma unroll
   for (int j = XT / 2; j < kLoads; ++j)
-    src.p[j] = a.w + (size_t)min(nb * WT + mm_w_tile(j, w), v_tiles - 1) * src.steps * 512;
+    src.p[j] = a.w + (size_t)min(nb * WT + mm_w_tile<XT>(j, w), v_tiles - 1) * src.steps * 512;
   f32x4 acc[WW][XW];
-  mm_ksteps(src, stages, w, acc);
+  mm_ksteps<XT>(src, stages, w, acc);
 #pragma unroll
   for (int i = 0; i < XW; ++i) {
     Top2 t2 = top2_empty();
@@ -312,11 +334,17 @@ int round8(int n) { return (n + 7) & ~7; }
 extern "C" hipError_t dflash_launch_mm(const WsArgs* a, int mode, hipStream_t st) {
   int total_nb = 0;
   for (int s = 0; s < a->nseg; ++s) total_nb += (2 * a->seg[s].units + WT - 1) / WT;
+  const int XT = a->mm_xt == MM_ROW_TILES / 2 ? MM_ROW_TILES / 2 : MM_ROW_TILES;
   const int MB = ((pad16(a->M) >> 4) + XT - 1) / XT;
   const int total = total_nb * a->ks * MB;
   const dim3 grid(round8(total)), block(256);
-  if (mode == WS_SWIGLU) launch_kernel(mm_kernel<WS_SWIGLU>, grid, block, 0, st, *a, total, MB);
-  else launch_kernel(mm_kernel<WS_PARTIAL>, grid, block, 0, st, *a, total, MB);
+  if (XT == MM_ROW_TILES / 2) {
+    if (mode == WS_SWIGLU) launch_kernel(mm_kernel<WS_SWIGLU, MM_ROW_TILES / 2>, grid, block, 0, st, *a, total, MB);
+    else launch_kernel(mm_kernel<WS_PARTIAL, MM_ROW_TILES / 2>, grid, block, 0, st, *a, total, MB);
+  } else {
+    if (mode == WS_SWIGLU) launch_kernel(mm_kernel<WS_SWIGLU, MM_ROW_TILES>, grid, block, 0, st, *a, total, MB);
+    else launch_kernel(mm_kernel<WS_PARTIAL, MM_ROW_TILES>, grid, block, 0, st, *a, total, MB);
+  }
   return hipGetLastError();
 }
 
@@ -328,7 +356,7 @@ extern "C" hipError_t dflash_launch_swiglu_finish(const WsArgs* a, hipStream_t s
 
 extern "C" hipError_t dflash_launch_lmhead_mm(const LmArgs* a, hipStream_t st) {
   const int NB = ((a->V >> 4) + WT - 1) / WT;
-  const int MB = ((pad16(a->M) >> 4) + XT - 1) / XT;
+  const int MB = ((pad16(a->M) >> 4) + MM_ROW_TILES - 1) / MM_ROW_TILES;
   const int total = NB * MB;
   launch_kernel(mm_lmhead_kernel, dim3(round8(total)), dim3(256), 0, st, *a, total, MB);
   return hipGetLastError();
