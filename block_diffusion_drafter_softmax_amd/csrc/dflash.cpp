@@ -67,8 +67,9 @@ int sample_chunk(int vocab, long long rows) {
                                                                             kSampleChunkMin * kSampleChunkMin));
 }
 
-// Partial top-2 per row that the LM head leaves for the argmax reduction.
-int lm_parts(int vocab, int M) { return M >= kMmMinRows ? (vocab + kMmCols - 1) / kMmCols : (vocab / 32 + 1) / 2; }
+// Partial top-2 per row that the LM head leaves for the argmax reduction:
+// one per 512 vocabulary rows (tiled, many rows) or per 64 (streaming).
+int lm_parts(int vocab, int M) { return M >= kMmMinRows ? (vocab + 2 * kMmCols - 1) / (2 * kMmCols) : (vocab / 32 + 1) / 2; }
 
 // Byte offsets of everything the library keeps in the caller's workspace.
 struct Layout {

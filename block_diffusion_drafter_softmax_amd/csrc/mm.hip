@@ -272,58 +272,129 @@ __global__ __launch_bounds__(256) void swiglu_finish_kernel(WsArgs a) {
   *reinterpret_cast<u16x4*>(dst + act_plane(a.M, a.n_cols)) = lo;
 }
 
-// LM head for many rows: the same tile loop over vocabulary tiles, then a
-// top-2 (value, lowest index) per row over the workgroup's WT*16 vocabulary
-// rows, written to part[column block][M]; argmax_reduce_kernel merges them.
-__global__ __launch_bounds__(256, 2) void mm_lmhead_kernel(LmArgs a, int total, int MB) {
-  constexpr int XT = MM_ROW_TILES;  // the vocabulary gives plenty of column blocks
-  using Gm = Geo<XT>;
-  constexpr int XW = Gm::XW, WW = Gm::WW, kStageBlocks = Gm::kStageBlocks, kLoads = Gm::kLoads;
-  __shared__ u32x4 stages[2][kStageBlocks * 64];
-  __shared__ Top2 red[2][XT * 16];
+// LM head for many rows: top-2 (value, lowest index) per row over each
+// workgroup's vocabulary rows, written to part[column block][M];
+// argmax_reduce_kernel merges them.
+//
+// The vocabulary gives every row block hundreds of column blocks, so this
+// product can use wider workgroups than the layer GEMMs: 8 waves, 128
+// activation rows x 512 vocabulary rows (each wave the same 64 x 128 as the
+// 4-wave loop), three LDS stages of one k step (48 KB each, one workgroup
+// per CU). The DMA of k step s+2 is issued during step s, two of the
+// workgroup's steps (~1.7 us at the MFMA rate) ahead of its use; the
+// two-stage loop keeps one step ahead, less than an L2 or HBM round trip.
+// Each step waits for its own stage with a counted vmcnt and a bare
+// s_barrier (the compiler's __syncthreads also waits for the DMA still in
+// flight); the loop is unrolled by the three stages so that every LDS
+// access names its stage statically.
+namespace {
+constexpr int L8_XT = MM_ROW_TILES, L8_WT = 2 * MM_COL_TILES;
+constexpr int L8_XW = L8_XT / 2, L8_WW = L8_WT / 4;  // per wave (2 x 4 waves)
+constexpr int L8_BLOCKS = 2 * L8_XT + L8_WT;         // 1 KB blocks per stage: X tile t plane p at 2t+p, W tile u at 2XT+u
+constexpr int L8_LOADS = L8_BLOCKS / 8;              // per wave and stage
+static_assert(L8_LOADS == 6, "the counted wait below assumes 6 loads per wave and stage");
+
+typedef u32x4 L8Stage[L8_BLOCKS * 64];
+
+DEV void l8_dma(L8Stage& st, const uint16_t* const* p, int s, int w) {
+#pragma unroll
+  for (int j = 0; j < L8_LOADS; ++j) dma16(p[j] + (size_t)s * 512, &st[(w + 8 * j) * 64]);
+}
+
+// One k step s, read from `cur`; the DMA of step s+2 goes to `nxt2`, the
+// stage every wave finished reading in step s-1.
+DEV void l8_step(const L8Stage& cur, L8Stage& nxt2, const uint16_t* const* p, int s, int steps, int w,
+                 f32x4 (&acc)[L8_WW][L8_XW]) {
+  if (s + 1 < steps) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");  // step s landed (step s+1 may not have)
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();  // every wave's part of step s landed; every wave is past step s-1
+  asm volatile("" ::: "memory");
+  const int lane = threadIdx.x & 63, wm = w & 1, wn = w >> 1;
+  bf16x8 xh[L8_XW], xl[L8_XW], wf[L8_WW];
+#pragma unroll
+  for (int i = 0; i < L8_XW; ++i) {
+    xh[i] = __builtin_bit_cast(bf16x8, cur[(2 * (wm * L8_XW + i)) * 64 + lane]);
+    xl[i] = __builtin_bit_cast(bf16x8, cur[(2 * (wm * L8_XW + i) + 1) * 64 + lane]);
+  }
+#pragma unroll
+  for (int t = 0; t < L8_WW; ++t) wf[t] = __builtin_bit_cast(bf16x8, cur[(2 * L8_XT + wn * L8_WW + t) * 64 + lane]);
+  if (s + 2 < steps) l8_dma(nxt2, p, s + 2, w);
+#pragma unroll
+  for (int t = 0; t < L8_WW; ++t)
+#pragma unroll
+    for (int i = 0; i < L8_XW; ++i) {
+      acc[t][i] = mfma16(wf[t], xh[i], acc[t][i]);
+      acc[t][i] = mfma16(wf[t], xl[i], acc[t][i]);
+    }
+}
+}  // namespace
+
+__global__ __launch_bounds__(512, 1) void mm_lmhead_kernel(LmArgs a, int total, int MB) {
+  __shared__ L8Stage st0, st1, st2;  // 144 KB
+  __shared__ Top2 red[4][L8_XT * 16];
   int nb, split, mb;
   if (!mm_place(total, MB, 1, nb, split, mb)) return;
-  if (a.row_count && mb * XT * 16 >= *a.row_count) return;  // compacted rows: nothing in this row block
+  if (a.row_count && mb * L8_XT * 16 >= *a.row_count) return;  // compacted rows: nothing in this row block
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), wm = w & 1, wn = w >> 1;
   const int r16 = lane & 15, g4 = (lane >> 4) * 4;
   const int m_tiles = pad16(a.M) >> 4;
   const int v_tiles = a.V >> 4;
-  MmSrc<XT> src;
-  src.steps = a.K >> 5;
-  mm_x_sources<XT>(src, a.act, act_plane(a.M, a.K), mb, m_tiles, src.steps, 0, w);
+  const int steps = a.K >> 5;
+  // wave w moves stage blocks w + 8j: j < 2 activation tile (w >> 1) + 4j,
+  // plane w & 1; then weight tile w + 8j - 2 XT (clamped to the last real
+  // tile: duplicates are computed and never written)
+  const uint16_t* p[L8_LOADS];
 #pragma unroll
-  for (int j = XT / 2; j < kLoads; ++j)
-    src.p[j] = a.w + (size_t)min(nb * WT + mm_w_tile<XT>(j, w), v_tiles - 1) * src.steps * 512;
-  f32x4 acc[WW][XW];
-  mm_ksteps<XT>(src, stages, w, acc);
+  for (int j = 0; j < 2; ++j) {
+    const int tm = min(mb * L8_XT + (w >> 1) + 4 * j, m_tiles - 1);
+    p[j] = a.act + (w & 1) * act_plane(a.M, a.K) + (size_t)tm * steps * 512 + lane * 8;
+  }
 #pragma unroll
-  for (int i = 0; i < XW; ++i) {
+  for (int j = 2; j < L8_LOADS; ++j)
+    p[j] = a.w + (size_t)min(nb * L8_WT + w + 8 * j - 2 * L8_XT, v_tiles - 1) * steps * 512 + lane * 8;
+  f32x4 acc[L8_WW][L8_XW];
+#pragma unroll
+  for (int t = 0; t < L8_WW; ++t)
+#pragma unroll
+    for (int i = 0; i < L8_XW; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  l8_dma(st0, p, 0, w);
+  if (steps > 1) l8_dma(st1, p, 1, w);
+  for (int s = 0; s < steps; s += 3) {
+    l8_step(st0, st2, p, s, steps, w, acc);
+    if (s + 1 < steps) l8_step(st1, st0, p, s + 1, steps, w, acc);
+    if (s + 2 < steps) l8_step(st2, st1, p, s + 2, steps, w, acc);
+  }
+#pragma unroll
+  for (int i = 0; i < L8_XW; ++i) {
     Top2 t2 = top2_empty();
 #pragma unroll
-    for (int t = 0; t < WW; ++t) {
-      const int vt = nb * WT + wn * WW + t;
+    for (int t = 0; t < L8_WW; ++t) {
+      const int vt = nb * L8_WT + wn * L8_WW + t;
       if (vt < v_tiles)
 #pragma unroll
         for (int j = 0; j < 4; ++j) t2 = top2_push(t2, acc[t][i][j], vt * 16 + g4 + j);
     }
     t2 = top2_shfl_xor(t2, 16);
     t2 = top2_shfl_xor(t2, 32);
-    if (lane < 16) red[wn][(wm * XW + i) * 16 + lane] = t2;
-    const int tm = mb * XT + wm * XW + i;
+    if (lane < 16) red[wn][(wm * L8_XW + i) * 16 + lane] = t2;
+    const int tm = mb * L8_XT + wm * L8_XW + i;
     const int m = tm * 16 + r16;
     if (a.dbg_logits && tm < m_tiles && m < a.M && (m % a.N) != 0) {
       float* dst = a.dbg_logits + ((size_t)(m / a.N) * (a.N - 1) + (m % a.N) - 1) * a.V;
 #pragma unroll
-      for (int t = 0; t < WW; ++t) {
-        const int vt = nb * WT + wn * WW + t;
+      for (int t = 0; t < L8_WW; ++t) {
+        const int vt = nb * L8_WT + wn * L8_WW + t;
         if (vt < v_tiles) *reinterpret_cast<f32x4*>(dst + vt * 16 + g4) = acc[t][i];
       }
     }
   }
   __syncthreads();
-  if (threadIdx.x < XT * 16) {
-    const int m = mb * XT * 16 + threadIdx.x;
-    if (m < a.M) a.part[(size_t)nb * a.M + m] = top2_merge(red[0][threadIdx.x], red[1][threadIdx.x]);
+  if (threadIdx.x < L8_XT * 16) {
+    const int m = mb * L8_XT * 16 + threadIdx.x;
+    Top2 t = red[0][threadIdx.x];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) t = top2_merge(t, red[q][threadIdx.x]);
+    if (m < a.M) a.part[(size_t)nb * a.M + m] = t;
   }
 }
 
@@ -355,9 +426,9 @@ extern "C" hipError_t dflash_launch_swiglu_finish(const WsArgs* a, hipStream_t s
 }
 
 extern "C" hipError_t dflash_launch_lmhead_mm(const LmArgs* a, hipStream_t st) {
-  const int NB = ((a->V >> 4) + WT - 1) / WT;
-  const int MB = ((pad16(a->M) >> 4) + MM_ROW_TILES - 1) / MM_ROW_TILES;
+  const int NB = ((a->V >> 4) + L8_WT - 1) / L8_WT;
+  const int MB = ((pad16(a->M) >> 4) + L8_XT - 1) / L8_XT;
   const int total = NB * MB;
-  launch_kernel(mm_lmhead_kernel, dim3(round8(total)), dim3(256), 0, st, *a, total, MB);
+  launch_kernel(mm_lmhead_kernel, dim3(round8(total)), dim3(512), 0, st, *a, total, MB);
   return hipGetLastError();
 }
