@@ -290,26 +290,85 @@ int pick_ks(int units, int K, int M, int n_cols, size_t cap_floats) {
 }
 
 // Few rows: the weight-streaming GEMM with a k split (none for SwiGLU).
-// Many rows: the tiled MFMA GEMM (sets g.mm_xt): 128-row workgroup tiles
-// while they give every CU two workgroups, else 64-row tiles (three fit a
-// CU, so a grid of 64-row tiles needs fewer k splits to fill the chip);
-// then a k split only while the grid is under its target.
+// Many rows: the tiled MFMA GEMM (sets g.mm_xt / g.mm_wt, returns the k
+// split). By default the 4-wave loop: 128-row tiles while they give every
+// CU two workgroups, else 64-row tiles (three fit a CU), then a k split
+// while the grid is under its target. The 8-wave loop (one workgroup per
+// CU, three LDS stages; 128-row tiles 256, 384 or 512 weight rows wide)
+// replaces it where one of its tile widths and k splits fills at least
+// three quarters of every round of the chip with k loops of 32 steps or
+// more, and is estimated faster. The
+// estimate: rounds of the chip times the busiest CU's share of a round
+// (workgroups held at once times a tile of work, at the fraction of the
+// MFMA rate measured for that loop and occupancy), plus the partial sums a
+// k split writes and its consumer reads again.
 int gemm_ks(WsArgs& g, int mode, size_t cap_floats) {
   const int units = g.unit_start[g.nseg];
+  g.mm_wt = 0;
   if (g.M < kMmMinRows) return mode == WS_SWIGLU ? 1 : pick_ks(units, g.K, g.M, g.n_cols, cap_floats);
-  int cblocks = 0;
-  for (int s = 0; s < g.nseg; ++s) cblocks += (2 * g.seg[s].units + MM_COL_TILES - 1) / MM_COL_TILES;
-  const int m_tiles = pad16(g.M) / 16;
-  const int full = cblocks * ((m_tiles + MM_ROW_TILES - 1) / MM_ROW_TILES);
+  const int m_tiles = pad16(g.M) / 16, steps = g.K / 32;
+  const size_t part_cols = (size_t)g.n_cols * (mode == WS_SWIGLU ? 2 : 1);
+  const double tile_step_us = 16.0 * 16 * 32 * 2 * 2 / 9.77e6;  // one 16x16x32 hi+lo tile step of a CU at its MFMA peak
+  auto col_blocks = [&](int wt) {
+    int cb = 0;
+    for (int s = 0; s < g.nseg; ++s) cb += (2 * g.seg[s].units + wt - 1) / wt;
+    return cb;
+  };
+  auto ks_cap = [&](int ks) {  // at least 8 k steps per split, within the partial buffer
+    ks = std::min(ks, std::max(1, steps / 8));
+    ks = std::min(ks, kKsMax);
+    ks = std::min<long long>(ks, (long long)(cap_floats / ((size_t)g.M * part_cols)));
+    return std::max(ks, 1);
+  };
+  // measured fraction of the MFMA rate: 4-wave loop by workgroups held per CU
+  // (128-row tiles: 1, 2; 64-row tiles: 1, 2, 3), 8-wave loop
+  auto eff4 = [](int xt, long long held) {
+    if (xt == MM_ROW_TILES) return held >= 2 ? 0.55 : 0.38;
+    return held >= 3 ? 0.48 : held == 2 ? 0.45 : 0.33;
+  };
+  constexpr double kEff8 = 0.52;
+  auto estimate = [&](int xt, int wt, int per_cu, long long held, double eff, long long wgs, int ks) {
+    const long long rounds = (wgs + 256LL * per_cu - 1) / (256LL * per_cu);
+    return rounds * held * (double)xt * wt * ((steps + ks - 1) / ks) * tile_step_us / eff +
+           (ks > 1 ? 2.0 * ks * g.M * part_cols * 4 / 6e6 : 0.0);
+  };
+  // the default plan
+  const int cb16 = col_blocks(MM_COL_TILES);
+  const int full = cb16 * ((m_tiles + MM_ROW_TILES - 1) / MM_ROW_TILES);
   g.mm_xt = full >= 2 * kMmTargetWgs ? MM_ROW_TILES : MM_ROW_TILES / 2;
-  const int blocks = cblocks * ((m_tiles + g.mm_xt - 1) / g.mm_xt);
+  const int blocks = cb16 * ((m_tiles + g.mm_xt - 1) / g.mm_xt);
   const int target = g.mm_xt == MM_ROW_TILES ? kMmTargetWgs : 2 * kMmTargetWgs;
-  int ks = (target + blocks - 1) / blocks;
-  ks = std::min(ks, std::max(1, (g.K / 32) / 8));
-  ks = std::min(ks, kKsMax);
-  const size_t cols = (size_t)g.n_cols * (mode == WS_SWIGLU ? 2 : 1);
-  ks = std::min<long long>(ks, (long long)(cap_floats / ((size_t)g.M * cols)));
-  return std::max(ks, 1);
+  const int ks = mode == WS_SWIGLU ? 1 : ks_cap((target + blocks - 1) / blocks);
+  {
+    const long long wgs = (long long)blocks * ks;
+    const int per_cu = g.mm_xt == MM_ROW_TILES ? 2 : 3;
+    const long long held = std::min<long long>(per_cu, (wgs + 255) / 256);
+    const double base = estimate(g.mm_xt, MM_COL_TILES, per_cu, held, eff4(g.mm_xt, held), wgs, ks);
+    double best = base;
+    int best_wt = 0, best_ks = ks;
+    for (int wt : {16, 24, 32}) {
+      const int b8 = col_blocks(wt) * ((m_tiles + MM_ROW_TILES - 1) / MM_ROW_TILES);
+      for (int k8 = 1; k8 <= (mode == WS_SWIGLU ? 1 : kKsMax); ++k8) {
+        if (k8 != ks_cap(k8)) break;
+        const long long w8 = (long long)b8 * k8;
+        const long long r8 = (w8 + 255) / 256;
+        if (w8 * 4 < r8 * 256 * 3) continue;  // at least three quarters of every round
+        if (steps / k8 < 32) break;          // the three-stage ring needs a long k loop to pay for its fill
+        const double e = estimate(MM_ROW_TILES, wt, 1, 1, kEff8, w8, k8);
+        if (e < best) {
+          best = e;
+          best_wt = wt;
+          best_ks = k8;
+        }
+      }
+    }
+    if (best_wt) {
+      g.mm_xt = MM_ROW_TILES;
+      g.mm_wt = best_wt;
+      return best_ks;
+    }
+  }
+  return ks;
 }
 
 hipError_t launch_gemm(const WsArgs& g, int mode, hipStream_t st) {
@@ -485,7 +544,7 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
   // Context K and V of every layer: fp32 split partials, columns
   // [layer][K | V], then one finisher (RoPE, bf16, page scatter).
   const int n_cols = D * 2 * kvd;
-  int ks = 1, mm_xt = MM_ROW_TILES;  // of the first launch: every launch writes the same partial layout
+  int ks = 1, mm_xt = MM_ROW_TILES, mm_wt = 0;  // of the first launch: every launch writes the same partial layout
   for (int l0 = 0; l0 < D; l0 += WS_MAX_SEG / 2) {
     WsArgs g = ws_base(rows, H, n_cols);
     g.part = ctx->at<float>(L.cpart);
@@ -497,9 +556,11 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
     if (l0 == 0) {
       ks = gemm_ks(g, WS_PARTIAL, L.cpart_floats);
       mm_xt = g.mm_xt;
+      mm_wt = g.mm_wt;
     }
     g.ks = ks;
     g.mm_xt = mm_xt;
+    g.mm_wt = mm_wt;
     if ((rc = ctx->launch(DFLASH_K_CTX_KV, stream, [&] { return launch_gemm(g, WS_PARTIAL, stream); })))
       return rc;
   }
@@ -704,6 +765,7 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
   la.V = c.vocab;
   la.N = N;
   la.part = ctx->at<Top2>(L.lmpart);
+  la.n_parts = lm_parts(c.vocab, M);  // one per LM-head workgroup along the vocabulary
   la.dbg_logits = row_cut ? nullptr : dbg_logits;
   la.row_count = row_cut ? na.row_count : nullptr;
   if ((rc = ctx->launch(DFLASH_K_LM_HEAD, stream, [&] {
@@ -713,7 +775,7 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
 
   ArgmaxArgs ma{};
   ma.part = la.part;
-  ma.n_parts = lm_parts(c.vocab, M);  // one per LM-head workgroup
+  ma.n_parts = la.n_parts;
   ma.M = M;
   ma.N = N;
   ma.V = c.vocab;

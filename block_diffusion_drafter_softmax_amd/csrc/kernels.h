@@ -66,7 +66,8 @@ struct WsArgs {
   int n_cols;   // row length of the partial buffer / SwiGLU features
   float* part;  // WS_PARTIAL: [ks][M][n_cols]; tiled WS_SWIGLU with ks > 1: [ks][M][2*n_cols] (gate | up)
   uint16_t* out;  // WS_SWIGLU: packed split activation, planes of act_plane(M, n_cols)
-  int mm_xt;      // tiled GEMM: activation tiles per workgroup (MM_ROW_TILES, or half of it)
+  int mm_xt;      // tiled GEMM, 4-wave loop: activation tiles per workgroup (MM_ROW_TILES, or half of it)
+  int mm_wt;      // tiled GEMM: 0, or the 8-wave loop with this many weight tiles per workgroup (16, 24, 32)
 };
 
 struct PackArgs {
@@ -191,13 +192,14 @@ struct LmArgs {
   const uint16_t* w;    // packed [V/16][K/32][512]
   const uint16_t* act;  // packed split activation of the normed rows
   int M, K, V, N;       // N = block rows per sequence
-  Top2* part;           // [n_parts][M]: one top-2 per workgroup (64 or 128 vocabulary rows)
+  Top2* part;           // [M][n_parts]: one top-2 per row and workgroup (64 or 512 vocabulary rows)
+  int n_parts;          // workgroups along the vocabulary
   float* dbg_logits;    // nullable [B][N-1][V]
   const int* row_count; // nullable: rows 0 .. *row_count-1 of act are compacted rows; row blocks past it are skipped
 };
 
 struct ArgmaxArgs {
-  const Top2* part;  // [n_parts][M]
+  const Top2* part;  // [M][n_parts]
   int n_parts, M, N, V;
   int* draft;        // [B][N-1]
   float* gap;        // nullable [B][N-1]

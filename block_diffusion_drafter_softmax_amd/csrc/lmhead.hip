@@ -58,7 +58,7 @@ __global__ __launch_bounds__(64 * LM_WAVES) void lmhead_kernel(LmArgs a) {
       const int m = mg * 16 + threadIdx.x;
       Top2 t = red[0][threadIdx.x];
       for (int w = 1; w < LM_WAVES; ++w) t = top2_merge(t, red[w][threadIdx.x]);
-      if (m < a.M) a.part[(size_t)blockIdx.x * a.M + m] = t;
+      if (m < a.M) a.part[(size_t)m * a.n_parts + blockIdx.x] = t;
     }
     __syncthreads();  // red is reused by the next m-group
   }
@@ -75,10 +75,11 @@ extern "C" hipError_t dflash_launch_lmhead(const LmArgs* a, hipStream_t st) {
 }
 
 // One workgroup of ARGMAX_THREADS per block row m (rows with m % N == 0 are
-// the anchors and produce nothing): every partial top-2 of the row is
-// requested in one batch of <= 8 loads per thread, then merged (the merge
-// is order independent).
+// the anchors and produce nothing): the row's partial top-2 (contiguous)
+// are requested in batches of ARGMAX_BATCH loads per thread, then merged
+// (the merge is order independent).
 #define ARGMAX_THREADS 1024
+#define ARGMAX_BATCH 4
 __global__ __launch_bounds__(ARGMAX_THREADS) LATENCY_BOUND void argmax_reduce_kernel(ArgmaxArgs a) {
   const int m = blockIdx.x;  // row of the partials
   int mo = m;                // block row it belongs to
@@ -88,12 +89,13 @@ __global__ __launch_bounds__(ARGMAX_THREADS) LATENCY_BOUND void argmax_reduce_ke
   }
   if (mo % a.N == 0) return;
   Top2 t = top2_empty();
-  for (int j0 = 0; j0 < a.n_parts; j0 += ARGMAX_THREADS * 8) {
-    Top2 v[8];
+  const Top2* row = a.part + (size_t)m * a.n_parts;
+  for (int j0 = 0; j0 < a.n_parts; j0 += ARGMAX_THREADS * ARGMAX_BATCH) {
+    Top2 v[ARGMAX_BATCH];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = a.part[(size_t)min(j0 + u * ARGMAX_THREADS + (int)threadIdx.x, a.n_parts - 1) * a.M + m];
+    for (int u = 0; u < ARGMAX_BATCH; ++u) v[u] = row[min(j0 + u * ARGMAX_THREADS + (int)threadIdx.x, a.n_parts - 1)];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)  // a clamped duplicate would corrupt the second value: skip it
+    for (int u = 0; u < ARGMAX_BATCH; ++u)  // a clamped duplicate would corrupt the second value: skip it
       if (j0 + u * ARGMAX_THREADS + (int)threadIdx.x < a.n_parts) t = top2_merge(t, v[u]);
   }
 #pragma unroll

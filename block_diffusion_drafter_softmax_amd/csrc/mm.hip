@@ -273,7 +273,7 @@ __global__ __launch_bounds__(256) void swiglu_finish_kernel(WsArgs a) {
 }
 
 // LM head for many rows: top-2 (value, lowest index) per row over each
-// workgroup's vocabulary rows, written to part[column block][M];
+// workgroup's vocabulary rows, written to part[M][column block];
 // argmax_reduce_kernel merges them.
 //
 // The vocabulary gives every row block hundreds of column blocks, so this
@@ -288,49 +288,196 @@ __global__ __launch_bounds__(256) void swiglu_finish_kernel(WsArgs a) {
 // flight); the loop is unrolled by the three stages so that every LDS
 // access names its stage statically.
 namespace {
-constexpr int L8_XT = MM_ROW_TILES, L8_WT = 2 * MM_COL_TILES;
-constexpr int L8_XW = L8_XT / 2, L8_WW = L8_WT / 4;  // per wave (2 x 4 waves)
-constexpr int L8_BLOCKS = 2 * L8_XT + L8_WT;         // 1 KB blocks per stage: X tile t plane p at 2t+p, W tile u at 2XT+u
-constexpr int L8_LOADS = L8_BLOCKS / 8;              // per wave and stage
-static_assert(L8_LOADS == 6, "the counted wait below assumes 6 loads per wave and stage");
+// 8 waves (2 row halves x 4 column quarters), 128 activation rows (8 tiles)
+// by WT8 weight tiles; each wave 4 x WT8/4 tiles.
+template <int WT8>
+struct G8 {
+  static constexpr int XT = MM_ROW_TILES, WT = WT8;
+  static constexpr int XW = XT / 2, WW = WT / 4;
+  static constexpr int BLOCKS = 2 * XT + WT;  // 1 KB blocks per stage: X tile t plane p at 2t+p, W tile u at 2XT+u
+  static constexpr int LOADS = BLOCKS / 8;    // per wave and stage: wave w moves blocks w + 8j
+  static_assert(BLOCKS % 8 == 0 && XT == 8 && WT % 4 == 0 && LOADS <= 6, "8-wave stage geometry");
+  typedef u32x4 Stage[BLOCKS * 64];
+};
 
-typedef u32x4 L8Stage[L8_BLOCKS * 64];
-
-DEV void l8_dma(L8Stage& st, const uint16_t* const* p, int s, int w) {
+template <int WT8>
+DEV void g8_dma(typename G8<WT8>::Stage& st, const uint16_t* const* p, int s, int w) {
 #pragma unroll
-  for (int j = 0; j < L8_LOADS; ++j) dma16(p[j] + (size_t)s * 512, &st[(w + 8 * j) * 64]);
+  for (int j = 0; j < G8<WT8>::LOADS; ++j) dma16(p[j] + (size_t)s * 512, &st[(w + 8 * j) * 64]);
 }
 
 // One k step s, read from `cur`; the DMA of step s+2 goes to `nxt2`, the
 // stage every wave finished reading in step s-1.
-DEV void l8_step(const L8Stage& cur, L8Stage& nxt2, const uint16_t* const* p, int s, int steps, int w,
-                 f32x4 (&acc)[L8_WW][L8_XW]) {
-  if (s + 1 < steps) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");  // step s landed (step s+1 may not have)
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+template <int WT8>
+DEV void g8_step(const typename G8<WT8>::Stage& cur, typename G8<WT8>::Stage& nxt2, const uint16_t* const* p, int s,
+                 int steps, int w, f32x4 (&acc)[G8<WT8>::WW][G8<WT8>::XW]) {
+  using G = G8<WT8>;
+  // step s landed (step s+1 may not have): s_waitcnt vmcnt(LOADS), or vmcnt(0) at the last step
+  if (s + 1 < steps) __builtin_amdgcn_s_waitcnt(0x0F70 | G::LOADS);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
   __builtin_amdgcn_s_barrier();  // every wave's part of step s landed; every wave is past step s-1
   asm volatile("" ::: "memory");
   const int lane = threadIdx.x & 63, wm = w & 1, wn = w >> 1;
-  bf16x8 xh[L8_XW], xl[L8_XW], wf[L8_WW];
+  bf16x8 xh[G::XW], xl[G::XW], wf[G::WW];
 #pragma unroll
-  for (int i = 0; i < L8_XW; ++i) {
-    xh[i] = __builtin_bit_cast(bf16x8, cur[(2 * (wm * L8_XW + i)) * 64 + lane]);
-    xl[i] = __builtin_bit_cast(bf16x8, cur[(2 * (wm * L8_XW + i) + 1) * 64 + lane]);
+  for (int i = 0; i < G::XW; ++i) {
+    xh[i] = __builtin_bit_cast(bf16x8, cur[(2 * (wm * G::XW + i)) * 64 + lane]);
+    xl[i] = __builtin_bit_cast(bf16x8, cur[(2 * (wm * G::XW + i) + 1) * 64 + lane]);
   }
 #pragma unroll
-  for (int t = 0; t < L8_WW; ++t) wf[t] = __builtin_bit_cast(bf16x8, cur[(2 * L8_XT + wn * L8_WW + t) * 64 + lane]);
-  if (s + 2 < steps) l8_dma(nxt2, p, s + 2, w);
+  for (int t = 0; t < G::WW; ++t) wf[t] = __builtin_bit_cast(bf16x8, cur[(2 * G::XT + wn * G::WW + t) * 64 + lane]);
+  if (s + 2 < steps) g8_dma<WT8>(nxt2, p, s + 2, w);
 #pragma unroll
-  for (int t = 0; t < L8_WW; ++t)
+  for (int t = 0; t < G::WW; ++t)
 #pragma unroll
-    for (int i = 0; i < L8_XW; ++i) {
+    for (int i = 0; i < G::XW; ++i) {
       acc[t][i] = mfma16(wf[t], xh[i], acc[t][i]);
       acc[t][i] = mfma16(wf[t], xl[i], acc[t][i]);
     }
 }
+
+// The whole k loop over `steps` k steps: two stages requested ahead, the
+// loop unrolled by the three stages so every LDS access names its stage.
+template <int WT8>
+DEV void g8_ksteps(typename G8<WT8>::Stage& st0, typename G8<WT8>::Stage& st1, typename G8<WT8>::Stage& st2,
+                   const uint16_t* const* p, int steps, int w, f32x4 (&acc)[G8<WT8>::WW][G8<WT8>::XW]) {
+#pragma unroll
+  for (int t = 0; t < G8<WT8>::WW; ++t)
+#pragma unroll
+    for (int i = 0; i < G8<WT8>::XW; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  g8_dma<WT8>(st0, p, 0, w);
+  if (steps > 1) g8_dma<WT8>(st1, p, 1, w);
+  for (int s = 0; s < steps; s += 3) {
+    g8_step<WT8>(st0, st2, p, s, steps, w, acc);
+    if (s + 1 < steps) g8_step<WT8>(st1, st0, p, s + 1, steps, w, acc);
+    if (s + 2 < steps) g8_step<WT8>(st2, st1, p, s + 2, steps, w, acc);
+  }
+  __syncthreads();  // every wave's last LDS reads are done before an epilogue reuses LDS
+}
+}  // namespace
+
+// Layer GEMMs for many rows with the 8-wave loop (one workgroup per CU):
+// picked by the host where a tile width of WT8 weight tiles and a k split
+// make the grid a whole number of rounds of the chip. SwiGLU blocks: weight
+// tiles u < WT8/2 are the gates of feature tiles nb*WT8/2 + u, the rest the
+// ups of the same features, so wave (wm, wn) with wn < 2 holds gates and
+// wave (wm, wn + 2) the ups of the same rows and features.
+template <int MODE, int WT8>
+__global__ __launch_bounds__(512, 1) void mm8_kernel(WsArgs a, int total, int MB) {
+  using G = G8<WT8>;
+  __shared__ typename G::Stage st0, st1, st2;
+  int nb, split, mb;
+  if (!mm_place(total, MB, a.ks, nb, split, mb)) return;
+  int s = 0;  // segment of column block nb (each makes ceil(2 units / WT8) blocks)
+  while (s + 1 < a.nseg) {
+    const int blocks = (2 * a.seg[s].units + WT8 - 1) / WT8;
+    if (nb < blocks) break;
+    nb -= blocks;
+    ++s;
+  }
+  const WsSeg sg = a.seg[s];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), wm = w & 1, wn = w >> 1;
+  const int r16 = lane & 15, g4 = (lane >> 4) * 4;
+  const int m_tiles = pad16(a.M) >> 4;
+  const int steps = a.K >> 5;
+  const int s0 = split * steps / a.ks, n_steps = (split + 1) * steps / a.ks - s0;
+  const uint16_t* p[G::LOADS];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int tm = min(mb * G::XT + (w >> 1) + 4 * j, m_tiles - 1);
+    p[j] = sg.act + (w & 1) * act_plane(a.M, a.K) + ((size_t)tm * steps + s0) * 512 + lane * 8;
+  }
+#pragma unroll
+  for (int j = 2; j < G::LOADS; ++j) {
+    const int u = w + 8 * j - 2 * G::XT;  // weight tile within the block
+    const uint16_t* base = sg.w0;
+    int tl;
+    if (MODE == WS_SWIGLU) {
+      if (u >= WT8 / 2) base = sg.w1;
+      tl = min(nb * (WT8 / 2) + u % (WT8 / 2), sg.units - 1);
+    } else {
+      tl = min(nb * WT8 + u, 2 * sg.units - 1);
+    }
+    p[j] = base + ((size_t)tl * steps + s0) * 512 + lane * 8;
+  }
+  f32x4 acc[G::WW][G::XW];
+  g8_ksteps<WT8>(st0, st1, st2, p, n_steps, w, acc);
+
+  if (MODE == WS_PARTIAL || a.ks > 1) {  // fp32 partials (SwiGLU after a k split: gate | up)
+    const int up = MODE == WS_SWIGLU && wn >= 2;
+#pragma unroll
+    for (int i = 0; i < G::XW; ++i) {
+      const int tm = mb * G::XT + wm * G::XW + i;
+      const int m = tm * 16 + r16;
+      if (tm >= m_tiles || m >= a.M) continue;
+#pragma unroll
+      for (int t = 0; t < G::WW; ++t) {
+        if (MODE == WS_PARTIAL) {
+          const int tile = nb * WT8 + wn * G::WW + t;
+          if (tile < 2 * sg.units)
+            *reinterpret_cast<f32x4*>(a.part + ((size_t)split * a.M + m) * a.n_cols + sg.col0 + tile * 16 + g4) =
+                acc[t][i];
+        } else {
+          const int f = nb * (WT8 / 2) + (wn & 1) * G::WW + t;  // feature tile
+          if (f < sg.units)
+            *reinterpret_cast<f32x4*>(a.part + ((size_t)split * a.M + m) * 2 * a.n_cols + up * a.n_cols + sg.col0 +
+                                      f * 16 + g4) = acc[t][i];
+        }
+      }
+    }
+    return;
+  }
+
+  // SwiGLU in registers: per row half, the two up waves park their
+  // accumulators in the (free) stage buffers and the gate waves combine.
+  static_assert(G::WW * G::XW * 64 <= G::BLOCKS * 64, "park fits a stage buffer");
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    f32x4* park = reinterpret_cast<f32x4*>((wn & 1) ? st1 : st0);  // [t][i][lane]
+    if (wm == half && wn >= 2) {
+#pragma unroll
+      for (int t = 0; t < G::WW; ++t)
+#pragma unroll
+        for (int i = 0; i < G::XW; ++i) park[(t * G::XW + i) * 64 + lane] = acc[t][i];
+    }
+    __syncthreads();
+    if (wm == half && wn < 2) {
+#pragma unroll
+      for (int i = 0; i < G::XW; ++i) {
+        const int tm = mb * G::XT + wm * G::XW + i;
+        const int m = tm * 16 + r16;
+        if (tm >= m_tiles || m >= a.M) continue;
+#pragma unroll
+        for (int t = 0; t < G::WW; ++t) {
+          const int f = nb * (WT8 / 2) + wn * G::WW + t;  // feature tile
+          if (f >= sg.units) continue;
+          const f32x4 upv = park[(t * G::XW + i) * 64 + lane];
+          f32x4 y;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float gt = acc[t][i][j];
+            y[j] = gt / (1.0f + __expf(-gt)) * upv[j];
+          }
+          u16x4 hi, lo;
+          split4(y, hi, lo);
+          uint16_t* dst = a.out + pk_index(m, sg.col0 + f * 16 + g4, a.n_cols);
+          *reinterpret_cast<u16x4*>(dst) = hi;
+          *reinterpret_cast<u16x4*>(dst + act_plane(a.M, a.n_cols)) = lo;
+        }
+      }
+    }
+    __syncthreads();  // the park area is reused by the second row half
+  }
+}
+
+namespace {
+constexpr int L8_XT = MM_ROW_TILES, L8_WT = 2 * MM_COL_TILES;
+constexpr int L8_XW = L8_XT / 2, L8_WW = L8_WT / 4;
 }  // namespace
 
 __global__ __launch_bounds__(512, 1) void mm_lmhead_kernel(LmArgs a, int total, int MB) {
-  __shared__ L8Stage st0, st1, st2;  // 144 KB
+  using G = G8<L8_WT>;
+  __shared__ G::Stage st0, st1, st2;  // 144 KB
   __shared__ Top2 red[4][L8_XT * 16];
   int nb, split, mb;
   if (!mm_place(total, MB, 1, nb, split, mb)) return;
@@ -343,27 +490,17 @@ __global__ __launch_bounds__(512, 1) void mm_lmhead_kernel(LmArgs a, int total, 
   // wave w moves stage blocks w + 8j: j < 2 activation tile (w >> 1) + 4j,
   // plane w & 1; then weight tile w + 8j - 2 XT (clamped to the last real
   // tile: duplicates are computed and never written)
-  const uint16_t* p[L8_LOADS];
+  const uint16_t* p[G::LOADS];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int tm = min(mb * L8_XT + (w >> 1) + 4 * j, m_tiles - 1);
     p[j] = a.act + (w & 1) * act_plane(a.M, a.K) + (size_t)tm * steps * 512 + lane * 8;
   }
 #pragma unroll
-  for (int j = 2; j < L8_LOADS; ++j)
+  for (int j = 2; j < G::LOADS; ++j)
     p[j] = a.w + (size_t)min(nb * L8_WT + w + 8 * j - 2 * L8_XT, v_tiles - 1) * steps * 512 + lane * 8;
   f32x4 acc[L8_WW][L8_XW];
-#pragma unroll
-  for (int t = 0; t < L8_WW; ++t)
-#pragma unroll
-    for (int i = 0; i < L8_XW; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  l8_dma(st0, p, 0, w);
-  if (steps > 1) l8_dma(st1, p, 1, w);
-  for (int s = 0; s < steps; s += 3) {
-    l8_step(st0, st2, p, s, steps, w, acc);
-    if (s + 1 < steps) l8_step(st1, st0, p, s + 1, steps, w, acc);
-    if (s + 2 < steps) l8_step(st2, st1, p, s + 2, steps, w, acc);
-  }
+  g8_ksteps<L8_WT>(st0, st1, st2, p, steps, w, acc);
 #pragma unroll
   for (int i = 0; i < L8_XW; ++i) {
     Top2 t2 = top2_empty();
@@ -394,7 +531,7 @@ __global__ __launch_bounds__(512, 1) void mm_lmhead_kernel(LmArgs a, int total, 
     Top2 t = red[0][threadIdx.x];
 #pragma unroll
     for (int q = 1; q < 4; ++q) t = top2_merge(t, red[q][threadIdx.x]);
-    if (m < a.M) a.part[(size_t)nb * a.M + m] = t;
+    if (m < a.M) a.part[(size_t)m * a.n_parts + nb] = t;
   }
 }
 
@@ -402,7 +539,24 @@ namespace {
 int round8(int n) { return (n + 7) & ~7; }
 }  // namespace
 
+template <int WT8>
+void launch_mm8(const WsArgs* a, int mode, hipStream_t st) {
+  int total_nb = 0;
+  for (int s = 0; s < a->nseg; ++s) total_nb += (2 * a->seg[s].units + WT8 - 1) / WT8;
+  const int MB = ((pad16(a->M) >> 4) + MM_ROW_TILES - 1) / MM_ROW_TILES;
+  const int total = total_nb * a->ks * MB;
+  const dim3 grid(round8(total)), block(512);
+  if (mode == WS_SWIGLU) launch_kernel(mm8_kernel<WS_SWIGLU, WT8>, grid, block, 0, st, *a, total, MB);
+  else launch_kernel(mm8_kernel<WS_PARTIAL, WT8>, grid, block, 0, st, *a, total, MB);
+}
+
 extern "C" hipError_t dflash_launch_mm(const WsArgs* a, int mode, hipStream_t st) {
+  switch (a->mm_wt) {
+    case 16: launch_mm8<16>(a, mode, st); return hipGetLastError();
+    case 24: launch_mm8<24>(a, mode, st); return hipGetLastError();
+    case 32: launch_mm8<32>(a, mode, st); return hipGetLastError();
+    default: break;
+  }
   int total_nb = 0;
   for (int s = 0; s < a->nseg; ++s) total_nb += (2 * a->seg[s].units + WT - 1) / WT;
   const int XT = a->mm_xt == MM_ROW_TILES / 2 ? MM_ROW_TILES / 2 : MM_ROW_TILES;
