@@ -275,8 +275,11 @@ def run_batched(args, name):
 
     def step_first():
         dr.ctx_len.copy_(ctx0)
-        dr.ctx_append(seq, n_new_t, step_hid, max_new)
-        dr.draft_block(seq, anchor, draft)
+        if args.separate_append:
+            dr.ctx_append(seq, n_new_t, step_hid, max_new)
+            dr.draft_block(seq, anchor, draft)
+        else:
+            dr.append_draft(seq, n_new_t, step_hid, anchor, draft, max_new=max_new)
         dr.verify(seq, draft, logits, acc, nxt, com, temperature=temp, seed=1, step=0)
 
     def timed(fn):
@@ -459,6 +462,9 @@ def main():
     ap.add_argument("--accept-draws", type=int, default=32,
                     help="logits draws of the agreement model behind mean_accept / committed_tok_s")
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append and draft as two calls (dflash_ctx_append, dflash_draft_block) instead of "
+                         "dflash_append_draft")
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=[WORKLOAD, "qwen3_8b_batched", "gpt_oss_20b", "qwen3_4b", "qwen3_4b_fc"])
     ap.add_argument("--sampled", type=float, default=0.0,
@@ -539,8 +545,11 @@ def main():
 
     def step():
         rewind()
-        dr.ctx_append(seq, n_new_t, step_hidden, n_new)
-        dr.draft_block(seq, anchor_t, draft)
+        if args.separate_append:
+            dr.ctx_append(seq, n_new_t, step_hidden, n_new)
+            dr.draft_block(seq, anchor_t, draft)
+        else:  # the same two calls as one (fewer launches, the same results)
+            dr.append_draft(seq, n_new_t, step_hidden, anchor_t, draft, max_new=n_new)
         dr.verify(seq, draft, logits, acc, nxt, com)
 
     tau = args.sampled
@@ -618,7 +627,9 @@ def main():
                                "I 12288, V 151936), "
                                + (f"drafts sampled at temperature {tau}, lossless temperature-1 verify"
                                   if tau > 0 else "greedy verify") + "; batch 1",
-                   "global_batch": 1, "seq_len": L, "block": N, "launch": "graph" if graph else "eager"},
+                   "global_batch": 1, "seq_len": L, "block": N, "launch": "graph" if graph else "eager",
+                   "calls": ("dflash_ctx_append + dflash_draft_block" if args.separate_append
+                             else "dflash_append_draft") + " + dflash_verify"},
         "roofline": roof,
         "step_roofline": {"bound": "hbm", "bytes": sb["total"], "t_roof_us": round(t_roof_us, 1),
                           "achieved_GBs": round(sb["total"] / (ms_step / 1e3) / 1e9, 1),

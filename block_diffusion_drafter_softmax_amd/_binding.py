@@ -34,7 +34,7 @@ KERNEL_NAMES = ["fuse", "ctx_kv", "norm", "qkv", "attn", "attn_merge", "o_proj",
 
 EXPORTS = [
     "dflash_workspace_bytes", "dflash_create", "dflash_destroy", "dflash_ctx_append",
-    "dflash_draft_block", "dflash_verify", "dflash_verify_noalloc", "dflash_d2sd_draft", "dflash_verify_multi",
+    "dflash_draft_block", "dflash_append_draft", "dflash_verify", "dflash_verify_noalloc", "dflash_d2sd_draft", "dflash_verify_multi",
     "dflash_draft_sample", "dflash_verify_sample",
     "dflash_last_error", "dflash_read_error", "dflash_kernel_timer", "dflash_kernel_timer_read",
 ]
@@ -80,6 +80,7 @@ def _load():
         "dflash_destroy": (None, [vp]),
         "dflash_ctx_append": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, vp]),
         "dflash_draft_block": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "dflash_append_draft": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp]),
         "dflash_verify": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, ctypes.c_float, u64, u64, vp, vp, vp, vp]),
         "dflash_verify_noalloc": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, ctypes.c_float, u64, u64, vp, vp, vp,
                                                  vp]),
@@ -135,6 +136,10 @@ def dflash_ctx_append(ctx, B, seq_ids, n_new, target_hidden, max_new, stream):
 
 def dflash_draft_block(ctx, B, seq_ids, anchor, draft, top2_gap, dbg_hidden, dbg_logits, stream):
     return lib.dflash_draft_block(ctx, B, seq_ids, anchor, draft, top2_gap, dbg_hidden, dbg_logits, stream)
+
+
+def dflash_append_draft(ctx, B, seq_ids, n_new, target_hidden, max_new, anchor, draft, top2_gap, stream):
+    return lib.dflash_append_draft(ctx, B, seq_ids, n_new, target_hidden, max_new, anchor, draft, top2_gap, stream)
 
 
 def dflash_verify(ctx, B, seq_ids, draft, target_logits, logits_dtype, temperature, seed, step,

@@ -376,6 +376,136 @@ hipError_t launch_gemm(const WsArgs& g, int mode, hipStream_t st) {
 }
 
 
+// ------------------------------------------------------------ context append
+
+// An append's launch arguments: the fusion (and its plan) and the context
+// finisher (k split set by append_kv); rows = B * max_new.
+struct AppendCall {
+  FuseArgs fa;
+  CtxFinishArgs ca;
+  int rows;
+};
+
+int append_check(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* n_new,
+                 const uint16_t* target_hidden, int32_t max_new) {
+  if (!ctx) return fail(DFLASH_ERR_INVALID_ARG, "ctx is null");
+  const dflash_config& c = ctx->c;
+  if (B < 1 || B > c.max_batch) return fail(DFLASH_ERR_INVALID_ARG, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
+  if (max_new < 1 || max_new > c.max_new)
+    return fail(DFLASH_ERR_INVALID_ARG, "max_new=%d outside [1, %d]", max_new, c.max_new);
+  if (!seq_ids || !n_new || !target_hidden) return fail(DFLASH_ERR_INVALID_ARG, "null input pointer");
+  return DFLASH_OK;
+}
+
+AppendCall append_args(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* n_new,
+                       const uint16_t* target_hidden, int32_t max_new) {
+  const dflash_config& c = ctx->c;
+  const Layout& L = ctx->L;
+  const int rows = B * max_new;
+  const int H = c.hidden, D = c.n_layers, kvd = c.n_kv_heads * c.head_dim;
+  AppendCall ap{};
+  ap.rows = rows;
+  FuseArgs& fa = ap.fa;
+  fa.hidden = target_hidden;
+  fa.alpha = ctx->at<float>(L.alpha);
+  fa.g_fuse = ctx->w.g_fuse;
+  fa.f = ctx->at<uint16_t>(L.f);
+  fa.B = B;
+  fa.max_new = max_new;
+  fa.seq_ids = seq_ids;
+  fa.n_new = n_new;
+  fa.ctx_len = ctx->kv.ctx_len;
+  fa.page_table = ctx->kv.page_table;
+  fa.max_seqs = c.max_seqs;
+  fa.max_pages_per_seq = c.max_pages_per_seq;
+  fa.n_pages = c.n_pages;
+  fa.max_pos = c.max_pos;
+  fa.row_pos = ctx->at<int>(L.rowpos_a);
+  fa.row_seq = ctx->at<int>(L.rowseq_a);
+  fa.err = ctx->kv.error_word;
+  fa.rows = rows;
+  fa.T = c.n_target_layers;
+  fa.H = H;
+  fa.D = D;
+  fa.eps = c.rms_eps;
+  if (c.fusion == DFLASH_FUSION_FC) {
+    fa.raw = 1;
+    fa.f = ctx->at<uint16_t>(L.fraw);
+  }
+  CtxFinishArgs& ca = ap.ca;
+  ca.part = ctx->at<float>(L.cpart);
+  ca.ks = 1;
+  ca.M = rows;
+  ca.D = D;
+  ca.n_kv = c.n_kv_heads;
+  ca.d = c.head_dim;
+  ca.row_pos = fa.row_pos;
+  ca.row_seq = fa.row_seq;
+  ca.B = B;
+  ca.max_new = max_new;
+  ca.n_new = n_new;
+  ca.ctx_len = ctx->kv.ctx_len;
+  ca.page_table = ctx->kv.page_table;
+  ca.max_pages_per_seq = c.max_pages_per_seq;
+  ca.n_pages = c.n_pages;
+  ca.rope = c.use_rope ? ctx->at<float>(L.rope) : nullptr;
+  ca.kv_pages = ctx->kv.kv_pages;
+  ca.layer_stride = (long long)c.n_pages * 2 * kvd * 16;
+  return ap;
+}
+
+// After the fusion: DFlash's FC fusion layer (GEMM, then norm) if so
+// configured, then the context K and V of every layer as fp32 split
+// partials, columns [layer][K | V]; sets the finisher's k split.
+int append_kv(dflash_ctx* ctx, AppendCall& ap, hipStream_t stream) {
+  const dflash_config& c = ctx->c;
+  const Layout& L = ctx->L;
+  const int rows = ap.rows, H = c.hidden, D = c.n_layers, kvd = c.n_kv_heads * c.head_dim;
+  const bool fc = c.fusion == DFLASH_FUSION_FC;
+  int rc;
+  if (fc) {  // DFlash's FC fusion: c = RMSNorm(W_fc [h^(0); ...; h^(T-1)]) * g_fc, one context for all layers
+    const int TH = c.n_target_layers * H;
+    WsArgs g = ws_base(rows, TH, H);
+    g.part = ctx->at<float>(L.cpart);
+    add_seg(g, ctx->at<uint16_t>(L.wfc), nullptr, ap.fa.f, H / 32, 0);
+    g.ks = gemm_ks(g, WS_PARTIAL, L.cpart_floats);
+    if ((rc = ctx->launch(DFLASH_K_CTX_KV, stream, [&] { return launch_gemm(g, WS_PARTIAL, stream); }))) return rc;
+    NormArgs na{};
+    na.mode = 2;
+    na.part = g.part;
+    na.ks = g.ks;
+    na.g = ctx->w.g_fc;
+    na.h = ctx->at<uint16_t>(L.f);
+    na.H = H;
+    na.M = rows;
+    na.eps = c.rms_eps;
+    if ((rc = ctx->launch(DFLASH_K_FUSE, stream, [&] { return dflash_launch_norm(&na, stream); }))) return rc;
+  }
+  const int n_cols = D * 2 * kvd;
+  int ks = 1, mm_xt = MM_ROW_TILES, mm_wt = 0;  // of the first launch: every launch writes the same partial layout
+  for (int l0 = 0; l0 < D; l0 += WS_MAX_SEG / 2) {
+    WsArgs g = ws_base(rows, H, n_cols);
+    g.part = ctx->at<float>(L.cpart);
+    for (int i = l0; i < D && i < l0 + WS_MAX_SEG / 2; ++i) {
+      const uint16_t* act = ctx->at<uint16_t>(L.f) + (fc ? 0 : (size_t)i * 2 * act_plane(rows, H));
+      add_seg(g, ctx->at<uint16_t>(L.wk_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd);
+      add_seg(g, ctx->at<uint16_t>(L.wv_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd + kvd);
+    }
+    if (l0 == 0) {
+      ks = gemm_ks(g, WS_PARTIAL, L.cpart_floats);
+      mm_xt = g.mm_xt;
+      mm_wt = g.mm_wt;
+    }
+    g.ks = ks;
+    g.mm_xt = mm_xt;
+    g.mm_wt = mm_wt;
+    if ((rc = ctx->launch(DFLASH_K_CTX_KV, stream, [&] { return launch_gemm(g, WS_PARTIAL, stream); })))
+      return rc;
+  }
+  ap.ca.ks = ks;
+  return DFLASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -481,109 +611,12 @@ void dflash_destroy(dflash_ctx* ctx) {
 
 int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* n_new,
                       const uint16_t* target_hidden, int32_t max_new, hipStream_t stream) {
-  if (!ctx) return fail(DFLASH_ERR_INVALID_ARG, "ctx is null");
-  const dflash_config& c = ctx->c;
-  if (B < 1 || B > c.max_batch) return fail(DFLASH_ERR_INVALID_ARG, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
-  if (max_new < 1 || max_new > c.max_new)
-    return fail(DFLASH_ERR_INVALID_ARG, "max_new=%d outside [1, %d]", max_new, c.max_new);
-  if (!seq_ids || !n_new || !target_hidden) return fail(DFLASH_ERR_INVALID_ARG, "null input pointer");
-  const Layout& L = ctx->L;
-  const int rows = B * max_new;
-  const int H = c.hidden, D = c.n_layers, kvd = c.n_kv_heads * c.head_dim;
-  int rc;
-
-  FuseArgs fa{};
-  fa.hidden = target_hidden;
-  fa.alpha = ctx->at<float>(L.alpha);
-  fa.g_fuse = ctx->w.g_fuse;
-  fa.f = ctx->at<uint16_t>(L.f);
-  fa.B = B;
-  fa.max_new = max_new;
-  fa.seq_ids = seq_ids;
-  fa.n_new = n_new;
-  fa.ctx_len = ctx->kv.ctx_len;
-  fa.page_table = ctx->kv.page_table;
-  fa.max_seqs = c.max_seqs;
-  fa.max_pages_per_seq = c.max_pages_per_seq;
-  fa.n_pages = c.n_pages;
-  fa.max_pos = c.max_pos;
-  fa.row_pos = ctx->at<int>(L.rowpos_a);
-  fa.row_seq = ctx->at<int>(L.rowseq_a);
-  fa.err = ctx->kv.error_word;
-  fa.rows = rows;
-  fa.T = c.n_target_layers;
-  fa.H = H;
-  fa.D = D;
-  fa.eps = c.rms_eps;
-  const bool fc = c.fusion == DFLASH_FUSION_FC;
-  if (fc) {
-    fa.raw = 1;
-    fa.f = ctx->at<uint16_t>(L.fraw);
-  }
-  if ((rc = ctx->launch(DFLASH_K_FUSE, stream, [&] { return dflash_launch_fuse(&fa, stream); }))) return rc;
-
-  if (fc) {  // DFlash's FC fusion: c = RMSNorm(W_fc [h^(0); ...; h^(T-1)]) * g_fc, one context for all layers
-    const int TH = c.n_target_layers * H;
-    WsArgs g = ws_base(rows, TH, H);
-    g.part = ctx->at<float>(L.cpart);
-    add_seg(g, ctx->at<uint16_t>(L.wfc), nullptr, fa.f, H / 32, 0);
-    g.ks = gemm_ks(g, WS_PARTIAL, L.cpart_floats);
-    if ((rc = ctx->launch(DFLASH_K_CTX_KV, stream, [&] { return launch_gemm(g, WS_PARTIAL, stream); }))) return rc;
-    NormArgs na{};
-    na.mode = 2;
-    na.part = g.part;
-    na.ks = g.ks;
-    na.g = ctx->w.g_fc;
-    na.h = ctx->at<uint16_t>(L.f);
-    na.H = H;
-    na.M = rows;
-    na.eps = c.rms_eps;
-    if ((rc = ctx->launch(DFLASH_K_FUSE, stream, [&] { return dflash_launch_norm(&na, stream); }))) return rc;
-  }
-
-  // Context K and V of every layer: fp32 split partials, columns
-  // [layer][K | V], then one finisher (RoPE, bf16, page scatter).
-  const int n_cols = D * 2 * kvd;
-  int ks = 1, mm_xt = MM_ROW_TILES, mm_wt = 0;  // of the first launch: every launch writes the same partial layout
-  for (int l0 = 0; l0 < D; l0 += WS_MAX_SEG / 2) {
-    WsArgs g = ws_base(rows, H, n_cols);
-    g.part = ctx->at<float>(L.cpart);
-    for (int i = l0; i < D && i < l0 + WS_MAX_SEG / 2; ++i) {
-      const uint16_t* act = ctx->at<uint16_t>(L.f) + (fc ? 0 : (size_t)i * 2 * act_plane(rows, H));
-      add_seg(g, ctx->at<uint16_t>(L.wk_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd);
-      add_seg(g, ctx->at<uint16_t>(L.wv_t) + (size_t)i * kvd * H, nullptr, act, kvd / 32, i * 2 * kvd + kvd);
-    }
-    if (l0 == 0) {
-      ks = gemm_ks(g, WS_PARTIAL, L.cpart_floats);
-      mm_xt = g.mm_xt;
-      mm_wt = g.mm_wt;
-    }
-    g.ks = ks;
-    g.mm_xt = mm_xt;
-    g.mm_wt = mm_wt;
-    if ((rc = ctx->launch(DFLASH_K_CTX_KV, stream, [&] { return launch_gemm(g, WS_PARTIAL, stream); })))
-      return rc;
-  }
-  CtxFinishArgs ca{};
-  ca.part = ctx->at<float>(L.cpart);
-  ca.ks = ks;
-  ca.M = rows;
-  ca.D = D;
-  ca.n_kv = c.n_kv_heads;
-  ca.d = c.head_dim;
-  ca.row_pos = fa.row_pos;
-  ca.row_seq = fa.row_seq;
-  ca.B = B;
-  ca.max_new = max_new;
-  ca.n_new = n_new;
-  ca.ctx_len = ctx->kv.ctx_len;
-  ca.page_table = ctx->kv.page_table;
-  ca.max_pages_per_seq = c.max_pages_per_seq;
-  ca.n_pages = c.n_pages;
-  ca.rope = c.use_rope ? ctx->at<float>(L.rope) : nullptr;
-  ca.kv_pages = ctx->kv.kv_pages;
-  ca.layer_stride = (long long)c.n_pages * 2 * kvd * 16;
-  return ctx->launch(DFLASH_K_CTX_FINISH, stream, [&] { return dflash_launch_ctx_finish(&ca, stream); });
+  int rc = append_check(ctx, B, seq_ids, n_new, target_hidden, max_new);
+  if (rc) return rc;
+  AppendCall ap = append_args(ctx, B, seq_ids, n_new, target_hidden, max_new);
+  if ((rc = ctx->launch(DFLASH_K_FUSE, stream, [&] { return dflash_launch_fuse(&ap.fa, stream); }))) return rc;
+  if ((rc = append_kv(ctx, ap, stream))) return rc;
+  return ctx->launch(DFLASH_K_CTX_FINISH, stream, [&] { return dflash_launch_ctx_finish(&ap.ca, stream); });
 }
 
 }  // extern "C"
@@ -597,9 +630,14 @@ namespace {
 // `row_cut` [B] (device, nullable): block b needs draft positions
 // row_cut[b] .. N-1 only (a dual-pass candidate keeps the first draft before
 // its cut), so the LM head runs on those rows alone, compacted.
+// `app` (nullable): an append of the same call, launched with the draft:
+// its fusion shares the draft's first launch (the embedding norm, which
+// takes the context length the append leaves), its context K/V projection
+// runs before the first QKV projection, and its finisher shares the first
+// layer's QKV finisher launch.
 int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor, const int32_t* tokens,
                int32_t* draft, float* top2_gap, float* conf, float* dbg_hidden, float* dbg_logits,
-               hipStream_t stream, int grp = 1, const int32_t* row_cut = nullptr) {
+               hipStream_t stream, int grp = 1, const int32_t* row_cut = nullptr, AppendCall* app = nullptr) {
   const dflash_config& c = ctx->c;
   const Layout& L = ctx->L;
   const int N = c.block_size, M = B * N;
@@ -640,7 +678,12 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
   na.H = H;
   na.M = M;
   na.eps = c.rms_eps;
-  if ((rc = ctx->launch(DFLASH_K_NORM, stream, [&] { return dflash_launch_norm(&na, stream); }))) return rc;
+  if (app) {
+    if ((rc = ctx->launch(DFLASH_K_FUSE, stream, [&] { return dflash_launch_fuse_norm(&app->fa, &na, stream); })))
+      return rc;
+  } else if ((rc = ctx->launch(DFLASH_K_NORM, stream, [&] { return dflash_launch_norm(&na, stream); }))) {
+    return rc;
+  }
 
   QkvFinishArgs qa{};
   qa.part = gpart;
@@ -700,10 +743,17 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
       add_seg(g, ctx->at<uint16_t>(L.wv_d) + (size_t)i * kvd * H, nullptr, h, kvd / 32, qd + kvd);
       g.ks = gemm_ks(g, WS_PARTIAL, L.gpart_floats);
       qa.ks = g.ks;
+      if (i == 0 && app && (rc = append_kv(ctx, *app, stream))) return rc;
       if ((rc = ctx->launch(DFLASH_K_QKV, stream, [&] { return launch_gemm(g, WS_PARTIAL, stream); })))
         return rc;
-      if ((rc = ctx->launch(DFLASH_K_QKV_FINISH, stream, [&] { return dflash_launch_qkv_finish(&qa, stream); })))
+      if (i == 0 && app) {
+        if ((rc = ctx->launch(DFLASH_K_CTX_FINISH, stream,
+                              [&] { return dflash_launch_finish2(&app->ca, &qa, stream); })))
+          return rc;
+      } else if ((rc = ctx->launch(DFLASH_K_QKV_FINISH, stream,
+                                   [&] { return dflash_launch_qkv_finish(&qa, stream); }))) {
         return rc;
+      }
     }
     aa.pages = ctx->kv.kv_pages + (size_t)i * layer_stride;
     if ((rc = ctx->launch(DFLASH_K_ATTN, stream, [&] { return dflash_launch_attn(&aa, B, c.head_dim, stream); })))
@@ -859,6 +909,21 @@ int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const
   if (B < 1 || B > c.max_batch) return fail(DFLASH_ERR_INVALID_ARG, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
   if (!seq_ids || !anchor || !draft) return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
   return draft_impl(ctx, B, seq_ids, anchor, nullptr, draft, top2_gap, nullptr, dbg_hidden, dbg_logits, stream);
+}
+
+int dflash_append_draft(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* n_new,
+                        const uint16_t* target_hidden, int32_t max_new, const int32_t* anchor, int32_t* draft,
+                        float* top2_gap, hipStream_t stream) {
+  int rc = append_check(ctx, B, seq_ids, n_new, target_hidden, max_new);
+  if (rc) return rc;
+  if (!anchor || !draft) return fail(DFLASH_ERR_INVALID_ARG, "null input/output pointer");
+  if (ctx->c.fusion == DFLASH_FUSION_FC) {  // its FC layer sits between fusion and projection: the two calls
+    if ((rc = dflash_ctx_append(ctx, B, seq_ids, n_new, target_hidden, max_new, stream))) return rc;
+    return draft_impl(ctx, B, seq_ids, anchor, nullptr, draft, top2_gap, nullptr, nullptr, nullptr, stream);
+  }
+  AppendCall ap = append_args(ctx, B, seq_ids, n_new, target_hidden, max_new);
+  return draft_impl(ctx, B, seq_ids, anchor, nullptr, draft, top2_gap, nullptr, nullptr, nullptr, stream, 1, nullptr,
+                    &ap);
 }
 
 int dflash_d2sd_draft(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor, int32_t K,

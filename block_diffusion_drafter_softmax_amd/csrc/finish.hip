@@ -26,12 +26,11 @@ DEV void rotate(float& x1, float& x2, const float* rope, int pos, int half, int 
 
 // One thread per (row, rotation pair of a query or block-key head) or per
 // (row, block-value element).
-__global__ __launch_bounds__(256) LATENCY_BOUND void qkv_finish_kernel(QkvFinishArgs a) {
+DEV void qkv_finish_body(const QkvFinishArgs& a, int idx) {
   const int d = a.d, half = d / 2;
   const int pq = a.n_q * half, pk = a.n_kv * half, nv = a.n_kv * d;
   const int per_row = pq + pk + nv;
   const int n_cols = (a.n_q + 2 * a.n_kv) * d;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= a.M * per_row) return;
   const int m = idx / per_row, j = idx % per_row;
   const int b = m / a.N, n = m % a.N;
@@ -61,6 +60,10 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void qkv_finish_kernel(QkvFinish
   }
 }
 
+__global__ __launch_bounds__(256) LATENCY_BOUND void qkv_finish_kernel(QkvFinishArgs a) {
+  qkv_finish_body(a, blockIdx.x * blockDim.x + threadIdx.x);
+}
+
 extern "C" hipError_t dflash_launch_qkv_finish(const QkvFinishArgs* a, hipStream_t st) {
   const int per_row = (a->n_q + a->n_kv) * (a->d / 2) + a->n_kv * a->d;
   const int total = a->M * per_row;
@@ -71,13 +74,12 @@ extern "C" hipError_t dflash_launch_qkv_finish(const QkvFinishArgs* a, hipStream
 // One thread per (appended row, layer, key rotation pair or value element);
 // the first B threads also advance the context length of the call's
 // sequences (the append's last kernel: nothing after it reads the old one).
-__global__ __launch_bounds__(256) LATENCY_BOUND void ctx_finish_kernel(CtxFinishArgs a) {
+DEV void ctx_finish_body(const CtxFinishArgs& a, int idx) {
   const int d = a.d, half = d / 2, kvd = a.n_kv * d;
   const int pk = a.n_kv * half;
   const int per_layer = pk + kvd;
   const int per_row = a.D * per_layer;
   const int n_cols = a.D * 2 * kvd;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx < a.B) {
     const int m0 = idx * a.max_new;
     if (a.row_pos[m0] >= 0) a.ctx_len[a.row_seq[m0]] = a.row_pos[m0] + a.n_new[idx];
@@ -108,9 +110,29 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void ctx_finish_kernel(CtxFinish
   }
 }
 
+__global__ __launch_bounds__(256) LATENCY_BOUND void ctx_finish_kernel(CtxFinishArgs a) {
+  ctx_finish_body(a, blockIdx.x * blockDim.x + threadIdx.x);
+}
+
 extern "C" hipError_t dflash_launch_ctx_finish(const CtxFinishArgs* a, hipStream_t st) {
   const int per_row = a->D * (a->n_kv * (a->d / 2) + a->n_kv * a->d);
   const int total = a->M * per_row;
   launch_kernel(ctx_finish_kernel, dim3((total + 255) / 256), dim3(256), 0, st, *a);
+  return hipGetLastError();
+}
+
+// Append and draft launched together: the context finisher (all layers;
+// it also advances ctx_len) and the first draft layer's query/key/value
+// finisher in one launch of independent workgroups.
+__global__ __launch_bounds__(256) LATENCY_BOUND void finish2_kernel(CtxFinishArgs ca, QkvFinishArgs qa, int n_ctx) {
+  const int x = blockIdx.x;
+  if (x < n_ctx) ctx_finish_body(ca, x * blockDim.x + threadIdx.x);
+  else qkv_finish_body(qa, (x - n_ctx) * blockDim.x + threadIdx.x);
+}
+
+extern "C" hipError_t dflash_launch_finish2(const CtxFinishArgs* ca, const QkvFinishArgs* qa, hipStream_t st) {
+  const int n_ctx = (ca->M * ca->D * (ca->n_kv * (ca->d / 2) + ca->n_kv * ca->d) + 255) / 256;
+  const int n_qkv = (qa->M * ((qa->n_q + qa->n_kv) * (qa->d / 2) + qa->n_kv * qa->d) + 255) / 256;
+  launch_kernel(finish2_kernel, dim3(n_ctx + n_qkv), dim3(256), 0, st, *ca, *qa, n_ctx);
   return hipGetLastError();
 }

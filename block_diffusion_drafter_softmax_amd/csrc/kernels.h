@@ -285,6 +285,8 @@ hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_
 hipError_t dflash_launch_attn_merge(const AttnArgs* a, int B, int head_dim, hipStream_t st);
 hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st);
 hipError_t dflash_launch_norm(const NormArgs* a, hipStream_t st);
+hipError_t dflash_launch_fuse_norm(const FuseArgs* fa, const NormArgs* na, hipStream_t st);
+hipError_t dflash_launch_finish2(const CtxFinishArgs* ca, const QkvFinishArgs* qa, hipStream_t st);
 hipError_t dflash_launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
 hipError_t dflash_launch_lmhead(const LmArgs* a, hipStream_t st);
 hipError_t dflash_launch_lmhead_mm(const LmArgs* a, hipStream_t st);

@@ -29,27 +29,10 @@ DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); 
 // group (one workgroup reduction for the group), s = sum_j alpha[i][j] * h_j
 // (ascending j) and f = s / sqrt(mean(s^2) + eps) * g are formed and written
 // as the packed split activation of the context K/V projection.
-template <int MAXV, int DG>
-__global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
-  const int m = blockIdx.x, i0 = blockIdx.y * DG;
-  const int b = m / a.max_new, t = m % a.max_new;
-  __shared__ float red[16][DG];
-  __shared__ float al_s[FUSE_DMAX * FUSE_TMAX];  // alpha, [layer][j], zero past T
-  __shared__ int plan[4];  // seq, L, n, bad
-  // the row's target states are requested before the plan, which takes
-  // three dependent reads
-  const uint16_t* h = a.hidden + (size_t)m * a.T * a.H;
-  u16x4 x[MAXV][FUSE_TMAX];
-#pragma unroll
-  for (int v = 0; v < MAXV; ++v) {
-    const int k = min((v * (int)blockDim.x + (int)threadIdx.x) * 4, a.H - 4);  // clamped: no branch around loads
-#pragma unroll
-    for (int j = 0; j < FUSE_TMAX; ++j) x[v][j] = *reinterpret_cast<const u16x4*>(h + (size_t)min(j, a.T - 1) * a.H + k);
-  }
-  for (int q = threadIdx.x; q < FUSE_DMAX * FUSE_TMAX; q += blockDim.x) {
-    const int i = q / FUSE_TMAX, j = q % FUSE_TMAX;
-    al_s[q] = (i < a.D && j < a.T) ? a.alpha[(size_t)i * a.T + j] : 0.f;  // weights past T are 0
-  }
+// Append plan of sequence b (a whole workgroup takes part; two barriers):
+// plan = (sequence, context length before the append (clamped), rows the
+// append writes, error bits). A failed check skips the whole append.
+DEV void append_plan(const FuseArgs& a, int b, int* plan) {
   if (threadIdx.x == 0) {
     int bad = 0;
     const int s_raw = a.seq_ids[b];
@@ -76,6 +59,29 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
     }
   }
   __syncthreads();
+}
+
+template <int MAXV, int DG>
+DEV void fuse_body(const FuseArgs& a, int m, int i0) {
+  const int b = m / a.max_new, t = m % a.max_new;
+  __shared__ float red[16][DG];
+  __shared__ float al_s[FUSE_DMAX * FUSE_TMAX];  // alpha, [layer][j], zero past T
+  __shared__ int plan[4];  // seq, L, n, bad
+  // the row's target states are requested before the plan, which takes
+  // three dependent reads
+  const uint16_t* h = a.hidden + (size_t)m * a.T * a.H;
+  u16x4 x[MAXV][FUSE_TMAX];
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) {
+    const int k = min((v * (int)blockDim.x + (int)threadIdx.x) * 4, a.H - 4);  // clamped: no branch around loads
+#pragma unroll
+    for (int j = 0; j < FUSE_TMAX; ++j) x[v][j] = *reinterpret_cast<const u16x4*>(h + (size_t)min(j, a.T - 1) * a.H + k);
+  }
+  for (int q = threadIdx.x; q < FUSE_DMAX * FUSE_TMAX; q += blockDim.x) {
+    const int i = q / FUSE_TMAX, j = q % FUSE_TMAX;
+    al_s[q] = (i < a.D && j < a.T) ? a.alpha[(size_t)i * a.T + j] : 0.f;  // weights past T are 0
+  }
+  append_plan(a, b, plan);
   const int bad = plan[3];
   const int pos = (!bad && t < plan[2]) ? plan[1] + t : -1;
   if (blockIdx.y == 0 && threadIdx.x == 0) {
@@ -162,6 +168,11 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
   }
 }
 
+template <int MAXV, int DG>
+__global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_kernel(FuseArgs a) {
+  fuse_body<MAXV, DG>(a, blockIdx.x, blockIdx.y * DG);
+}
+
 extern "C" hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st) {
   const int threads = std::min(1024, ((a->H / 4 + 63) / 64) * 64);
   constexpr int DG = 8;
@@ -188,8 +199,10 @@ extern "C" hipError_t dflash_launch_fuse(const FuseArgs* a, hipStream_t st) {
 // kernel of a draft call) embeds the block's tokens (the anchor and masks,
 // or given input tokens) and also checks the call's sequence ids, tokens
 // and position capacity.
-__global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
-  const int m = blockIdx.x;
+// `app` (with_app): the block's context length is the one after the
+// append of the same call (checked as the append checks it), for a draft
+// launched together with that append.
+DEV void norm_body(const NormArgs& a, int m, const FuseArgs& app, bool with_app) {
   __shared__ float red[16];
   const int nv = (a.H / 4 + blockDim.x - 1) / blockDim.x;
   float xv[NORM_MAXV][4];
@@ -200,7 +213,12 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
     tok = a.tokens ? a.tokens[m] : (n == 0) ? a.anchor[b] : a.mask_id;
     const int s_raw = a.seq_ids[b];
     const int seq = clampi(s_raw, 0, a.max_seqs - 1);
-    const int L = a.ctx_len[seq];
+    int L = a.ctx_len[seq];
+    if (with_app) {  // the context length after the append, as its finisher will set it
+      __shared__ int ap[4];
+      append_plan(app, b, ap);
+      if (!ap[3]) L = ap[1] + ap[2];
+    }
     if (threadIdx.x == 0) {
       int bad = (tok < 0 || tok >= a.V) ? DFLASH_DEV_BAD_TOKEN : 0;
       if (n == 0) {
@@ -281,9 +299,41 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
   }
 }
 
+__global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
+  norm_body(a, blockIdx.x, FuseArgs{}, false);
+}
+
 extern "C" hipError_t dflash_launch_norm(const NormArgs* a, hipStream_t st) {
   const int threads = std::min(1024, ((a->H / 4 + 63) / 64) * 64);
   launch_kernel(norm_kernel, dim3(a->M), dim3(threads), 0, st, *a);
+  return hipGetLastError();
+}
+
+// Append and draft launched together: the fusion's workgroups (as
+// fuse_kernel, row-major over (row, layer group)) and the draft's first norm
+// (embedding; the context length the append leaves) in one launch. Both
+// use the same workgroup size (one float4 of a hidden row per thread).
+template <int MAXV, int DG>
+__global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_norm_kernel(FuseArgs fa, NormArgs na, int n_fuse) {
+  const int x = blockIdx.x;
+  if (x < n_fuse) fuse_body<MAXV, DG>(fa, x % fa.rows, (x / fa.rows) * DG);
+  else norm_body(na, x - n_fuse, fa, true);
+}
+
+extern "C" hipError_t dflash_launch_fuse_norm(const FuseArgs* fa, const NormArgs* na, hipStream_t st) {
+  const int threads = std::min(1024, ((fa->H / 4 + 63) / 64) * 64);
+  constexpr int DG = 8;
+  if (fa->raw || na->mode != 0 || na->H != fa->H) return hipErrorInvalidValue;
+  if (fa->H > 4 * threads) {
+    const int n_fuse = fa->rows * fa->D;
+    launch_kernel((fuse_norm_kernel<2, 1>), dim3(n_fuse + na->M), dim3(threads), 0, st, *fa, *na, n_fuse);
+  } else if (fa->rows < 128) {
+    const int n_fuse = fa->rows * fa->D;
+    launch_kernel((fuse_norm_kernel<1, 1>), dim3(n_fuse + na->M), dim3(threads), 0, st, *fa, *na, n_fuse);
+  } else {
+    const int n_fuse = fa->rows * ((fa->D + DG - 1) / DG);
+    launch_kernel((fuse_norm_kernel<1, DG>), dim3(n_fuse + na->M), dim3(threads), 0, st, *fa, *na, n_fuse);
+  }
   return hipGetLastError();
 }
 

@@ -153,6 +153,23 @@ class Drafter:
                                   p(gap), p(dbg_hidden), p(dbg_logits), _stream(stream))
         return B.check(rc, "dflash_draft_block")
 
+    def append_draft(self, seq_ids, n_new, hidden, anchor, draft, gap=None, max_new=None, stream=None):
+        """ctx_append then draft_block for the same sequences, as one call
+        (the same results, fewer launches)."""
+        Bn = seq_ids.numel()
+        max_new = max_new or hidden.shape[1]
+        N, V, H, D, T = self._dims()
+        _need("seq_ids", seq_ids, (Bn,), I32)
+        _need("n_new", n_new, (Bn,), I32)
+        _need("hidden", hidden, (Bn, max_new, T, H), BF16)
+        _need("anchor", anchor, (Bn,), I32)
+        _need("draft", draft, (Bn, N - 1), I32)
+        _need("gap", gap, (Bn, N - 1), F32, optional=True)
+        rc = B.dflash_append_draft(self.handle, Bn, seq_ids.data_ptr(), n_new.data_ptr(), hidden.data_ptr(), max_new,
+                                   anchor.data_ptr(), draft.data_ptr(), gap.data_ptr() if gap is not None else None,
+                                   _stream(stream))
+        return B.check(rc, "dflash_append_draft")
+
     def verify(self, seq_ids, draft, logits, accept_len, next_token, commit_len=None, temperature=0.0,
                seed=0, step=0, stream=None):
         Bn = seq_ids.numel()

@@ -65,8 +65,7 @@ class Rollout:
 
     def step(self, s):
         dr = self.dr
-        dr.ctx_append(self.seq, self.n_new, self.hidden[s], self.N)
-        dr.draft_block(self.seq, self.anchor, self.draft[s])
+        dr.append_draft(self.seq, self.n_new, self.hidden[s], self.anchor, self.draft[s], max_new=self.N)
         self._target(s)
         dr.verify(self.seq, self.draft[s], self.logits, self.accept[s], self.next_token[s], self.commit[s])
         # the next step appends the committed rows and drafts from the next token

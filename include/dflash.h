@@ -8,6 +8,7 @@
  *                       accepted tokens per draft layer and append their
  *                       context keys/values to the paged cache;
  *   dflash_draft_block  draft a whole block of tokens in one forward pass;
+ *   dflash_append_draft the two above as one call, in fewer launches;
  *   dflash_verify       verify the block against the target's logits and
  *                       return the longest accepted prefix.
  *
@@ -185,6 +186,20 @@ int dflash_ctx_append(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const 
 int dflash_draft_block(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* anchor,
                        int32_t* draft, float* top2_gap, float* dbg_hidden, float* dbg_logits,
                        hipStream_t stream);
+
+/* dflash_ctx_append followed by dflash_draft_block for the same B sequences
+ * [DFLASH Methodology 2, 4; DFLARE 2.1, 2.2], with the same results bit for
+ * bit (the draft sees the context the append leaves), in fewer launches:
+ * the fusion shares the draft's first launch (the block embedding norm,
+ * which applies the append's checks itself to find the context length the
+ * append leaves) and the context finisher shares the first draft layer's
+ * QKV finisher launch. Arguments as the two calls (draft without debug
+ * outputs); validated on the host before anything is enqueued. With FC
+ * fusion (an FC layer between fusion and projection) it issues the two
+ * calls in turn. Device-side errors set the same bits as the two calls. */
+int dflash_append_draft(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t* n_new,
+                        const uint16_t* target_hidden, int32_t max_new, const int32_t* anchor, int32_t* draft,
+                        float* top2_gap, hipStream_t stream);
 
 /* Verify the drafted blocks [DFLASH Methodology 3, 4; D2SD Methodology 5].
  * target_logits [B, N, V] (bf16 or fp32 per logits_dtype): row r predicts
