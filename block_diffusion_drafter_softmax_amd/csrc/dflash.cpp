@@ -338,7 +338,7 @@ int gemm_ks(WsArgs& g, int mode, size_t cap_floats) {
   g.mm_xt = full >= 2 * kMmTargetWgs ? MM_ROW_TILES : MM_ROW_TILES / 2;
   const int blocks = cb16 * ((m_tiles + g.mm_xt - 1) / g.mm_xt);
   const int target = g.mm_xt == MM_ROW_TILES ? kMmTargetWgs : 2 * kMmTargetWgs;
-  const int ks = mode == WS_SWIGLU ? 1 : ks_cap((target + blocks - 1) / blocks);
+  const int ks = ks_cap((target + blocks - 1) / blocks);  // a split SwiGLU product is finished by swiglu_finish
   {
     const long long wgs = (long long)blocks * ks;
     const int per_cu = g.mm_xt == MM_ROW_TILES ? 2 : 3;
@@ -348,7 +348,7 @@ int gemm_ks(WsArgs& g, int mode, size_t cap_floats) {
     int best_wt = 0, best_ks = ks;
     for (int wt : {16, 24, 32}) {
       const int b8 = col_blocks(wt) * ((m_tiles + MM_ROW_TILES - 1) / MM_ROW_TILES);
-      for (int k8 = 1; k8 <= (mode == WS_SWIGLU ? 1 : kKsMax); ++k8) {
+      for (int k8 = 1; k8 <= kKsMax; ++k8) {
         if (k8 != ks_cap(k8)) break;
         const long long w8 = (long long)b8 * k8;
         const long long r8 = (w8 + 255) / 256;
