@@ -65,7 +65,302 @@ DEV int krow(int k) {
 }
 // Chunk key held by lane group g, accumulator i, of key tile j.
 DEV int tile_key(int j, int g, int i) { return (j >> 1) * 32 + 8 * g + (j & 1) * 4 + i; }
+// Chunk key held in LDS row `row` (the inverse of krow).
+DEV int kinv(int row) {
+  const int r = row & 31;
+  return (row & ~31) + ((r >> 2) & 3) * 8 + (r >> 4) * 4 + (r & 3);
+}
+// DMA layout: key rows of D elements with no padding; the 16-byte units of
+// row r are XOR-permuted by kswz(r), so that the 16 lanes that read one unit
+// of 16 consecutive rows hit 16 distinct bank groups.
+template <int D>
+DEV int kswz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
 }  // namespace
+
+// Masking of invalid keys (masked: the block item, or the context's last
+// chunk) and the online-softmax update of one half of S held by a wave: S
+// becomes its numerators exp2(S - max), the running max and sum advance,
+// and (MULTI) the O accumulators are rescaled.
+template <int D, int NTH, bool MULTI>
+DEV void softmax_update(f32x4 (&s)[NTH], const int* ccnt, bool masked, int hv, int g, float& mx, float& l,
+                        f32x4 (&acc)[D / 16]) {
+  constexpr int DT = D / 16;
+  if (masked) {
+#pragma unroll
+    for (int j = 0; j < NTH; ++j) {
+      const int k0 = tile_key(hv * NTH + j, g, 0);  // 4 keys k0 .. k0+3 of one page
+      const int nj = ccnt[k0 >> 4] - (k0 & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[j][i] = i < nj ? s[j][i] : -INFINITY;
+    }
+  }
+  float cm = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NTH; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cm = fmaxf(cm, s[j][i]);
+  cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+  cm = fmaxf(cm, __shfl_xor(cm, 32, 64));  // -inf for a half with no valid key
+  // mx stays -inf while a wave has met no valid key (the second key
+  // group can meet none); mref keeps the exponents defined then
+  const float mn = fmaxf(mx, cm);
+  const float mref = mn == -INFINITY ? 0.f : mn;
+  const float scale = exp2f(mx - mref);  // 0 at the first update
+  mx = mn;
+  float cs = 0.f;
+#pragma unroll
+  for (int j = 0; j < NTH; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[j][i] = __builtin_amdgcn_exp2f(s[j][i] - mref);  // <= 1; results under 2^-126 flush to 0
+      cs += s[j][i];
+    }
+  cs += __shfl_xor(cs, 16, 64);
+  cs += __shfl_xor(cs, 32, 64);
+  l = l * scale + cs;
+  if (MULTI) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[t] *= scale;
+  }
+}
+
+// P of key tiles j, j + 1 (32 keys: the lane's 8 slots of one page) as a
+// split hi/lo MFMA operand.
+DEV void p_operand(const f32x4& s0, const f32x4& s1, bf16x8& ph, bf16x8& pl) {
+  u16x4 h0, l0, h1, l1;
+  split4(s0, h0, l0);
+  split4(s1, h1, l1);
+  ph = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+  pl = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// S = K Q^T, the online-softmax update and O^T += V^T P^T of one chunk (or
+// of the block item) for one computing wave: key row r of the LDS stage at
+// kb + r * KP (units swizzled with SWZ), V at vb as [page slot][half][d][8
+// slots]; ccnt: valid keys of each page slot of the chunk.
+template <int D, int NACC, bool MULTI, int KS, int KP, bool SWZ>
+DEV void chunk_compute(const uint16_t* kb, const uint16_t* vb, const int* ccnt, bool blk_item, int nv, int kh,
+                       int r16, int g, const bf16x8 (&qh)[D / 32], const bf16x8 (&ql)[D / 32],
+                       f32x4 (&acc)[D / 16], float& mx, float& l) {
+  constexpr int KD = D / 32, DT = D / 16, NT = CH / 16;
+  // Key tile j = LDS rows 16j .. 16j+15; the lane holds S for keys
+  // tile_key(j, g, 0..3) of its query. Multi-chunk items take a chunk as
+  // HV = 2 halves of 64 keys, each with its own online-softmax update, so
+  // that the O accumulators kept across chunks fit the registers; with
+  // KS = 2 each key group takes its own half.
+  constexpr int HV = MULTI || KS == 2 ? 2 : 1, NTH = NT / HV;
+  // key tiles with work: the block item's two (its keys, then a masked
+  // page), all of a context chunk's (wave-uniform)
+  const int nt_act = blk_item ? 2 : NTH;
+#pragma unroll
+  for (int hh = 0; hh < (KS == 2 ? 1 : HV); ++hh) {
+    const int hv = KS == 2 ? kh : hh;  // the half: a key group's own one with KS = 2
+    if (blk_item && hv > 0) break;
+    f32x4 s[NTH];
+    {
+      f32x4 sa[NACC][NTH];
+#pragma unroll
+      for (int h = 0; h < NACC; ++h)
+#pragma unroll
+        for (int j = 0; j < NTH; ++j) sa[h][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // the ring's d_h-128 kernel (registers to spare): every K fragment of
+      // the half requested at once, so LDS latency is paid once, not per kd
+      constexpr bool PF = SWZ && D == 128;
+      constexpr int KB = PF ? KD : 1;  // kd steps whose fragments are read together
+#pragma unroll
+      for (int kd0 = 0; kd0 < KD; kd0 += KB) {
+        bf16x8 kf[KB][NTH];
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+          for (int j = 0; j < NTH; ++j) {
+            const int row = 16 * (hv * NTH + j) + r16, u = (kd0 + kk) * 4 + g;
+            kf[kk][j] = *reinterpret_cast<const bf16x8*>(kb + row * KP + (SWZ ? (u ^ kswz<D>(row)) : u) * 8);
+          }
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+          for (int j = 0; j < NTH; ++j) {
+            sa[0][j] = mfma16(kf[kk][j], qh[kd0 + kk], sa[0][j]);
+            sa[NACC - 1][j] = mfma16(kf[kk][j], ql[kd0 + kk], sa[NACC - 1][j]);
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < NTH; ++j) s[j] = NACC == 2 ? sa[0][j] + sa[NACC - 1][j] : sa[0][j];
+    }
+    // the ring's d_h-128 kernel: the half's V fragments requested before
+    // the softmax (they do not depend on it), in flight while it runs
+    constexpr bool VPF_ON = SWZ && D == 128;
+    constexpr int VPF = VPF_ON ? NTH / 2 : 1;
+    bf16x8 vpre[VPF][VPF_ON ? DT : 1];
+    if constexpr (VPF_ON) {
+#pragma unroll
+      for (int jj = 0; jj < VPF; ++jj) {
+        const uint16_t* vp = vb + (hv * NTH + 2 * jj + (g >> 1)) * D * 16 + (g & 1) * D * 8 + r16 * 8;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) vpre[jj][t] = *reinterpret_cast<const bf16x8*>(vp + t * 128);
+      }
+    }
+    softmax_update<D, NTH, MULTI>(s, ccnt, blk_item || nv < CH, hv, g, mx, l, acc);
+
+#pragma unroll
+    for (int j = 0; j < NTH; j += 2) {  // k-step: key tiles j and j+1 (32 keys, 2 pages)
+      if (j < nt_act) {
+        // lane's keys: slots 8*(g&1) .. +7 of the step's page g>>1
+        const uint16_t* vp = vb + (hv * NTH + j + (g >> 1)) * D * 16 + (g & 1) * D * 8 + r16 * 8;
+        bf16x8 ph, pl;
+        p_operand(s[j], s[j + 1], ph, pl);
+        if constexpr (VPF_ON) {
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            acc[t] = mfma16(vpre[j / 2][t], ph, acc[t]);
+            acc[t] = mfma16(vpre[j / 2][t], pl, acc[t]);
+          }
+        } else {
+          constexpr int TB = MULTI ? DT / 2 : DT;  // V fragments read at once
+#pragma unroll
+          for (int t0 = 0; t0 < DT; t0 += TB) {
+            bf16x8 vf[TB];
+#pragma unroll
+            for (int t = 0; t < TB; ++t) vf[t] = *reinterpret_cast<const bf16x8*>(vp + (t0 + t) * 128);
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+              acc[t0 + t] = mfma16(vf[t], ph, acc[t0 + t]);
+              acc[t0 + t] = mfma16(vf[t], pl, acc[t0 + t]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// Stage K (rows krow(key)) and V ([page slot][half][d][8 slots]) of the
+// PAGES page slots of a chunk in LDS through registers: per page, 2*D*16
+// bf16 = UPP = 4*D 16-byte units, K units first. Thread t moves unit t %
+// UPP of page slots t / UPP + SP*i, so the unit -- K or V, its source
+// offset, its LDS place -- is fixed per thread and a whole wave works on
+// one page slot (UPP is a multiple of 64): page lookups and the K/V choice
+// are wave-uniform. Slots past the chunk's pages read the block (valid
+// memory) and count 0 valid keys, so every V value of an invalid key is
+// stored as 0 and the MFMAs never meet stale values; K of invalid keys is
+// masked in S. The block item stages its one page (one load per thread)
+// and the masked page's V as zeros.
+template <int D, bool MULTI, int KP, bool SWZ>
+DEV void stage_regs(uint16_t* kst, uint16_t* vst, const long long* cpo, const int* ccnt, bool blk_item, bool isk,
+                    int tid, int nthreads, const uint16_t* blk_k, const uint16_t* blk_v, const uint16_t* pages,
+                    int n_kv) {
+  constexpr int UPP = 4 * D;
+  constexpr int UB = MULTI ? 4 : 8;  // loads per thread and batch (registers: O is live across chunks)
+  const int SP = nthreads / UPP;     // page slots per pass (nthreads >= 512 >= UPP)
+  const int passes = (PAGES + SP - 1) / SP;
+  const int w = tid % UPP;
+  const int p0 = __builtin_amdgcn_readfirstlane(tid / UPP);
+  const int e = w - 2 * D;  // V unit: dim e/2, slots 8*(e&1) .. +7
+  const int kslot = w / (D / 8), kunit = w % (D / 8);
+  const int src_off = isk ? kslot * D + kunit * 8 : e * 8;
+  const int v_off = (e & 1) * D * 8 + (e >> 1) * 8;
+  auto k_off = [&](int pi) {  // this thread's K unit of page slot pi
+    const int row = krow(pi * 16 + kslot);
+    return row * KP + (SWZ ? (kunit ^ kswz<D>(row)) : kunit) * 8;
+  };
+  const uint16_t* blk = (isk ? blk_k : blk_v) + src_off;
+  const uint16_t* pgs = pages + (isk ? 0 : (size_t)n_kv * 16 * D) + src_off;
+  if (blk_item) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (p0 == 0) v = *reinterpret_cast<const u32x4*>(blk);
+    for (int pi = p0; pi < 2; pi += SP) {
+      if (isk) {
+        if (pi == 0) *reinterpret_cast<u32x4*>(&kst[k_off(0)]) = v;
+      } else {
+        const int valid = ccnt[pi] - (e & 1) * 8;
+        u32x4 m;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          m[q] = (2 * q < valid ? 0xFFFFu : 0u) | (2 * q + 1 < valid ? 0xFFFF0000u : 0u);
+        *reinterpret_cast<u32x4*>(&vst[pi * D * 16 + v_off]) = v & m;
+      }
+    }
+  } else if (p0 < SP) {
+    for (int i0 = 0; i0 < passes; i0 += UB) {
+      u32x4 buf[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {  // clamped slots: duplicate loads, not stored
+        const long long o = cpo[min((i0 + u) * SP + p0, PAGES - 1)];
+        buf[u] = *reinterpret_cast<const u32x4*>(o < 0 ? blk : pgs + o);
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int pi = (i0 + u) * SP + p0;
+        if (i0 + u >= passes || pi >= PAGES) break;
+        if (isk) {
+          *reinterpret_cast<u32x4*>(&kst[k_off(pi)]) = buf[u];
+        } else {
+          const int valid = ccnt[pi] - (e & 1) * 8;
+          u32x4 m;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            m[q] = (2 * q < valid ? 0xFFFFu : 0u) | (2 * q + 1 < valid ? 0xFFFF0000u : 0u);
+          *reinterpret_cast<u32x4*>(&vst[pi * D * 16 + v_off]) = buf[u] & m;
+        }
+      }
+    }
+  }
+}
+
+// Direct-to-LDS staging of one chunk (DMA layout) by a workgroup of 8 waves
+// into a stage's K array (CH rows of D) and V array ([page slot][half][d][8
+// slots]): each wave instruction moves one 1 KB block, lane l to byte 16l
+// of it, from wherever that unit lives in the cache pages. The first half
+// of a thread's instructions fill K, the second half V; a block is all of
+// one page slot (K: 4 rows of d_h 128 or 8 rows of 64 in one 8-key run of
+// krow's order; V: 64 dims of one half page), so the page lookup is one
+// broadcast LDS read per instruction. Slots past the chunk's pages read the
+// block (valid memory); their V is zeroed once landed.
+template <int D>
+DEV void stage_dma(uint16_t* kst, uint16_t* vst, const long long* cpo, int wave, int lane, const uint16_t* blk_k,
+                   const uint16_t* blk_v, const uint16_t* pages, int n_kv) {
+  constexpr int KU = CH * D / 8, LPC = 2 * KU / 64 / 8;  // K units (= V units), loads per thread
+  static_assert(KU == 64 * 8 * (LPC / 2), "K blocks are the first half of every wave's loads");
+  const uint16_t* pages_v = pages + (size_t)n_kv * 16 * D;
+#pragma unroll
+  for (int i = 0; i < LPC; ++i) {
+    const int blk = (i % (LPC / 2)) * 8 + wave;  // block of the K or V array
+    const int u = blk * 64 + lane;
+    if (i < LPC / 2) {
+      const int row = u / (D / 8), key = kinv(row), c = (u % (D / 8)) ^ kswz<D>(row);
+      const long long o = cpo[key >> 4];
+      dma16((o < 0 ? blk_k : pages + o) + (key & 15) * D + c * 8, reinterpret_cast<u32x4*>(kst) + blk * 64);
+    } else {
+      const int pi = u / (2 * D), half = (u / D) & 1, dim = u % D;
+      const long long o = cpo[pi];
+      dma16((o < 0 ? blk_v : pages_v + o) + dim * 16 + half * 8, reinterpret_cast<u32x4*>(vst) + blk * 64);
+    }
+  }
+}
+
+// V values of invalid key slots of a landed DMA stage set to 0 (P is 0
+// there, but a stale value could be a NaN or an infinity); 512 threads,
+// straight-line code (a loop here would cost the ring its precise waits).
+template <int D>
+DEV void zero_invalid_v(uint16_t* vb, const int* ccnt, int tid) {
+  constexpr int UNITS = PAGES * 2 * D;
+  static_assert(UNITS % 512 == 0, "whole passes");
+#pragma unroll
+  for (int i = 0; i < UNITS / 512; ++i) {
+    const int u = i * 512 + tid;
+    const int valid = ccnt[u / (2 * D)] - ((u / D) & 1) * 8;
+    if (valid < 8) {
+      u32x4* p = reinterpret_cast<u32x4*>(vb) + u;
+      u32x4 m;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) m[q] = (2 * q < valid ? 0xFFFFu : 0u) | (2 * q + 1 < valid ? 0xFFFF0000u : 0u);
+      *p = *p & m;
+    }
+  }
+}
 
 // NACC: accumulator sets for the S products (2: hi and lo separately, more
 // independent MFMA chains; 1 where 1024-thread workgroups cap the registers).
@@ -75,12 +370,31 @@ DEV int tile_key(int j, int g, int i) { return (j >> 1) * 32 + 8 * g + (j & 1) *
 // group takes the second half of every chunk's keys for the same rows,
 // with its own online softmax, and hands (max, sum, O) to its partner
 // through LDS at the end.
-template <int D, int NACC, bool MULTI, int KS>
-__global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs a) {
-  constexpr int KP = D + 8;  // padded LDS row of one key (bf16 elements)
+// DMA (multi-chunk items, 8 waves): a ring of two LDS stages filled by
+// direct-to-LDS loads; chunk i + 1 lands while chunk i is computed. Its
+// 128 KB at d_h 128 leave one workgroup per CU (two at d_h 64).
+// The ring's workgroup is 8 waves and LDS holds it to one per CU at d_h 128,
+// so it may take 256 VGPRs there (a spill reload would be counted with the
+// loads in flight and wait for them all); two per CU at d_h 64, 128 VGPRs.
+template <int D, int NACC, bool MULTI, int KS, int RING>
+__global__ __launch_bounds__(RING ? 512 : 1024)
+__attribute__((amdgpu_waves_per_eu(RING && D == 128 ? 1 : 4, RING && D == 128 ? 2 : 4)))
+void attn_chunk_kernel(AttnArgs a) {
+  constexpr bool DMA = RING > 0;
+  static_assert(!DMA || (MULTI && RING >= 2 && RING <= CPI_MAX), "the DMA ring takes multi-chunk items");
+  constexpr int KP = DMA ? D : D + 8;  // LDS row of one key (bf16 elements): padded, or swizzled
   constexpr int K_ELEMS = CH * KP, V_ELEMS = PAGES * D * 16;
   constexpr int SLOTS = (MULTI ? CPI_MAX : 1) * PAGES;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[K_ELEMS + V_ELEMS];
+  // register staging: one stage, lds = K then V. The ring: stage 0 = (lds,
+  // ldv0), stage 1 = (ldk1, ldv1), four arrays, so that every LDS access is
+  // a short index off its own array: the compiler then keeps the alias
+  // information that lets a read of one stage proceed while the other
+  // stage's loads are in flight (with long address chains it drops it and
+  // waits for all of them).
+  __shared__ __attribute__((aligned(16))) uint16_t lds[DMA ? K_ELEMS : K_ELEMS + V_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t ldv0[DMA ? V_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t ldk1[DMA ? K_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t ldv1[DMA ? V_ELEMS : 8];
   __shared__ long long poff[SLOTS];  // element offset in `pages` of each page slot's K block (this kv head); -1: block
   __shared__ int cnt[SLOTS];         // valid key slots of each page slot
 
@@ -167,7 +481,7 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
   const int cand = wc / n_wr, b = b0 + cand;  // the wave's block
   const int r = (wc % n_wr) * 16 + r16;
   const int hq = kvh * G + r / a.N, n = r % a.N;
-  constexpr int KD = D / 32, DT = D / 16, NT = CH / 16;
+  constexpr int KD = D / 32, DT = D / 16;
 
   // queries (softmax scale already applied): in flight with the page reads
   bf16x8 qh[KD], ql[KD];
@@ -185,194 +499,72 @@ __global__ __launch_bounds__(1024) LATENCY_BOUND void attn_chunk_kernel(AttnArgs
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mx = -INFINITY, l = 0.f;
-  // the block item's compute takes two key tiles: its keys, then a masked
-  // page (V stored as zeros, K masked in S)
-  const int st_pages = 2;
-  for (int ci = 0; ci < n_chunks; ++ci) {
-    const int nv = min(item_nv - ci * CH, CH);  // keys in this chunk
-    const long long* cpo = poff + ci * PAGES;
-    const int* ccnt = cnt + ci * PAGES;
-    __syncthreads();  // page slots written; the previous chunk's LDS reads done
-
-    // Stage K (slot-major rows) and V (dim-major) of all PAGES page slots
-    // in LDS: per page, 2*D*16 bf16 = UPP = 4*D 16-byte units, K units
-    // first. Thread t moves unit t % UPP of page slots t / UPP + SP*i, so
-    // the unit -- K or V, its source offset, its LDS place -- is fixed per
-    // thread and a whole wave works on one page slot (UPP is a multiple of
-    // 64): page lookups and the K/V choice are wave-uniform. Slots past the
-    // chunk's pages read the block (valid memory) and count 0 valid keys,
-    // so every V value of an invalid key is stored as 0 and the MFMAs never
-    // meet stale values; K of invalid keys is masked in S.
-    {
-      constexpr int UPP = 4 * D;
-      constexpr int UB = MULTI ? 4 : 8;  // loads per thread and batch (registers: O is live across chunks)
-      const int SP = nthreads / UPP;     // page slots per pass (nthreads >= 512 >= UPP)
-      const int passes = (PAGES + SP - 1) / SP;
-      const int w = tid % UPP;
-      const int p0 = __builtin_amdgcn_readfirstlane(tid / UPP);
-      const bool isk = isk_wave;
-      const int e = w - 2 * D;  // V unit: dim e/2, slots 8*(e&1) .. +7
-      const int src_off = isk ? (w / (D / 8)) * D + (w % (D / 8)) * 8 : e * 8;
-      const int lds_off = isk ? (w % (D / 8)) * 8 : K_ELEMS + (e & 1) * D * 8 + (e >> 1) * 8;
-      const uint16_t* blk = (isk ? blk_k : blk_v) + src_off;
-      const uint16_t* pgs = a.pages + (isk ? 0 : (size_t)a.n_kv * 16 * D) + src_off;
-      if (blk_item) {  // the block page (one load per thread), and the masked page's V as zeros
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (p0 == 0) v = *reinterpret_cast<const u32x4*>(blk);
-        for (int pi = p0; pi < st_pages; pi += SP) {
-          if (isk) {
-            if (pi == 0) *reinterpret_cast<u32x4*>(&lds[krow(w / (D / 8)) * KP + lds_off]) = v;
-          } else {
-            const int valid = ccnt[pi] - (e & 1) * 8;
-            u32x4 m;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              m[q] = (2 * q < valid ? 0xFFFFu : 0u) | (2 * q + 1 < valid ? 0xFFFF0000u : 0u);
-            *reinterpret_cast<u32x4*>(&lds[pi * D * 16 + lds_off]) = v & m;
-          }
-        }
-      } else if (p0 < SP) {
-        for (int i0 = 0; i0 < passes; i0 += UB) {
-          u32x4 buf[UB];
-#pragma unroll
-          for (int u = 0; u < UB; ++u) {  // clamped slots: duplicate loads, not stored
-            const long long o = cpo[min((i0 + u) * SP + p0, PAGES - 1)];
-            buf[u] = *reinterpret_cast<const u32x4*>(o < 0 ? blk : pgs + o);
-          }
-#pragma unroll
-          for (int u = 0; u < UB; ++u) {
-            const int pi = (i0 + u) * SP + p0;
-            if (i0 + u >= passes || pi >= PAGES) break;
-            if (isk) {
-              *reinterpret_cast<u32x4*>(&lds[krow(pi * 16 + w / (D / 8)) * KP + lds_off]) = buf[u];
-            } else {
-              const int valid = ccnt[pi] - (e & 1) * 8;
-              u32x4 m;
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                m[q] = (2 * q < valid ? 0xFFFFu : 0u) | (2 * q + 1 < valid ? 0xFFFF0000u : 0u);
-              *reinterpret_cast<u32x4*>(&lds[pi * D * 16 + lds_off]) = buf[u] & m;
-            }
-          }
-        }
-      }
+  if (!DMA || n_chunks != RING) {
+    // stage a chunk through registers, then compute it (the block item: its
+    // keys and one masked page, two key tiles; with the ring, also a
+    // sequence's last item when it has fewer chunks than the ring)
+    uint16_t* kst = lds;
+    uint16_t* vst = DMA ? ldv0 : lds + K_ELEMS;
+    for (int ci = 0; ci < n_chunks; ++ci) {
+      const int nv = min(item_nv - ci * CH, CH);  // keys in this chunk
+      __syncthreads();  // page slots written; the previous chunk's LDS reads done
+      stage_regs<D, MULTI, KP, DMA>(kst, vst, poff + ci * PAGES, cnt + ci * PAGES, blk_item, isk_wave, tid, nthreads,
+                                    blk_k, blk_v, a.pages, a.n_kv);
+      __syncthreads();
+      if (computing)
+        chunk_compute<D, NACC, MULTI, KS, KP, DMA>(kst, vst, cnt + ci * PAGES, blk_item, nv, kh, r16, g, qh, ql, acc,
+                                                   mx, l);
     }
-    __syncthreads();
-    if (!computing) continue;
-
-    // Key tile j = LDS rows 16j .. 16j+15; the lane holds S for keys
-    // tile_key(j, g, 0..3) of its query. Multi-chunk items take a chunk as
-    // HV = 2 halves of 64 keys, each with its own online-softmax update, so
-    // that the O accumulators kept across chunks fit the registers; with
-    // KS = 2 each key group takes its own half.
-    constexpr int HV = MULTI || KS == 2 ? 2 : 1, NTH = NT / HV;
-    // key tiles with work: the block item's two (its keys, then a masked
-    // page), all of a context chunk's (wave-uniform)
-    const int nt_act = blk_item ? 2 : NTH;
+  } else if constexpr (DMA) {
+    // The ring, for items of exactly RING chunks: chunks 0 and 1 requested
+    // at once; then per chunk, wait for its own loads (the next chunk's stay
+    // in flight), compute it, and request the chunk after next into the
+    // stage it leaves. Fully unrolled with every load request and wait fixed
+    // at compile time: only then does the compiler let the reads of one
+    // stage run while the other stage's loads are in flight (a request or a
+    // wait under a run-time condition makes it wait for all of them before
+    // every read). Waits are explicit vmcnt counts and bare barriers (the
+    // compiler's __syncthreads would also wait for the loads in flight).
+    constexpr int LPC = 2 * CH * D / 8 / 64 / 8;  // DMA loads per thread and chunk
+    __syncthreads();                              // page slots written
+    stage_dma<D>(lds, ldv0, poff, wave, lane, blk_k, blk_v, a.pages, a.n_kv);
+    stage_dma<D>(ldk1, ldv1, poff + PAGES, wave, lane, blk_k, blk_v, a.pages, a.n_kv);
 #pragma unroll
-    for (int hh = 0; hh < (KS == 2 ? 1 : HV); ++hh) {
-      const int hv = KS == 2 ? kh : hh;  // the half: a key group's own one with KS = 2
-      if (blk_item && hv > 0) break;
-      f32x4 s[NTH];
-      {
-        f32x4 sa[NACC][NTH];
-#pragma unroll
-        for (int h = 0; h < NACC; ++h)
-#pragma unroll
-          for (int j = 0; j < NTH; ++j) sa[h][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kd = 0; kd < KD; ++kd) {
-          bf16x8 kf[NTH];
-#pragma unroll
-          for (int j = 0; j < NTH; ++j)
-            kf[j] = *reinterpret_cast<const bf16x8*>(&lds[(16 * (hv * NTH + j) + r16) * KP + kd * 32 + 8 * g]);
-#pragma unroll
-          for (int j = 0; j < NTH; ++j) {
-            if (true) {
-              sa[0][j] = mfma16(kf[j], qh[kd], sa[0][j]);
-              sa[NACC - 1][j] = mfma16(kf[j], ql[kd], sa[NACC - 1][j]);
-            }
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < NTH; ++j) s[j] = NACC == 2 ? sa[0][j] + sa[NACC - 1][j] : sa[0][j];
+    for (int ci = 0; ci < RING; ++ci) {
+      uint16_t* kst = (ci & 1) ? ldk1 : lds;
+      uint16_t* vst = (ci & 1) ? ldv1 : ldv0;
+      if (ci + 1 < RING) __builtin_amdgcn_s_waitcnt(0x0F70 | LPC);
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+      __builtin_amdgcn_s_barrier();  // chunk ci landed for every wave
+      const int nv = min(item_nv - ci * CH, CH);
+      if (nv < CH) {  // the context's last chunk: V of its invalid slots to 0
+        zero_invalid_v<D>(vst, cnt + ci * PAGES, tid);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
       }
-      if (blk_item || nv < CH) {  // block item, or the context's last chunk: mask invalid keys
-#pragma unroll
-        for (int j = 0; j < NTH; ++j) {
-          const int k0 = tile_key(hv * NTH + j, g, 0);  // 4 keys k0 .. k0+3 of one page
-          const int nj = ccnt[k0 >> 4] - (k0 & 15);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[j][i] = i < nj ? s[j][i] : -INFINITY;
-        }
-      }
-      float cm = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < NTH; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cm = fmaxf(cm, s[j][i]);
-      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));  // -inf for a half with no valid key
-      // mx stays -inf while a wave has met no valid key (the second key
-      // group can meet none); mref keeps the exponents defined then
-      const float mn = fmaxf(mx, cm);
-      const float mref = mn == -INFINITY ? 0.f : mn;
-      const float scale = exp2f(mx - mref);  // 0 at the first update
-      mx = mn;
-      float cs = 0.f;
-#pragma unroll
-      for (int j = 0; j < NTH; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s[j][i] = __builtin_amdgcn_exp2f(s[j][i] - mref);  // <= 1; results under 2^-126 flush to 0
-          cs += s[j][i];
-        }
-      cs += __shfl_xor(cs, 16, 64);
-      cs += __shfl_xor(cs, 32, 64);
-      l = l * scale + cs;
-      if (MULTI) {
-#pragma unroll
-        for (int t = 0; t < DT; ++t) acc[t] *= scale;
-      }
-
-#pragma unroll
-      for (int j = 0; j < NTH; j += 2) {  // k-step: key tiles j and j+1 (32 keys, 2 pages)
-        if (j < nt_act) {
-          // lane's keys: slots 8*(g&1) .. +7 of the step's page g>>1
-          const uint16_t* vp = &lds[K_ELEMS + (hv * NTH + j + (g >> 1)) * D * 16 + (g & 1) * D * 8 + r16 * 8];
-          u16x4 h0, l0, h1, l1;
-          split4(s[j], h0, l0);
-          split4(s[j + 1], h1, l1);
-          const bf16x8 ph = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
-          const bf16x8 pl = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
-          constexpr int TB = MULTI ? DT / 2 : DT;  // V fragments read at once
-#pragma unroll
-          for (int t0 = 0; t0 < DT; t0 += TB) {
-            bf16x8 vf[TB];
-#pragma unroll
-            for (int t = 0; t < TB; ++t) vf[t] = *reinterpret_cast<const bf16x8*>(vp + (t0 + t) * 128);
-#pragma unroll
-            for (int t = 0; t < TB; ++t) {
-              acc[t0 + t] = mfma16(vf[t], ph, acc[t0 + t]);
-              acc[t0 + t] = mfma16(vf[t], pl, acc[t0 + t]);
-            }
-          }
-        }
-      }
+      if (computing)
+        chunk_compute<D, NACC, true, KS, KP, true>(kst, vst, cnt + ci * PAGES, false, nv, kh, r16, g, qh, ql, acc, mx,
+                                                   l);
+      __builtin_amdgcn_s_barrier();  // every wave is done with this stage
+      if (ci + 2 < RING) stage_dma<D>(kst, vst, poff + (ci + 2) * PAGES, wave, lane, blk_k, blk_v, a.pages, a.n_kv);
     }
   }
   if (KS == 2) {  // the second key group's (max, sum, O) to its partner, lane by lane
-    static_assert(4 * (DT + 1) * 64 * 16 <= (K_ELEMS + V_ELEMS) * 2, "hand-off area");
-    f32x4* xl = reinterpret_cast<f32x4*>(lds) + (size_t)wc * (DT + 1) * 64 + lane;  // wc < n_comp <= 4
+    // O parts [wave][t][lane] and (max, sum) [wave][lane]; wc < n_comp <= 4
+    static_assert(DMA ? (4 * DT * 64 * 16 <= V_ELEMS * 2 && 4 * 64 * 16 <= K_ELEMS * 2)
+                      : 4 * (DT + 1) * 64 * 16 <= (K_ELEMS + V_ELEMS) * 2,
+                  "hand-off area");
+    f32x4* xl = reinterpret_cast<f32x4*>(DMA ? ldv0 : lds) + (size_t)wc * DT * 64 + lane;
+    f32x4* xm = reinterpret_cast<f32x4*>(lds) + (DMA ? 0 : 4 * DT * 64) + (size_t)wc * 64 + lane;
     __syncthreads();  // every LDS read of the last chunk done
     if (computing && kh == 1) {
 #pragma unroll
       for (int t = 0; t < DT; ++t) xl[t * 64] = acc[t];
-      xl[DT * 64] = f32x4{mx, l, 0.f, 0.f};
+      *xm = f32x4{mx, l, 0.f, 0.f};
     }
     __syncthreads();
     if (computing && kh == 0) {
-      const f32x4 ml1 = xl[DT * 64];
+      const f32x4 ml1 = *xm;
       const float M = fmaxf(mx, ml1[0]);  // finite: the first group's first half holds a valid key
       const float w0 = exp2f(mx - M), w1 = exp2f(ml1[0] - M);
       l = l * w0 + ml1[1] * w1;
@@ -492,6 +684,13 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
   *reinterpret_cast<u16x4*>(dst + act_plane(B * a.N, qd)) = lo;
 }
 
+template <int D, int NACC, int KS>
+void launch_ring(const AttnArgs* a, dim3 grid, dim3 block, hipStream_t st) {
+  if (a->cpi == 2) launch_kernel((attn_chunk_kernel<D, NACC, true, KS, 2>), grid, block, 0, st, *a);
+  else if (a->cpi == 4) launch_kernel((attn_chunk_kernel<D, NACC, true, KS, 4>), grid, block, 0, st, *a);
+  else launch_kernel((attn_chunk_kernel<D, NACC, true, KS, 8>), grid, block, 0, st, *a);
+}
+
 extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
   const int G = a->n_q / a->n_kv, n_wr = G * a->N / 16;
   const int waves = std::max(a->cand * n_wr, MIN_WAVES);
@@ -503,22 +702,28 @@ extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim,
   dim3 grid(items, a->n_kv, wgs_z);
   if (a->xcd_order) grid = dim3((a->xcd_tuples + 7) / 8 * 8 * a->xcd_items * a->grp);  // whole XCD rounds
   const dim3 block(64 * waves);
+  // multi-chunk items of 2, 4 or 8 chunks with 8 waves: the DMA ring
+  const bool dma = waves == 8 && (a->cpi == 2 || a->cpi == 4 || a->cpi == 8);
   if (head_dim == 128) {
     if (a->cpi > 1) {
-      if (ks2) launch_kernel((attn_chunk_kernel<128, 1, true, 2>), grid, block, 0, st, *a);
-      else launch_kernel((attn_chunk_kernel<128, 1, true, 1>), grid, block, 0, st, *a);
+      if (dma && ks2) launch_ring<128, 1, 2>(a, grid, block, st);
+      else if (dma) launch_ring<128, 1, 1>(a, grid, block, st);
+      else if (ks2) launch_kernel((attn_chunk_kernel<128, 1, true, 2, 0>), grid, block, 0, st, *a);
+      else launch_kernel((attn_chunk_kernel<128, 1, true, 1, 0>), grid, block, 0, st, *a);
     } else if (waves <= 8) {
-      launch_kernel((attn_chunk_kernel<128, 2, false, 1>), grid, block, 0, st, *a);
+      launch_kernel((attn_chunk_kernel<128, 2, false, 1, 0>), grid, block, 0, st, *a);
     } else {
-      launch_kernel((attn_chunk_kernel<128, 1, false, 1>), grid, block, 0, st, *a);
+      launch_kernel((attn_chunk_kernel<128, 1, false, 1, 0>), grid, block, 0, st, *a);
     }
   } else if (a->cpi > 1) {
-    if (ks2) launch_kernel((attn_chunk_kernel<64, 2, true, 2>), grid, block, 0, st, *a);
-    else launch_kernel((attn_chunk_kernel<64, 2, true, 1>), grid, block, 0, st, *a);
+    if (dma && ks2) launch_ring<64, 2, 2>(a, grid, block, st);
+    else if (dma) launch_ring<64, 1, 1>(a, grid, block, st);  // one S accumulator set: 128 VGPRs, two workgroups per CU
+    else if (ks2) launch_kernel((attn_chunk_kernel<64, 2, true, 2, 0>), grid, block, 0, st, *a);
+    else launch_kernel((attn_chunk_kernel<64, 2, true, 1, 0>), grid, block, 0, st, *a);
   } else if (waves <= 8) {
-    launch_kernel((attn_chunk_kernel<64, 2, false, 1>), grid, block, 0, st, *a);
+    launch_kernel((attn_chunk_kernel<64, 2, false, 1, 0>), grid, block, 0, st, *a);
   } else {
-    launch_kernel((attn_chunk_kernel<64, 1, false, 1>), grid, block, 0, st, *a);
+    launch_kernel((attn_chunk_kernel<64, 1, false, 1, 0>), grid, block, 0, st, *a);
   }
   return hipGetLastError();
 }

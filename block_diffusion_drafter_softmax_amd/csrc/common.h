@@ -66,6 +66,12 @@ DEV void split4(const f32x4& x, u16x4& hi, u16x4& lo) {
   lo = __builtin_bit_cast(u16x4, (uint32_t __attribute__((ext_vector_type(2)))){l0, l1});
 }
 
+// Direct-to-LDS load (global_load_lds, 16 bytes per lane): lane l's 16
+// bytes from src land at byte 16 l of the wave's LDS block dst (dst must be
+// wave-uniform). Counted by vmcnt like any load.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+DEV void dma16(const uint16_t* src, u32x4* dst) { __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 16, 0, 0); }
+
 // 16 bytes = 8 bf16 from global memory.
 DEV bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 

@@ -722,7 +722,8 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
     aa.cand = std::max(1, std::min(grp, kAttnMaxWaves / n_wr));
     const long long wgs_z = (long long)(B / grp) * ((grp + aa.cand - 1) / aa.cand);
     const long long chunks = wgs_z * c.n_kv_heads * L.n_ck;
-    aa.cpi = (int)std::min<long long>(8, std::max<long long>(1, (chunks + kAttnItems - 1) / kAttnItems));
+    const long long cpi = std::min<long long>(8, std::max<long long>(1, (chunks + kAttnItems - 1) / kAttnItems));
+    aa.cpi = cpi <= 2 ? (int)cpi : cpi <= 4 ? 4 : 8;  // 1, 2, 4 or 8: the attention's DMA ring is built for these
     aa.n_blocks = B;
     aa.xcd_order = aa.cand == 1;
     aa.xcd_items = 1 + (L.n_ck - 1 + aa.cpi - 1) / aa.cpi;

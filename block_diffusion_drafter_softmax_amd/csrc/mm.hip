@@ -62,10 +62,8 @@ struct MmSrc {
   int steps;  // k steps of the split
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // 16 bytes per lane from global memory straight into LDS (one 1 KB block per wave instruction).
-DEV void dma16(const uint16_t* src, u32x4* dst) { __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 16, 0, 0); }
 
 // Stage k step s into `stage` (kStageBlocks blocks of 1 KB): each wave
 // instruction writes one whole block, lane l at byte 16 l.

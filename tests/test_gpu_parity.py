@@ -186,16 +186,35 @@ def test_attention_multi_chunk_items():
     # GPT-OSS attention geometry (d_h 64, 8 kv heads, 128 query rows per kv
     # head) with a page pool (300 pages per sequence) whose chunk grid
     # (4 x 8 x 38 = 1216) is between 2 and 3 times the attention's target of
-    # 512 work items: every work item then takes 3 chunks of 128 virtual
-    # keys in a row (384 keys). Virtual key counts 1216 (the last item holds
-    # one partial chunk), 399 (ends 15 keys into an item's first chunk), 16
-    # (the block alone) and 2333 (7 items, the last with 29 keys).
+    # 512 work items: every work item then takes 4 chunks of 128 keys in a
+    # row (the count is rounded up to 1, 2, 4 or 8), 512 keys, through the
+    # direct-to-LDS ring when it has all 4, else staged through registers.
+    # Context lengths after the append: 1208 (items of 512, 512 and 184
+    # keys: two chunks), 388 (one item whose fourth chunk holds 4 keys),
+    # 0 (the block alone) and 2333 (5 items, the last with 285 keys).
     cfg = small_cfg(hidden=512, n_q_heads=64, n_kv_heads=8, head_dim=64, intermediate=512, vocab=2048,
                     block_size=16)
     ctx, n_new = [1200, 383, 0, 2317], [8, 5, 0, 16]
     pps_min = (max(ctx) + 16 + 15) // 16
     run_step(Case(cfg, ctx=ctx, n_new=n_new, seed=51, page_order="shuffled", prefill_chunk=256,
                   extra_pages=300 - pps_min))
+
+
+@pytest.mark.parametrize("head_dim,n_q", [(128, 32), (64, 64)])
+def test_attention_ring_eight_chunks(head_dim, n_q):
+    # A page pool of 2000 pages per sequence makes the chunk grid (2 x 8 x
+    # 251 = 4016) about 8 times the attention's 512 work items: items of 8
+    # chunks (1024 keys), so the direct-to-LDS ring runs its 8-chunk form
+    # (d_h 128: two key groups per item; d_h 64, GQA 8:1: one). Contexts
+    # after the append: 2508 (ring items of 1024 and 1024 keys, then 460
+    # keys in 4 chunks staged through registers) and 1000 (one ring item of
+    # 8 chunks whose last holds 104 keys: its invalid V slots are zeroed in
+    # LDS); the last page of each sequence is partly filled.
+    cfg = small_cfg(hidden=512, n_q_heads=n_q, n_kv_heads=8, head_dim=head_dim, intermediate=512, vocab=2048,
+                    block_size=16)
+    ctx, n_new = [2500, 1000], [8, 0]
+    run_step(Case(cfg, ctx=ctx, n_new=n_new, seed=58, page_order="shuffled", prefill_chunk=512,
+                  extra_pages=2000 - (max(ctx) + 16 + 15) // 16))
 
 
 def test_long_context_multi_chunk_head_dim_128():
