@@ -585,28 +585,34 @@ void attn_chunk_kernel(AttnArgs a) {
   }
 }
 
-// One workgroup per (sequence, kv head, query row): thread (cg, dq) merges
-// work items cg, cg + CG, ... for dims 4*dq .. 4*dq+3 (all its loads in one
-// batch of <= 8), then the CG partial merges are combined in cg order
-// through LDS; the result is normalised and written as the O projection's
-// packed split activation. Deterministic (fixed order).
-template <int D>
+// One workgroup per RW query rows of one (sequence, kv head): thread (row,
+// cg, dq) merges work items cg, cg + CG, ... of its row for dims 4*dq ..
+// 4*dq+3 (all its loads in one batch of <= 8), then the CG partial merges
+// of the row are combined in cg order through LDS; the result is
+// normalised and written as the O projection's packed split activation.
+// Deterministic (fixed order). CG is sized by the host to the items a row
+// can have (about four per thread), RW = 256 / (CG * D/4): rows with few
+// items (long items at large batches) share a workgroup instead of leaving
+// most of its item groups idle.
+template <int D, int CG>
 __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs a, int B) {
-  constexpr int TPR = D / 4, CG = 256 / TPR;
-  __shared__ float sm[CG], sd[CG];
-  __shared__ f32x4 sn[CG][TPR];
-  const int G = a.n_q / a.n_kv, R = G * a.N;
-  // The rows of one (block, kv head) are dealt to one XCD, the XCD whose
+  constexpr int TPR = D / 4, RW = 256 / (TPR * CG);
+  static_assert(RW >= 1 && RW * TPR * CG == 256, "whole rows per workgroup");
+  __shared__ float sm[RW][CG], sd[RW][CG];
+  __shared__ f32x4 sn[RW][CG][TPR];
+  const int G = a.n_q / a.n_kv, R = G * a.N, RB = R / RW;  // row groups per (block, kv head)
+  // The row groups of one (block, kv head) are dealt to one XCD, the XCD whose
   // attention workgroups wrote the head's partials when the attention grid
   // is XCD-ordered (tuple (block, head) -> XCD tuple % 8 there too, with one
   // block per sequence group): the partials are read from that XCD's L2.
   const int local = blockIdx.x >> 3;
-  const int T = (local / R) * 8 + (blockIdx.x & 7);  // b * n_kv + kvh
+  const int T = (local / RB) * 8 + (blockIdx.x & 7);  // b * n_kv + kvh
   if (T >= B * a.n_kv) return;
-  const int r = local % R;
+  const int rr = threadIdx.x / (TPR * CG);
+  const int r = (local % RB) * RW + rr;
   const int kvh = T % a.n_kv;
   const int b = T / a.n_kv;
-  const int dq = threadIdx.x % TPR, cg = threadIdx.x / TPR;
+  const int dq = threadIdx.x % TPR, cg = (threadIdx.x / TPR) % CG;
   const size_t unit0 = ((size_t)b * a.n_kv + kvh) * a.n_ck;
   constexpr int GRP = 8;  // loads in flight per thread (more costs time on gfx950)
   // One chunk per item (small batches): the first batch is requested before
@@ -661,17 +667,17 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs 
     }
   }
   if (dq == 0) {
-    sm[cg] = M;
-    sd[cg] = den;
+    sm[rr][cg] = M;
+    sd[rr][cg] = den;
   }
-  sn[cg][dq] = num;
+  sn[rr][cg][dq] = num;
   __syncthreads();
   if (cg != 0) return;
   for (int k = 1; k < CG && k < nc; ++k) {  // group k holds >= 1 chunk
-    const float Mn = fmaxf(M, sm[k]);
-    const float wo = exp2f(M - Mn), wn = exp2f(sm[k] - Mn);
-    den = den * wo + sd[k] * wn;
-    num = num * wo + sn[k][dq] * wn;
+    const float Mn = fmaxf(M, sm[rr][k]);
+    const float wo = exp2f(M - Mn), wn = exp2f(sm[rr][k] - Mn);
+    den = den * wo + sd[rr][k] * wn;
+    num = num * wo + sn[rr][k][dq] * wn;
     M = Mn;
   }
   const float inv = 1.0f / den;
@@ -730,8 +736,25 @@ extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim,
 
 extern "C" hipError_t dflash_launch_attn_merge(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
   const int G = a->n_q / a->n_kv, R = G * a->N;
-  const dim3 grid((B * a->n_kv + 7) / 8 * 8 * R), block(256);  // whole XCD rounds of (block, kv head) tuples
-  if (head_dim == 128) launch_kernel(attn_merge_kernel<128>, grid, block, 0, st, *a, B);
-  else launch_kernel(attn_merge_kernel<64>, grid, block, 0, st, *a, B);
+  // item groups per row: about four items per thread for the most a block
+  // can have, at most a whole workgroup per row; RW rows per workgroup
+  const int max_items = 1 + (a->n_ck - 1 + a->cpi - 1) / a->cpi;
+  const int tpr = head_dim / 4;
+  int cg = 1;
+  while (cg < 256 / tpr && cg * 4 < max_items) cg *= 2;
+  cg = std::max(cg, 2);
+  while (R % (256 / (tpr * cg))) cg *= 2;  // whole row groups per (block, head)
+  const int rw = 256 / (tpr * cg);
+  const dim3 grid((B * a->n_kv + 7) / 8 * 8 * (R / rw)), block(256);  // whole XCD rounds of (block, kv head) tuples
+  if (head_dim == 128) {
+    if (cg == 2) launch_kernel((attn_merge_kernel<128, 2>), grid, block, 0, st, *a, B);
+    else if (cg == 4) launch_kernel((attn_merge_kernel<128, 4>), grid, block, 0, st, *a, B);
+    else launch_kernel((attn_merge_kernel<128, 8>), grid, block, 0, st, *a, B);
+  } else {
+    if (cg == 2) launch_kernel((attn_merge_kernel<64, 2>), grid, block, 0, st, *a, B);
+    else if (cg == 4) launch_kernel((attn_merge_kernel<64, 4>), grid, block, 0, st, *a, B);
+    else if (cg == 8) launch_kernel((attn_merge_kernel<64, 8>), grid, block, 0, st, *a, B);
+    else launch_kernel((attn_merge_kernel<64, 16>), grid, block, 0, st, *a, B);
+  }
   return hipGetLastError();
 }
