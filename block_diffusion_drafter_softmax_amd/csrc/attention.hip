@@ -591,9 +591,9 @@ void attn_chunk_kernel(AttnArgs a) {
 // of the row are combined in cg order through LDS; the result is
 // normalised and written as the O projection's packed split activation.
 // Deterministic (fixed order). CG is sized by the host to the items a row
-// can have (about four per thread), RW = 256 / (CG * D/4): rows with few
-// items (long items at large batches) share a workgroup instead of leaving
-// most of its item groups idle.
+// can have (about eight per thread, one load batch), RW = 256 / (CG *
+// D/4): rows with few items (long items at large batches) share a
+// workgroup instead of leaving most of its item groups idle.
 template <int D, int CG>
 __global__ __launch_bounds__(256) LATENCY_BOUND void attn_merge_kernel(AttnArgs a, int B) {
   constexpr int TPR = D / 4, RW = 256 / (TPR * CG);
@@ -736,12 +736,13 @@ extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim,
 
 extern "C" hipError_t dflash_launch_attn_merge(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
   const int G = a->n_q / a->n_kv, R = G * a->N;
-  // item groups per row: about four items per thread for the most a block
-  // can have, at most a whole workgroup per row; RW rows per workgroup
+  // item groups per row: about eight items per thread (one load batch) for
+  // the most a block can have, at most a whole workgroup per row; RW rows
+  // per workgroup
   const int max_items = 1 + (a->n_ck - 1 + a->cpi - 1) / a->cpi;
   const int tpr = head_dim / 4;
   int cg = 1;
-  while (cg < 256 / tpr && cg * 4 < max_items) cg *= 2;
+  while (cg < 256 / tpr && cg * 8 < max_items) cg *= 2;
   cg = std::max(cg, 2);
   while (R % (256 / (tpr * cg))) cg *= 2;  // whole row groups per (block, head)
   const int rw = 256 / (tpr * cg);
