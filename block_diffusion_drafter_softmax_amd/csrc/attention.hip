@@ -33,7 +33,11 @@
 // consecutive chunks, taken one after the other by the
 // same workgroup (stage, compute, stage, ...) with the running max, sum and
 // O rescaled per half chunk as in any online softmax, and one partial per
-// item goes to the merge: cpi times fewer partial bytes.
+// item goes to the merge: cpi times fewer partial bytes. With 8-wave
+// workgroups and cpi = 2, 4 or 8 every context item streams its chunks
+// through a direct-to-LDS ring of two stages (ring_item), and at d_h 128
+// with two key groups one persistent workgroup per CU slot takes item after
+// item from a per-XCD list, longest first (attn_persist_kernel).
 //
 // Blocks that share a sequence (the dual-pass drafter's candidates: grp
 // consecutive blocks) share its context: a workgroup takes `cand` of them
@@ -362,6 +366,52 @@ DEV void zero_invalid_v(uint16_t* vb, const int* ccnt, int tid) {
   }
 }
 
+// One context item of NR chunks through the DMA ring of two LDS stages
+// (k0, v0) and (k1, v1): chunks 0 and 1 requested at once; then per chunk,
+// wait for its own loads (the next chunk's stay in flight), compute it, and
+// request the chunk after next into the stage it leaves. Fully unrolled
+// with every load request and wait fixed at compile time: only then does
+// the compiler let the reads of one stage run while the other stage's loads
+// are in flight (a request or a wait under a run-time condition makes it
+// wait for all of them before every read). Waits are explicit vmcnt counts
+// and bare barriers (the compiler's __syncthreads would also wait for the
+// loads in flight). The caller has written the page slots and synchronised.
+template <int D, int NACC, int KS, int NR>
+DEV void ring_item(uint16_t* k0, uint16_t* v0, uint16_t* k1, uint16_t* v1, const long long* poff, const int* cnt,
+                   int item_nv, bool computing, int wave, int lane, int tid, int kh, int r16, int g,
+                   const uint16_t* blk_k, const uint16_t* blk_v, const uint16_t* pages, int n_kv,
+                   const bf16x8 (&qh)[D / 32], const bf16x8 (&ql)[D / 32], f32x4 (&acc)[D / 16], float& mx,
+                   float& l) {
+  constexpr int LPC = 2 * CH * D / 8 / 64 / 8;  // DMA loads per thread and chunk
+  stage_dma<D>(k0, v0, poff, wave, lane, blk_k, blk_v, pages, n_kv);
+  if constexpr (NR > 1) stage_dma<D>(k1, v1, poff + PAGES, wave, lane, blk_k, blk_v, pages, n_kv);
+#pragma unroll
+  for (int ci = 0; ci < NR; ++ci) {
+    uint16_t* kst = (ci & 1) ? k1 : k0;
+    uint16_t* vst = (ci & 1) ? v1 : v0;
+    if (ci + 1 < NR) __builtin_amdgcn_s_waitcnt(0x0F70 | LPC);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_barrier();  // chunk ci landed for every wave
+    const int nv = min(item_nv - ci * CH, CH);
+    if (nv < CH) {  // the context's last chunk: V of its invalid slots to 0
+      zero_invalid_v<D>(vst, cnt + ci * PAGES, tid);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+    }
+    if (computing)
+      chunk_compute<D, NACC, true, KS, D, true>(kst, vst, cnt + ci * PAGES, false, nv, kh, r16, g, qh, ql, acc, mx, l);
+    __builtin_amdgcn_s_barrier();  // every wave is done with this stage
+    if (ci + 2 < NR) stage_dma<D>(kst, vst, poff + (ci + 2) * PAGES, wave, lane, blk_k, blk_v, pages, n_kv);
+  }
+}
+
+// One work item of one kv head: item 0 = the block's own keys for block b0
+// (n_cand = 1), item i >= 1 = context chunks from cpi * CH * (i - 1) for
+// blocks b0 .. b0 + n_cand - 1; stages the keys into the workgroup's LDS
+// arrays, computes every query row's (max, sum, O) over them and writes
+// them as the item's partials. Called by the whole workgroup (every
+// thread; the non-computing waves return at the end).
+//
 // NACC: accumulator sets for the S products (2: hi and lo separately, more
 // independent MFMA chains; 1 where 1024-thread workgroups cap the registers).
 // MULTI: work items of up to CPI_MAX chunks.
@@ -376,6 +426,164 @@ DEV void zero_invalid_v(uint16_t* vb, const int* ccnt, int tid) {
 // The ring's workgroup is 8 waves and LDS holds it to one per CU at d_h 128,
 // so it may take 256 VGPRs there (a spill reload would be counted with the
 // loads in flight and wait for them all); two per CU at d_h 64, 128 VGPRs.
+template <int D, int NACC, bool MULTI, int KS, int RING>
+DEV void attn_item(const AttnArgs& a, int b0, int kvh, int item, int n_cand, uint16_t* lds, uint16_t* ldv0,
+                   uint16_t* ldk1, uint16_t* ldv1, long long* poff, int* cnt) {
+  constexpr bool DMA = RING > 0;
+  constexpr int KP = DMA ? D : D + 8;  // LDS row of one key (bf16 elements): padded, or swizzled
+  constexpr int K_ELEMS = CH * KP, V_ELEMS = PAGES * D * 16;
+  const bool blk_item = item == 0;
+  const int cpi = MULTI ? a.cpi : 1;
+  // the thread index as an opaque value: in the persistent kernel's item loop
+  // the compiler would otherwise keep every per-lane offset derived from it
+  // (staging and fragment addresses) live across the loop, and spill
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int nthreads = blockDim.x;
+  // page-table entry of page slot tid (< SLOTS <= nthreads), requested with
+  // the plan from the call's per-block copy; clamped, used only if valid
+  int raw_slot = 0;
+  if (!blk_item && tid < cpi * PAGES)
+    raw_slot = a.blk_pages[(size_t)b0 * a.max_pages_per_seq +
+                           clampi((item - 1) * cpi * PAGES + tid, 0, a.max_pages_per_seq - 1)];
+  const int2 pl = *reinterpret_cast<const int2*>(a.plan + 2 * b0);  // (sequence, context length)
+  const int seq = clampi(pl.x, 0, a.max_seqs - 1);
+  const int L = clampi(pl.y, 0, a.max_pages_per_seq * 16);
+  const int c_begin = (item - 1) * cpi * CH;  // context items: first key
+  const int item_nv = blk_item ? a.N : min(L, c_begin + cpi * CH) - c_begin;  // keys in this item
+  if (item_nv <= 0) return;
+  const int n_chunks = MULTI && !blk_item ? (item_nv + CH - 1) / CH : 1;
+  const size_t page_elems = (size_t)2 * a.n_kv * 16 * D;
+
+  // Page slots of the item (the block item's slot 0 is the block; slots
+  // past the keys point at the block, valid memory, and hold 0 valid keys).
+  const uint16_t* blk_k = a.kblk + ((size_t)b0 * a.n_kv + kvh) * 16 * D;
+  const uint16_t* blk_v = a.vblk + ((size_t)b0 * a.n_kv + kvh) * D * 16;
+  if (tid < n_chunks * PAGES) {  // n_chunks * PAGES <= SLOTS <= nthreads: one slot per thread
+    const int t = tid;
+    long long off = -1;
+    int n_ok = 0;
+    if (blk_item) {
+      n_ok = t == 0 ? a.N : 0;
+    } else if (16 * t < item_nv) {
+      const int raw = raw_slot;
+      if (raw < 0 || raw >= a.n_pages) set_error(a.err, DFLASH_DEV_BAD_PAGE);
+      off = (long long)clampi(raw, 0, a.n_pages - 1) * page_elems + (long long)kvh * 16 * D;
+      n_ok = min(16, item_nv - 16 * t);
+    }
+    poff[t] = off;
+    cnt[t] = n_ok;
+  }
+
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  // the divisors as opaque scalars: a division's reciprocal would otherwise
+  // be computed once before the persistent kernel's item loop and held in
+  // vector registers across it
+  int n_q = a.n_q, n_kv = a.n_kv, N = a.N;
+  asm volatile("" : "+s"(n_q), "+s"(n_kv), "+s"(N));
+  const int G = n_q / n_kv, R = G * N, n_wr = R / 16;
+  const int n_comp = n_cand * n_wr;  // computing waves per key group
+  const bool computing = wave < KS * n_comp;
+  const int kh = KS == 2 && wave >= n_comp ? 1 : 0;  // the wave's key group (wave-uniform)
+  // staging: thread t moves unit t % (4D) of its page slots, K units first
+  const bool isk_wave = __builtin_amdgcn_readfirstlane((int)(tid % (4 * D) < 2 * D));
+  const int wc = min(wave - kh * n_comp, n_comp - 1);
+  const int cand = wc / n_wr, b = b0 + cand;  // the wave's block
+  const int r = (wc % n_wr) * 16 + r16;
+  const int hq = kvh * G + r / N, n = r % N;
+  constexpr int KD = D / 32, DT = D / 16;
+
+  // queries (softmax scale already applied): in flight with the page reads
+  bf16x8 qh[KD], ql[KD];
+  {
+    const uint16_t* qp = a.q + ((size_t)(b * a.N + n) * a.n_q + hq) * D + 8 * g;
+    const size_t q_lo = (size_t)a.n_blocks * a.N * a.n_q * D;
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) {
+      qh[kd] = ld8(qp + kd * 32);
+      ql[kd] = ld8(qp + q_lo + kd * 32);
+    }
+  }
+
+  f32x4 acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mx = -INFINITY, l = 0.f;
+  if (!DMA || blk_item) {
+    // stage a chunk through registers, then compute it (the block item: its
+    // keys and one masked page, two key tiles)
+    uint16_t* kst = lds;
+    uint16_t* vst = DMA ? ldv0 : lds + K_ELEMS;
+    for (int ci = 0; ci < n_chunks; ++ci) {
+      const int nv = min(item_nv - ci * CH, CH);  // keys in this chunk
+      __syncthreads();  // page slots written; the previous chunk's LDS reads done
+      stage_regs<D, MULTI, KP, DMA>(kst, vst, poff + ci * PAGES, cnt + ci * PAGES, blk_item, isk_wave, tid, nthreads,
+                                    blk_k, blk_v, a.pages, a.n_kv);
+      __syncthreads();
+      if (computing)
+        chunk_compute<D, NACC, MULTI, KS, KP, DMA>(kst, vst, cnt + ci * PAGES, blk_item, nv, kh, r16, g, qh, ql, acc,
+                                                   mx, l);
+    }
+  } else if constexpr (DMA) {
+    // a context item: the ring, unrolled for its chunk count (1 .. RING; a
+    // sequence's last item may have fewer chunks than the others)
+    __syncthreads();  // page slots written
+#define RING_CASE(NR)                                                                                      \
+  case NR:                                                                                                 \
+    if constexpr (NR <= RING)                                                                              \
+      ring_item<D, NACC, KS, NR>(lds, ldv0, ldk1, ldv1, poff, cnt, item_nv, computing, wave, lane, tid, kh, \
+                                 r16, g, blk_k, blk_v, a.pages, a.n_kv, qh, ql, acc, mx, l);               \
+    break;
+    switch (n_chunks) {
+      RING_CASE(1)
+      RING_CASE(2)
+      RING_CASE(3)
+      RING_CASE(4)
+      RING_CASE(5)
+      RING_CASE(6)
+      RING_CASE(7)
+      RING_CASE(8)
+      default: break;
+    }
+#undef RING_CASE
+  }
+  if (KS == 2) {  // the second key group's (max, sum, O) to its partner, lane by lane
+    // O parts [wave][t][lane] and (max, sum) [wave][lane]; wc < n_comp <= 4
+    static_assert(DMA ? (4 * DT * 64 * 16 <= V_ELEMS * 2 && 4 * 64 * 16 <= K_ELEMS * 2)
+                      : 4 * (DT + 1) * 64 * 16 <= (K_ELEMS + V_ELEMS) * 2,
+                  "hand-off area");
+    f32x4* xl = reinterpret_cast<f32x4*>(DMA ? ldv0 : lds) + (size_t)wc * DT * 64 + lane;
+    f32x4* xm = reinterpret_cast<f32x4*>(lds) + (DMA ? 0 : 4 * DT * 64) + (size_t)wc * 64 + lane;
+    __syncthreads();  // every LDS read of the last chunk done
+    if (computing && kh == 1) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) xl[t * 64] = acc[t];
+      *xm = f32x4{mx, l, 0.f, 0.f};
+    }
+    __syncthreads();
+    if (computing && kh == 0) {
+      const f32x4 ml1 = *xm;
+      const float M = fmaxf(mx, ml1[0]);  // finite: the first group's first half holds a valid key
+      const float w0 = exp2f(mx - M), w1 = exp2f(ml1[0] - M);
+      l = l * w0 + ml1[1] * w1;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) acc[t] = acc[t] * w0 + xl[t * 64] * w1;
+      mx = M;
+    }
+  }
+  if (!computing || kh == 1) return;
+
+  const size_t unit = ((size_t)b * a.n_kv + kvh) * a.n_ck + item;
+  float* po = a.part_o + (unit * R + r) * D;
+#pragma unroll
+  for (int t = 0; t < DT; ++t) *reinterpret_cast<f32x4*>(po + t * 16 + 4 * g) = acc[t];
+  if (g == 0) {
+    a.part_ml[(unit * R + r) * 2 + 0] = mx;
+    a.part_ml[(unit * R + r) * 2 + 1] = l;
+  }
+}
+
 template <int D, int NACC, bool MULTI, int KS, int RING>
 __global__ __launch_bounds__(RING ? 512 : 1024)
 __attribute__((amdgpu_waves_per_eu(RING && D == 128 ? 1 : 4, RING && D == 128 ? 2 : 4)))
@@ -431,157 +639,128 @@ void attn_chunk_kernel(AttnArgs a) {
     item = bx - a.cand + 1;
   }
   const int b0 = bz / splits * a.grp + c0;   // the workgroup's first block
-  const bool blk_item = item == 0;
-  const int cpi = MULTI ? a.cpi : 1;
-  const int tid = threadIdx.x, nthreads = blockDim.x;
-  // page-table entry of page slot tid (< SLOTS <= nthreads), requested with
-  // the plan from the call's per-block copy; clamped, used only if valid
-  int raw_slot = 0;
-  if (!blk_item && tid < cpi * PAGES)
-    raw_slot = a.blk_pages[(size_t)b0 * a.max_pages_per_seq +
-                           clampi((item - 1) * cpi * PAGES + tid, 0, a.max_pages_per_seq - 1)];
-  const int2 pl = *reinterpret_cast<const int2*>(a.plan + 2 * b0);  // (sequence, context length)
-  const int seq = clampi(pl.x, 0, a.max_seqs - 1);
-  const int L = clampi(pl.y, 0, a.max_pages_per_seq * 16);
-  const int c_begin = (item - 1) * cpi * CH;  // context items: first key
-  const int item_nv = blk_item ? a.N : min(L, c_begin + cpi * CH) - c_begin;  // keys in this item
-  if (item_nv <= 0) return;
-  const int n_chunks = MULTI && !blk_item ? (item_nv + CH - 1) / CH : 1;
-  const size_t page_elems = (size_t)2 * a.n_kv * 16 * D;
+  attn_item<D, NACC, MULTI, KS, RING>(a, b0, kvh, item, n_cand, lds, ldv0, ldk1, ldv1, poff, cnt);
+}
 
-  // Page slots of the item (the block item's slot 0 is the block; slots
-  // past the keys point at the block, valid memory, and hold 0 valid keys).
-  const uint16_t* blk_k = a.kblk + ((size_t)b0 * a.n_kv + kvh) * 16 * D;
-  const uint16_t* blk_v = a.vblk + ((size_t)b0 * a.n_kv + kvh) * D * 16;
-  if (tid < n_chunks * PAGES) {  // n_chunks * PAGES <= SLOTS <= nthreads: one slot per thread
-    const int t = tid;
-    long long off = -1;
-    int n_ok = 0;
-    if (blk_item) {
-      n_ok = t == 0 ? a.N : 0;
-    } else if (16 * t < item_nv) {
-      const int raw = raw_slot;
-      if (raw < 0 || raw >= a.n_pages) set_error(a.err, DFLASH_DEV_BAD_PAGE);
-      off = (long long)clampi(raw, 0, a.n_pages - 1) * page_elems + (long long)kvh * 16 * D;
-      n_ok = min(16, item_nv - 16 * t);
+// The work list of one XCD for the persistent ring kernel: its tuples are
+// (sequence group, kv head) T = 8j + x, j < J <= 64. Longest first: every
+// full item (cpi chunks) of every tuple, tuple by tuple; then each tuple's
+// last, partial item, the most chunks first; then the block items. A
+// position is pos = u * grp + candidate.
+struct AttnList {
+  int F, Tt, J;
+};
+
+// The job at list position pos: (first block, kv head, item), or b0 = -1
+// past the end. s_pref[j]: full items of the tuples before j; s_f[j]: full
+// items of tuple j; s_tail[k]: tuple of the k-th partial item.
+DEV int3 attn_job(const AttnArgs& a, const AttnList& w, int pos, int x, const int* s_pref, const int* s_f,
+                  const int* s_tail) {
+  int grp = a.grp, n_kv = a.n_kv;  // opaque: no reciprocal held across the item loop
+  asm volatile("" : "+s"(grp), "+s"(n_kv));
+  const int u = pos / grp, gi = pos % grp;
+  int j, item;
+  if (pos < 0) {
+    return int3{-1, 0, 0};
+  } else if (u < w.F) {  // the last tuple whose full items start at or before u
+    int lo = 0, hi = w.J - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] <= u) lo = mid;
+      else hi = mid - 1;
     }
-    poff[t] = off;
-    cnt[t] = n_ok;
+    j = lo;
+    item = 1 + u - s_pref[j];
+  } else if (u < w.F + w.Tt) {
+    j = s_tail[u - w.F];
+    item = 1 + s_f[j];
+  } else if (u < w.F + w.Tt + w.J) {
+    j = u - w.F - w.Tt;
+    item = 0;
+  } else {
+    return int3{-1, 0, 0};
   }
+  const int T = 8 * j + x;
+  return int3{T / n_kv * grp + gi, T % n_kv, item};
+}
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int G = a.n_q / a.n_kv, R = G * a.N, n_wr = R / 16;
-  const int n_comp = n_cand * n_wr;  // computing waves per key group
-  const bool computing = wave < KS * n_comp;
-  const int kh = KS == 2 && wave >= n_comp ? 1 : 0;  // the wave's key group (wave-uniform)
-  // staging: thread t moves unit t % (4D) of its page slots, K units first
-  const bool isk_wave = __builtin_amdgcn_readfirstlane((int)(tid % (4 * D) < 2 * D));
-  const int wc = min(wave - kh * n_comp, n_comp - 1);
-  const int cand = wc / n_wr, b = b0 + cand;  // the wave's block
-  const int r = (wc % n_wr) * 16 + r16;
-  const int hq = kvh * G + r / a.N, n = r % a.N;
-  constexpr int KD = D / 32, DT = D / 16;
-
-  // queries (softmax scale already applied): in flight with the page reads
-  bf16x8 qh[KD], ql[KD];
-  {
-    const uint16_t* qp = a.q + ((size_t)(b * a.N + n) * a.n_q + hq) * D + 8 * g;
-    const size_t q_lo = (size_t)a.n_blocks * a.N * a.n_q * D;
-#pragma unroll
-    for (int kd = 0; kd < KD; ++kd) {
-      qh[kd] = ld8(qp + kd * 32);
-      ql[kd] = ld8(qp + q_lo + kd * 32);
+// The DMA ring as a persistent kernel (one block per work item, cand == 1):
+// gridDim.x = 8 * P workgroups, all resident at once; workgroup i serves
+// XCD x = i % 8 (the hardware deals workgroups to the XCDs round robin)
+// and takes the items of x's work list: position i / 8 first, then the
+// position a per-XCD counter hands out (P + its count), until the list
+// ends. Versus one workgroup per item slot: no workgroups for the slots
+// that a short sequence leaves empty, no workgroup launch per item, and the
+// longest items first so that the last ones to finish are short. The
+// counters (attn_ctr[8]) are zeroed by the kernel before the attention in
+// the stream (the Q/K/V finisher). Which workgroup computes an item does
+// not change its partials: the results are the same in any order.
+template <int D, int NACC, int KS, int RING>
+__global__ __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 4, D == 128 ? 2 : 4)))
+void attn_persist_kernel(AttnArgs a) {
+  static_assert(RING >= 2 && RING <= CPI_MAX, "the DMA ring takes multi-chunk items");
+  constexpr int K_ELEMS = CH * D, V_ELEMS = PAGES * D * 16, SLOTS = CPI_MAX * PAGES;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t ldv0[V_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t ldk1[K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t ldv1[V_ELEMS];
+  __shared__ long long poff[SLOTS];
+  __shared__ int cnt[SLOTS];
+  __shared__ int s_pref[64], s_f[64], s_tail[64];
+  __shared__ int s_list[3];
+  __shared__ int3 s_job[2];
+  const int x = blockIdx.x & 7, P = gridDim.x >> 3, tid = threadIdx.x;
+  if (tid < 64) {  // the list, in wave 0: lane t = tuple t of this XCD
+    const int t = tid, J = min(64, (a.xcd_tuples - x + 7) / 8);
+    const int ik = a.cpi * CH;  // keys per full item
+    int f = 0, tc = 0;
+    if (t < J) {
+      const int T = 8 * t + x, b = T / a.n_kv * a.grp;
+      const int L = clampi(a.plan[2 * b + 1], 0, a.max_pages_per_seq * 16);
+      f = L / ik;
+      tc = (L % ik + CH - 1) / CH;  // chunks of the partial item (0: none)
     }
-  }
-
-  f32x4 acc[DT];
+    int incl = f;  // inclusive prefix over the lanes
 #pragma unroll
-  for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mx = -INFINITY, l = 0.f;
-  if (!DMA || n_chunks != RING) {
-    // stage a chunk through registers, then compute it (the block item: its
-    // keys and one masked page, two key tiles; with the ring, also a
-    // sequence's last item when it has fewer chunks than the ring)
-    uint16_t* kst = lds;
-    uint16_t* vst = DMA ? ldv0 : lds + K_ELEMS;
-    for (int ci = 0; ci < n_chunks; ++ci) {
-      const int nv = min(item_nv - ci * CH, CH);  // keys in this chunk
-      __syncthreads();  // page slots written; the previous chunk's LDS reads done
-      stage_regs<D, MULTI, KP, DMA>(kst, vst, poff + ci * PAGES, cnt + ci * PAGES, blk_item, isk_wave, tid, nthreads,
-                                    blk_k, blk_v, a.pages, a.n_kv);
-      __syncthreads();
-      if (computing)
-        chunk_compute<D, NACC, MULTI, KS, KP, DMA>(kst, vst, cnt + ci * PAGES, blk_item, nv, kh, r16, g, qh, ql, acc,
-                                                   mx, l);
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (t >= d) incl += v;
     }
-  } else if constexpr (DMA) {
-    // The ring, for items of exactly RING chunks: chunks 0 and 1 requested
-    // at once; then per chunk, wait for its own loads (the next chunk's stay
-    // in flight), compute it, and request the chunk after next into the
-    // stage it leaves. Fully unrolled with every load request and wait fixed
-    // at compile time: only then does the compiler let the reads of one
-    // stage run while the other stage's loads are in flight (a request or a
-    // wait under a run-time condition makes it wait for all of them before
-    // every read). Waits are explicit vmcnt counts and bare barriers (the
-    // compiler's __syncthreads would also wait for the loads in flight).
-    constexpr int LPC = 2 * CH * D / 8 / 64 / 8;  // DMA loads per thread and chunk
-    __syncthreads();                              // page slots written
-    stage_dma<D>(lds, ldv0, poff, wave, lane, blk_k, blk_v, a.pages, a.n_kv);
-    stage_dma<D>(ldk1, ldv1, poff + PAGES, wave, lane, blk_k, blk_v, a.pages, a.n_kv);
+    int rank = 0, n_tail = 0;  // partial items: the most chunks first, then by tuple
 #pragma unroll
-    for (int ci = 0; ci < RING; ++ci) {
-      uint16_t* kst = (ci & 1) ? ldk1 : lds;
-      uint16_t* vst = (ci & 1) ? ldv1 : ldv0;
-      if (ci + 1 < RING) __builtin_amdgcn_s_waitcnt(0x0F70 | LPC);
-      else __builtin_amdgcn_s_waitcnt(0x0F70);
-      __builtin_amdgcn_s_barrier();  // chunk ci landed for every wave
-      const int nv = min(item_nv - ci * CH, CH);
-      if (nv < CH) {  // the context's last chunk: V of its invalid slots to 0
-        zero_invalid_v<D>(vst, cnt + ci * PAGES, tid);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-      }
-      if (computing)
-        chunk_compute<D, NACC, true, KS, KP, true>(kst, vst, cnt + ci * PAGES, false, nv, kh, r16, g, qh, ql, acc, mx,
-                                                   l);
-      __builtin_amdgcn_s_barrier();  // every wave is done with this stage
-      if (ci + 2 < RING) stage_dma<D>(kst, vst, poff + (ci + 2) * PAGES, wave, lane, blk_k, blk_v, a.pages, a.n_kv);
+    for (int c = CPI_MAX; c >= 1; --c) {
+      const unsigned long long m = __ballot(tc == c);
+      if (tc == c) rank = n_tail + __popcll(m & ((1ull << t) - 1));
+      n_tail += __popcll(m);
+    }
+    if (t < J) {
+      s_pref[t] = incl - f;
+      s_f[t] = f;
+    }
+    if (tc > 0) s_tail[rank] = t;
+    if (t == 63) {
+      s_list[0] = incl;
+      s_list[1] = n_tail;
+      s_list[2] = J;
     }
   }
-  if (KS == 2) {  // the second key group's (max, sum, O) to its partner, lane by lane
-    // O parts [wave][t][lane] and (max, sum) [wave][lane]; wc < n_comp <= 4
-    static_assert(DMA ? (4 * DT * 64 * 16 <= V_ELEMS * 2 && 4 * 64 * 16 <= K_ELEMS * 2)
-                      : 4 * (DT + 1) * 64 * 16 <= (K_ELEMS + V_ELEMS) * 2,
-                  "hand-off area");
-    f32x4* xl = reinterpret_cast<f32x4*>(DMA ? ldv0 : lds) + (size_t)wc * DT * 64 + lane;
-    f32x4* xm = reinterpret_cast<f32x4*>(lds) + (DMA ? 0 : 4 * DT * 64) + (size_t)wc * 64 + lane;
-    __syncthreads();  // every LDS read of the last chunk done
-    if (computing && kh == 1) {
-#pragma unroll
-      for (int t = 0; t < DT; ++t) xl[t * 64] = acc[t];
-      *xm = f32x4{mx, l, 0.f, 0.f};
-    }
-    __syncthreads();
-    if (computing && kh == 0) {
-      const f32x4 ml1 = *xm;
-      const float M = fmaxf(mx, ml1[0]);  // finite: the first group's first half holds a valid key
-      const float w0 = exp2f(mx - M), w1 = exp2f(ml1[0] - M);
-      l = l * w0 + ml1[1] * w1;
-#pragma unroll
-      for (int t = 0; t < DT; ++t) acc[t] = acc[t] * w0 + xl[t * 64] * w1;
-      mx = M;
-    }
-  }
-  if (!computing || kh == 1) return;
-
-  const size_t unit = ((size_t)b * a.n_kv + kvh) * a.n_ck + item;
-  float* po = a.part_o + (unit * R + r) * D;
-#pragma unroll
-  for (int t = 0; t < DT; ++t) *reinterpret_cast<f32x4*>(po + t * 16 + 4 * g) = acc[t];
-  if (g == 0) {
-    a.part_ml[(unit * R + r) * 2 + 0] = mx;
-    a.part_ml[(unit * R + r) * 2 + 1] = l;
+  __syncthreads();
+  const AttnList w{s_list[0], s_list[1], s_list[2]};
+  if (tid == 0) s_job[0] = attn_job(a, w, blockIdx.x >> 3, x, s_pref, s_f, s_tail);
+  __syncthreads();
+  for (int it = 0;; ++it) {
+    // the job is the same for every thread: wave-uniform values (scalar
+    // registers, uniform branches) for everything derived from it
+    const int3 job = s_job[it & 1];
+    const int b0 = __builtin_amdgcn_readfirstlane(job.x);
+    if (b0 < 0) break;
+    const int kvh = __builtin_amdgcn_readfirstlane(job.y), item = __builtin_amdgcn_readfirstlane(job.z);
+    int nxt = 0;
+    if (tid == 0) nxt = P + atomicAdd(a.attn_ctr + x, 1);
+    attn_item<D, NACC, true, KS, RING>(a, b0, kvh, item, 1, lds, ldv0, ldk1, ldv1, poff, cnt);
+    if (tid == 0) s_job[(it + 1) & 1] = attn_job(a, w, nxt, x, s_pref, s_f, s_tail);
+    __syncthreads();  // the item's LDS reads done; the next job visible
   }
 }
 
@@ -697,6 +876,36 @@ void launch_ring(const AttnArgs* a, dim3 grid, dim3 block, hipStream_t st) {
   else launch_kernel((attn_chunk_kernel<D, NACC, true, KS, 8>), grid, block, 0, st, *a);
 }
 
+// Workgroups of the persistent ring kernel: every CU's resident count, whole
+// XCD rounds (0 if the device cannot be queried: the item-slot grid then).
+template <int D, int NACC, int KS, int RING>
+int persist_wgs() {
+  static const int n = [] {
+    int dev = 0, cus = 0, occ = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attn_persist_kernel<D, NACC, KS, RING>, 512, 0) !=
+            hipSuccess)
+      return 0;
+    return cus >= 8 && occ >= 1 ? cus / 8 * 8 * occ : 0;
+  }();
+  return n;
+}
+
+template <int D, int NACC, int KS>
+bool launch_persist(const AttnArgs* a, hipStream_t st) {
+  int n = 0;
+  if (a->cpi == 2) n = persist_wgs<D, NACC, KS, 2>();
+  else if (a->cpi == 4) n = persist_wgs<D, NACC, KS, 4>();
+  else n = persist_wgs<D, NACC, KS, 8>();
+  if (n <= 0) return false;
+  const dim3 grid(n), block(512);
+  if (a->cpi == 2) launch_kernel((attn_persist_kernel<D, NACC, KS, 2>), grid, block, 0, st, *a);
+  else if (a->cpi == 4) launch_kernel((attn_persist_kernel<D, NACC, KS, 4>), grid, block, 0, st, *a);
+  else launch_kernel((attn_persist_kernel<D, NACC, KS, 8>), grid, block, 0, st, *a);
+  return true;
+}
+
 extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim, hipStream_t st) {
   const int G = a->n_q / a->n_kv, n_wr = G * a->N / 16;
   const int waves = std::max(a->cand * n_wr, MIN_WAVES);
@@ -708,8 +917,14 @@ extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim,
   dim3 grid(items, a->n_kv, wgs_z);
   if (a->xcd_order) grid = dim3((a->xcd_tuples + 7) / 8 * 8 * a->xcd_items * a->grp);  // whole XCD rounds
   const dim3 block(64 * waves);
-  // multi-chunk items of 2, 4 or 8 chunks with 8 waves: the DMA ring
+  // multi-chunk items of 2, 4 or 8 chunks with 8 waves: the DMA ring; as a
+  // persistent kernel where one block per workgroup lets it take the XCD
+  // work lists (at most 64 tuples per XCD), at d_h 128 with two key groups
+  // (the variant whose item loop fits the registers)
   const bool dma = waves == 8 && (a->cpi == 2 || a->cpi == 4 || a->cpi == 8);
+  if (dma && ks2 && head_dim == 128 && a->xcd_order && a->attn_ctr && (a->xcd_tuples + 7) / 8 <= 64 &&
+      launch_persist<128, 1, 2>(a, st))
+    return hipGetLastError();
   if (head_dim == 128) {
     if (a->cpi > 1) {
       if (dma && ks2) launch_ring<128, 1, 2>(a, grid, block, st);
@@ -722,7 +937,7 @@ extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim,
       launch_kernel((attn_chunk_kernel<128, 1, false, 1, 0>), grid, block, 0, st, *a);
     }
   } else if (a->cpi > 1) {
-    if (dma && ks2) launch_ring<64, 2, 2>(a, grid, block, st);
+    if (dma && ks2) launch_ring<64, 1, 2>(a, grid, block, st);  // one S accumulator set: no spills
     else if (dma) launch_ring<64, 1, 1>(a, grid, block, st);  // one S accumulator set: 128 VGPRs, two workgroups per CU
     else if (ks2) launch_kernel((attn_chunk_kernel<64, 2, true, 2, 0>), grid, block, 0, st, *a);
     else launch_kernel((attn_chunk_kernel<64, 2, true, 1, 0>), grid, block, 0, st, *a);

@@ -88,7 +88,7 @@ struct Layout {
   // and each block's page-table row, read by the attention with the plan
   size_t blk_pages;
   // compacted LM-head rows of a dual-pass second pass: block row of each, count
-  size_t lm_inv, lm_count;
+  size_t lm_inv, lm_count, attn_ctr;
   size_t gpart_floats, cpart_floats;
   int n_ck, n_vchunks, n_schunks, m_max, rows_a_max;
 };
@@ -166,6 +166,7 @@ Layout make_layout(const dflash_config& c) {
   L.blk_pages = take((size_t)Bm * c.max_pages_per_seq * 4);
   L.lm_inv = take(Bm * N * 4);
   L.lm_count = take(4);
+  L.attn_ctr = take(8 * 4);
   L.total = off;
   return L;
 }
@@ -696,6 +697,7 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
   qa.q = ctx->at<uint16_t>(L.q);
   qa.kblk = ctx->at<uint16_t>(L.kblk);
   qa.vblk = ctx->at<uint16_t>(L.vblk);
+  qa.attn_ctr = ctx->at<int>(L.attn_ctr);
 
   AttnArgs aa{};
   aa.q = qa.q;
@@ -728,6 +730,7 @@ int draft_impl(dflash_ctx* ctx, int32_t B, const int32_t* seq_ids, const int32_t
     aa.xcd_order = aa.cand == 1;
     aa.xcd_items = 1 + (L.n_ck - 1 + aa.cpi - 1) / aa.cpi;
     aa.xcd_tuples = (B / grp) * c.n_kv_heads;
+    aa.attn_ctr = ctx->at<int>(L.attn_ctr);
   }
   aa.max_pages_per_seq = c.max_pages_per_seq;
   aa.n_pages = c.n_pages;

@@ -27,6 +27,7 @@ DEV void rotate(float& x1, float& x2, const float* rope, int pos, int half, int 
 // One thread per (row, rotation pair of a query or block-key head) or per
 // (row, block-value element).
 DEV void qkv_finish_body(const QkvFinishArgs& a, int idx) {
+  if (a.attn_ctr && idx < 8) a.attn_ctr[idx] = 0;  // the next attention's work counters
   const int d = a.d, half = d / 2;
   const int pq = a.n_q * half, pk = a.n_kv * half, nv = a.n_kv * d;
   const int per_row = pq + pk + nv;

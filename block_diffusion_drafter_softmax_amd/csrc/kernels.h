@@ -85,6 +85,7 @@ struct QkvFinishArgs {
   uint16_t* q;        // split: hi [M][n_q][d], lo at + M*n_q*d
   uint16_t* kblk;     // [B][n_kv][16][d]
   uint16_t* vblk;     // [B][n_kv][d][16]
+  int* attn_ctr;      // nullable: the attention's 8 work counters, set to 0 here
 };
 
 struct CtxFinishArgs {
@@ -125,6 +126,8 @@ struct AttnArgs {
   int n_blocks;            // B, the blocks of the call
   int xcd_order;           // cand == 1: 1-D grid, all workgroups of a (sequence group, kv head) on one XCD
   int xcd_items, xcd_tuples;  // items per (block, kv head); (B / grp) * n_kv (sequence groups x kv heads)
+  int* attn_ctr;           // [8] per-XCD work counters of the persistent ring kernel, zeroed by the Q/K/V
+                           // finisher before every attention launch (null: no persistent kernel)
 };
 
 // ------------------------------------------------------------ small kernels

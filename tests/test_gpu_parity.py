@@ -217,6 +217,22 @@ def test_attention_ring_eight_chunks(head_dim, n_q):
                   extra_pages=2000 - (max(ctx) + 16 + 15) // 16))
 
 
+def test_attention_persistent_ring_list_edges():
+    # d_h 128, GQA 4:1, items of 8 chunks with two key groups: the
+    # persistent ring kernel, whose per-XCD work lists order full items,
+    # then partial last items (most chunks first), then block items.
+    # Contexts after the append: 1024 (one full item, no partial one), 0
+    # (the block item alone), 2049 (two full items and a 1-key partial
+    # item) and 1023 (one partial item of 8 chunks, its last holding 127
+    # keys); 560 pages per sequence give 71 chunk slots per (sequence, kv
+    # head), 2272 chunks in all: 8 chunks per item.
+    cfg = small_cfg(hidden=512, n_q_heads=32, n_kv_heads=8, head_dim=128, intermediate=512, vocab=2048,
+                    block_size=16)
+    ctx, n_new = [1016, 0, 2041, 1023], [8, 0, 8, 0]
+    run_step(Case(cfg, ctx=ctx, n_new=n_new, seed=59, page_order="shuffled", prefill_chunk=512,
+                  extra_pages=560 - (max(ctx) + 16 + 15) // 16))
+
+
 def test_long_context_multi_chunk_head_dim_128():
     # One sequence at 32000 tokens with the Qwen3 attention geometry (d_h
     # 128, GQA 4:1, block 16) at a small width: the chunk grid (8 kv heads x
