@@ -616,10 +616,20 @@ void attn_chunk_kernel(AttnArgs a) {
   // that XCD's L2.
   int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
   if (a.xcd_order) {
-    const int L = blockIdx.x, local = L >> 3, per = a.xcd_items * a.grp;
-    const int T = (local / per) * 8 + (L & 7);  // (sequence group, kv head), head fastest
+    // the context items first, tuple by tuple; the (short) block items of
+    // every tuple last, where they fill the final round of workgroups
+    const int L = blockIdx.x, local = L >> 3, J = (a.xcd_tuples + 7) / 8;
+    const int per = (a.xcd_items - 1) * a.grp;  // context item slots of a tuple
+    int j, rem;
+    if (local < J * per) {
+      j = local / per;
+      rem = local % per + a.grp;  // slot (item 1 + rem / grp - 1, candidate rem % grp)
+    } else {
+      j = (local - J * per) / a.grp;
+      rem = (local - J * per) % a.grp;
+    }
+    const int T = j * 8 + (L & 7);  // (sequence group, kv head), head fastest
     if (T >= a.xcd_tuples) return;
-    const int rem = local % per;
     bx = rem / a.grp;
     by = T % a.n_kv;
     bz = T / a.n_kv * a.grp + rem % a.grp;
