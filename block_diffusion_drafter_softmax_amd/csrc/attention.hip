@@ -83,13 +83,38 @@ DEV int kswz(int row) {
 }
 }  // namespace
 
+// Reductions over the four lane groups g that hold one query's keys (lanes
+// l, l ^ 16, l ^ 32, l ^ 48): the gfx950 row swaps, no lane-index
+// arithmetic; every lane ends with the same value, summed in the same
+// order (groups 0 + 1, then 2 + 3, then the two pairs).
+DEV float group_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+DEV float group_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Growth of a row's max (log2 units) that the running max absorbs without
+// a rescale: numerators exp2(S - max) stay below 2^8.
+constexpr float MAX_SLACK = 8.0f;
+
 // Masking of invalid keys (masked: the block item, or the context's last
 // chunk) and the online-softmax update of one half of S held by a wave: S
 // becomes its numerators exp2(S - max), the running max and sum advance,
-// and (MULTI) the O accumulators are rescaled.
+// and (MULTI) the O accumulators are rescaled. shifted: S arrives as S -
+// max (the MFMAs started from -max; every row of the wave has a finite
+// max), and the max moves only when some row's S exceeds it by more than
+// MAX_SLACK -- the (max, sum, O) triple stays exact for any max it keeps,
+// and most halves then skip the rescale.
 template <int D, int NTH, bool MULTI>
-DEV void softmax_update(f32x4 (&s)[NTH], const int* ccnt, bool masked, int hv, int g, float& mx, float& l,
-                        f32x4 (&acc)[D / 16]) {
+DEV void softmax_update(f32x4 (&s)[NTH], const int* ccnt, bool masked, bool shifted, int hv, int g, float& mx,
+                        float& l, f32x4 (&acc)[D / 16]) {
   constexpr int DT = D / 16;
   if (masked) {
 #pragma unroll
@@ -105,29 +130,42 @@ DEV void softmax_update(f32x4 (&s)[NTH], const int* ccnt, bool masked, int hv, i
   for (int j = 0; j < NTH; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) cm = fmaxf(cm, s[j][i]);
-  cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-  cm = fmaxf(cm, __shfl_xor(cm, 32, 64));  // -inf for a half with no valid key
-  // mx stays -inf while a wave has met no valid key (the second key
-  // group can meet none); mref keeps the exponents defined then
-  const float mn = fmaxf(mx, cm);
-  const float mref = mn == -INFINITY ? 0.f : mn;
-  const float scale = exp2f(mx - mref);  // 0 at the first update
-  mx = mn;
+  cm = group_max(cm);  // -inf for a half with no valid key
+  // a new running max: the first update (mx -inf: sub keeps the exponents
+  // defined while a wave has met no valid key -- the second key group can
+  // meet none), or a row's S beyond the slack (wave-uniform choice)
+  float sub = 0.f, scale = 1.f;
+  const bool move = !shifted || __ballot(cm > MAX_SLACK);
+  if (move) {
+    if (!shifted) {
+      const float mn = fmaxf(mx, cm);
+      sub = mn == -INFINITY ? 0.f : mn;
+      scale = exp2f(mx - sub);  // 0 at the first update
+      mx = mn;
+    } else {
+      sub = fmaxf(cm, 0.f);
+      scale = __builtin_amdgcn_exp2f(-sub);
+      mx += sub;
+    }
+#pragma unroll
+    for (int j = 0; j < NTH; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[j][i] -= sub;
+    l *= scale;
+    if (MULTI) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) acc[t] *= scale;
+    }
+  }
   float cs = 0.f;
 #pragma unroll
   for (int j = 0; j < NTH; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s[j][i] = __builtin_amdgcn_exp2f(s[j][i] - mref);  // <= 1; results under 2^-126 flush to 0
+      s[j][i] = __builtin_amdgcn_exp2f(s[j][i]);  // <= 2^MAX_SLACK; results under 2^-126 flush to 0
       cs += s[j][i];
     }
-  cs += __shfl_xor(cs, 16, 64);
-  cs += __shfl_xor(cs, 32, 64);
-  l = l * scale + cs;
-  if (MULTI) {
-#pragma unroll
-    for (int t = 0; t < DT; ++t) acc[t] *= scale;
-  }
+  l += group_sum(cs);
 }
 
 // P of key tiles j, j + 1 (32 keys: the lane's 8 slots of one page) as a
@@ -163,12 +201,16 @@ DEV void chunk_compute(const uint16_t* kb, const uint16_t* vb, const int* ccnt, 
     const int hv = KS == 2 ? kh : hh;  // the half: a key group's own one with KS = 2
     if (blk_item && hv > 0) break;
     f32x4 s[NTH];
+    // once every row of the wave has a finite running max (multi-chunk
+    // items after their first half), S - max straight from the MFMAs
+    const bool shifted = MULTI && !__ballot(mx == -INFINITY);
     {
+      const float c0 = shifted ? -mx : 0.f;
       f32x4 sa[NACC][NTH];
 #pragma unroll
       for (int h = 0; h < NACC; ++h)
 #pragma unroll
-        for (int j = 0; j < NTH; ++j) sa[h][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NTH; ++j) sa[h][j] = h == 0 ? f32x4{c0, c0, c0, c0} : f32x4{0.f, 0.f, 0.f, 0.f};
       // the ring's d_h-128 kernel (registers to spare): every K fragment of
       // the half requested at once, so LDS latency is paid once, not per kd
       constexpr bool PF = SWZ && D == 128;
@@ -207,7 +249,7 @@ DEV void chunk_compute(const uint16_t* kb, const uint16_t* vb, const int* ccnt, 
         for (int t = 0; t < DT; ++t) vpre[jj][t] = *reinterpret_cast<const bf16x8*>(vp + t * 128);
       }
     }
-    softmax_update<D, NTH, MULTI>(s, ccnt, blk_item || nv < CH, hv, g, mx, l, acc);
+    softmax_update<D, NTH, MULTI>(s, ccnt, blk_item || nv < CH, shifted, hv, g, mx, l, acc);
 
 #pragma unroll
     for (int j = 0; j < NTH; j += 2) {  // k-step: key tiles j and j+1 (32 keys, 2 pages)
