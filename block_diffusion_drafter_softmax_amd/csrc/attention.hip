@@ -972,7 +972,7 @@ extern "C" hipError_t dflash_launch_attn(const AttnArgs* a, int B, int head_dim,
   // multi-chunk items of 2, 4 or 8 chunks with 8 waves: the DMA ring; as a
   // persistent kernel where one block per workgroup lets it take the XCD
   // work lists (at most 64 tuples per XCD), at d_h 128 with two key groups
-  // (the variant whose item loop fits the registers)
+  // (at d_h 64, two workgroups per CU, the item-slot grid was faster)
   const bool dma = waves == 8 && (a->cpi == 2 || a->cpi == 4 || a->cpi == 8);
   if (dma && ks2 && head_dim == 128 && a->xcd_order && a->attn_ctr && (a->xcd_tuples + 7) / 8 <= 64 &&
       launch_persist<128, 1, 2>(a, st))

@@ -127,6 +127,26 @@ def test_d2sd_gpt_oss_geometry_all_cuts():
     check_verify_multi(case, orc, K)
 
 
+def test_d2sd_gpt_oss_geometry_long_contexts_ring():
+    # d_h 64, GQA 8:1, block 16, K = 3: the second pass runs 4 candidate
+    # blocks per sequence. A pool of 2000 pages per sequence makes its
+    # chunk grid (2 sequences x 4 candidates x 2 kv heads x 251 chunks)
+    # about 8 times the attention's 512 work items: items of 8 chunks
+    # through the persistent DMA ring, whose per-XCD list keeps the 4
+    # candidates of an item together (the first pass: items of 2 chunks).
+    # Contexts after the append: 1508 (a full item of 1024 keys and a
+    # partial one of 4 chunks) and 603 (one partial item of 5 chunks).
+    cfg = small_cfg(hidden=512, n_q_heads=16, n_kv_heads=2, head_dim=64, intermediate=512, vocab=4096,
+                    n_target_layers=9, block_size=16)
+    K = 3
+    ctx = [1500, 600]
+    pps_min = (max(ctx) + 16 + 15) // 16
+    case = Case(cfg, ctx=ctx, n_new=[8, 3], seed=69, page_order="shuffled", prefill_chunk=256,
+                extra_pages=2000 - pps_min, max_batch=2 * (K + 1))
+    _, orc = run_d2sd(case, K)
+    check_verify_multi(case, orc, K)
+
+
 def test_d2sd_head_dim_128_shared_context_multi_chunk():
     # d_h 128, GQA 4:1, block 16: 64 query rows (4 computing waves) per kv
     # head, so one 8-wave attention workgroup takes 2 candidates of a

@@ -200,16 +200,16 @@ def test_attention_multi_chunk_items():
                   extra_pages=300 - pps_min))
 
 
-@pytest.mark.parametrize("head_dim,n_q", [(128, 32), (64, 64)])
+@pytest.mark.parametrize("head_dim,n_q", [(128, 32), (64, 64), (128, 64)])
 def test_attention_ring_eight_chunks(head_dim, n_q):
     # A page pool of 2000 pages per sequence makes the chunk grid (2 x 8 x
     # 251 = 4016) about 8 times the attention's 512 work items: items of 8
-    # chunks (1024 keys), so the direct-to-LDS ring runs its 8-chunk form
-    # (d_h 128: two key groups per item; d_h 64, GQA 8:1: one). Contexts
-    # after the append: 2508 (ring items of 1024 and 1024 keys, then 460
-    # keys in 4 chunks staged through registers) and 1000 (one ring item of
-    # 8 chunks whose last holds 104 keys: its invalid V slots are zeroed in
-    # LDS); the last page of each sequence is partly filled.
+    # chunks (1024 keys) through the persistent direct-to-LDS ring (d_h 128,
+    # GQA 4:1: two key groups per item; GQA 8:1 at d_h 64 and 128: one).
+    # Contexts after the append: 2508 (full items of 1024 and 1024 keys,
+    # then a partial item of 460 keys in 4 chunks) and 1000 (one partial
+    # item of 8 chunks whose last holds 104 keys: its invalid V slots are
+    # zeroed in LDS); the last page of each sequence is partly filled.
     cfg = small_cfg(hidden=512, n_q_heads=n_q, n_kv_heads=8, head_dim=head_dim, intermediate=512, vocab=2048,
                     block_size=16)
     ctx, n_new = [2500, 1000], [8, 0]
