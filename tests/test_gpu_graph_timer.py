@@ -1,8 +1,9 @@
 """A decode step captured as a HIP graph and replayed gives, on every replay,
 bit-identical results to the same step launched eagerly (the library puts
-no memset nodes in a capture and keeps no counters across launches: its
-passes are separated by kernel boundaries); and the kernel timer reports
-launch durations for the kinds a step runs."""
+no memset nodes in a capture and its passes are separated by kernel
+boundaries; the one counter set, the persistent attention's per-XCD work
+counters, is zeroed by the kernel before each attention launch); and the
+kernel timer reports launch durations for the kinds a step runs."""
 import numpy as np
 import pytest
 import torch
@@ -20,9 +21,20 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _step_setup(temperature):
-    cfg = synth.config("tiny")
-    case = Case(cfg, ctx=[77, 130, 16], n_new=[8, 5, 0], seed=21, prefill_chunk=64, page_order="shuffled")
+def _step_setup(temperature, geometry="tiny"):
+    if geometry == "tiny":
+        cfg = synth.config("tiny")
+        case = Case(cfg, ctx=[77, 130, 16], n_new=[8, 5, 0], seed=21, prefill_chunk=64, page_order="shuffled")
+    else:
+        # d_h 128, GQA 4:1, 2000 pages per sequence: 8-chunk attention items
+        # through the persistent ring kernel and its work counters
+        cfg = synth.config("tiny")
+        cfg.update(hidden=512, n_q_heads=32, n_kv_heads=8, head_dim=128, intermediate=512, vocab=2048,
+                   block_size=16)
+        cfg["mask_token_id"] = cfg["vocab"] - 1
+        ctx = [2500, 1000]
+        case = Case(cfg, ctx=ctx, n_new=[8, 0], seed=22, prefill_chunk=512, page_order="shuffled",
+                    extra_pages=2000 - (max(ctx) + 16 + 15) // 16)
     case.prefill()
     torch.cuda.synchronize()
     dr, dev = case.dr, case.dev
@@ -61,9 +73,9 @@ def _outputs(case, io):
     return out
 
 
-@pytest.mark.parametrize("temperature", [0.0, 1.0])
-def test_graph_replay_matches_eager(temperature):
-    case, io, step = _step_setup(temperature)
+@pytest.mark.parametrize("temperature,geometry", [(0.0, "tiny"), (1.0, "tiny"), (0.0, "ring")])
+def test_graph_replay_matches_eager(temperature, geometry):
+    case, io, step = _step_setup(temperature, geometry)
     step()
     ref = _outputs(case, io)
     assert case.dr.read_error() == 0
@@ -93,7 +105,7 @@ def test_graph_replay_matches_eager(temperature):
                 a, b = a.view(np.uint32), b.view(np.uint32)
             assert np.array_equal(a, b), (r, k)
     assert case.dr.read_error() == 0
-    say(f"  temperature {temperature}: 4 replays bit-identical, accept {ref['acc'].tolist()}")
+    say(f"  {geometry}, temperature {temperature}: 4 replays bit-identical, accept {ref['acc'].tolist()}")
 
 
 def test_kernel_timer_reports_every_kind_of_a_step():
