@@ -24,40 +24,57 @@ DEV void rotate(float& x1, float& x2, const float* rope, int pos, int half, int 
 }
 }  // namespace
 
-// One thread per (row, rotation pair of a query or block-key head) or per
-// (row, block-value element).
+// One thread per (row, 4 consecutive rotation pairs of a query or block-key
+// head) or per (row, 4 consecutive block-value elements): 16-byte loads of
+// every split partial and of the cos/sin pairs, 8-byte query and key
+// stores (d_h is 64 or 128: a head holds whole groups of 4).
 DEV void qkv_finish_body(const QkvFinishArgs& a, int idx) {
   if (a.attn_ctr && idx < 8) a.attn_ctr[idx] = 0;  // the next attention's work counters
   const int d = a.d, half = d / 2;
-  const int pq = a.n_q * half, pk = a.n_kv * half, nv = a.n_kv * d;
+  const int pq = a.n_q * half / 4, pk = a.n_kv * half / 4, nv = a.n_kv * d / 4;  // groups of 4 per row
   const int per_row = pq + pk + nv;
   const int n_cols = (a.n_q + 2 * a.n_kv) * d;
   if (idx >= a.M * per_row) return;
   const int m = idx / per_row, j = idx % per_row;
   const int b = m / a.N, n = m % a.N;
+  const size_t plane = (size_t)a.M * n_cols, row = (size_t)m * n_cols;
   if (j < pq + pk) {
     const bool isq = j < pq;
-    const int jj = isq ? j : j - pq;
-    const int head = jj / half, i = jj % half;
+    const int jj = (isq ? j : j - pq) * 4;
+    const int head = jj / half, i = jj % half;  // pairs (i .. i+3, i+half .. i+half+3)
     const int col = (isq ? 0 : a.n_q * d) + head * d + i;
-    float x1 = split_sum(a.part, a.ks, a.M, n_cols, m, col);
-    float x2 = split_sum(a.part, a.ks, a.M, n_cols, m, col + half);
-    rotate(x1, x2, a.rope, m, half, i);  // the call's plan holds row m's cos/sin
+    f32x4 x1 = split_sum4(a.part, a.ks, plane, row + col);
+    f32x4 x2 = split_sum4(a.part, a.ks, plane, row + col + half);
+    if (a.rope) {  // the call's plan holds row m's cos/sin
+      const f32x4* cs = reinterpret_cast<const f32x4*>(a.rope + ((size_t)m * half + i) * 2);
+      const f32x4 p0 = cs[0], p1 = cs[1];  // (cos, sin) of pairs i, i+1 and i+2, i+3
+      const f32x4 c = {p0[0], p0[2], p1[0], p1[2]}, sn = {p0[1], p0[3], p1[1], p1[3]};
+      const f32x4 y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
+      x1 = y1;
+      x2 = y2;
+    }
     if (isq) {  // query, scaled for a log2-domain softmax: split activation of the attention
       uint16_t* dst = a.q + ((size_t)m * a.n_q + head) * d;
       const size_t lo = (size_t)a.M * a.n_q * d;
-      split_bf16(x1 * a.q_scale, dst[i], dst[lo + i]);
-      split_bf16(x2 * a.q_scale, dst[i + half], dst[lo + i + half]);
+      u16x4 h1, l1, h2, l2;
+      split4(x1 * a.q_scale, h1, l1);
+      split4(x2 * a.q_scale, h2, l2);
+      *reinterpret_cast<u16x4*>(dst + i) = h1;
+      *reinterpret_cast<u16x4*>(dst + lo + i) = l1;
+      *reinterpret_cast<u16x4*>(dst + i + half) = h2;
+      *reinterpret_cast<u16x4*>(dst + lo + i + half) = l2;
     } else {  // block key: bf16 storage
       uint16_t* dst = a.kblk + (((size_t)b * a.n_kv + head) * 16 + n) * d;
-      dst[i] = f2bf(x1);
-      dst[i + half] = f2bf(x2);
+      *reinterpret_cast<u16x4*>(dst + i) = u16x4{f2bf(x1[0]), f2bf(x1[1]), f2bf(x1[2]), f2bf(x1[3])};
+      *reinterpret_cast<u16x4*>(dst + i + half) = u16x4{f2bf(x2[0]), f2bf(x2[1]), f2bf(x2[2]), f2bf(x2[3])};
     }
-  } else {
-    const int jj = j - pq - pk;
+  } else {  // block value: dim-major, slot n of 16
+    const int jj = (j - pq - pk) * 4;
     const int head = jj / d, dd = jj % d;
-    const float v = split_sum(a.part, a.ks, a.M, n_cols, m, (a.n_q + a.n_kv) * d + jj);
-    a.vblk[(((size_t)b * a.n_kv + head) * d + dd) * 16 + n] = f2bf(v);
+    const f32x4 v = split_sum4(a.part, a.ks, plane, row + (a.n_q + a.n_kv) * d + jj);
+    uint16_t* dst = a.vblk + (((size_t)b * a.n_kv + head) * d + dd) * 16 + n;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dst[t * 16] = f2bf(v[t]);
   }
 }
 
@@ -66,7 +83,7 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void qkv_finish_kernel(QkvFinish
 }
 
 extern "C" hipError_t dflash_launch_qkv_finish(const QkvFinishArgs* a, hipStream_t st) {
-  const int per_row = (a->n_q + a->n_kv) * (a->d / 2) + a->n_kv * a->d;
+  const int per_row = ((a->n_q + a->n_kv) * (a->d / 2) + a->n_kv * a->d) / 4;  // groups of 4
   const int total = a->M * per_row;
   launch_kernel(qkv_finish_kernel, dim3((total + 255) / 256), dim3(256), 0, st, *a);
   return hipGetLastError();
@@ -133,7 +150,7 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void finish2_kernel(CtxFinishArg
 
 extern "C" hipError_t dflash_launch_finish2(const CtxFinishArgs* ca, const QkvFinishArgs* qa, hipStream_t st) {
   const int n_ctx = (ca->M * ca->D * (ca->n_kv * (ca->d / 2) + ca->n_kv * ca->d) + 255) / 256;
-  const int n_qkv = (qa->M * ((qa->n_q + qa->n_kv) * (qa->d / 2) + qa->n_kv * qa->d) + 255) / 256;
+  const int n_qkv = (qa->M * (((qa->n_q + qa->n_kv) * (qa->d / 2) + qa->n_kv * qa->d) / 4) + 255) / 256;
   launch_kernel(finish2_kernel, dim3(n_ctx + n_qkv), dim3(256), 0, st, *ca, *qa, n_ctx);
   return hipGetLastError();
 }
