@@ -299,13 +299,27 @@ DEV void norm_body(const NormArgs& a, int m, const FuseArgs& app, bool with_app)
   }
 }
 
+// From 128 rows on, the 16 rows of one tile of the packed output are
+// normed on one XCD (the hardware deals workgroups to the 8 XCDs round
+// robin): a row's 16-byte pieces share cache lines with the other rows of
+// its tile, and those partial-line writes then merge in one L2.
+// (A separate instantiation: the plain one-row-per-workgroup kernel of small
+// batches stays as it was; the extra branch cost it time.)
+template <bool XCD_TILES>
 __global__ __launch_bounds__(1024) LATENCY_BOUND void norm_kernel(NormArgs a) {
-  norm_body(a, blockIdx.x, FuseArgs{}, false);
+  int m = blockIdx.x;
+  if constexpr (XCD_TILES) {
+    const int local = blockIdx.x >> 3;
+    m = ((local >> 4) * 8 + (int)(blockIdx.x & 7)) * 16 + (local & 15);
+    if (m >= a.M) return;
+  }
+  norm_body(a, m, FuseArgs{}, false);
 }
 
 extern "C" hipError_t dflash_launch_norm(const NormArgs* a, hipStream_t st) {
   const int threads = std::min(1024, ((a->H / 4 + 63) / 64) * 64);
-  launch_kernel(norm_kernel, dim3(a->M), dim3(threads), 0, st, *a);
+  if (a->M >= 128) launch_kernel(norm_kernel<true>, dim3((a->M + 127) / 128 * 128), dim3(threads), 0, st, *a);
+  else launch_kernel(norm_kernel<false>, dim3(a->M), dim3(threads), 0, st, *a);
   return hipGetLastError();
 }
 
