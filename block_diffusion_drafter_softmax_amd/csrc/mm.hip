@@ -251,11 +251,16 @@ __global__ __launch_bounds__(256, XT == 4 ? 3 : 2) void mm_kernel(WsArgs a, int 
 // SwiGLU after a k-split gate/up product: y = silu(sum of gate splits) *
 // (sum of up splits), the splits added in order, written as the packed
 // split activation of the down projection. One thread per 4 features.
+// One workgroup per 16 rows x 64 columns (thread: row tid / 16, columns
+// 4 (tid % 16) .. +3; the last block may hold 32): its output is whole 1 KB
+// blocks of each plane of the packed activation (16 rows x 32 columns
+// each), so no cache line is shared with another workgroup's writes; each
+// row's partials are read as 256 contiguous bytes per split.
 __global__ __launch_bounds__(256) void swiglu_finish_kernel(WsArgs a) {
-  const int q = a.n_cols / 4;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.M * q) return;
-  const int m = idx / q, f = (idx % q) * 4;
+  const int cb = (a.n_cols + 63) / 64;  // column blocks (n_cols: a multiple of 32)
+  const int m = (blockIdx.x / cb) * 16 + (int)(threadIdx.x >> 4);
+  const int f = (blockIdx.x % cb) * 64 + (int)(threadIdx.x & 15) * 4;
+  if (m >= a.M || f >= a.n_cols) return;
   const size_t off = (size_t)m * 2 * a.n_cols + f;
   const size_t stride = (size_t)a.M * 2 * a.n_cols;
   const f32x4 gt = split_sum4(a.part, a.ks, stride, off);
@@ -572,8 +577,7 @@ extern "C" hipError_t dflash_launch_mm(const WsArgs* a, int mode, hipStream_t st
 }
 
 extern "C" hipError_t dflash_launch_swiglu_finish(const WsArgs* a, hipStream_t st) {
-  const int n = a->M * (a->n_cols / 4);
-  launch_kernel(swiglu_finish_kernel, dim3((n + 255) / 256), dim3(256), 0, st, *a);
+  launch_kernel(swiglu_finish_kernel, dim3((a->M + 15) / 16 * ((a->n_cols + 63) / 64)), dim3(256), 0, st, *a);
   return hipGetLastError();
 }
 
