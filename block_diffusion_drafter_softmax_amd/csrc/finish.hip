@@ -9,16 +9,15 @@
 namespace {
 DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-DEV float split_sum(const float* part, int ks, int M, int n_cols, int m, int col) {
-  return split_sum1(part, ks, (size_t)M * n_cols, (size_t)m * n_cols + col);
-}
-
-DEV void rotate(float& x1, float& x2, const float* rope, int pos, int half, int j) {
+// RoPE of 4 consecutive rotate-half pairs (i .. i+3, i+half .. i+half+3; i a
+// multiple of 4) at position pos: the 8 cos/sin values are two 16-byte loads
+// of the table [pos][half][cos, sin].
+DEV void rotate4(f32x4& x1, f32x4& x2, const float* rope, int pos, int half, int i) {
   if (rope == nullptr) return;
-  const float c = rope[((size_t)pos * half + j) * 2 + 0];
-  const float s = rope[((size_t)pos * half + j) * 2 + 1];
-  const float y1 = x1 * c - x2 * s;
-  const float y2 = x2 * c + x1 * s;
+  const f32x4* cs = reinterpret_cast<const f32x4*>(rope + ((size_t)pos * half + i) * 2);
+  const f32x4 p0 = cs[0], p1 = cs[1];  // (cos, sin) of pairs i, i+1 and i+2, i+3
+  const f32x4 c = {p0[0], p0[2], p1[0], p1[2]}, sn = {p0[1], p0[3], p1[1], p1[3]};
+  const f32x4 y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
   x1 = y1;
   x2 = y2;
 }
@@ -45,14 +44,7 @@ DEV void qkv_finish_body(const QkvFinishArgs& a, int idx) {
     const int col = (isq ? 0 : a.n_q * d) + head * d + i;
     f32x4 x1 = split_sum4(a.part, a.ks, plane, row + col);
     f32x4 x2 = split_sum4(a.part, a.ks, plane, row + col + half);
-    if (a.rope) {  // the call's plan holds row m's cos/sin
-      const f32x4* cs = reinterpret_cast<const f32x4*>(a.rope + ((size_t)m * half + i) * 2);
-      const f32x4 p0 = cs[0], p1 = cs[1];  // (cos, sin) of pairs i, i+1 and i+2, i+3
-      const f32x4 c = {p0[0], p0[2], p1[0], p1[2]}, sn = {p0[1], p0[3], p1[1], p1[3]};
-      const f32x4 y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
-      x1 = y1;
-      x2 = y2;
-    }
+    rotate4(x1, x2, a.rope, m, half, i);  // the call's plan holds row m's cos/sin
     if (isq) {  // query, scaled for a log2-domain softmax: split activation of the attention
       uint16_t* dst = a.q + ((size_t)m * a.n_q + head) * d;
       const size_t lo = (size_t)a.M * a.n_q * d;
@@ -89,13 +81,14 @@ extern "C" hipError_t dflash_launch_qkv_finish(const QkvFinishArgs* a, hipStream
   return hipGetLastError();
 }
 
-// One thread per (appended row, layer, key rotation pair or value element);
-// the first B threads also advance the context length of the call's
-// sequences (the append's last kernel: nothing after it reads the old one).
+// One thread per (appended row, layer, 4 consecutive key rotation pairs or
+// value elements of a head); the first B threads also advance the context
+// length of the call's sequences (the append's last kernel: nothing after it
+// reads the old one).
 DEV void ctx_finish_body(const CtxFinishArgs& a, int idx) {
   const int d = a.d, half = d / 2, kvd = a.n_kv * d;
-  const int pk = a.n_kv * half;
-  const int per_layer = pk + kvd;
+  const int pk = a.n_kv * half / 4, pv = kvd / 4;  // groups of 4
+  const int per_layer = pk + pv;
   const int per_row = a.D * per_layer;
   const int n_cols = a.D * 2 * kvd;
   if (idx < a.B) {
@@ -111,20 +104,22 @@ DEV void ctx_finish_body(const CtxFinishArgs& a, int idx) {
   const int page = clampi(a.page_table[(size_t)seq * a.max_pages_per_seq + pos / 16], 0, a.n_pages - 1);
   const int slot = pos % 16;
   uint16_t* base = a.kv_pages + layer * a.layer_stride + (size_t)page * 2 * kvd * 16;
-  if (j < pk) {
-    const int head = j / half, i = j % half;
+  const size_t plane = (size_t)a.M * n_cols, row = (size_t)m * n_cols;
+  if (j < pk) {  // key: rotated, slot-major
+    const int jj = j * 4, head = jj / half, i = jj % half;
     const int col = layer * 2 * kvd + head * d + i;
-    float x1 = split_sum(a.part, a.ks, a.M, n_cols, m, col);
-    float x2 = split_sum(a.part, a.ks, a.M, n_cols, m, col + half);
-    rotate(x1, x2, a.rope, pos, half, i);
+    f32x4 x1 = split_sum4(a.part, a.ks, plane, row + col);
+    f32x4 x2 = split_sum4(a.part, a.ks, plane, row + col + half);
+    rotate4(x1, x2, a.rope, pos, half, i);
     uint16_t* dst = base + ((size_t)head * 16 + slot) * d;
-    dst[i] = f2bf(x1);
-    dst[i + half] = f2bf(x2);
-  } else {
-    const int jj = j - pk;
-    const int head = jj / d, dd = jj % d;
-    const float v = split_sum(a.part, a.ks, a.M, n_cols, m, layer * 2 * kvd + kvd + jj);
-    base[(size_t)kvd * 16 + ((size_t)head * d + dd) * 16 + slot] = f2bf(v);
+    *reinterpret_cast<u16x4*>(dst + i) = u16x4{f2bf(x1[0]), f2bf(x1[1]), f2bf(x1[2]), f2bf(x1[3])};
+    *reinterpret_cast<u16x4*>(dst + i + half) = u16x4{f2bf(x2[0]), f2bf(x2[1]), f2bf(x2[2]), f2bf(x2[3])};
+  } else {  // value: dim-major
+    const int jj = (j - pk) * 4, head = jj / d, dd = jj % d;
+    const f32x4 v = split_sum4(a.part, a.ks, plane, row + layer * 2 * kvd + kvd + jj);
+    uint16_t* dst = base + (size_t)kvd * 16 + ((size_t)head * d + dd) * 16 + slot;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dst[t * 16] = f2bf(v[t]);
   }
 }
 
@@ -133,7 +128,7 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void ctx_finish_kernel(CtxFinish
 }
 
 extern "C" hipError_t dflash_launch_ctx_finish(const CtxFinishArgs* a, hipStream_t st) {
-  const int per_row = a->D * (a->n_kv * (a->d / 2) + a->n_kv * a->d);
+  const int per_row = a->D * ((a->n_kv * (a->d / 2) + a->n_kv * a->d) / 4);  // groups of 4
   const int total = a->M * per_row;
   launch_kernel(ctx_finish_kernel, dim3((total + 255) / 256), dim3(256), 0, st, *a);
   return hipGetLastError();
@@ -149,7 +144,7 @@ __global__ __launch_bounds__(256) LATENCY_BOUND void finish2_kernel(CtxFinishArg
 }
 
 extern "C" hipError_t dflash_launch_finish2(const CtxFinishArgs* ca, const QkvFinishArgs* qa, hipStream_t st) {
-  const int n_ctx = (ca->M * ca->D * (ca->n_kv * (ca->d / 2) + ca->n_kv * ca->d) + 255) / 256;
+  const int n_ctx = (ca->M * ca->D * ((ca->n_kv * (ca->d / 2) + ca->n_kv * ca->d) / 4) + 255) / 256;
   const int n_qkv = (qa->M * (((qa->n_q + qa->n_kv) * (qa->d / 2) + qa->n_kv * qa->d) / 4) + 255) / 256;
   launch_kernel(finish2_kernel, dim3(n_ctx + n_qkv), dim3(256), 0, st, *ca, *qa, n_ctx);
   return hipGetLastError();
