@@ -327,11 +327,22 @@ extern "C" hipError_t dflash_launch_norm(const NormArgs* a, hipStream_t st) {
 // fuse_kernel, row-major over (row, layer group)) and the draft's first norm
 // (embedding; the context length the append leaves) in one launch. Both
 // use the same workgroup size (one float4 of a hidden row per thread).
-template <int MAXV, int DG>
+// XCD_TILES (appended rows and block rows multiples of 128): the 16 rows
+// of one tile of either packed output on one XCD, as in norm_kernel.
+DEV int xcd_tile_row(int i) {
+  const int local = i >> 3;
+  return ((local >> 4) * 8 + (i & 7)) * 16 + (local & 15);
+}
+
+template <int MAXV, int DG, bool XCD_TILES>
 __global__ __launch_bounds__(1024) LATENCY_BOUND void fuse_norm_kernel(FuseArgs fa, NormArgs na, int n_fuse) {
   const int x = blockIdx.x;
-  if (x < n_fuse) fuse_body<MAXV, DG>(fa, x % fa.rows, (x / fa.rows) * DG);
-  else norm_body(na, x - n_fuse, fa, true);
+  if (x < n_fuse) {
+    const int r = x % fa.rows;
+    fuse_body<MAXV, DG>(fa, XCD_TILES ? xcd_tile_row(r) : r, (x / fa.rows) * DG);
+  } else {
+    norm_body(na, XCD_TILES ? xcd_tile_row(x - n_fuse) : x - n_fuse, fa, true);
+  }
 }
 
 extern "C" hipError_t dflash_launch_fuse_norm(const FuseArgs* fa, const NormArgs* na, hipStream_t st) {
@@ -340,13 +351,16 @@ extern "C" hipError_t dflash_launch_fuse_norm(const FuseArgs* fa, const NormArgs
   if (fa->raw || na->mode != 0 || na->H != fa->H) return hipErrorInvalidValue;
   if (fa->H > 4 * threads) {
     const int n_fuse = fa->rows * fa->D;
-    launch_kernel((fuse_norm_kernel<2, 1>), dim3(n_fuse + na->M), dim3(threads), 0, st, *fa, *na, n_fuse);
+    launch_kernel((fuse_norm_kernel<2, 1, false>), dim3(n_fuse + na->M), dim3(threads), 0, st, *fa, *na, n_fuse);
   } else if (fa->rows < 128) {
     const int n_fuse = fa->rows * fa->D;
-    launch_kernel((fuse_norm_kernel<1, 1>), dim3(n_fuse + na->M), dim3(threads), 0, st, *fa, *na, n_fuse);
+    launch_kernel((fuse_norm_kernel<1, 1, false>), dim3(n_fuse + na->M), dim3(threads), 0, st, *fa, *na, n_fuse);
   } else {
     const int n_fuse = fa->rows * ((fa->D + DG - 1) / DG);
-    launch_kernel((fuse_norm_kernel<1, DG>), dim3(n_fuse + na->M), dim3(threads), 0, st, *fa, *na, n_fuse);
+    if (fa->rows % 128 == 0 && na->M % 128 == 0)  // n_fuse a multiple of 8: both parts keep the XCD of their index
+      launch_kernel((fuse_norm_kernel<1, DG, true>), dim3(n_fuse + na->M), dim3(threads), 0, st, *fa, *na, n_fuse);
+    else
+      launch_kernel((fuse_norm_kernel<1, DG, false>), dim3(n_fuse + na->M), dim3(threads), 0, st, *fa, *na, n_fuse);
   }
   return hipGetLastError();
 }

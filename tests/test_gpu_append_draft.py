@@ -2,8 +2,9 @@
 dflash_draft_block gives: the drafts, their top-2 gaps, the context lengths,
 every context K/V page and the error word. Cases: a ragged batch (one
 sequence appending nothing) on shuffled pages, a batch large enough for the
-tiled GEMMs (128 block rows), an append whose page check fails (the draft
-then sees the old context) and an append with n_new above max_new."""
+tiled GEMMs (128 block rows), one whose appended and block rows fill whole
+XCD tiles, an append whose page check fails (the draft then sees the old
+context) and an append with n_new above max_new."""
 import numpy as np
 import pytest
 import torch
@@ -84,6 +85,21 @@ def test_append_draft_tiled_gemm_batch():
                 page_order="shuffled")
     case.prefill()
     a, b = _both(case, case.n_new, 8)
+    _same(a, b)
+    assert a["err"] == 0
+
+
+def test_append_draft_rows_in_whole_xcd_tiles():
+    # 8 sequences x 16 appended-row slots and 8 blocks of 16 rows: both
+    # multiples of 128, so the fused launch places the 16 rows of each
+    # output tile on one XCD (fusion and first norm); ragged appends of
+    # 0 .. 16 rows
+    cfg = small_cfg(block_size=16)
+    ctx = [40 + 37 * b for b in range(8)]
+    case = Case(cfg, ctx=ctx, n_new=[(5 * b) % 17 for b in range(8)], seed=34, prefill_chunk=64,
+                page_order="shuffled")
+    case.prefill()
+    a, b = _both(case, case.n_new, 16)
     _same(a, b)
     assert a["err"] == 0
 
