@@ -127,6 +127,18 @@ def test_diverse_gqa_8_to_1_multi_chunk():
                   extra_pages=300 - pps_min), positions=3)
 
 
+def test_diverse_persistent_ring():
+    # d_h 128, GQA 4:1, block 16 with 8-chunk attention items through the
+    # persistent ring (560 pages per sequence); contexts after the append
+    # 1024 (a full item), 2049 (two full items and a 1-key partial one) and
+    # 1023 (one partial item of 8 chunks)
+    cfg = small_cfg(hidden=512, n_q_heads=32, n_kv_heads=8, head_dim=128, intermediate=512, vocab=4096,
+                    block_size=16, **SHARP)
+    ctx, n_new = [1016, 2041, 1023], [8, 8, 0]
+    run_step(Case(cfg, ctx=ctx, n_new=n_new, seed=81, page_order="shuffled", prefill_chunk=512,
+                  extra_pages=560 - (max(ctx) + 16 + 15) // 16), positions=3)
+
+
 def test_diverse_fc_fusion_tied():
     cfg = small_cfg(fusion="fc", tied_kv=1, n_target_layers=5, block_size=16, n_q_heads=8, n_kv_heads=2,
                     **SHARP)
