@@ -98,19 +98,25 @@ def write_stats(stats_csv, out_md, command, trace_csv=None, skip_last=0, last_ke
 
 def step_breakdown(trace_csv, last_kernel="verify_rows", steps=10, skip_last=0):
     """Per-kernel time of one decode step, averaged over `steps` steps of a
-    kernel trace (a step ends with the verification kernel), leaving out the
-    final `skip_last` steps (e.g. a pass run with a kernel timer attached).
+    kernel trace (a step ends with the verification kernel `last_kernel` and
+    holds an LM head launch), leaving out the final `skip_last` steps (e.g. a
+    pass run with a kernel timer attached).
     Kernels between the dual-pass drafter's selection and assembly kernels
     are listed as its second pass."""
     rows = _rows(trace_csv)
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    ends = [i for i, r in enumerate(rows) if r["Kernel_Name"].replace("void ", "", 1).startswith(last_kernel)]
+    name = [r["Kernel_Name"].replace("void ", "", 1) for r in rows]
+    ends = [i for i, k in enumerate(name) if k.startswith(last_kernel)]
+    # a step holds an LM head launch: verification passes run after the
+    # timed steps (acceptance draws) end with the same kernel but are no step
+    segs = [(a + 1, b + 1) for a, b in zip(ends[:-1], ends[1:])
+            if any(k.startswith(("lmhead", "mm_lmhead")) for k in name[a + 1:b + 1])]
     if skip_last:
-        ends = ends[:-skip_last]
-    steps = min(steps, len(ends) - 1)
+        segs = segs[:-skip_last]
+    steps = min(steps, len(segs))
     agg, span, busy = {}, 0.0, 0.0
-    for a, b in zip(ends[-steps - 1:-1], ends[-steps:]):
-        seg = rows[a + 1: b + 1]
+    for a, b in segs[-steps:]:
+        seg = rows[a:b]
         span += (int(seg[-1]["End_Timestamp"]) - int(seg[0]["Start_Timestamp"])) / 1e3
         second = False
         for r in seg:
